@@ -1,0 +1,225 @@
+"""CPU oracle for batched speculative-sampling verification -- TEST INFRASTRUCTURE ONLY.
+
+This package wraps ``spec_oracle.c`` (plain single-threaded C in IEEE double)
+with ctypes. Only the test suite, the package smoke check and the benchmark's
+CPU-baseline leg may import it; the HIP library and its Python binding never do.
+
+What the oracle computes, and the readings it takes where the pages are silent,
+is stated at the top of ``spec_oracle.c``. Parity status of each function:
+
+* ``philox4x32_10`` / ``philox_words`` / ``uniform24`` -- pinned against the
+  header-only Philox4x32-10 engine that ships with PyTorch's C++ headers
+  (an independent library implementation of the SC'11 definition).
+* ``row_lse`` -- pinned against ``scipy.special.logsumexp`` and closed forms.
+* ``row_argmax`` -- pinned against ``numpy.argmax`` (first index on ties).
+* ``inverse_cdf`` -- pinned by exhaustive sweeps of the uniform grid.
+* ``verify`` / ``verify_sequence`` -- pinned by the closed-form acceptance
+  probability sum_v min(p_v, q_v), the output-marginal gate (chi-square and KS
+  at 0.01 over 10,000 draws) and the degenerate cases (gamma = 0, p = q,
+  disjoint support, greedy).
+* ``accept_logprobs`` -- pinned by agreement with ``verify`` on the gathered
+  pairs and by the closed-form acceptance probability min(1, p/q).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spec_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+
+
+def build() -> str:
+    """Compile the oracle with gcc: -O2, no fast-math, no FP contraction."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, u64, f32, f64 = ctypes.c_int, ctypes.c_uint64, ctypes.c_float, ctypes.c_double
+    lib.oracle_philox4x32_10.argtypes = [P, P, P]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_philox_words.argtypes = [u64, u64, ctypes.c_int64, i32, P]
+    lib.oracle_philox_words.restype = None
+    lib.oracle_uniform24.argtypes = [ctypes.c_uint32]
+    lib.oracle_uniform24.restype = f64
+    lib.oracle_row_lse.argtypes = [P, i32, ctypes.c_size_t, i32, f32]
+    lib.oracle_row_lse.restype = f64
+    lib.oracle_row_argmax.argtypes = [P, i32, ctypes.c_size_t, i32]
+    lib.oracle_row_argmax.restype = i32
+    lib.oracle_inverse_cdf.argtypes = [P, i32, f64, P]
+    lib.oracle_inverse_cdf.restype = i32
+    lib.oracle_verify_sequence.argtypes = [i32, i32, i32, P, ctypes.c_size_t, P,
+                                           ctypes.c_size_t, P, f32, P, P, P, P, P, P, P]
+    lib.oracle_verify_sequence.restype = None
+    lib.oracle_verify.argtypes = [i32, i32, i32, i32, P, P, P, P, u64, u64, P,
+                                  P, P, P, P, P]
+    lib.oracle_verify.restype = None
+    lib.oracle_accept_logprobs.argtypes = [i32, i32, P, u64, u64, P, P, P]
+    lib.oracle_accept_logprobs.restype = None
+    lib.oracle_gather_logprobs.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
+    lib.oracle_gather_logprobs.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _logits(a: np.ndarray) -> tuple[np.ndarray, int]:
+    """Accept float32 logits, or bf16 logits given as their uint16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    raise TypeError(f"logits must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    _load().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def philox_words(seed: int, offset: int, b: int, i: int) -> np.ndarray:
+    out = np.zeros(4, dtype=np.uint32)
+    _load().oracle_philox_words(seed, offset, b, i, _ptr(out))
+    return out
+
+
+def uniform24(word: int) -> float:
+    return _load().oracle_uniform24(word)
+
+
+def row_lse(z: np.ndarray, temperature: float) -> float:
+    """LSE of fl32(z * fl32(1/T)) over one row, T > 0."""
+    z, dt = _logits(z.reshape(-1))
+    inv_t = np.float32(1.0) / np.float32(temperature)
+    return _load().oracle_row_lse(_ptr(z), dt, 0, z.size, float(inv_t))
+
+
+def row_argmax(z: np.ndarray) -> int:
+    z, dt = _logits(z.reshape(-1))
+    return _load().oracle_row_argmax(_ptr(z), dt, 0, z.size)
+
+
+def inverse_cdf(r: np.ndarray, u: float) -> tuple[int, float]:
+    r = np.ascontiguousarray(r, dtype=np.float64)
+    m = ctypes.c_double(0.0)
+    j = _load().oracle_inverse_cdf(_ptr(r), r.size, float(u), ctypes.byref(m))
+    return j, m.value
+
+
+def verify_sequence(logits_draft, logits_target, draft_tokens, temperature, u_acc, u_res):
+    """One sequence with explicit uniforms. logits_draft [G, V], logits_target [G+1, V]."""
+    zp, dt = _logits(logits_target)
+    G = zp.shape[0] - 1
+    V = zp.shape[1]
+    if G > 0:
+        zq, dq = _logits(logits_draft)
+        assert dq == dt and zq.shape == (G, V)
+    else:
+        zq = np.zeros((1, V), dtype=zp.dtype)
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(max(G, 1))
+    ua = np.ascontiguousarray(u_acc, dtype=np.float64).reshape(-1)
+    ur = np.ascontiguousarray(u_res, dtype=np.float64).reshape(-1)
+    assert ua.size >= G and ur.size >= G + 1
+    alen = ctypes.c_int32(0)
+    tokens = np.zeros(G + 1, dtype=np.int32)
+    lse = np.zeros(2 * G + 1, dtype=np.float64)
+    am = np.zeros(max(G, 1), dtype=np.float64)
+    rm = ctypes.c_double(0.0)
+    _load().oracle_verify_sequence(G, V, dt, _ptr(zq), 0, _ptr(zp), 0, _ptr(tok),
+                                   float(np.float32(temperature)), _ptr(ua), _ptr(ur),
+                                   ctypes.byref(alen), _ptr(tokens), _ptr(lse), _ptr(am),
+                                   ctypes.byref(rm))
+    return dict(accept_len=alen.value, tokens=tokens, lse=lse, acc_margin=am[:G],
+                res_margin=rm.value)
+
+
+def verify(logits_draft, logits_target, draft_tokens, temperature, seed=0, offset=0,
+           seq_ids=None):
+    """The batched call. logits_draft [B, G, V], logits_target [B, G+1, V] (float32 or
+    bf16 bits as uint16), draft_tokens [B, G] int32, temperature [B] float32.
+    ``seq_ids`` gives the global sequence index of each row (for sampled checks)."""
+    zp, dt = _logits(logits_target)
+    B, G1, V = zp.shape
+    G = G1 - 1
+    if G > 0:
+        zq, dq = _logits(logits_draft)
+        assert dq == dt and zq.shape == (B, G, V)
+        tok = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+        assert tok.shape == (B, G)
+    else:
+        zq = np.zeros((1,), dtype=zp.dtype)
+        tok = np.zeros((1,), dtype=np.int32)
+    temp = np.ascontiguousarray(temperature, dtype=np.float32).reshape(B)
+    ids = None if seq_ids is None else np.ascontiguousarray(seq_ids, dtype=np.int64)
+    if ids is not None:
+        assert ids.shape == (B,)
+    alen = np.zeros(B, dtype=np.int32)
+    tokens = np.zeros((B, G + 1), dtype=np.int32)
+    lse = np.zeros((B, 2 * G + 1), dtype=np.float64)
+    am = np.zeros((B, max(G, 1)), dtype=np.float64)
+    rm = np.zeros(B, dtype=np.float64)
+    _load().oracle_verify(B, G, V, dt, _ptr(zq), _ptr(zp), _ptr(tok), _ptr(temp),
+                          seed, offset, _ptr(ids), _ptr(alen), _ptr(tokens), _ptr(lse),
+                          _ptr(am), _ptr(rm))
+    return dict(accept_len=alen, tokens=tokens, lse=lse, acc_margin=am[:, :G],
+                res_margin=rm)
+
+
+def accept_logprobs(logprobs, seed=0, offset=0, seq_ids=None):
+    """Scalar-only mode: logprobs [B, G, 2] float32 ([...,0] = log q, [...,1] = log p)."""
+    lp = np.ascontiguousarray(logprobs, dtype=np.float32)
+    B, G, two = lp.shape
+    assert two == 2
+    ids = None if seq_ids is None else np.ascontiguousarray(seq_ids, dtype=np.int64)
+    alen = np.zeros(B, dtype=np.int32)
+    am = np.zeros((B, max(G, 1)), dtype=np.float64)
+    _load().oracle_accept_logprobs(B, G, _ptr(lp), seed, offset, _ptr(ids), _ptr(alen),
+                                   _ptr(am))
+    return dict(accept_len=alen, acc_margin=am[:, :G])
+
+
+def gather_logprobs(logits_draft, logits_target, draft_tokens, temperature):
+    """[B, G, 2] float64 pairs (log q, log p) of the draft tokens; NaN where undefined."""
+    zp, dt = _logits(logits_target)
+    B, G1, V = zp.shape
+    G = G1 - 1
+    zq, dq = _logits(logits_draft)
+    assert dq == dt and zq.shape == (B, G, V)
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    temp = np.ascontiguousarray(temperature, dtype=np.float32).reshape(B)
+    out = np.zeros((B, G, 2), dtype=np.float64)
+    _load().oracle_gather_logprobs(B, G, V, dt, _ptr(zq), _ptr(zp), _ptr(tok), _ptr(temp),
+                                   _ptr(out))
+    return out

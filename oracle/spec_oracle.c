@@ -1,0 +1,472 @@
+/*
+ * spec_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded CPU reference for batched speculative-sampling
+ * verification, written for readability, not speed. Only the test suite, the
+ * package smoke check and the benchmark's CPU-baseline leg may load it. The
+ * HIP library never links, calls or includes anything from this directory, and
+ * this file includes nothing from the HIP library.
+ *
+ * Every floating-point step after the two fp32 roundings named in step 3 below
+ * is done in IEEE double, with the obvious loop order. No blocking, no fusion.
+ *
+ * What is computed, per sequence b (sources are the pages' titles and sections):
+ *   1. Temperature is applied to the logits BEFORE the log-softmax, and the test
+ *      works in log space on two log-probability scalars per draft token, one
+ *      from the draft model and one from the target
+ *      (FlashSpec technical summary, Methodology section 1, "on-device
+ *      verification kernel": mechanism and numerical-stability bullets; the
+ *      "engineering rigour" bullet of its Significance section repeats the
+ *      temperature-order lesson).
+ *   2. The verification outcome is the number of accepted draft tokens plus
+ *      one extra token: drawn from the residual distribution at the first
+ *      rejected position, or the "bonus" token when all are accepted
+ *      (Speculative Speculative Decoding summary, section 2: central concept
+ *      item 1 names the outcome (#accepted, bonus token); Saguaro challenge 2
+ *      names the residual distribution the bonus token is sampled from).
+ *   3. The result must have exactly the target model's output distribution
+ *      (FlashSpec summary, Methodology intro and Theorem 1 in Significance).
+ *      The pages give no formulas for 1-3; the accept rule u < min(1, p/q) and
+ *      the residual norm(max(0, p - q)) used here are the standard speculative
+ *      sampling rule (Leviathan, Kalman and Matias, ICML 2023; Chen et al.
+ *      2023), the rule that has the exactness property the pages claim.
+ *
+ * Readings taken where the pages are silent (each is stated again where used):
+ *   R1 target position i scores draft token i; target position gamma is the bonus;
+ *   R3 x = fl32(z * fl32(1/T)), one temperature per sequence for draft and target;
+ *   R4 T == 0 is greedy: accept iff token == argmax of raw target logits (lowest
+ *      index on ties); the extra token is that argmax; no uniforms are used;
+ *   R5 uniforms are 24-bit in [0, 1), the accept test is a strict '<';
+ *   R6 Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with key
+ *      (lo32(seed), hi32(seed)) and counter (i, b, lo32(offset), hi32(offset));
+ *      word 0 gives the accept uniform of position i, word 1 the resample
+ *      uniform used at the first rejected position (or at gamma for the bonus);
+ *   R7 the residual CDF runs in vocabulary-index order; the token is the first
+ *      index whose inclusive prefix sum exceeds u * S;
+ *   R8 a residual with S <= 0 (impossible in exact arithmetic after a
+ *      rejection) falls back to p at that position;
+ *   R12 gamma == 0 means no draft rows; accept length 0 and a bonus draw;
+ *   R13 -inf logits are allowed; +inf / NaN logits are a precondition violation;
+ *   sentinel: a sequence whose temperature is NaN, negative, +inf or whose
+ *      reciprocal overflows, or whose draft token lies outside [0, V), or one
+ *      of whose rows has no finite logit, gets accept_len = -1 and tokens -1.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* binary32 expressions must be evaluated in binary32 for step 3 to hold */
+#if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
+#error "the oracle needs FLT_EVAL_METHOD == 0"
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* ---------------------------------------------------------------- inputs -- */
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static float bf16_bits_to_float(uint16_t h)
+{
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Raw logit z at flat element index idx of a row-major array. */
+static float raw_logit(const void *base, int dtype, size_t idx)
+{
+    if (dtype == ORACLE_BF16)
+        return bf16_bits_to_float(((const uint16_t *)base)[idx]);
+    return ((const float *)base)[idx];
+}
+
+/* ---------------------------------------------------- Philox4x32-10 -------- */
+
+/*
+ * Philox4x32 with 10 rounds, from its published definition (Salmon et al.,
+ * SC'11, section on the Philox S-box): each round multiplies counter words 0
+ * and 2 by two fixed 32-bit constants into 64-bit products, and the new
+ * counter is (hi(c2*M1) ^ c1 ^ k0, lo(c2*M1), hi(c0*M0) ^ c3 ^ k1, lo(c0*M0)).
+ * Between rounds the key is bumped by the two Weyl constants.
+ */
+void oracle_philox4x32_10(const uint32_t counter[4], const uint32_t key[2],
+                          uint32_t out[4])
+{
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = counter[0], c1 = counter[1], c2 = counter[2], c3 = counter[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        uint64_t prod0 = (uint64_t)M0 * (uint64_t)c0;
+        uint64_t prod1 = (uint64_t)M1 * (uint64_t)c2;
+        uint32_t hi0 = (uint32_t)(prod0 >> 32), lo0 = (uint32_t)prod0;
+        uint32_t hi1 = (uint32_t)(prod1 >> 32), lo1 = (uint32_t)prod1;
+        uint32_t n0 = hi1 ^ c1 ^ k0;
+        uint32_t n1 = lo1;
+        uint32_t n2 = hi0 ^ c3 ^ k1;
+        uint32_t n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The four Philox words of block (b, i) for a given seed and offset (R6). */
+void oracle_philox_words(uint64_t seed, uint64_t offset, int64_t b, int i,
+                         uint32_t out[4])
+{
+    uint32_t key[2] = { (uint32_t)seed, (uint32_t)(seed >> 32) };
+    uint32_t ctr[4] = { (uint32_t)i, (uint32_t)b,
+                        (uint32_t)offset, (uint32_t)(offset >> 32) };
+    oracle_philox4x32_10(ctr, key, out);
+}
+
+/* 24-bit uniform in [0, 1) from one 32-bit word (R5): top 24 bits times 2^-24. */
+double oracle_uniform24(uint32_t word)
+{
+    return (double)(word >> 8) * (1.0 / 16777216.0);
+}
+
+/* ------------------------------------------------------- row reductions -- */
+
+/* The temperature-scaled logit of R3: x = fl32(z * fl32(1/T)), one binary32
+ * multiply rounded to nearest (the file is built with contraction off). */
+static float scaled(float z, float inv_t)
+{
+    float x = z * inv_t;
+    return x;
+}
+
+/*
+ * Log-sum-exp of one row of scaled logits, two passes in double:
+ * M = max_v x_v over finite entries, lse = M + log(sum_v exp(x_v - M)).
+ * Returns -inf when the row has no finite entry.
+ */
+double oracle_row_lse(const void *row_base, int dtype, size_t row_elem0,
+                      int vocab, float inv_t)
+{
+    double m = -INFINITY;
+    for (int v = 0; v < vocab; ++v) {
+        double x = scaled(raw_logit(row_base, dtype, row_elem0 + (size_t)v), inv_t);
+        if (x > m)
+            m = x;
+    }
+    if (!(m > -INFINITY))
+        return -INFINITY;
+    double s = 0.0;
+    for (int v = 0; v < vocab; ++v) {
+        double x = scaled(raw_logit(row_base, dtype, row_elem0 + (size_t)v), inv_t);
+        s += exp(x - m);
+    }
+    return m + log(s);
+}
+
+/* Index of the largest raw logit of a row, lowest index on ties (R4); -1 when
+ * the row has no finite entry. */
+int oracle_row_argmax(const void *row_base, int dtype, size_t row_elem0, int vocab)
+{
+    int best = -1;
+    float best_z = -INFINITY;
+    for (int v = 0; v < vocab; ++v) {
+        float z = raw_logit(row_base, dtype, row_elem0 + (size_t)v);
+        if (z > best_z) {
+            best_z = z;
+            best = v;
+        }
+    }
+    return best;
+}
+
+/*
+ * Inverse-CDF draw from weights r_v >= 0 (R7): S = sum r in index order,
+ * tau = u * S, token = first j whose inclusive prefix C_j exceeds tau.
+ * Also returns the log-margin of the draw: the log-ratio distance of tau to
+ * the two edges of the chosen bin, min(log(tau / C_{j-1}), log(C_j / tau)),
+ * with C_{-1} = 0 giving +inf, and 0 when tau == 0.
+ * Returns -1 when S <= 0.
+ */
+int oracle_inverse_cdf(const double *r, int vocab, double u, double *margin)
+{
+    double total = 0.0;
+    for (int v = 0; v < vocab; ++v)
+        total += r[v];
+    if (!(total > 0.0)) {
+        if (margin)
+            *margin = 0.0;
+        return -1;
+    }
+    double tau = u * total;
+    double prefix = 0.0;
+    for (int j = 0; j < vocab; ++j) {
+        double before = prefix;
+        prefix += r[j];
+        if (prefix > tau) {
+            if (margin) {
+                if (tau == 0.0) {
+                    *margin = 0.0;
+                } else {
+                    double lower = before > 0.0 ? log(tau / before) : INFINITY;
+                    double upper = log(prefix / tau);
+                    *margin = lower < upper ? lower : upper;
+                }
+            }
+            return j;
+        }
+    }
+    /* unreachable: tau < total and the last prefix equals total */
+    if (margin)
+        *margin = 0.0;
+    return -1;
+}
+
+/* ----------------------------------------------------- the verification -- */
+
+static int temperature_valid(float t, float *inv_t_out)
+{
+    if (isnan(t) || t < 0.0f || isinf(t))
+        return 0;
+    if (t == 0.0f) {
+        *inv_t_out = 0.0f;
+        return 1;
+    }
+    float inv_t = 1.0f / t;
+    if (isinf(inv_t))
+        return 0;
+    *inv_t_out = inv_t;
+    return 1;
+}
+
+/*
+ * One sequence, with its uniforms given explicitly (the Philox draw is done by
+ * the caller, so a test can sweep them). u_acc[i] for i < gamma and u_res[i]
+ * for i <= gamma. x_q rows are draft positions 0..gamma-1, x_p rows target
+ * positions 0..gamma. Element offsets of row i are q_row0 + i*V, p_row0 + i*V.
+ *
+ * Outputs: *accept_len, tokens[0..gamma], lse[0..2*gamma] (draft rows first,
+ * then target rows; NaN where not computed), acc_margin[0..gamma-1]
+ * ((lp - lq) - log u for evaluated positions, NaN elsewhere) and *res_margin.
+ */
+void oracle_verify_sequence(int gamma, int vocab, int dtype,
+                            const void *logits_draft, size_t q_row0,
+                            const void *logits_target, size_t p_row0,
+                            const int32_t *draft_tokens, float temperature,
+                            const double *u_acc, const double *u_res,
+                            int32_t *accept_len, int32_t *tokens,
+                            double *lse, double *acc_margin, double *res_margin)
+{
+    const int G = gamma, V = vocab;
+    for (int i = 0; i <= G; ++i)
+        tokens[i] = -1;
+    for (int i = 0; i < 2 * G + 1; ++i)
+        lse[i] = NAN;
+    for (int i = 0; i < G; ++i)
+        acc_margin[i] = NAN;
+    *res_margin = NAN;
+    *accept_len = -1;
+
+    float inv_t = 0.0f;
+    if (!temperature_valid(temperature, &inv_t))
+        return;
+    for (int i = 0; i < G; ++i)
+        if (draft_tokens[i] < 0 || draft_tokens[i] >= V)
+            return;
+
+    if (temperature == 0.0f) {
+        /* R4: greedy verification on raw target logits. */
+        int *amax = (int *)malloc(sizeof(int) * (size_t)(G + 1));
+        for (int i = 0; i <= G; ++i) {
+            amax[i] = oracle_row_argmax(logits_target, dtype, p_row0 + (size_t)i * V, V);
+            if (amax[i] < 0) {
+                free(amax);
+                return;
+            }
+        }
+        int k = G;
+        for (int i = 0; i < G; ++i) {
+            if (draft_tokens[i] != amax[i]) {
+                k = i;
+                break;
+            }
+        }
+        for (int i = 0; i < k; ++i)
+            tokens[i] = draft_tokens[i];
+        tokens[k] = amax[k];
+        *accept_len = k;
+        *res_margin = INFINITY;
+        free(amax);
+        return;
+    }
+
+    /* Log-normalisers of every row this sequence uses. */
+    double *lse_q = lse;          /* [G]   */
+    double *lse_p = lse + G;      /* [G+1] */
+    for (int i = 0; i < G; ++i)
+        lse_q[i] = oracle_row_lse(logits_draft, dtype, q_row0 + (size_t)i * V, V, inv_t);
+    for (int i = 0; i <= G; ++i)
+        lse_p[i] = oracle_row_lse(logits_target, dtype, p_row0 + (size_t)i * V, V, inv_t);
+    for (int i = 0; i < 2 * G + 1; ++i)
+        if (!(lse[i] > -INFINITY))
+            return;
+
+    /* Gather two log-probabilities per draft token, then the log-space test
+     * log u < log p - log q, evaluated with IEEE semantics for -inf. */
+    int k = G;
+    for (int i = 0; i < G; ++i) {
+        int t = draft_tokens[i];
+        double xq = scaled(raw_logit(logits_draft, dtype, q_row0 + (size_t)i * V + t), inv_t);
+        double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)i * V + t), inv_t);
+        double lq = xq - lse_q[i];
+        double lp = xp - lse_p[i];
+        double log_u = log(u_acc[i]);
+        acc_margin[i] = (lp - lq) - log_u;
+        int accept = log_u < (lp - lq);
+        if (!accept) {
+            k = i;
+            break;
+        }
+    }
+
+    /* Residual max(0, p - q) at the first rejection, or p at gamma (bonus). */
+    double *r = (double *)malloc(sizeof(double) * (size_t)V);
+    for (int v = 0; v < V; ++v) {
+        double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)k * V + v), inv_t);
+        double p = exp(xp - lse_p[k]);
+        if (k < G) {
+            double xq = scaled(raw_logit(logits_draft, dtype, q_row0 + (size_t)k * V + v), inv_t);
+            double q = exp(xq - lse_q[k]);
+            r[v] = p - q > 0.0 ? p - q : 0.0;
+        } else {
+            r[v] = p;
+        }
+    }
+    double margin = 0.0;
+    int j = oracle_inverse_cdf(r, V, u_res[k], &margin);
+    if (j < 0 && k < G) {
+        /* R8: empty residual, draw from p at the same position instead. */
+        for (int v = 0; v < V; ++v) {
+            double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)k * V + v), inv_t);
+            r[v] = exp(xp - lse_p[k]);
+        }
+        j = oracle_inverse_cdf(r, V, u_res[k], &margin);
+    }
+    free(r);
+
+    for (int i = 0; i < k; ++i)
+        tokens[i] = draft_tokens[i];
+    tokens[k] = j;
+    *accept_len = k;
+    *res_margin = margin;
+}
+
+/*
+ * The batched call. seq_ids (may be NULL, meaning 0..B-1) gives the global
+ * sequence index used in the Philox counter, so a sample of sequences taken
+ * out of a larger batch is verified with the uniforms the full batch uses.
+ * Array shapes: draft [B, G, V], target [B, G+1, V], draft_tokens [B, G],
+ * temperature [B], accept_len [B], tokens [B, G+1], lse [B, 2G+1],
+ * acc_margin [B, G] (may be NULL iff G == 0), res_margin [B].
+ */
+void oracle_verify(int batch, int gamma, int vocab, int dtype,
+                   const void *logits_draft, const void *logits_target,
+                   const int32_t *draft_tokens, const float *temperature,
+                   uint64_t seed, uint64_t offset, const int64_t *seq_ids,
+                   int32_t *accept_len, int32_t *tokens, double *lse,
+                   double *acc_margin, double *res_margin)
+{
+    const int G = gamma;
+    double *u_acc = (double *)malloc(sizeof(double) * (size_t)(G + 1));
+    double *u_res = (double *)malloc(sizeof(double) * (size_t)(G + 1));
+    double dummy_margin[1];
+    for (int b = 0; b < batch; ++b) {
+        int64_t gb = seq_ids ? seq_ids[b] : (int64_t)b;
+        for (int i = 0; i <= G; ++i) {
+            uint32_t w[4];
+            oracle_philox_words(seed, offset, gb, i, w);
+            u_acc[i] = oracle_uniform24(w[0]);
+            u_res[i] = oracle_uniform24(w[1]);
+        }
+        oracle_verify_sequence(G, vocab, dtype,
+                               logits_draft, (size_t)b * G * vocab,
+                               logits_target, (size_t)b * (G + 1) * vocab,
+                               draft_tokens + (size_t)b * G, temperature[b],
+                               u_acc, u_res, accept_len + b,
+                               tokens + (size_t)b * (G + 1),
+                               lse + (size_t)b * (2 * G + 1),
+                               G > 0 ? acc_margin + (size_t)b * G : dummy_margin,
+                               res_margin + b);
+    }
+    free(u_acc);
+    free(u_res);
+}
+
+/*
+ * Scalar-only mode: the gathered pairs logprobs[b, i, 0] = log q (draft) and
+ * logprobs[b, i, 1] = log p (target), temperature already applied upstream
+ * (FlashSpec summary, Methodology section 1: two log-probability scalars per
+ * candidate, one from each model; traffic O(B*gamma)). Same counters and the
+ * same accept test as the full call; only the accept length is produced.
+ */
+void oracle_accept_logprobs(int batch, int gamma, const float *logprobs,
+                            uint64_t seed, uint64_t offset, const int64_t *seq_ids,
+                            int32_t *accept_len, double *acc_margin)
+{
+    const int G = gamma;
+    for (int b = 0; b < batch; ++b) {
+        int64_t gb = seq_ids ? seq_ids[b] : (int64_t)b;
+        int k = G;
+        for (int i = 0; i < G; ++i)
+            acc_margin[(size_t)b * G + i] = NAN;
+        for (int i = 0; i < G; ++i) {
+            uint32_t w[4];
+            oracle_philox_words(seed, offset, gb, i, w);
+            double log_u = log(oracle_uniform24(w[0]));
+            double lq = (double)logprobs[((size_t)b * G + i) * 2 + 0];
+            double lp = (double)logprobs[((size_t)b * G + i) * 2 + 1];
+            acc_margin[(size_t)b * G + i] = (lp - lq) - log_u;
+            if (!(log_u < (lp - lq))) {
+                k = i;
+                break;
+            }
+        }
+        accept_len[b] = k;
+    }
+}
+
+/*
+ * The gathered pairs themselves, as the full call sees them: for every
+ * sequence with T > 0 that is valid, out[b, i, 0] = x_q[i][t_i] - lse_q[i] and
+ * out[b, i, 1] = x_p[i][t_i] - lse_p[i] in double; NaN for other sequences.
+ */
+void oracle_gather_logprobs(int batch, int gamma, int vocab, int dtype,
+                            const void *logits_draft, const void *logits_target,
+                            const int32_t *draft_tokens, const float *temperature,
+                            double *out)
+{
+    const int G = gamma, V = vocab;
+    for (int b = 0; b < batch; ++b) {
+        float inv_t = 0.0f;
+        int ok = temperature_valid(temperature[b], &inv_t) && temperature[b] > 0.0f;
+        for (int i = 0; i < G && ok; ++i)
+            if (draft_tokens[(size_t)b * G + i] < 0 || draft_tokens[(size_t)b * G + i] >= V)
+                ok = 0;
+        for (int i = 0; i < G; ++i) {
+            double *o = out + ((size_t)b * G + i) * 2;
+            o[0] = o[1] = NAN;
+            if (!ok)
+                continue;
+            int t = draft_tokens[(size_t)b * G + i];
+            size_t q0 = ((size_t)b * G + i) * V, p0 = ((size_t)b * (G + 1) + i) * V;
+            double lq = oracle_row_lse(logits_draft, dtype, q0, V, inv_t);
+            double lp = oracle_row_lse(logits_target, dtype, p0, V, inv_t);
+            o[0] = (double)scaled(raw_logit(logits_draft, dtype, q0 + t), inv_t) - lq;
+            o[1] = (double)scaled(raw_logit(logits_target, dtype, p0 + t), inv_t) - lp;
+        }
+    }
+}
