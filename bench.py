@@ -1,0 +1,222 @@
+"""Throughput of batched speculative-sampling verification on one MI355X.
+
+One step = one spec_verify call (row normalisers, accept, residual draw) over
+the B=256, gamma=8, V=152064 bf16 workload (target correlated rho=0.8 with the
+draft, per-sequence temperature U[0.3, 1.5], 10 % greedy sequences), inputs
+resident in HBM before the timed region. Three copies of the inputs are
+rotated so no step finds the previous step's rows in the 256 MB last-level
+cache. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified sequences/sec and achieved HBM GB/s (% of peak) at B×(γ+1)×V"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+WORKLOAD_CONFIG = 4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rownorm_B256_g8_V152064_traffic.json")
+KERNEL_SOURCES = ["device_draft_verification_amd/csrc/rownorm.hip",
+                  "device_draft_verification_amd/csrc/common.hpp",
+                  "device_draft_verification_amd/csrc/launch.hpp"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(rec, temperature: np.ndarray, accept_len: np.ndarray) -> dict:
+    """Bytes each kernel must move for one call (see the kernel headers):
+    row normalisers read (2G+1) rows per sampled sequence and G+1 target rows
+    per greedy one; the residual kernel reads 2 rows after a rejection, the
+    bonus row after a full accept, nothing for greedy sequences; the accept
+    kernel gathers 2 logits per position and writes the outcome."""
+    s = 2 if rec.dtype == "bf16" else 4
+    G, V = rec.gamma, rec.vocab
+    sampled = temperature > 0
+    greedy = temperature == 0
+    k1 = int(sampled.sum()) * (2 * G + 1) * V * s + int(greedy.sum()) * (G + 1) * V * s
+    valid = accept_len >= 0
+    rejected = sampled & valid & (accept_len < G)
+    bonus = sampled & valid & (accept_len == G)
+    k3 = int(rejected.sum()) * 2 * V * s + int(bonus.sum()) * V * s
+    k2 = rec.batch * (2 * G * s + 4 * G + 4 + 4 * (G + 2))
+    return dict(row_norm=k1, accept=k2, residual=k3)
+
+
+def cpu_baseline(rec, d, budget_s: float = 12.0) -> dict:
+    """The oracle, single-threaded, on the first sequences of the same inputs
+    until about budget_s seconds of CPU work have been spent."""
+    import oracle
+    oracle._load()
+    n = 0
+    t0 = time.perf_counter()
+    while n < rec.batch:
+        sl = slice(n, n + 1)
+        oracle.verify(d["logits_draft"][sl], d["logits_target"][sl], d["draft_tokens"][sl],
+                      d["temperature"][sl], seed=0, offset=0, seq_ids=d["seq_ids"][sl])
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "sequences/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {rec.batch} sequences of the {rec.name} workload, "
+                      f"one call per sequence, {dt:.1f} s single-threaded"}
+
+
+def load_traffic(k1_launch_bytes: int):
+    """HBM bytes per launch of the row-normaliser kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None when the kernel source has
+    changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return int(t["hbm_bytes_per_launch"])
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library's verification path runs "
+              "on a single device (multi-GPU sharding is not built)", file=sys.stderr)
+        return 2
+
+    import torch
+    import device_draft_verification_amd as sv
+    import specgen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sv.load_library()
+    dev = torch.device("cuda:0")
+    rec = specgen.config(WORKLOAD_CONFIG)
+    B, G, V = rec.batch, rec.gamma, rec.vocab
+    t0 = time.perf_counter()
+    d = specgen.generate(rec)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    draft0, target0 = bf16(d["logits_draft"]), bf16(d["logits_target"])
+    copies = [(draft0, target0)] + [(draft0.clone(), target0.clone()) for _ in range(args.copies - 1)]
+    tokens = torch.from_numpy(d["draft_tokens"]).to(dev)
+    temp = torch.from_numpy(d["temperature"]).to(dev)
+    alen = torch.empty(B, dtype=torch.int32, device=dev)
+    toks = torch.empty(B, G + 1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    ctx = sv.spec_verify_init(B, G, V, torch.bfloat16, stream=stream)
+    geo = sv.spec_verify_get_geometry(ctx)
+
+    def step(i):
+        zq, zp = copies[i % len(copies)]
+        sv.spec_verify(ctx, zq, zp, tokens, temp, 0, i, alen, toks)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps with per-kernel HIP events recorded by the library
+    # on the stream it launches on.
+    sv.spec_verify_enable_timing(ctx, args.steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per_kernel = np.array(sv.spec_verify_read_timing(ctx, args.steps))  # [K, 3] ms
+    sv.spec_verify_enable_timing(ctx, 0)
+    ms_per_step = total_ms / args.steps
+
+    # Algorithmic bytes per call: outputs are a pure function of (inputs, seed,
+    # offset), so each timed call's accept lengths are recomputed untimed.
+    k1_bytes = k3_bytes = k2_bytes = 0
+    for i in range(args.steps):
+        step(args.warmup + i)
+        torch.cuda.synchronize()
+        ab = algorithmic_bytes(rec, d["temperature"], alen.cpu().numpy())
+        k1_bytes += ab["row_norm"]
+        k2_bytes += ab["accept"]
+        k3_bytes += ab["residual"]
+    k1_bytes /= args.steps
+    k2_bytes /= args.steps
+    k3_bytes /= args.steps
+    k1_ms, k2_ms, k3_ms = per_kernel.mean(axis=0)
+    k1_gbs = k1_bytes / (k1_ms * 1e-3) / 1e9
+    k3_gbs = k3_bytes / (k3_ms * 1e-3) / 1e9
+    call_gbs = (k1_bytes + k2_bytes + k3_bytes) / (ms_per_step * 1e-3) / 1e9
+    value = B / (ms_per_step * 1e-3)
+    log(f"per step {ms_per_step * 1e3:.1f} us: row_norm {k1_ms * 1e3:.1f} us ({k1_gbs:.0f} GB/s), "
+        f"accept {k2_ms * 1e3:.1f} us, residual {k3_ms * 1e3:.1f} us ({k3_gbs:.0f} GB/s); "
+        f"whole call {call_gbs:.0f} GB/s")
+
+    traffic = load_traffic(int(k1_bytes))
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "sequences/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": rec.name, "batch": B, "gamma": G, "vocab": V,
+                   "logits": "bf16", "greedy_fraction": 0.1, "parallelism": "none"},
+        "hbm_gbs_whole_call": round(call_gbs, 1),
+        "hbm_frac_whole_call": round(call_gbs / HBM_PEAK_GBS, 4),
+        "kernels": {
+            "row_norm": {"us": round(k1_ms * 1e3, 2), "bytes": int(k1_bytes),
+                         "gbs": round(k1_gbs, 1), "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                         "splits": geo["row_splits"]},
+            "accept": {"us": round(k2_ms * 1e3, 2), "bytes": int(k2_bytes)},
+            "residual": {"us": round(k3_ms * 1e3, 2), "bytes": int(k3_bytes),
+                         "gbs": round(k3_gbs, 1), "frac": round(k3_gbs / HBM_PEAK_GBS, 4),
+                         "splits": geo["residual_splits"]},
+        },
+        "roofline": {"bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "row_norm_kernel"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(rec, d)
+    sv.spec_verify_destroy(ctx)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

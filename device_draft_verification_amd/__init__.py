@@ -1,0 +1,13 @@
+"""Batched speculative-sampling verification on AMD Instinct MI355X (gfx950).
+
+The work is done by hand-written HIP kernels in ``libspecverify.so`` behind the
+C ABI of ``include/spec_verify.h``; this package is a thin ctypes binding with
+the same function names (``binding``) and the build script (``build``).
+"""
+from .binding import (  # noqa: F401
+    EXPORTED, LIB_PATH, SPEC_BF16, SPEC_F32, Context, SpecVerifyError, dtype_code,
+    load_library, spec_accept_logprobs, spec_verify, spec_verify_copy_lse,
+    spec_verify_destroy, spec_verify_enable_timing, spec_verify_get_geometry,
+    spec_verify_init, spec_verify_philox_words, spec_verify_read_timing,
+    spec_verify_set_stream, spec_verify_strerror,
+)

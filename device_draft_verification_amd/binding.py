@@ -1,0 +1,212 @@
+"""ctypes binding of libspecverify.so (C ABI in include/spec_verify.h).
+
+Argument marshalling only: every function forwards device pointers
+(``tensor.data_ptr()``), sizes and the HIP stream handle to the C ABI of the
+same name, and raises ``SpecVerifyError`` on a negative status. All the work
+runs in the library's HIP kernels; there is no CPU fallback, and loading fails
+loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+SPEC_OK = 0
+SPEC_EINVAL = -1
+SPEC_EHIP = -2
+SPEC_ENOMEM = -3
+SPEC_ESTATE = -4
+
+EXPORTED = (
+    "spec_verify_init", "spec_verify_set_stream", "spec_verify", "spec_accept_logprobs",
+    "spec_verify_copy_lse", "spec_verify_philox_words", "spec_verify_enable_timing",
+    "spec_verify_read_timing", "spec_verify_get_geometry", "spec_verify_destroy",
+    "spec_verify_strerror",
+)
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, func: str, code: int):
+        self.code = code
+        super().__init__(f"{func} failed: {code} ({_strerror(code)})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P, i32, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
+    sig = {
+        "spec_verify_init": ([i32, i32, i32, i32, P, ctypes.POINTER(P)], i32),
+        "spec_verify_set_stream": ([P, P], i32),
+        "spec_verify": ([P, P, P, P, P, u64, u64, P, P], i32),
+        "spec_accept_logprobs": ([P, P, u64, u64, P], i32),
+        "spec_verify_copy_lse": ([P, P], i32),
+        "spec_verify_philox_words": ([P, u64, u64, P], i32),
+        "spec_verify_enable_timing": ([P, i32], i32),
+        "spec_verify_read_timing": ([P, P, i32], i32),
+        "spec_verify_get_geometry": ([P, P], i32),
+        "spec_verify_destroy": ([P], i32),
+        "spec_verify_strerror": ([i32], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _strerror(code: int) -> str:
+    try:
+        return load_library().spec_verify_strerror(code).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "unknown"
+
+
+def _check(func: str, rc: int) -> int:
+    if rc < 0:
+        raise SpecVerifyError(func, rc)
+    return rc
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the verification library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return SPEC_BF16
+    if dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {dtype}")
+
+
+class Context:
+    """Owns a spec_verify_ctx*; destroyed with spec_verify_destroy."""
+
+    def __init__(self, handle: ctypes.c_void_p, batch: int, gamma: int, vocab: int, dtype: int):
+        self.handle = handle
+        self.batch, self.gamma, self.vocab, self.dtype = batch, gamma, vocab, dtype
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                load_library().spec_verify_destroy(self.handle)
+            except Exception:
+                pass
+            self.handle = None
+
+
+def spec_verify_init(batch: int, gamma: int, vocab: int, dtype, stream=None) -> Context:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    h = ctypes.c_void_p()
+    _check("spec_verify_init", load_library().spec_verify_init(
+        batch, gamma, vocab, code, _stream_handle(stream), ctypes.byref(h)))
+    return Context(h, batch, gamma, vocab, code)
+
+
+def spec_verify_set_stream(ctx: Context, stream=None) -> None:
+    _check("spec_verify_set_stream",
+           load_library().spec_verify_set_stream(ctx.handle, _stream_handle(stream)))
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def spec_verify(ctx: Context, logits_draft, logits_target, draft_tokens, temperature,
+                seed: int, offset: int, out_accept_len, out_tokens) -> None:
+    B, G, V = ctx.batch, ctx.gamma, ctx.vocab
+    ldt = torch.bfloat16 if ctx.dtype == SPEC_BF16 else torch.float32
+    if G > 0:
+        _expect(logits_draft, (B, G, V), ldt, "logits_draft")
+        _expect(draft_tokens, (B, G), torch.int32, "draft_tokens")
+    _expect(logits_target, (B, G + 1, V), ldt, "logits_target")
+    _expect(temperature, (B,), torch.float32, "temperature")
+    _expect(out_accept_len, (B,), torch.int32, "out_accept_len")
+    _expect(out_tokens, (B, G + 1), torch.int32, "out_tokens")
+    _check("spec_verify", load_library().spec_verify(
+        ctx.handle, _ptr(logits_draft) if G > 0 else None, _ptr(logits_target),
+        _ptr(draft_tokens) if G > 0 else None, _ptr(temperature), seed, offset,
+        _ptr(out_accept_len), _ptr(out_tokens)))
+
+
+def spec_accept_logprobs(ctx: Context, logprobs, seed: int, offset: int, out_accept_len) -> None:
+    B, G = ctx.batch, ctx.gamma
+    _expect(logprobs, (B, G, 2), torch.float32, "logprobs")
+    _expect(out_accept_len, (B,), torch.int32, "out_accept_len")
+    _check("spec_accept_logprobs", load_library().spec_accept_logprobs(
+        ctx.handle, _ptr(logprobs), seed, offset, _ptr(out_accept_len)))
+
+
+def spec_verify_copy_lse(ctx: Context, out_lse) -> None:
+    _expect(out_lse, (ctx.batch, 2 * ctx.gamma + 1), torch.float64, "out_lse")
+    _check("spec_verify_copy_lse", load_library().spec_verify_copy_lse(ctx.handle, _ptr(out_lse)))
+
+
+def spec_verify_philox_words(ctx: Context, seed: int, offset: int, out_words) -> None:
+    _expect(out_words, (ctx.batch, ctx.gamma + 1, 4), torch.int32, "out_words")
+    _check("spec_verify_philox_words",
+           load_library().spec_verify_philox_words(ctx.handle, seed, offset, _ptr(out_words)))
+
+
+def spec_verify_enable_timing(ctx: Context, max_calls: int) -> None:
+    _check("spec_verify_enable_timing", load_library().spec_verify_enable_timing(ctx.handle, max_calls))
+
+
+def spec_verify_read_timing(ctx: Context, max_calls: int):
+    """Per-call kernel durations in ms: list of (row_norm, accept, residual)."""
+    buf = (ctypes.c_float * (3 * max(max_calls, 1)))()
+    n = _check("spec_verify_read_timing",
+               load_library().spec_verify_read_timing(ctx.handle, buf, max_calls))
+    return [(buf[3 * i], buf[3 * i + 1], buf[3 * i + 2]) for i in range(n)]
+
+
+def spec_verify_get_geometry(ctx: Context) -> dict:
+    out = (ctypes.c_int * 3)()
+    _check("spec_verify_get_geometry", load_library().spec_verify_get_geometry(ctx.handle, out))
+    return dict(row_splits=out[0], residual_splits=out[1], block=out[2])
+
+
+def spec_verify_destroy(ctx: Context) -> None:
+    if ctx.handle:
+        rc = load_library().spec_verify_destroy(ctx.handle)
+        ctx.handle = None
+        _check("spec_verify_destroy", rc)
+
+
+def spec_verify_strerror(code: int) -> str:
+    return _strerror(code)

@@ -1,0 +1,244 @@
+// Accept kernel: one 64-lane wavefront per sequence, lane i <-> draft position i.
+//
+// Per lane: merge the vocabulary splits of draft row i and target row i into
+// their log-normalisers, gather the two log-probabilities of draft token t_i
+// (FlashSpec technical summary, Methodology section 1: two log-probability
+// scalars per candidate, one per model), draw the Philox block of (b, i) and
+// run the log-space test log u < log p - log q in fp64. The first rejection is
+// one ballot and a count of trailing zeros. The kernel writes the accepted
+// prefix and the accept length, and leaves (k, u_res) for the residual kernel.
+// Greedy sequences (T == 0) compare t_i with the target argmax instead and
+// finish here. The verification outcome -- accepted count plus the extra
+// token -- is what the Speculative Speculative Decoding summary (section 2,
+// central concept, item 1) keys its speculation cache on.
+//
+// Also here: the scalar-only accept (O(B * gamma) bytes, nothing of size V)
+// and the Philox test export.
+#include <math.h>
+
+#include "launch.hpp"
+#include "philox.hpp"
+
+namespace specv {
+namespace {
+
+__device__ inline double lse_of(const RowNorm& r) {
+    return (static_cast<double>(r.m) + log2(r.s)) / static_cast<double>(kLog2e);
+}
+
+__device__ inline bool merge_sampled(const Partial* p, int nsplit, RowNorm* out) {
+    float m = kNegMax;
+    for (int c = 0; c < nsplit; ++c)
+        m = fmaxf(m, p[c].m);
+    double s = 0.0;
+    for (int c = 0; c < nsplit; ++c) {
+        const double f = (p[c].m == m) ? 1.0 : exp2(static_cast<double>(p[c].m) - static_cast<double>(m));
+        s = __builtin_fma(p[c].s, f, s);
+    }
+    *out = RowNorm{m, -1, s};
+    return s > 0.0;  // false: the row has no finite logit
+}
+
+__device__ inline bool merge_greedy(const Partial* p, int nsplit, RowNorm* out) {
+    float bv = -__builtin_huge_valf();
+    int bi = 0x7fffffff;
+    for (int c = 0; c < nsplit; ++c) {
+        if (p[c].m > bv || (p[c].m == bv && p[c].idx < bi)) {
+            bv = p[c].m;
+            bi = p[c].idx;
+        }
+    }
+    *out = RowNorm{bv, bi, 0.0};
+    return bv > -__builtin_huge_valf();
+}
+
+template <int DT>
+__global__ __launch_bounds__(64) void accept_kernel(
+    const void* __restrict__ draft, const void* __restrict__ target,
+    const int32_t* __restrict__ tokens, const float* __restrict__ temperature, int gamma,
+    int vocab, int nsplit, uint64_t seed, uint64_t offset, const Partial* __restrict__ part,
+    RowNorm* __restrict__ rn, double* __restrict__ lse_out, SeqState* __restrict__ seq,
+    int32_t* __restrict__ out_len, int32_t* __restrict__ out_tok) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int G = gamma;
+    const int rps = 2 * G + 1;
+    const size_t row0 = static_cast<size_t>(b) * rps;
+
+    float inv_t = 0.0f;
+    const int mode = temperature_mode(temperature[b], &inv_t);
+    bool bad = mode < 0;
+
+    // Pass 1: validate the draft tokens, merge the splits of every used row.
+    // Lane l handles positions i = l, l + 64, ...: draft row i and target row
+    // G + i, and is the only lane that ever touches those rows' entries of
+    // rn and lse_out in this kernel.
+    const double nan = __builtin_nan("");
+    for (int i0 = 0; i0 <= G; i0 += 64) {
+        const int i = i0 + lane;
+        if (i < G) {
+            const int t = tokens[static_cast<size_t>(b) * G + i];
+            if (t < 0 || t >= vocab)
+                bad = true;
+        }
+        if (i > G)
+            continue;
+        RowNorm r;
+        if (mode == 1) {
+            if (i < G) {
+                if (!merge_sampled(part + (row0 + i) * nsplit, nsplit, &r))
+                    bad = true;
+                rn[row0 + i] = r;
+                lse_out[row0 + i] = lse_of(r);
+            }
+            if (!merge_sampled(part + (row0 + G + i) * nsplit, nsplit, &r))
+                bad = true;
+            rn[row0 + G + i] = r;
+            lse_out[row0 + G + i] = lse_of(r);
+        } else {
+            if (mode == 0 && !merge_greedy(part + (row0 + G + i) * nsplit, nsplit, &r))
+                bad = true;
+            if (mode == 0)
+                rn[row0 + G + i] = r;
+            if (i < G)
+                lse_out[row0 + i] = nan;
+            lse_out[row0 + G + i] = nan;
+        }
+    }
+    bad = __ballot(bad) != 0ull;
+
+    if (bad) {
+        for (int i = lane; i <= G; i += 64) {
+            out_tok[static_cast<size_t>(b) * (G + 1) + i] = -1;
+            if (i < G)
+                lse_out[row0 + i] = nan;
+            lse_out[row0 + G + i] = nan;
+        }
+        if (lane == 0) {
+            out_len[b] = -1;
+            seq[b] = SeqState{0, 0, 0.0f, 0};
+        }
+        return;
+    }
+
+    // Pass 2: accept test per position, first rejection by ballot.
+    int k = G;
+    for (int i0 = 0; i0 < G; i0 += 64) {
+        const int i = i0 + lane;
+        bool reject = false;
+        if (i < G) {
+            const int t = tokens[static_cast<size_t>(b) * G + i];
+            const RowNorm np = rn[row0 + G + i];
+            if (mode == 0) {
+                reject = t != np.idx;
+            } else {
+                const RowNorm nq = rn[row0 + i];
+                const float xq = scale_logit(
+                    load_logit(row_ptr(draft, DT, static_cast<size_t>(b) * G + i, vocab), DT, t), inv_t);
+                const float xp = scale_logit(
+                    load_logit(row_ptr(target, DT, static_cast<size_t>(b) * (G + 1) + i, vocab), DT, t),
+                    inv_t);
+                const double lq = static_cast<double>(xq) - lse_of(nq);
+                const double lp = static_cast<double>(xp) - lse_of(np);
+                const Words4 w = verify_block(seed, offset, static_cast<uint32_t>(b), static_cast<uint32_t>(i));
+                const double log_u = log(static_cast<double>(uniform24(w.w0)));
+                reject = !(log_u < lp - lq);
+            }
+        }
+        const unsigned long long mask = __ballot(reject);
+        if (mask) {
+            k = i0 + __ffsll(static_cast<long long>(mask)) - 1;
+            break;
+        }
+    }
+
+    // Emit: accepted prefix, the greedy extra token, padding. The residual
+    // kernel writes the extra token of sampled sequences.
+    for (int i = lane; i <= G; i += 64) {
+        int v = -1;
+        if (i < k)
+            v = tokens[static_cast<size_t>(b) * G + i];
+        else if (i == k && mode == 0)
+            v = rn[row0 + G + k].idx;
+        out_tok[static_cast<size_t>(b) * (G + 1) + i] = v;
+    }
+    if (lane == 0) {
+        out_len[b] = k;
+        const Words4 w = verify_block(seed, offset, static_cast<uint32_t>(b), static_cast<uint32_t>(k));
+        seq[b] = SeqState{k, mode == 1 ? 1 : 0, uniform24(w.w1), 0};
+    }
+}
+
+__global__ __launch_bounds__(256) void accept_scalar_kernel(const float* __restrict__ logprobs,
+                                                            int batch, int gamma, uint64_t seed,
+                                                            uint64_t offset,
+                                                            int32_t* __restrict__ out_len) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= batch)
+        return;
+    int k = gamma;
+    for (int i = 0; i < gamma; ++i) {
+        const float2 pr = reinterpret_cast<const float2*>(logprobs)[static_cast<size_t>(b) * gamma + i];
+        const double d = static_cast<double>(pr.y) - static_cast<double>(pr.x);
+        const Words4 w = verify_block(seed, offset, static_cast<uint32_t>(b), static_cast<uint32_t>(i));
+        const double log_u = log(static_cast<double>(uniform24(w.w0)));
+        if (!(log_u < d)) {
+            k = i;
+            break;
+        }
+    }
+    out_len[b] = k;
+}
+
+__global__ __launch_bounds__(256) void philox_words_kernel(int batch, int gamma, uint64_t seed,
+                                                           uint64_t offset, uint32_t* __restrict__ out) {
+    const long n = static_cast<long>(batch) * (gamma + 1);
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= n)
+        return;
+    const uint32_t b = static_cast<uint32_t>(t / (gamma + 1));
+    const uint32_t i = static_cast<uint32_t>(t % (gamma + 1));
+    const Words4 w = verify_block(seed, offset, b, i);
+    reinterpret_cast<uint4*>(out)[t] = make_uint4(w.w0, w.w1, w.w2, w.w3);
+}
+
+}  // namespace
+
+hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const void* target,
+                         const int32_t* tokens, const float* temperature, uint64_t seed,
+                         uint64_t offset, const Partial* part, RowNorm* rn, double* lse_out,
+                         SeqState* seq, int32_t* out_len, int32_t* out_tok, hipStream_t stream) {
+    if (s.batch == 0)
+        return hipSuccess;
+    if (s.dtype == kBF16)
+        accept_kernel<kBF16><<<dim3(s.batch), dim3(64), 0, stream>>>(
+            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, part, rn,
+            lse_out, seq, out_len, out_tok);
+    else
+        accept_kernel<kF32><<<dim3(s.batch), dim3(64), 0, stream>>>(
+            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, part, rn,
+            lse_out, seq, out_len, out_tok);
+    return hipGetLastError();
+}
+
+hipError_t launch_accept_scalar(int batch, int gamma, const float* logprobs, uint64_t seed,
+                                uint64_t offset, int32_t* out_len, hipStream_t stream) {
+    if (batch == 0)
+        return hipSuccess;
+    const int blocks = (batch + 255) / 256;
+    accept_scalar_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(logprobs, batch, gamma, seed,
+                                                                 offset, out_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_philox_words(int batch, int gamma, uint64_t seed, uint64_t offset,
+                               uint32_t* out, hipStream_t stream) {
+    const long n = static_cast<long>(batch) * (gamma + 1);
+    if (n == 0)
+        return hipSuccess;
+    const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+    philox_words_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(batch, gamma, seed, offset, out);
+    return hipGetLastError();
+}
+
+}  // namespace specv

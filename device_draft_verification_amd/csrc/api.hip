@@ -1,0 +1,324 @@
+// The C ABI (include/spec_verify.h): context, workspace, argument checks and
+// the launch sequence row-normaliser -> accept -> residual on one stream.
+// Nothing here synchronises the host except spec_verify_read_timing and
+// spec_verify_destroy.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <new>
+#include <vector>
+
+#include "launch.hpp"
+#include "spec_verify.h"
+
+using namespace specv;
+
+struct spec_verify_ctx {
+    Shape shape{};
+    hipStream_t stream = nullptr;
+    int device = 0;
+    int nsplit_rows = 1;      // vocabulary splits of the row-normaliser kernel
+    int nsplit_residual = 1;  // vocabulary splits of the residual kernel
+
+    void* ws = nullptr;
+    Partial* part = nullptr;
+    RowNorm* rn = nullptr;
+    double* lse = nullptr;
+    SeqState* seq = nullptr;
+    double* chunk_sums = nullptr;
+    int* tickets = nullptr;
+    bool have_verified = false;
+
+    int timing_slots = 0;
+    int timing_count = 0;
+    std::vector<hipEvent_t> events;  // 4 per slot
+};
+
+namespace {
+
+// Workgroups that keep every CU of an MI355X busy with a few to spare
+// (256 CUs; several resident workgroups each).
+constexpr long kTargetBlocks = 4096;
+
+int env_int(const char* name, int fallback) {
+    const char* v = std::getenv(name);
+    if (!v || !*v)
+        return fallback;
+    return std::atoi(v);
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int group_width(int dtype) { return dtype == SPEC_BF16 ? 8 : 4; }
+
+// Splits per row: enough workgroups in total, at least one 16-byte group per
+// thread per split, at most kMaxSplit.
+int choose_split(long rows, long vocab, int dtype) {
+    if (rows <= 0)
+        return 1;
+    const long groups = vocab / group_width(dtype);
+    long n = (kTargetBlocks + rows - 1) / rows;
+    const long by_size = std::max(1L, groups / kBlock);
+    n = std::min(n, by_size);
+    n = std::max(1L, std::min(n, static_cast<long>(kMaxSplit)));
+    return static_cast<int>(n);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_verify_strerror(int code) {
+    switch (code) {
+    case SPEC_OK: return "ok";
+    case SPEC_EINVAL: return "invalid argument";
+    case SPEC_EHIP: return "HIP runtime error";
+    case SPEC_ENOMEM: return "out of device memory";
+    case SPEC_ESTATE: return "context in the wrong state for this call";
+    default: return "unknown status";
+    }
+}
+
+int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_stream,
+                     spec_verify_ctx** out_ctx) {
+    if (!out_ctx)
+        return SPEC_EINVAL;
+    *out_ctx = nullptr;
+    if (batch < 0 || gamma < 0 || vocab < 1 || (dtype != SPEC_F32 && dtype != SPEC_BF16))
+        return SPEC_EINVAL;
+    const long rows = static_cast<long>(batch) * (2L * gamma + 1);
+    if (rows >= (1L << 31) || static_cast<long>(batch) * (gamma + 1) >= (1L << 31))
+        return SPEC_EINVAL;
+
+    spec_verify_ctx* ctx = new (std::nothrow) spec_verify_ctx();
+    if (!ctx)
+        return SPEC_ENOMEM;
+    ctx->shape = Shape{batch, gamma, vocab, dtype};
+    ctx->stream = static_cast<hipStream_t>(hip_stream);
+    if (hipGetDevice(&ctx->device) != hipSuccess) {
+        delete ctx;
+        return SPEC_EHIP;
+    }
+    ctx->nsplit_rows = choose_split(rows, vocab, dtype);
+    ctx->nsplit_residual = choose_split(batch, vocab, dtype);
+    const int o1 = env_int("SPEC_VERIFY_ROW_SPLIT", 0), o3 = env_int("SPEC_VERIFY_RESIDUAL_SPLIT", 0);
+    if (o1 > 0)
+        ctx->nsplit_rows = std::min(o1, kMaxSplit);
+    if (o3 > 0)
+        ctx->nsplit_residual = std::min(o3, kMaxSplit);
+    // A dispatch holds fewer than 2^32 work-items.
+    const long long limit = 1LL << 32;
+    if (static_cast<long long>(rows) * ctx->nsplit_rows * kBlock >= limit ||
+        static_cast<long long>(batch) * ctx->nsplit_residual * kBlock >= limit) {
+        delete ctx;
+        return SPEC_EINVAL;
+    }
+
+    // Workspace: one allocation, 256-byte aligned sub-arrays.
+    const size_t n_part = static_cast<size_t>(rows) * ctx->nsplit_rows;
+    size_t off = 0;
+    const size_t o_part = off; off = align_up(off + n_part * sizeof(Partial), 256);
+    const size_t o_rn = off;   off = align_up(off + rows * sizeof(RowNorm), 256);
+    const size_t o_lse = off;  off = align_up(off + rows * sizeof(double), 256);
+    const size_t o_seq = off;  off = align_up(off + static_cast<size_t>(batch) * sizeof(SeqState), 256);
+    const size_t o_cs = off;   off = align_up(off + static_cast<size_t>(batch) * ctx->nsplit_residual * sizeof(double), 256);
+    const size_t o_tk = off;   off = align_up(off + static_cast<size_t>(batch) * sizeof(int), 256);
+    const size_t total = std::max<size_t>(off, 256);
+    if (hipMalloc(&ctx->ws, total) != hipSuccess) {
+        delete ctx;
+        return SPEC_ENOMEM;
+    }
+    char* base = static_cast<char*>(ctx->ws);
+    ctx->part = reinterpret_cast<Partial*>(base + o_part);
+    ctx->rn = reinterpret_cast<RowNorm*>(base + o_rn);
+    ctx->lse = reinterpret_cast<double*>(base + o_lse);
+    ctx->seq = reinterpret_cast<SeqState*>(base + o_seq);
+    ctx->chunk_sums = reinterpret_cast<double*>(base + o_cs);
+    ctx->tickets = reinterpret_cast<int*>(base + o_tk);
+    // Tickets must start at zero; the residual kernel returns them to zero.
+    if (hipMemset(ctx->ws, 0, total) != hipSuccess) {
+        (void)hipFree(ctx->ws);
+        delete ctx;
+        return SPEC_EHIP;
+    }
+    *out_ctx = ctx;
+    return SPEC_OK;
+}
+
+int spec_verify_set_stream(spec_verify_ctx* ctx, void* hip_stream) {
+    if (!ctx)
+        return SPEC_EINVAL;
+    ctx->stream = static_cast<hipStream_t>(hip_stream);
+    return SPEC_OK;
+}
+
+int spec_verify(spec_verify_ctx* ctx, const void* logits_draft, const void* logits_target,
+                const int32_t* draft_tokens, const float* temperature, uint64_t seed,
+                uint64_t offset, int32_t* out_accept_len, int32_t* out_tokens) {
+    if (!ctx)
+        return SPEC_EINVAL;
+    const Shape& s = ctx->shape;
+    if (s.batch == 0)
+        return SPEC_OK;
+    const size_t esz = s.dtype == SPEC_BF16 ? 2 : 4;
+    if (!logits_target || !temperature || !out_accept_len || !out_tokens)
+        return SPEC_EINVAL;
+    if (s.gamma > 0 && (!logits_draft || !draft_tokens))
+        return SPEC_EINVAL;
+    if (!aligned(logits_target, esz) || (logits_draft && !aligned(logits_draft, esz)) ||
+        !aligned(temperature, 4) || !aligned(out_accept_len, 4) || !aligned(out_tokens, 4) ||
+        (draft_tokens && !aligned(draft_tokens, 4)))
+        return SPEC_EINVAL;
+    if (s.gamma == 0)
+        logits_draft = logits_target;  // never read; keeps the kernels' pointers valid
+
+    // 16-byte groups need every row start 16-byte aligned.
+    const bool vec = (s.vocab % group_width(s.dtype)) == 0 && aligned(logits_target, 16) &&
+                     aligned(logits_draft, 16);
+
+    hipEvent_t* ev = nullptr;
+    if (ctx->timing_slots > 0) {
+        ev = &ctx->events[static_cast<size_t>(ctx->timing_count % ctx->timing_slots) * 4];
+        ++ctx->timing_count;
+    }
+    hipStream_t st = ctx->stream;
+    if (ev && hipEventRecord(ev[0], st) != hipSuccess)
+        return SPEC_EHIP;
+    if (launch_row_norm(s, vec, ctx->nsplit_rows, logits_draft, logits_target, temperature,
+                        ctx->part, st) != hipSuccess)
+        return SPEC_EHIP;
+    if (ev && hipEventRecord(ev[1], st) != hipSuccess)
+        return SPEC_EHIP;
+    if (launch_accept(s, ctx->nsplit_rows, logits_draft, logits_target, draft_tokens, temperature,
+                      seed, offset, ctx->part, ctx->rn, ctx->lse, ctx->seq, out_accept_len,
+                      out_tokens, st) != hipSuccess)
+        return SPEC_EHIP;
+    if (ev && hipEventRecord(ev[2], st) != hipSuccess)
+        return SPEC_EHIP;
+    if (launch_residual(s, vec, ctx->nsplit_residual, logits_draft, logits_target, temperature,
+                        ctx->seq, ctx->rn, ctx->chunk_sums, ctx->tickets, out_tokens,
+                        st) != hipSuccess)
+        return SPEC_EHIP;
+    if (ev && hipEventRecord(ev[3], st) != hipSuccess)
+        return SPEC_EHIP;
+    ctx->have_verified = true;
+    return SPEC_OK;
+}
+
+int spec_accept_logprobs(spec_verify_ctx* ctx, const float* logprobs, uint64_t seed,
+                         uint64_t offset, int32_t* out_accept_len) {
+    if (!ctx)
+        return SPEC_EINVAL;
+    const Shape& s = ctx->shape;
+    if (s.batch == 0)
+        return SPEC_OK;
+    if (!out_accept_len || (s.gamma > 0 && !logprobs))
+        return SPEC_EINVAL;
+    if ((logprobs && !aligned(logprobs, 8)) || !aligned(out_accept_len, 4))
+        return SPEC_EINVAL;
+    if (launch_accept_scalar(s.batch, s.gamma, logprobs, seed, offset, out_accept_len,
+                             ctx->stream) != hipSuccess)
+        return SPEC_EHIP;
+    return SPEC_OK;
+}
+
+int spec_verify_copy_lse(spec_verify_ctx* ctx, double* out_lse) {
+    if (!ctx || !out_lse)
+        return SPEC_EINVAL;
+    if (!ctx->have_verified)
+        return SPEC_ESTATE;
+    const size_t n = static_cast<size_t>(ctx->shape.batch) * (2 * ctx->shape.gamma + 1);
+    if (n == 0)
+        return SPEC_OK;
+    if (hipMemcpyAsync(out_lse, ctx->lse, n * sizeof(double), hipMemcpyDeviceToDevice,
+                       ctx->stream) != hipSuccess)
+        return SPEC_EHIP;
+    return SPEC_OK;
+}
+
+int spec_verify_philox_words(spec_verify_ctx* ctx, uint64_t seed, uint64_t offset,
+                             uint32_t* out_words) {
+    if (!ctx || !out_words || !aligned(out_words, 16))
+        return SPEC_EINVAL;
+    if (launch_philox_words(ctx->shape.batch, ctx->shape.gamma, seed, offset, out_words,
+                            ctx->stream) != hipSuccess)
+        return SPEC_EHIP;
+    return SPEC_OK;
+}
+
+int spec_verify_enable_timing(spec_verify_ctx* ctx, int max_calls) {
+    if (!ctx || max_calls < 0)
+        return SPEC_EINVAL;
+    for (hipEvent_t e : ctx->events)
+        (void)hipEventDestroy(e);
+    ctx->events.clear();
+    ctx->timing_slots = 0;
+    ctx->timing_count = 0;
+    if (max_calls == 0)
+        return SPEC_OK;
+    ctx->events.resize(static_cast<size_t>(max_calls) * 4, nullptr);
+    for (auto& e : ctx->events) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (hipEvent_t x : ctx->events)
+                if (x)
+                    (void)hipEventDestroy(x);
+            ctx->events.clear();
+            return SPEC_EHIP;
+        }
+    }
+    ctx->timing_slots = max_calls;
+    return SPEC_OK;
+}
+
+int spec_verify_read_timing(spec_verify_ctx* ctx, float* out_ms, int max_calls) {
+    if (!ctx || (max_calls > 0 && !out_ms))
+        return SPEC_EINVAL;
+    if (ctx->timing_slots == 0)
+        return SPEC_ESTATE;
+    const int recorded = std::min(ctx->timing_count, ctx->timing_slots);
+    const int first = ctx->timing_count - recorded;
+    int written = 0;
+    for (int n = 0; n < recorded && written < max_calls; ++n) {
+        hipEvent_t* ev = &ctx->events[static_cast<size_t>((first + n) % ctx->timing_slots) * 4];
+        if (hipEventSynchronize(ev[3]) != hipSuccess)
+            return SPEC_EHIP;
+        for (int kk = 0; kk < 3; ++kk) {
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, ev[kk], ev[kk + 1]) != hipSuccess)
+                return SPEC_EHIP;
+            out_ms[written * 3 + kk] = ms;
+        }
+        ++written;
+    }
+    ctx->timing_count = 0;
+    return written;
+}
+
+int spec_verify_get_geometry(spec_verify_ctx* ctx, int* out) {
+    if (!ctx || !out)
+        return SPEC_EINVAL;
+    out[0] = ctx->nsplit_rows;
+    out[1] = ctx->nsplit_residual;
+    out[2] = kBlock;
+    return SPEC_OK;
+}
+
+int spec_verify_destroy(spec_verify_ctx* ctx) {
+    if (!ctx)
+        return SPEC_EINVAL;
+    int rc = SPEC_OK;
+    if (hipStreamSynchronize(ctx->stream) != hipSuccess)
+        rc = SPEC_EHIP;
+    for (hipEvent_t e : ctx->events)
+        (void)hipEventDestroy(e);
+    if (ctx->ws && hipFree(ctx->ws) != hipSuccess)
+        rc = SPEC_EHIP;
+    delete ctx;
+    return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Host-side launchers of the verification kernels (one per translation unit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace specv {
+
+// Temperature classification shared by the kernels: -1 invalid, 0 greedy, 1 sampled.
+__device__ inline int temperature_mode(float t, float* inv_t) {
+    if (!(t >= 0.0f) || t == __builtin_huge_valf())
+        return -1;
+    if (t == 0.0f) {
+        *inv_t = 0.0f;
+        return 0;
+    }
+    const float r = 1.0f / t;  // correctly rounded binary32 division
+    if (r == __builtin_huge_valf())
+        return -1;
+    *inv_t = r;
+    return 1;
+}
+
+struct Shape {
+    int batch, gamma, vocab, dtype;
+};
+
+// Row normalisers: grid = B * (2G+1) * nsplit workgroups of kBlock threads.
+hipError_t launch_row_norm(const Shape& s, bool vec, int nsplit, const void* draft,
+                           const void* target, const float* temperature, Partial* part,
+                           hipStream_t stream);
+
+// Split merge, gather, accept test, first rejection and the emitted prefix:
+// one 64-lane wavefront per sequence.
+hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const void* target,
+                         const int32_t* tokens, const float* temperature, uint64_t seed,
+                         uint64_t offset, const Partial* part, RowNorm* rn, double* lse_out,
+                         SeqState* seq, int32_t* out_len, int32_t* out_tok, hipStream_t stream);
+
+// Residual / bonus draw at the first rejection: grid = B * nsplit workgroups.
+hipError_t launch_residual(const Shape& s, bool vec, int nsplit, const void* draft,
+                           const void* target, const float* temperature, const SeqState* seq,
+                           const RowNorm* rn, double* chunk_sums, int* tickets,
+                           int32_t* out_tok, hipStream_t stream);
+
+// Scalar-only accept on gathered log-probability pairs.
+hipError_t launch_accept_scalar(int batch, int gamma, const float* logprobs, uint64_t seed,
+                                uint64_t offset, int32_t* out_len, hipStream_t stream);
+
+// Raw Philox words of every (b, i) block, for tests.
+hipError_t launch_philox_words(int batch, int gamma, uint64_t seed, uint64_t offset,
+                               uint32_t* out, hipStream_t stream);
+
+}  // namespace specv

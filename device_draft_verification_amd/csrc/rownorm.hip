@@ -1,0 +1,191 @@
+// Row normaliser kernel: temperature scaling, then a single-pass online
+// max / log-sum-exp over the vocabulary of every draft and target row (sampled
+// sequences), or the raw-logit argmax of every target row (greedy sequences).
+//
+// This is the step that touches O(B * gamma * V) bytes: the FlashSpec summary
+// (Problem statement item 1; Methodology section 1, complexity bullet) puts
+// the cost of verification in this traffic and in the host sync that grows
+// with V. Temperature is applied before the normaliser (same section,
+// numerical-stability bullet).
+//
+// Layout of the work: workgroup w handles split c = w % nsplit of row
+// w / nsplit; row r of sequence b = r / (2G+1) is draft row j = r % (2G+1) when
+// j < G, else target row j - G. Each thread streams 16-byte groups (8 bf16 or
+// 4 fp32) at a stride of kBlock groups, U groups in flight, so every load
+// instruction of a wavefront reads 1 KiB of consecutive memory.
+//
+// Numerics: x = fl32(z * fl32(1/T)). Per batch of U groups the thread takes
+// the batch max, moves its base-2 reference m to max(m, fl32(max x * log2e)),
+// rescales its running sum by 2^(m_old - m_new) (skipped when unchanged) and
+// adds sum_e 2^(fma(x_e, log2e, -m)) summed pairwise in fp32. The running sum is
+// fp64. Threads are merged by rescaling each to the block max once and adding
+// in fp64 in a fixed tree, so the result is bitwise reproducible.
+#include "launch.hpp"
+
+namespace specv {
+namespace {
+
+template <int N>
+__device__ inline float pairwise_sum(float (&t)[N]) {
+#pragma unroll
+    for (int w = 1; w < N; w <<= 1) {
+#pragma unroll
+        for (int i = 0; i + w < N; i += 2 * w)
+            t[i] += t[i + w];
+    }
+    return t[0];
+}
+
+template <int N>
+__device__ inline void online_add(const float (&x)[N], float& m, double& s) {
+    float gm = x[0];
+#pragma unroll
+    for (int e = 1; e < N; ++e)
+        gm = fmaxf(gm, x[e]);
+    const float mn = fmaxf(m, gm * kLog2e);
+    float t[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        t[e] = fast_exp2(__builtin_fmaf(x[e], kLog2e, -mn));
+    const float g = pairwise_sum(t);
+    const float sc = (mn == m) ? 1.0f : fast_exp2(m - mn);
+    s = __builtin_fma(s, static_cast<double>(sc), static_cast<double>(g));
+    m = mn;
+}
+
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void row_norm_kernel(
+    const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, int gamma, int vocab, int nsplit,
+    Partial* __restrict__ part) {
+    using Ld = Loader<DT, VEC>;
+    constexpr int W = Ld::W;
+    const long blk = blockIdx.x;
+    const int c = static_cast<int>(blk % nsplit);
+    const long row = blk / nsplit;
+    const int rps = 2 * gamma + 1;
+    const long b = row / rps;
+    const int j = static_cast<int>(row % rps);
+
+    float inv_t = 0.0f;
+    const int mode = temperature_mode(temperature[b], &inv_t);
+    const bool is_draft = j < gamma;
+    if (mode < 0 || (mode == 0 && is_draft))
+        return;  // nothing of this row is used
+    const void* rp = is_draft
+        ? row_ptr(draft, DT, static_cast<size_t>(b) * gamma + j, vocab)
+        : row_ptr(target, DT, static_cast<size_t>(b) * (gamma + 1) + (j - gamma), vocab);
+
+    const long groups = vocab / W;
+    long g0, g1;
+    split_range(groups, nsplit, c, &g0, &g1);
+
+    __shared__ float lds_f[kWaves];
+    __shared__ double lds_d[kWaves];
+    __shared__ int lds_i[kWaves];
+
+    if (mode == 0) {
+        // Greedy row: largest raw logit, lowest index on ties. Each thread
+        // visits its indices in increasing order, so a strict '>' keeps the
+        // lowest index of equal values.
+        float bv = -__builtin_huge_valf();
+        int bi = 0x7fffffff;
+        for (long g = g0 + threadIdx.x; g < g1; g += kBlock) {
+            float z[W];
+            Ld::unpack(Ld::load(rp, g), z);
+#pragma unroll
+            for (int e = 0; e < W; ++e) {
+                if (z[e] > bv) {
+                    bv = z[e];
+                    bi = static_cast<int>(g * W + e);
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int oi = __shfl_xor(bi, off, 64);
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (lane == 0) {
+            lds_f[wid] = bv;
+            lds_i[wid] = bi;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 1; w < kWaves; ++w) {
+                if (lds_f[w] > bv || (lds_f[w] == bv && lds_i[w] < bi)) {
+                    bv = lds_f[w];
+                    bi = lds_i[w];
+                }
+            }
+            part[blk] = Partial{bv, bi, 0.0};
+        }
+        return;
+    }
+
+    float m = kNegMax;
+    double s = 0.0;
+    long g = g0 + threadIdx.x;
+    for (; g + static_cast<long>(U - 1) * kBlock < g1; g += static_cast<long>(U) * kBlock) {
+        typename Ld::raw_t q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            q[u] = Ld::load(rp, g + static_cast<long>(u) * kBlock);
+        float x[U * W];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float z[W];
+            Ld::unpack(q[u], z);
+#pragma unroll
+            for (int e = 0; e < W; ++e)
+                x[u * W + e] = scale_logit(z[e], inv_t);
+        }
+        online_add(x, m, s);
+    }
+    for (; g < g1; g += kBlock) {
+        float z[W], x[W];
+        Ld::unpack(Ld::load(rp, g), z);
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            x[e] = scale_logit(z[e], inv_t);
+        online_add(x, m, s);
+    }
+
+    const float bm = block_max(m, lds_f);
+    const float sc = (m == bm) ? 1.0f : fast_exp2(m - bm);
+    const double bs = block_sum(s * static_cast<double>(sc), lds_d);
+    if (threadIdx.x == 0)
+        part[blk] = Partial{bm, -1, bs};
+}
+
+template <int DT, bool VEC>
+hipError_t launch_typed(const Shape& sh, int nsplit, const void* draft, const void* target,
+                        const float* temperature, Partial* part, hipStream_t stream) {
+    constexpr int U = VEC ? (DT == kBF16 ? 4 : 4) : 8;
+    const long rows = static_cast<long>(sh.batch) * (2 * sh.gamma + 1);
+    const long blocks = rows * nsplit;
+    if (blocks == 0)
+        return hipSuccess;
+    row_norm_kernel<DT, VEC, U><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream>>>(
+        draft, target, temperature, sh.gamma, sh.vocab, nsplit, part);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_row_norm(const Shape& s, bool vec, int nsplit, const void* draft,
+                           const void* target, const float* temperature, Partial* part,
+                           hipStream_t stream) {
+    if (s.dtype == kBF16)
+        return vec ? launch_typed<kBF16, true>(s, nsplit, draft, target, temperature, part, stream)
+                   : launch_typed<kBF16, false>(s, nsplit, draft, target, temperature, part, stream);
+    return vec ? launch_typed<kF32, true>(s, nsplit, draft, target, temperature, part, stream)
+               : launch_typed<kF32, false>(s, nsplit, draft, target, temperature, part, stream);
+}
+
+}  // namespace specv

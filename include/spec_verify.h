@@ -1,0 +1,174 @@
+/*
+ * spec_verify.h -- C ABI of the batched speculative-sampling verification
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources: the pages' titles and sections):
+ *   Given draft logits [B, G, V], target logits [B, G+1, V], draft tokens
+ *   [B, G] and a temperature per sequence, decide on the device how many of
+ *   the G draft tokens each sequence keeps and which extra token follows them,
+ *   with no host round trip (FlashSpec technical summary, Problem statement
+ *   item 1: host-side verification forces a device-to-host sync per decoding
+ *   step; Methodology section 1: verification entirely on the device, two
+ *   log-probability scalars per candidate token, log-space arithmetic,
+ *   temperature applied before the log-softmax). The result is the
+ *   "verification outcome" -- accepted count plus one token -- that the
+ *   Speculative Speculative Decoding summary (section 2, central concept,
+ *   item 1) consumes; the extra token comes from the residual distribution at
+ *   the first rejection, or is the bonus token from the target when every
+ *   draft token is kept (same summary, section 2, Saguaro challenge 2).
+ *   The accept rule u < min(1, p/q) and the residual norm(max(0, p - q)) are
+ *   those of standard speculative sampling (Leviathan, Kalman and Matias,
+ *   ICML 2023), which keeps the target's output distribution exactly, as the
+ *   FlashSpec summary requires (Methodology intro; Theorem 1).
+ *
+ * Precise definition, per sequence b with T = temperature[b], t_i = draft
+ * token i:
+ *   x = fl32(z * fl32(1/T)) for every logit z (binary32, round to nearest);
+ *   lse_q[i] = log sum_v exp(xq[i][v]) over draft row i (i < G);
+ *   lse_p[i] = log sum_v exp(xp[i][v]) over target row i (i <= G);
+ *   position i < G is accepted iff log(u_acc(b,i)) < (xp[i][t_i] - lse_p[i])
+ *                                                  - (xq[i][t_i] - lse_q[i]);
+ *   k = first rejected position, or G;
+ *   if k < G the extra token is drawn from r_v = max(0, p_k(v) - q_k(v)),
+ *   if k == G from r_v = p_G(v), by inversion: the first index v (in
+ *   vocabulary order) whose inclusive prefix sum of r exceeds u_res(b,k) * S,
+ *   S = sum_v r_v; an empty residual (S == 0) draws from p_k instead.
+ *   T == 0 is greedy: position i is accepted iff t_i == argmax_v z_p[i][v]
+ *   (raw logits, lowest index on ties) and the extra token is argmax z_p[k].
+ *   Uniforms: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), key
+ *   (lo32(seed), hi32(seed)), counter (i, b, lo32(offset), hi32(offset)) for
+ *   i = 0..G; u_acc(b,i) = (word0 >> 8) * 2^-24, u_res(b,i) = (word1 >> 8) *
+ *   2^-24. Outputs are a pure function of the inputs and (seed, offset); the
+ *   caller advances offset by one per call.
+ *
+ * Layouts: every array is dense, row-major, with the vocabulary innermost.
+ * Logits are binary32 (SPEC_F32) or bfloat16 (SPEC_BF16); pointers must be
+ * aligned to the element size. Tokens and lengths are int32. Every pointer
+ * passed to spec_verify / spec_accept_logprobs / the test hooks is a DEVICE
+ * pointer owned by the caller, and must stay valid until the work queued on
+ * the context's stream has completed. The library owns only its workspace.
+ *
+ * Asynchrony: calls enqueue kernels on the context's stream and return
+ * without synchronising the host. One context per stream; a context is not
+ * thread-safe and two calls on one context must not run concurrently.
+ *
+ * Errors: host-detectable problems (NULL context or pointer, bad shape or
+ * dtype, misaligned pointer) return a negative status before any launch. A
+ * failed launch returns SPEC_EHIP. Bad DATA is reported per sequence without
+ * a host sync: a temperature that is NaN, negative or +inf, or whose
+ * reciprocal overflows, a draft token outside [0, V), or a row the sequence
+ * uses that has no finite logit gives out_accept_len[b] = -1 and
+ * out_tokens[b, :] = -1. Logits equal to +inf or NaN are a precondition
+ * violation: the result is unspecified but no out-of-bounds access happens.
+ * If a kernel is aborted mid-call the context must be destroyed and created
+ * again (its internal counters may be left non-zero).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spec_verify_ctx spec_verify_ctx;
+
+enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };
+
+enum spec_status {
+    SPEC_OK = 0,
+    SPEC_EINVAL = -1, /* bad argument: NULL, shape, dtype, alignment        */
+    SPEC_EHIP = -2,   /* a HIP runtime call or kernel launch failed          */
+    SPEC_ENOMEM = -3, /* workspace allocation failed                         */
+    SPEC_ESTATE = -4  /* context in the wrong state for this call           */
+};
+
+/*
+ * Create a context for batches of `batch` sequences, `gamma` >= 0 draft
+ * tokens each and a vocabulary of `vocab` >= 1 entries, logits of `dtype`,
+ * launching on `hip_stream` (a hipStream_t; NULL = the null stream).
+ * Allocates the device workspace (a few MB at the largest shapes) and
+ * zeroes its counters. The shape is fixed for the context's lifetime.
+ * batch * (2*gamma+1) and vocab must each be below 2^31.
+ * Returns SPEC_OK and *out_ctx, or a negative status and *out_ctx = NULL.
+ */
+int spec_verify_init(int batch, int gamma, int vocab, int dtype, void *hip_stream,
+                     spec_verify_ctx **out_ctx);
+
+/* Move later launches of this context to another stream (hipStream_t). */
+int spec_verify_set_stream(spec_verify_ctx *ctx, void *hip_stream);
+
+/*
+ * The full verification (definition above). Device pointers:
+ *   logits_draft   [B, G, V]    dtype; may be NULL iff G == 0
+ *   logits_target  [B, G+1, V]  dtype
+ *   draft_tokens   [B, G]       int32; may be NULL iff G == 0
+ *   temperature    [B]          float32; 0 selects greedy verification
+ *   out_accept_len [B]          int32: k, or -1 for a rejected sequence
+ *   out_tokens     [B, G+1]     int32: tokens[0..k) = draft, tokens[k] =
+ *                               the extra token, the rest -1
+ * Enqueues three kernels on the context's stream (row normalisers; gather,
+ * accept and first rejection; residual or bonus draw) and returns.
+ */
+int spec_verify(spec_verify_ctx *ctx, const void *logits_draft,
+                const void *logits_target, const int32_t *draft_tokens,
+                const float *temperature, uint64_t seed, uint64_t offset,
+                int32_t *out_accept_len, int32_t *out_tokens);
+
+/*
+ * Scalar-only mode: reads only the gathered log-probability pairs, O(B*G)
+ * bytes, nothing of size V (FlashSpec summary, Methodology section 1,
+ * mechanism and complexity bullets). Device pointers:
+ *   logprobs       [B, G, 2] float32: [..., 0] = log q (draft),
+ *                  [..., 1] = log p (target), temperature already applied
+ *   out_accept_len [B] int32
+ * Same counters and accept test as spec_verify: position i is accepted iff
+ * log(u_acc(b,i)) < (double)lp - (double)lq (IEEE: NaN rejects). No extra
+ * token is drawn (there is no distribution to draw from) and no greedy mode.
+ */
+int spec_accept_logprobs(spec_verify_ctx *ctx, const float *logprobs, uint64_t seed,
+                         uint64_t offset, int32_t *out_accept_len);
+
+/*
+ * Test hook: copy the row log-normalisers of the last spec_verify call into
+ * out_lse [B, 2G+1] float64 (device): draft rows 0..G-1, then target rows
+ * 0..G. Rows not computed (greedy or rejected sequences) are NaN. Enqueued
+ * on the context's stream.
+ */
+int spec_verify_copy_lse(spec_verify_ctx *ctx, double *out_lse);
+
+/*
+ * Test hook: the raw Philox words the kernels use, out_words [B, G+1, 4]
+ * uint32 (device), for (seed, offset). Enqueued on the context's stream.
+ */
+int spec_verify_philox_words(spec_verify_ctx *ctx, uint64_t seed, uint64_t offset,
+                             uint32_t *out_words);
+
+/*
+ * Per-kernel timing. spec_verify_enable_timing(ctx, n) makes each following
+ * spec_verify call record HIP events around its three kernels, on the
+ * context's stream, into a ring of n slots (n = 0 turns it off).
+ * spec_verify_read_timing waits for the recorded calls, writes up to
+ * max_calls rows of three durations in milliseconds (row normalisers,
+ * accept, residual) into out_ms (HOST memory, [max_calls, 3]), returns the
+ * number of rows written (or a negative status) and empties the ring.
+ */
+int spec_verify_enable_timing(spec_verify_ctx *ctx, int max_calls);
+int spec_verify_read_timing(spec_verify_ctx *ctx, float *out_ms, int max_calls);
+
+/* Launch geometry chosen at init: vocabulary splits of the row-normaliser and
+ * residual kernels, and threads per workgroup. Host memory out[3]. */
+int spec_verify_get_geometry(spec_verify_ctx *ctx, int *out);
+
+/* Free the workspace and the context (waits for the context's stream). */
+int spec_verify_destroy(spec_verify_ctx *ctx);
+
+/* A static description of a status code. */
+const char *spec_verify_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

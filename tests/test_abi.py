@@ -1,0 +1,78 @@
+"""The C ABI library without a GPU: it loads, exports every function that
+include/spec_verify.h declares, and rejects bad arguments on the host before
+touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import device_draft_verification_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w \*]*?\b(spec_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.LIB_PATH):
+        pytest.fail("libspecverify.so is not built (run __graft_entry__.build())")
+    return sv.load_library()
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("spec_verify_init", "spec_verify", "spec_accept_logprobs", "spec_verify_destroy"):
+        assert n in names
+    assert set(names) == set(sv.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_is_built_for_gfx950():
+    data = open(sv.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_strerror(lib):
+    assert sv.spec_verify_strerror(0) == "ok"
+    assert sv.spec_verify_strerror(-1) == "invalid argument"
+    assert sv.spec_verify_strerror(-77) == "unknown status"
+
+
+def test_host_argument_checks(lib):
+    h = ctypes.c_void_p()
+    assert lib.spec_verify_init(4, 2, 100, 7, None, ctypes.byref(h)) == sv.binding.SPEC_EINVAL
+    assert not h.value
+    assert lib.spec_verify_init(-1, 2, 100, 1, None, ctypes.byref(h)) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify_init(4, -1, 100, 1, None, ctypes.byref(h)) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify_init(4, 2, 0, 1, None, ctypes.byref(h)) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify_init(4, 2, 10, 1, None, None) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify(None, None, None, None, None, 0, 0, None, None) == sv.binding.SPEC_EINVAL
+    assert lib.spec_accept_logprobs(None, None, 0, 0, None) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify_copy_lse(None, None) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify_destroy(None) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify_enable_timing(None, 4) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify_get_geometry(None, None) == sv.binding.SPEC_EINVAL
+
+
+def test_binding_refuses_missing_library(tmp_path, lib):
+    saved = sv.binding._lib
+    sv.binding._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            sv.binding.load_library(str(tmp_path / "missing.so"))
+    finally:
+        sv.binding._lib = saved

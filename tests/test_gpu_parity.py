@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Sizes: the five workloads at full size (oracle on all sequences for the two
+small ones, on a seeded sample of sequences for the three large ones, in the
+same launch configuration the benchmark times), plus small cases that span
+several vocabulary splits and a ragged tail, and the edge cases of the method.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import device_draft_verification_amd as sv
+import oracle
+import specgen
+from gpu_helpers import assert_parity, compare, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _oracle(d, rows=None, seed=0, offset=0):
+    if rows is None:
+        return oracle.verify(d["logits_draft"], d["logits_target"], d["draft_tokens"],
+                             d["temperature"], seed=seed, offset=offset, seq_ids=d["seq_ids"])
+    rows = np.asarray(rows)
+    return oracle.verify(np.ascontiguousarray(d["logits_draft"][rows]),
+                         np.ascontiguousarray(d["logits_target"][rows]),
+                         np.ascontiguousarray(d["draft_tokens"][rows]),
+                         d["temperature"][rows], seed=seed, offset=offset,
+                         seq_ids=d["seq_ids"][rows])
+
+
+def _report(label, rep):
+    print(f"\n[{label}] n={rep['n']} exact={rep['exact']} flagged_accept={rep['flagged_accept']} "
+          f"flagged_resample={rep['flagged_resample']} fails={len(rep['fails'])} "
+          f"lse_max_abs={rep['lse_max_abs']:.3g} lse_max_rel={rep['lse_max_rel']:.3g}", flush=True)
+
+
+# ------------------------------------------------------------------ Philox --
+
+@pytest.mark.parametrize("seed,offset", [(0, 0), (1, 7), (2**64 - 1, 2**63 + 5), (0xDEADBEEF, 2**32)])
+def test_philox_words_bitwise(seed, offset):
+    B, G = 37, 6
+    ctx = sv.spec_verify_init(B, G, 64, torch.float32)
+    out = torch.empty((B, G + 1, 4), dtype=torch.int32, device="cuda")
+    sv.spec_verify_philox_words(ctx, seed, offset, out)
+    got = out.cpu().numpy().view(np.uint32)
+    for b in range(B):
+        for i in range(G + 1):
+            assert np.array_equal(got[b, i], oracle.philox_words(seed, offset, b, i)), (b, i)
+
+
+# ------------------------------------------------- full-size small configs --
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_small_config_full_parity(cfg):
+    d = specgen.generate(specgen.config(cfg))
+    gpu = run_gpu(to_device(d))
+    ref = _oracle(d)
+    rep = compare(gpu, ref, d["temperature"])
+    _report(f"config {cfg}", rep)
+    assert_parity(rep, f"config {cfg}")
+
+
+# --------------------------------------- splits, ragged tails, odd shapes --
+
+CASES = [
+    # (config recipe, overrides)
+    (4, dict(batch=12, vocab=20008)),             # 16-byte groups, ragged last split
+    (4, dict(batch=12, vocab=20011)),             # V % 8 != 0: element path
+    (1, dict(batch=6, vocab=10003)),              # fp32 element path
+    (1, dict(batch=6, vocab=12000, gamma=3)),     # fp32 16-byte groups
+    (2, dict(batch=3, vocab=700, gamma=70)),      # more positions than one wavefront
+    (2, dict(batch=5, vocab=4096, gamma=0)),      # bonus draw only
+    (3, dict(batch=4, vocab=33000)),              # Zipf rows
+    (5, dict(batch=9, vocab=257)),                # tiny vocabulary
+    (2, dict(batch=2, vocab=1)),                  # V = 1
+    (2, dict(batch=2, vocab=5)),                  # V < 8
+]
+
+
+@pytest.mark.parametrize("cfg,over", CASES)
+def test_small_shapes_parity(cfg, over):
+    rec = specgen.config(cfg).replace(**over)
+    d = specgen.generate(rec)
+    for seed, offset in [(0, 0), (12345, 3)]:
+        gpu = run_gpu(to_device(d), seed=seed, offset=offset)
+        ref = _oracle(d, seed=seed, offset=offset)
+        rep = compare(gpu, ref, d["temperature"])
+        _report(f"{rec.name} {over}", rep)
+        assert_parity(rep, str(over))
+
+
+# ------------------------------------------- full-size large configs, sampled --
+
+@pytest.fixture(scope="module", params=[3, 4, 5])
+def big(request):
+    cfg = request.param
+    rec = specgen.config(cfg)
+    d = specgen.generate(rec)
+    t = to_device(d)
+    gpu = run_gpu(t, seed=0, offset=0)
+    yield cfg, rec, d, t, gpu
+    del t
+    torch.cuda.empty_cache()
+
+
+def _sample_rows(rec, d, n=14):
+    rng = np.random.default_rng(1000 + rec.seed)
+    rows = set(rng.choice(rec.batch, size=min(n, rec.batch), replace=False).tolist())
+    greedy = np.nonzero(d["temperature"] == 0)[0]
+    rows.update(greedy[:3].tolist())
+    rows.update([0, rec.batch - 1])
+    return np.array(sorted(rows))
+
+
+def test_large_config_sampled_parity(big):
+    cfg, rec, d, t, gpu = big
+    rows = _sample_rows(rec, d)
+    ref = _oracle(d, rows=rows)
+    rep = compare(gpu, ref, d["temperature"][rows], rows=rows)
+    _report(f"config {cfg} sampled", rep)
+    assert_parity(rep, f"config {cfg}")
+
+
+def test_large_config_invariants(big):
+    """Properties that hold for every sequence, checked on all of them."""
+    cfg, rec, d, t, gpu = big
+    k = gpu["accept_len"]
+    toks = gpu["tokens"]
+    G, V = rec.gamma, rec.vocab
+    assert np.all((k >= 0) & (k <= G))
+    for b in range(rec.batch):
+        kb = k[b]
+        assert np.array_equal(toks[b, :kb], d["draft_tokens"][b, :kb])
+        assert 0 <= toks[b, kb] < V
+        assert np.all(toks[b, kb + 1:] == -1)
+    lse = gpu["lse"]
+    sampled = d["temperature"] > 0
+    assert np.all(np.isfinite(lse[sampled]))
+    assert np.all(np.isnan(lse[~sampled]))
+
+
+def test_large_config_deterministic(big):
+    cfg, rec, d, t, gpu = big
+    again = run_gpu(t, seed=0, offset=0)
+    assert np.array_equal(again["accept_len"], gpu["accept_len"])
+    assert np.array_equal(again["tokens"], gpu["tokens"])
+    assert np.array_equal(again["lse"].view(np.uint64), gpu["lse"].view(np.uint64))
+
+
+def test_config5_scalar_mode():
+    """Scalar-only mode on the oracle's gathered log-probabilities of the
+    B=512, gamma=4, V=201088 workload, rounded to fp32: [512, 4, 2]."""
+    rec = specgen.config(5)
+    d = specgen.generate(rec)
+    pairs = oracle.gather_logprobs(d["logits_draft"], d["logits_target"], d["draft_tokens"],
+                                   d["temperature"]).astype(np.float32)
+    ref = oracle.accept_logprobs(pairs, seed=0, offset=0)
+    ctx = sv.spec_verify_init(rec.batch, rec.gamma, rec.vocab, torch.bfloat16)
+    lp = torch.from_numpy(pairs).cuda()
+    out = torch.full((rec.batch,), -7, dtype=torch.int32, device="cuda")
+    sv.spec_accept_logprobs(ctx, lp, 0, 0, out)
+    got = out.cpu().numpy()
+    diff = np.nonzero(got != ref["accept_len"])[0]
+    for b in diff:
+        k = min(got[b], ref["accept_len"][b])
+        assert np.min(np.abs(ref["acc_margin"][b, :k + 1])) < 1e-5, b
+    print(f"\n[config 5 scalar] mismatched-but-flagged={len(diff)} of {rec.batch}", flush=True)
+    # cross-mode: the full call decides the same lengths, up to flagged decisions
+    full = run_gpu(to_device(d), with_lse=False)
+    cross = np.nonzero(full["accept_len"] != got)[0]
+    for b in cross:
+        k = min(got[b], full["accept_len"][b])
+        assert np.min(np.abs(ref["acc_margin"][b, :k + 1])) < 1e-5, b
+
+
+# ------------------------------------------------------------- edge cases --
+
+def test_sentinel_sequences():
+    rng = np.random.default_rng(8)
+    B, G, V = 7, 3, 640
+    zq = rng.normal(0, 1, size=(B, G, V)).astype(np.float32)
+    zp = rng.normal(0, 1, size=(B, G + 1, V)).astype(np.float32)
+    toks = rng.integers(0, V, size=(B, G)).astype(np.int32)
+    temp = np.array([1.0, np.nan, -0.5, np.inf, 1.0, 1.0, 0.0], np.float32)
+    toks[4, 1] = V
+    zp[5, 2, :] = -np.inf
+    zp[6, 0, :] = -np.inf  # greedy sequence with an empty target row
+    d = dict(logits_draft=zq, logits_target=zp, draft_tokens=toks, temperature=temp,
+             seq_ids=np.arange(B))
+    gpu = run_gpu(to_device(d))
+    ref = _oracle(d)
+    assert np.array_equal(gpu["accept_len"], ref["accept_len"])
+    assert np.array_equal(gpu["tokens"], ref["tokens"])
+    assert list(gpu["accept_len"][1:]) == [-1] * 6
+
+
+def test_identical_rows_accept_all_and_bonus():
+    rng = np.random.default_rng(4)
+    B, G, V = 64, 5, 3000
+    base = rng.normal(0, 2.0, size=(G + 1, V)).astype(np.float32)
+    zp = np.ascontiguousarray(np.broadcast_to(base, (B, G + 1, V)))
+    zq = np.ascontiguousarray(zp[:, :G])
+    r2 = np.random.default_rng(5)
+    toks = np.stack([specgen.gumbel_max_tokens(base[:G], 0.8, r2) for _ in range(B)])
+    d = dict(logits_draft=zq, logits_target=zp, draft_tokens=toks,
+             temperature=np.full(B, 0.8, np.float32), seq_ids=np.arange(B))
+    gpu = run_gpu(to_device(d))
+    assert np.all(gpu["accept_len"] == G)
+    rep = compare(gpu, _oracle(d), d["temperature"])
+    assert_parity(rep, "p == q")
+
+
+def test_disjoint_support_rejects_all():
+    G, V, B = 2, 64, 200
+    rng = np.random.default_rng(5)
+    zq = np.full((G, V), -np.inf, np.float32)
+    zp = np.full((G + 1, V), -np.inf, np.float32)
+    zq[:, :32] = rng.normal(0, 1, size=(G, 32))
+    zp[:, 32:] = rng.normal(0, 1, size=(G + 1, 32))
+    r2 = np.random.default_rng(6)
+    toks = np.stack([specgen.gumbel_max_tokens(zq, 1.0, r2) for _ in range(B)])
+    d = dict(logits_draft=np.ascontiguousarray(np.broadcast_to(zq, (B, G, V))),
+             logits_target=np.ascontiguousarray(np.broadcast_to(zp, (B, G + 1, V))),
+             draft_tokens=toks, temperature=np.ones(B, np.float32), seq_ids=np.arange(B))
+    gpu = run_gpu(to_device(d))
+    assert np.all(gpu["accept_len"] == 0)
+    assert np.all(gpu["tokens"][:, 0] >= 32)
+    assert_parity(compare(gpu, _oracle(d), d["temperature"]), "disjoint")
+
+
+def test_greedy_ties_lowest_index():
+    rng = np.random.default_rng(6)
+    B, G, V = 32, 4, 2048
+    zp = rng.integers(-4, 5, size=(B, G + 1, V)).astype(np.float32)  # many exact ties
+    zq = rng.normal(0, 1, size=(B, G, V)).astype(np.float32)
+    amax = np.argmax(zp, axis=-1)
+    toks = amax[:, :G].astype(np.int32).copy()
+    flip = rng.random((B, G)) < 0.3
+    toks[flip] = (toks[flip] + 1) % V
+    d = dict(logits_draft=zq, logits_target=zp, draft_tokens=toks,
+             temperature=np.zeros(B, np.float32), seq_ids=np.arange(B))
+    gpu = run_gpu(to_device(d))
+    ref = _oracle(d)
+    assert np.array_equal(gpu["accept_len"], ref["accept_len"])
+    assert np.array_equal(gpu["tokens"], ref["tokens"])
+
+
+def test_statistical_gate_on_gpu():
+    """The CI gate (10,000 draws, V = 8, chi-square at 0.01) on the GPU's own
+    output, plus parity of every draw with the oracle."""
+    from scipy.special import softmax
+    from scipy.stats import chisquare
+    rng = np.random.default_rng(1234)
+    G, V, N, T = 3, 8, 10_000, 0.9
+    base = rng.normal(0, 1.2, size=(G + 1, V))
+    zp = (base + rng.normal(0, 0.8, size=base.shape)).astype(np.float32)
+    zq = base[:G].astype(np.float32)
+    r2 = np.random.default_rng(99)
+    toks = np.stack([specgen.gumbel_max_tokens(zq, T, r2) for _ in range(N)])
+    d = dict(logits_draft=np.ascontiguousarray(np.broadcast_to(zq, (N, G, V))),
+             logits_target=np.ascontiguousarray(np.broadcast_to(zp, (N, G + 1, V))),
+             draft_tokens=toks, temperature=np.full(N, T, np.float32), seq_ids=np.arange(N))
+    gpu = run_gpu(to_device(d), seed=2024, offset=7)
+    rep = compare(gpu, _oracle(d, seed=2024, offset=7), d["temperature"])
+    _report("V=8 gate", rep)
+    assert_parity(rep, "gate")
+    inv_t = np.float32(1.0) / np.float32(T)
+    p = softmax((zp * inv_t).astype(np.float64), axis=-1)
+    first = gpu["tokens"][:, 0]
+    assert chisquare(np.bincount(first, minlength=V), p[0] * N).pvalue > 0.01
+
+
+def test_runs_on_a_side_stream_and_times_kernels():
+    rec = specgen.config(2).replace(batch=8, vocab=32000)
+    d = specgen.generate(rec)
+    t = to_device(d)
+    s = torch.cuda.Stream()
+    ctx = sv.spec_verify_init(rec.batch, rec.gamma, rec.vocab, torch.bfloat16, stream=s)
+    sv.spec_verify_enable_timing(ctx, 8)
+    alen = torch.empty(rec.batch, dtype=torch.int32, device="cuda")
+    toks = torch.empty(rec.batch, rec.gamma + 1, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(s):
+        for i in range(3):
+            sv.spec_verify(ctx, t["logits_draft"], t["logits_target"], t["draft_tokens"],
+                           t["temperature"], 0, 0, alen, toks)
+    times = sv.spec_verify_read_timing(ctx, 8)
+    assert len(times) == 3
+    assert all(x > 0 for row in times for x in row)
+    s.synchronize()
+    ref = _oracle(d)
+    gpu = dict(accept_len=alen.cpu().numpy(), tokens=toks.cpu().numpy())
+    assert_parity(compare(gpu, ref, d["temperature"], check_lse=False), "side stream")
+    geo = sv.spec_verify_get_geometry(ctx)
+    assert geo["block"] == 256 and geo["row_splits"] >= 1
+
+
+def test_argument_errors_on_device():
+    ctx = sv.spec_verify_init(4, 2, 100, torch.float32)
+    lib = sv.load_library()
+    ok = torch.zeros((4, 3, 100), device="cuda")
+    alen = torch.zeros(4, dtype=torch.int32, device="cuda")
+    assert lib.spec_verify(ctx.handle, None, ok.data_ptr(), None, None, 0, 0,
+                           alen.data_ptr(), alen.data_ptr()) == sv.binding.SPEC_EINVAL
+    with pytest.raises(ValueError):
+        sv.spec_verify(ctx, ok, ok, alen, alen, 0, 0, alen, alen)
+    with pytest.raises(sv.SpecVerifyError):
+        sv.spec_verify_copy_lse(ctx, torch.empty((4, 5), dtype=torch.float64, device="cuda"))
