@@ -68,42 +68,73 @@ __global__ __launch_bounds__(64) void accept_kernel(
     float inv_t = 0.0f;
     const int mode = temperature_mode(temperature[b], &inv_t);
     bool bad = mode < 0;
-
-    // Pass 1: validate the draft tokens, merge the splits of every used row.
-    // Lane l handles positions i = l, l + 64, ...: draft row i and target row
-    // G + i, and is the only lane that ever touches those rows' entries of
-    // rn and lse_out in this kernel.
     const double nan = __builtin_nan("");
+
+    // One pass over the positions, 64 at a time. Lane l handles position
+    // i = i0 + l: it validates draft token t_i, merges the splits of draft row
+    // i and target row i, gathers x_q[i][t_i] and x_p[i][t_i] (only for a valid
+    // token) and decides acceptance. Lane l is the only lane that touches the
+    // entries of rows i and G + i in rn and lse_out. Decisions made for a
+    // sequence that turns out to be invalid are discarded below.
+    int k = G;
     for (int i0 = 0; i0 <= G; i0 += 64) {
         const int i = i0 + lane;
-        if (i < G) {
-            const int t = tokens[static_cast<size_t>(b) * G + i];
-            if (t < 0 || t >= vocab)
+        const bool has_draft = i < G;
+        const bool has_target = i <= G;
+        int t = 0;
+        bool t_ok = false;
+        if (has_draft) {
+            t = tokens[static_cast<size_t>(b) * G + i];
+            t_ok = t >= 0 && t < vocab;
+            if (!t_ok)
                 bad = true;
         }
-        if (i > G)
-            continue;
-        RowNorm r;
-        if (mode == 1) {
-            if (i < G) {
-                if (!merge_sampled(part + (row0 + i) * nsplit, nsplit, &r))
-                    bad = true;
-                rn[row0 + i] = r;
-                lse_out[row0 + i] = lse_of(r);
+        bool reject = false;
+        if (mode == 1 && has_target) {
+            // gathers first: their latency overlaps the split merges
+            float zq = 0.0f, zp = 0.0f;
+            if (t_ok) {
+                zq = load_logit(row_ptr(draft, DT, static_cast<size_t>(b) * G + i, vocab), DT, t);
+                zp = load_logit(row_ptr(target, DT, static_cast<size_t>(b) * (G + 1) + i, vocab), DT, t);
             }
-            if (!merge_sampled(part + (row0 + G + i) * nsplit, nsplit, &r))
+            RowNorm rq{}, rp;
+            if (has_draft) {
+                if (!merge_sampled(part + (row0 + i) * nsplit, nsplit, &rq))
+                    bad = true;
+                rn[row0 + i] = rq;
+            }
+            if (!merge_sampled(part + (row0 + G + i) * nsplit, nsplit, &rp))
                 bad = true;
-            rn[row0 + G + i] = r;
-            lse_out[row0 + G + i] = lse_of(r);
-        } else {
-            if (mode == 0 && !merge_greedy(part + (row0 + G + i) * nsplit, nsplit, &r))
+            rn[row0 + G + i] = rp;
+            const double lse_p = lse_of(rp);
+            lse_out[row0 + G + i] = lse_p;
+            if (has_draft) {
+                const double lse_q = lse_of(rq);
+                lse_out[row0 + i] = lse_q;
+                const double lq = static_cast<double>(scale_logit(zq, inv_t)) - lse_q;
+                const double lp = static_cast<double>(scale_logit(zp, inv_t)) - lse_p;
+                const Words4 w = verify_block(seed, offset, static_cast<uint32_t>(b), static_cast<uint32_t>(i));
+                const double log_u = log(static_cast<double>(uniform24(w.w0)));
+                reject = !(log_u < lp - lq);
+            }
+        } else if (mode == 0 && has_target) {
+            RowNorm rp;
+            if (!merge_greedy(part + (row0 + G + i) * nsplit, nsplit, &rp))
                 bad = true;
-            if (mode == 0)
-                rn[row0 + G + i] = r;
-            if (i < G)
+            rn[row0 + G + i] = rp;
+            if (has_draft) {
+                lse_out[row0 + i] = nan;
+                reject = t != rp.idx;
+            }
+            lse_out[row0 + G + i] = nan;
+        } else if (has_target) {
+            if (has_draft)
                 lse_out[row0 + i] = nan;
             lse_out[row0 + G + i] = nan;
         }
+        const unsigned long long mask = __ballot(reject);
+        if (mask && k == G)
+            k = i0 + __ffsll(static_cast<long long>(mask)) - 1;
     }
     bad = __ballot(bad) != 0ull;
 
@@ -121,39 +152,9 @@ __global__ __launch_bounds__(64) void accept_kernel(
         return;
     }
 
-    // Pass 2: accept test per position, first rejection by ballot.
-    int k = G;
-    for (int i0 = 0; i0 < G; i0 += 64) {
-        const int i = i0 + lane;
-        bool reject = false;
-        if (i < G) {
-            const int t = tokens[static_cast<size_t>(b) * G + i];
-            const RowNorm np = rn[row0 + G + i];
-            if (mode == 0) {
-                reject = t != np.idx;
-            } else {
-                const RowNorm nq = rn[row0 + i];
-                const float xq = scale_logit(
-                    load_logit(row_ptr(draft, DT, static_cast<size_t>(b) * G + i, vocab), DT, t), inv_t);
-                const float xp = scale_logit(
-                    load_logit(row_ptr(target, DT, static_cast<size_t>(b) * (G + 1) + i, vocab), DT, t),
-                    inv_t);
-                const double lq = static_cast<double>(xq) - lse_of(nq);
-                const double lp = static_cast<double>(xp) - lse_of(np);
-                const Words4 w = verify_block(seed, offset, static_cast<uint32_t>(b), static_cast<uint32_t>(i));
-                const double log_u = log(static_cast<double>(uniform24(w.w0)));
-                reject = !(log_u < lp - lq);
-            }
-        }
-        const unsigned long long mask = __ballot(reject);
-        if (mask) {
-            k = i0 + __ffsll(static_cast<long long>(mask)) - 1;
-            break;
-        }
-    }
-
     // Emit: accepted prefix, the greedy extra token, padding. The residual
-    // kernel writes the extra token of sampled sequences.
+    // kernels write the extra token of sampled sequences. Lane l reads back
+    // only rows it wrote itself.
     for (int i = lane; i <= G; i += 64) {
         int v = -1;
         if (i < k)

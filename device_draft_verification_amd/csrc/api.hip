@@ -20,6 +20,8 @@ struct spec_verify_ctx {
     hipStream_t stream = nullptr;
     int device = 0;
     int nsplit_rows = 1;      // vocabulary splits of the row-normaliser kernel
+    int row_unroll = 4;       // 16-byte groups in flight per thread in that kernel
+    bool row_nontemporal = true;
     int nsplit_residual = 1;  // vocabulary splits of the residual kernel
 
     void* ws = nullptr;
@@ -27,8 +29,7 @@ struct spec_verify_ctx {
     RowNorm* rn = nullptr;
     double* lse = nullptr;
     SeqState* seq = nullptr;
-    double* chunk_sums = nullptr;
-    int* tickets = nullptr;
+    float* tile_sums = nullptr;
     bool have_verified = false;
 
     int timing_slots = 0;
@@ -38,9 +39,11 @@ struct spec_verify_ctx {
 
 namespace {
 
-// Workgroups that keep every CU of an MI355X busy with a few to spare
-// (256 CUs; several resident workgroups each).
-constexpr long kTargetBlocks = 4096;
+// Workgroup counts per launch: the row kernel wants several waves of
+// workgroups over the 256 CUs so the last wave is short; the residual kernel's
+// workgroups are short-lived, so fewer, longer ones.
+constexpr long kRowTargetBlocks = 16384;
+constexpr long kResidualTargetBlocks = 4096;
 
 int env_int(const char* name, int fallback) {
     const char* v = std::getenv(name);
@@ -53,14 +56,14 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int group_width(int dtype) { return dtype == SPEC_BF16 ? 8 : 4; }
 
-// Splits per row: enough workgroups in total, at least one 16-byte group per
-// thread per split, at most kMaxSplit.
-int choose_split(long rows, long vocab, int dtype) {
+// Splits per row: about target_blocks workgroups in total, at least
+// min_groups 16-byte groups per split, at most kMaxSplit.
+int choose_split(long rows, long vocab, int dtype, long target_blocks, long min_groups) {
     if (rows <= 0)
         return 1;
     const long groups = vocab / group_width(dtype);
-    long n = (kTargetBlocks + rows - 1) / rows;
-    const long by_size = std::max(1L, groups / kBlock);
+    long n = (target_blocks + rows - 1) / rows;
+    const long by_size = std::max(1L, groups / min_groups);
     n = std::min(n, by_size);
     n = std::max(1L, std::min(n, static_cast<long>(kMaxSplit)));
     return static_cast<int>(n);
@@ -103,13 +106,17 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
         delete ctx;
         return SPEC_EHIP;
     }
-    ctx->nsplit_rows = choose_split(rows, vocab, dtype);
-    ctx->nsplit_residual = choose_split(batch, vocab, dtype);
+    ctx->nsplit_rows = choose_split(rows, vocab, dtype, kRowTargetBlocks, 4L * kBlock);
+    ctx->nsplit_residual = choose_split(batch, vocab, dtype, kResidualTargetBlocks, 16L * 64);
     const int o1 = env_int("SPEC_VERIFY_ROW_SPLIT", 0), o3 = env_int("SPEC_VERIFY_RESIDUAL_SPLIT", 0);
     if (o1 > 0)
         ctx->nsplit_rows = std::min(o1, kMaxSplit);
     if (o3 > 0)
         ctx->nsplit_residual = std::min(o3, kMaxSplit);
+    const int ou = env_int("SPEC_VERIFY_ROW_UNROLL", 0);
+    if (ou == 2 || ou == 4 || ou == 8)
+        ctx->row_unroll = ou;
+    ctx->row_nontemporal = env_int("SPEC_VERIFY_ROW_NT", ctx->row_nontemporal ? 1 : 0) != 0;
     // A dispatch holds fewer than 2^32 work-items.
     const long long limit = 1LL << 32;
     if (static_cast<long long>(rows) * ctx->nsplit_rows * kBlock >= limit ||
@@ -125,8 +132,7 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     const size_t o_rn = off;   off = align_up(off + rows * sizeof(RowNorm), 256);
     const size_t o_lse = off;  off = align_up(off + rows * sizeof(double), 256);
     const size_t o_seq = off;  off = align_up(off + static_cast<size_t>(batch) * sizeof(SeqState), 256);
-    const size_t o_cs = off;   off = align_up(off + static_cast<size_t>(batch) * ctx->nsplit_residual * sizeof(double), 256);
-    const size_t o_tk = off;   off = align_up(off + static_cast<size_t>(batch) * sizeof(int), 256);
+    const size_t o_ts = off;   off = align_up(off + static_cast<size_t>(batch) * residual_tiles_per_row(vocab) * sizeof(float), 256);
     const size_t total = std::max<size_t>(off, 256);
     if (hipMalloc(&ctx->ws, total) != hipSuccess) {
         delete ctx;
@@ -137,9 +143,8 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     ctx->rn = reinterpret_cast<RowNorm*>(base + o_rn);
     ctx->lse = reinterpret_cast<double*>(base + o_lse);
     ctx->seq = reinterpret_cast<SeqState*>(base + o_seq);
-    ctx->chunk_sums = reinterpret_cast<double*>(base + o_cs);
-    ctx->tickets = reinterpret_cast<int*>(base + o_tk);
-    // Tickets must start at zero; the residual kernel returns them to zero.
+    ctx->tile_sums = reinterpret_cast<float*>(base + o_ts);
+    // Defined contents before the first call (every entry is rewritten by it).
     if (hipMemset(ctx->ws, 0, total) != hipSuccess) {
         (void)hipFree(ctx->ws);
         delete ctx;
@@ -188,8 +193,9 @@ int spec_verify(spec_verify_ctx* ctx, const void* logits_draft, const void* logi
     hipStream_t st = ctx->stream;
     if (ev && hipEventRecord(ev[0], st) != hipSuccess)
         return SPEC_EHIP;
-    if (launch_row_norm(s, vec, ctx->nsplit_rows, logits_draft, logits_target, temperature,
-                        ctx->part, st) != hipSuccess)
+    const RowTuning tu{ctx->nsplit_rows, ctx->row_unroll, ctx->row_nontemporal};
+    if (launch_row_norm(s, vec, tu, logits_draft, logits_target, temperature, ctx->part, st) !=
+        hipSuccess)
         return SPEC_EHIP;
     if (ev && hipEventRecord(ev[1], st) != hipSuccess)
         return SPEC_EHIP;
@@ -200,8 +206,7 @@ int spec_verify(spec_verify_ctx* ctx, const void* logits_draft, const void* logi
     if (ev && hipEventRecord(ev[2], st) != hipSuccess)
         return SPEC_EHIP;
     if (launch_residual(s, vec, ctx->nsplit_residual, logits_draft, logits_target, temperature,
-                        ctx->seq, ctx->rn, ctx->chunk_sums, ctx->tickets, out_tokens,
-                        st) != hipSuccess)
+                        ctx->seq, ctx->rn, ctx->tile_sums, out_tokens, st) != hipSuccess)
         return SPEC_EHIP;
     if (ev && hipEventRecord(ev[3], st) != hipSuccess)
         return SPEC_EHIP;

@@ -61,6 +61,25 @@ struct Loader {
         return reinterpret_cast<const raw_t*>(row)[g];
     }
 
+    // Streaming load: marked non-temporal so it does not displace reusable lines.
+    __device__ static inline raw_t load_nt(const void* row, long g) {
+        if constexpr (VEC) {
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + g);
+            return make_uint4(v.x, v.y, v.z, v.w);
+        } else {
+            return __builtin_nontemporal_load(reinterpret_cast<const raw_t*>(row) + g);
+        }
+    }
+
+    template <bool NT>
+    __device__ static inline raw_t load_as(const void* row, long g) {
+        if constexpr (NT)
+            return load_nt(row, g);
+        else
+            return load(row, g);
+    }
+
     __device__ static inline void unpack(const raw_t& q, float (&z)[W]) {
         if constexpr (VEC) {
             if constexpr (DT == kBF16) {

@@ -27,8 +27,15 @@ struct Shape {
     int batch, gamma, vocab, dtype;
 };
 
+// Launch geometry of the row-normaliser kernel.
+struct RowTuning {
+    int nsplit;        // vocabulary splits per row
+    int unroll;        // 16-byte groups in flight per thread: 2, 4 or 8
+    bool nontemporal;  // streaming loads marked non-temporal
+};
+
 // Row normalisers: grid = B * (2G+1) * nsplit workgroups of kBlock threads.
-hipError_t launch_row_norm(const Shape& s, bool vec, int nsplit, const void* draft,
+hipError_t launch_row_norm(const Shape& s, bool vec, const RowTuning& tu, const void* draft,
                            const void* target, const float* temperature, Partial* part,
                            hipStream_t stream);
 
@@ -39,11 +46,14 @@ hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const vo
                          uint64_t offset, const Partial* part, RowNorm* rn, double* lse_out,
                          SeqState* seq, int32_t* out_len, int32_t* out_tok, hipStream_t stream);
 
-// Residual / bonus draw at the first rejection: grid = B * nsplit workgroups.
+// Residual / bonus draw at the first rejection: per-tile sums (B * nsplit
+// workgroups), then one locating wavefront per sequence. tile_sums holds
+// B * residual_tiles_per_row(vocab) floats.
+int residual_tiles_per_row(int vocab);
 hipError_t launch_residual(const Shape& s, bool vec, int nsplit, const void* draft,
                            const void* target, const float* temperature, const SeqState* seq,
-                           const RowNorm* rn, double* chunk_sums, int* tickets,
-                           int32_t* out_tok, hipStream_t stream);
+                           const RowNorm* rn, float* tile_sums, int32_t* out_tok,
+                           hipStream_t stream);
 
 // Scalar-only accept on gathered log-probability pairs.
 hipError_t launch_accept_scalar(int batch, int gamma, const float* logprobs, uint64_t seed,

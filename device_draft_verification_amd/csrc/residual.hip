@@ -1,4 +1,4 @@
-// Residual / bonus kernel: draws the extra token of every sampled sequence.
+// Residual / bonus kernels: draw the extra token of every sampled sequence.
 //
 // At the first rejected position k < G the token comes from the residual
 // r_v = max(0, p_k(v) - q_k(v)); when all G drafts were kept it is the bonus
@@ -8,281 +8,400 @@
 // vocabulary order: the token is the first v whose inclusive prefix exceeds
 // u_res * S, S = sum_v r_v.
 //
-// Work layout: grid = B * nsplit workgroups; workgroup (b, c) streams split c
-// of the one or two rows of sequence b and publishes the split's sum of r.
-// An agent-scope ticket elects the last workgroup of the sequence, which scans
-// the split sums in order, finds the split holding u_res * S and re-reads only
-// that split, in index order, to find the token. Atomics choose who finishes,
-// never the order of any sum, so the result is bitwise reproducible.
+// Work layout. The vocabulary of a row is cut into tiles of 64 groups (a group
+// is one 16-byte load: 8 bf16 or 4 fp32 logits; one logit on the element path).
+//   residual_tiles: grid = B * nsplit workgroups of four wavefronts; each
+//     wavefront streams whole tiles (lane l reads group 64*t + l of both rows,
+//     so one load instruction covers 1 KiB of consecutive memory), and stores
+//     one fp32 sum per tile: the groups' pairwise fp32 sums reduced by a fixed
+//     xor butterfly.
+//   residual_locate: one wavefront per sequence prefix-sums the tile sums in
+//     fp64, finds the tile holding u_res * S, recomputes that tile's group sums
+//     with the same arithmetic, scans them in fp64 to find the group and walks
+//     the group's elements to find the token.
+// The kernel boundary makes the tile sums visible to every XCD; all sums have
+// a fixed order, so the result is bitwise reproducible.
 //
 // p and q are recomputed from the row normalisers of the row kernel:
 // p_v = 2^(fma(x_v, log2e, -m)) / s, which sums to one under the same
-// normaliser the accept test used. r is formed in fp32 and accumulated in fp64.
+// normaliser the accept test used.
 #include "launch.hpp"
 
 namespace specv {
 namespace {
 
+constexpr int kTile = 64;  // groups per tile = lanes per wavefront
+
 struct RowCoef {
-    float m;     // base-2 reference of the row
-    float inv_s; // 1 / s
+    float m;      // base-2 reference of the row
+    float inv_s;  // 1 / s
 };
 
-template <int DT, bool VEC>
-__device__ inline void residual_group(const void* prow, const void* qrow, bool p_only,
-                                      float inv_t, RowCoef cp, RowCoef cq, long g,
-                                      float (&r)[Group<DT, VEC>::W]) {
-    using Ld = Loader<DT, VEC>;
-    constexpr int W = Ld::W;
-    float zp[W];
-    Ld::unpack(Ld::load(prow, g), zp);
-    if (p_only) {
-#pragma unroll
-        for (int e = 0; e < W; ++e)
-            r[e] = fast_exp2(__builtin_fmaf(scale_logit(zp[e], inv_t), kLog2e, -cp.m)) * cp.inv_s;
-        return;
+// The one or two rows of a sequence at its first rejection.
+struct SeqRows {
+    const void* prow;
+    const void* qrow;
+    bool p_only;  // bonus row (or the empty-residual fallback): r = p
+    float inv_t;
+    RowCoef cp, cq;
+};
+
+template <int DT>
+__device__ inline SeqRows seq_rows(const void* draft, const void* target, const float* temperature,
+                                   int G, int vocab, long b, int k, const RowNorm* rn) {
+    SeqRows s;
+    temperature_mode(temperature[b], &s.inv_t);
+    s.p_only = k == G;
+    const size_t row0 = static_cast<size_t>(b) * (2 * G + 1);
+    s.prow = row_ptr(target, DT, static_cast<size_t>(b) * (G + 1) + k, vocab);
+    s.qrow = s.p_only ? s.prow : row_ptr(draft, DT, static_cast<size_t>(b) * G + k, vocab);
+    const RowNorm np = rn[row0 + G + k];
+    s.cp = RowCoef{np.m, static_cast<float>(1.0 / np.s)};
+    s.cq = RowCoef{0.0f, 0.0f};
+    if (!s.p_only) {
+        const RowNorm nq = rn[row0 + k];
+        s.cq = RowCoef{nq.m, static_cast<float>(1.0 / nq.s)};
     }
-    float zq[W];
-    Ld::unpack(Ld::load(qrow, g), zq);
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-        const float p = fast_exp2(__builtin_fmaf(scale_logit(zp[e], inv_t), kLog2e, -cp.m)) * cp.inv_s;
-        const float q = fast_exp2(__builtin_fmaf(scale_logit(zq[e], inv_t), kLog2e, -cq.m)) * cq.inv_s;
-        r[e] = fmaxf(p - q, 0.0f);
-    }
+    return s;
 }
 
-// Sum of r over groups [g0, g1) with a kBlock-strided, U-deep load pattern.
-template <int DT, bool VEC, int U>
-__device__ inline double range_sum(const void* prow, const void* qrow, bool p_only, float inv_t,
-                                   RowCoef cp, RowCoef cq, long g0, long g1, double* lds_d) {
-    constexpr int W = Group<DT, VEC>::W;
-    double acc = 0.0;
-    long g = g0 + threadIdx.x;
-    for (; g + static_cast<long>(U - 1) * kBlock < g1; g += static_cast<long>(U) * kBlock) {
-        float r[U][W];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            residual_group<DT, VEC>(prow, qrow, p_only, inv_t, cp, cq, g + static_cast<long>(u) * kBlock, r[u]);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float t = 0.0f;
+template <int DT, bool VEC, bool NT>
+struct GroupIO {
+    using Ld = Loader<DT, VEC>;
+    static constexpr int W = Ld::W;
+    typename Ld::raw_t p, q;
+
+    __device__ inline void load(const SeqRows& s, long g) {
+        p = Ld::template load_as<NT>(s.prow, g);
+        if (!s.p_only)
+            q = Ld::template load_as<NT>(s.qrow, g);
+    }
+
+    // r of the group's elements, in index order.
+    __device__ inline void residual(const SeqRows& s, float (&r)[W]) const {
+        float zp[W];
+        Ld::unpack(p, zp);
+        if (s.p_only) {
 #pragma unroll
             for (int e = 0; e < W; ++e)
-                t += r[u][e];
-            acc += static_cast<double>(t);
+                r[e] = fast_exp2(__builtin_fmaf(scale_logit(zp[e], s.inv_t), kLog2e, -s.cp.m)) * s.cp.inv_s;
+            return;
+        }
+        float zq[W];
+        Ld::unpack(q, zq);
+#pragma unroll
+        for (int e = 0; e < W; ++e) {
+            const float pv = fast_exp2(__builtin_fmaf(scale_logit(zp[e], s.inv_t), kLog2e, -s.cp.m)) * s.cp.inv_s;
+            const float qv = fast_exp2(__builtin_fmaf(scale_logit(zq[e], s.inv_t), kLog2e, -s.cq.m)) * s.cq.inv_s;
+            r[e] = fmaxf(pv - qv, 0.0f);
         }
     }
-    for (; g < g1; g += kBlock) {
-        float r[W];
-        residual_group<DT, VEC>(prow, qrow, p_only, inv_t, cp, cq, g, r);
-        float t = 0.0f;
-#pragma unroll
-        for (int e = 0; e < W; ++e)
-            t += r[e];
-        acc += static_cast<double>(t);
-    }
-    return block_sum(acc, lds_d);
-}
-
-struct ScanLds {
-    double d[kWaves];
-    int i[kWaves];
-    int result;
 };
 
-// First element v of groups [g0, g1) (index order) at which P + prefix(r)
-// exceeds tau, with r_v > 0. Each thread takes kGpt consecutive groups, the
-// block scans the per-thread sums, and the thread holding the crossing walks
-// its elements. When the range ends first (possible only through rounding at
-// its last edge) returns -2 - (last element with r > 0), which is <= -2.
-template <int DT, bool VEC>
-__device__ int scan_range(const void* prow, const void* qrow, bool p_only, float inv_t,
-                          RowCoef cp, RowCoef cq, long g0, long g1, double P, double tau,
-                          ScanLds& lds) {
-    constexpr int W = Group<DT, VEC>::W;
-    constexpr int kGpt = VEC ? 4 : 16;
-    int last_pos = -1;
-    for (long base = g0; base < g1; base += static_cast<long>(kBlock) * kGpt) {
-        const long my0 = base + static_cast<long>(threadIdx.x) * kGpt;
-        float r[kGpt][W];
+template <int N>
+__device__ inline float pairwise(const float (&r)[N]) {
+    float t[N];
 #pragma unroll
-        for (int q = 0; q < kGpt; ++q) {
-            if (my0 + q < g1) {
-                residual_group<DT, VEC>(prow, qrow, p_only, inv_t, cp, cq, my0 + q, r[q]);
-            } else {
+    for (int e = 0; e < N; ++e)
+        t[e] = r[e];
 #pragma unroll
-                for (int e = 0; e < W; ++e)
-                    r[q][e] = 0.0f;
-            }
-        }
-        double mine = 0.0;
-        int my_last = -1;
+    for (int w = 1; w < N; w <<= 1) {
 #pragma unroll
-        for (int q = 0; q < kGpt; ++q) {
-#pragma unroll
-            for (int e = 0; e < W; ++e) {
-                mine += static_cast<double>(r[q][e]);
-                if (r[q][e] > 0.0f)
-                    my_last = static_cast<int>((my0 + q) * W + e);
-            }
-        }
-        double total;
-        const double excl = block_exclusive_scan(mine, lds.d, &total);
-        double a = P + excl;
-        int hit = -1;
-#pragma unroll
-        for (int q = 0; q < kGpt; ++q) {
-#pragma unroll
-            for (int e = 0; e < W; ++e) {
-                a += static_cast<double>(r[q][e]);
-                if (hit < 0 && r[q][e] > 0.0f && a > tau)
-                    hit = static_cast<int>((my0 + q) * W + e);
-            }
-        }
-        const int first = block_first(hit >= 0, lds.i);
-        if (first < kBlock) {
-            if (static_cast<int>(threadIdx.x) == first)
-                lds.result = hit;
-            __syncthreads();
-            return lds.result;
-        }
-        const int lp = block_max_int(my_last, lds.i);
-        last_pos = lp > last_pos ? lp : last_pos;
-        P = P + total;
+        for (int i = 0; i + w < N; i += 2 * w)
+            t[i] += t[i + w];
     }
-    return -2 - last_pos;
+    return t[0];
 }
 
-template <int DT, bool VEC, int U>
-__global__ __launch_bounds__(kBlock) void residual_kernel(
+// Tile sum: fixed xor butterfly over the 64 lanes' group sums (all lanes get it).
+__device__ inline float tile_reduce(float v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int DT, bool VEC, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
     const void* __restrict__ draft, const void* __restrict__ target,
-    const float* __restrict__ temperature, int gamma, int vocab, int nsplit,
+    const float* __restrict__ temperature, int gamma, int vocab, int nsplit, int tiles_per_row,
     const SeqState* __restrict__ seq, const RowNorm* __restrict__ rn,
-    double* __restrict__ chunk_sums, int* __restrict__ tickets, int32_t* __restrict__ out_tok) {
-    constexpr int W = Group<DT, VEC>::W;
+    float* __restrict__ tile_sums) {
+    using IO = GroupIO<DT, VEC, NT>;
+    constexpr int W = IO::W;
     const long blk = blockIdx.x;
     const int c = static_cast<int>(blk % nsplit);
     const long b = blk / nsplit;
     const SeqState st = seq[b];
     if (st.mode != 1)
         return;  // greedy or rejected sequence: nothing to draw
-    const int G = gamma;
-    const int k = st.k;
-    float inv_t = 0.0f;
-    temperature_mode(temperature[b], &inv_t);
-    const bool bonus = k == G;
-    const size_t row0 = static_cast<size_t>(b) * (2 * G + 1);
-    const void* prow = row_ptr(target, DT, static_cast<size_t>(b) * (G + 1) + k, vocab);
-    const void* qrow = bonus ? prow : row_ptr(draft, DT, static_cast<size_t>(b) * G + k, vocab);
-    const RowNorm np = rn[row0 + G + k];
-    const RowCoef cp{np.m, static_cast<float>(1.0 / np.s)};
-    RowCoef cq{0.0f, 0.0f};
-    if (!bonus) {
-        const RowNorm nq = rn[row0 + k];
-        cq = RowCoef{nq.m, static_cast<float>(1.0 / nq.s)};
-    }
-
-    __shared__ double lds_d[kWaves];
-    __shared__ ScanLds scan_lds;
-    __shared__ double s_sums[kMaxSplit];
-    __shared__ int s_last;
-    __shared__ double s_P, s_tau;
-    __shared__ int s_cstar, s_fallback;
-
+    const SeqRows s = seq_rows<DT>(draft, target, temperature, gamma, vocab, b, st.k, rn);
     const long groups = vocab / W;
-    long g0, g1;
-    split_range(groups, nsplit, c, &g0, &g1);
-    const double mine = range_sum<DT, VEC, U>(prow, qrow, bonus, inv_t, cp, cq, g0, g1, lds_d);
+    const long ntiles = (groups + kTile - 1) / kTile;
+    long t0, t1;
+    split_range(ntiles, nsplit, c, &t0, &t1);
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float* out = tile_sums + b * tiles_per_row;
 
-    if (threadIdx.x == 0) {
-        chunk_sums[b * nsplit + c] = mine;
-        const int before = __hip_atomic_fetch_add(&tickets[b], 1, __ATOMIC_ACQ_REL,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        s_last = before == nsplit - 1;
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
-
-    // The last workgroup of sequence b: locate the split, then the token.
-    if (threadIdx.x == 0) {
-        double S = 0.0;
-        for (int cc = 0; cc < nsplit; ++cc) {
-            s_sums[cc] = __hip_atomic_load(&chunk_sums[b * nsplit + cc], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-            S += s_sums[cc];
+    for (long t = t0 + wid; t < t1; t += static_cast<long>(kWaves) * U) {
+        IO io[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long g = (t + static_cast<long>(u) * kWaves) * kTile + lane;
+            if (t + u * kWaves < t1 && g < groups)
+                io[u].load(s, g);
         }
-        __hip_atomic_store(&tickets[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (S > 0.0) {
-            const double tau = static_cast<double>(st.u_res) * S;
-            double P = 0.0;
-            int cstar = nsplit - 1;
-            for (int cc = 0; cc < nsplit; ++cc) {
-                if (P + s_sums[cc] > tau) {
-                    cstar = cc;
-                    break;
-                }
-                P += s_sums[cc];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long tt = t + static_cast<long>(u) * kWaves;
+            if (tt >= t1)
+                break;  // wave-uniform
+            const long g = tt * kTile + lane;
+            float gs = 0.0f;
+            if (g < groups) {
+                float r[W];
+                io[u].residual(s, r);
+                gs = pairwise(r);
             }
-            s_P = P;
-            s_tau = tau;
-            s_cstar = cstar;
-            s_fallback = 0;
-        } else {
-            s_fallback = 1;
+            const float ts = tile_reduce(gs);
+            if (lane == 0)
+                out[tt] = ts;
         }
     }
-    __syncthreads();
+}
+
+// Inclusive prefix over the 64 lanes in fp64 (lane order).
+__device__ inline double wave_inclusive_scan(double v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(v, off, 64);
+        if (lane >= off)
+            v += o;
+    }
+    return v;
+}
+
+__device__ inline int first_lane(bool flag) {
+    const unsigned long long m = __ballot(flag);
+    return m ? __ffsll(static_cast<long long>(m)) - 1 : 64;
+}
+
+__device__ inline int wave_max_int(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const int o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Locate the tile holding tau given the per-tile sums `ts` (fp32) of one row:
+// lane l sums a contiguous run of tiles, the wavefront scans the runs in fp64
+// and the lane whose run crosses tau walks it. Returns the tile and writes the
+// fp64 prefix before it; when tau lies beyond the total (rounding only),
+// returns the last tile with mass and writes -1 (take its last positive element).
+__device__ inline long locate_tile(const float* ts, long ntiles, double tau, double* P_out) {
+    const int lane = threadIdx.x & 63;
+    const long per = (ntiles + 63) / 64;
+    const long a0 = lane * per;
+    const long a1 = a0 + per < ntiles ? a0 + per : ntiles;
+    double mine = 0.0;
+    int last_pos = -1;
+    for (long t = a0; t < a1; ++t) {
+        const float v = ts[t];
+        mine += static_cast<double>(v);
+        if (v > 0.0f)
+            last_pos = static_cast<int>(t);
+    }
+    const double excl = wave_inclusive_scan(mine) - mine;
+    int hit = -1;
+    double before = 0.0;
+    double acc = excl;
+    for (long t = a0; t < a1 && hit < 0; ++t) {
+        const float v = ts[t];
+        const double next = acc + static_cast<double>(v);
+        if (v > 0.0f && next > tau) {
+            hit = static_cast<int>(t);
+            before = acc;
+        }
+        acc = next;
+    }
+    const int fl = first_lane(hit >= 0);
+    if (fl < 64) {
+        *P_out = __shfl(before, fl, 64);
+        return __shfl(hit, fl, 64);
+    }
+    *P_out = -1.0;
+    return wave_max_int(last_pos);
+}
+
+// Token inside one tile: lane l recomputes group 64*tile + l exactly as the
+// tile kernel did, the wavefront scans the group sums in fp64 from P, and the
+// first lane whose elements carry the running prefix past tau names the token.
+// P < 0 asks for the tile's last positive element.
+template <int DT, bool VEC, bool NT>
+__device__ inline int scan_tile(const SeqRows& s, long tile, long groups, double P, double tau) {
+    using IO = GroupIO<DT, VEC, NT>;
+    constexpr int W = IO::W;
+    const int lane = threadIdx.x & 63;
+    const long g = tile * kTile + lane;
+    float r[W];
+    float gs = 0.0f;
+    if (g < groups) {
+        IO io;
+        io.load(s, g);
+        io.residual(s, r);
+        gs = pairwise(r);
+    } else {
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            r[e] = 0.0f;
+    }
+    int my_last = -1;
+#pragma unroll
+    for (int e = 0; e < W; ++e)
+        if (r[e] > 0.0f)
+            my_last = static_cast<int>(g * W + e);
+    const int tile_last = wave_max_int(my_last);
+    if (P < 0.0)
+        return tile_last;
+    const double inc = wave_inclusive_scan(static_cast<double>(gs));
+    int hit = -1;
+    double a = P + (inc - static_cast<double>(gs));
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+        a += static_cast<double>(r[e]);
+        if (hit < 0 && r[e] > 0.0f && a > tau)
+            hit = static_cast<int>(g * W + e);
+    }
+    // a group whose scanned sum crosses tau while its element walk falls
+    // short by rounding: its last positive element
+    if (hit < 0 && gs > 0.0f && P + inc > tau)
+        hit = my_last;
+    const int fl = first_lane(hit >= 0);
+    if (fl < 64)
+        return __shfl(hit, fl, 64);
+    return tile_last;
+}
+
+template <int DT, bool VEC, bool NT>
+__device__ inline double tile_sum_of(const SeqRows& s, long t, long groups) {
+    using IO = GroupIO<DT, VEC, NT>;
+    constexpr int W = IO::W;
+    const long g = t * kTile + (threadIdx.x & 63);
+    float gs = 0.0f;
+    if (g < groups) {
+        IO io;
+        io.load(s, g);
+        float r[W];
+        io.residual(s, r);
+        gs = pairwise(r);
+    }
+    return static_cast<double>(tile_reduce(gs));
+}
+
+template <int DT, bool VEC, bool NT>
+__global__ __launch_bounds__(64) void residual_locate_kernel(
+    const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, int gamma, int vocab, int tiles_per_row,
+    const SeqState* __restrict__ seq, const RowNorm* __restrict__ rn,
+    const float* __restrict__ tile_sums, int32_t* __restrict__ out_tok) {
+    constexpr int W = Group<DT, VEC>::W;
+    const long b = blockIdx.x;
+    const SeqState st = seq[b];
+    if (st.mode != 1)
+        return;
+    const int G = gamma, k = st.k;
+    SeqRows s = seq_rows<DT>(draft, target, temperature, G, vocab, b, k, rn);
+    const long groups = vocab / W;
+    const long ntiles = (groups + kTile - 1) / kTile;
+    const float* ts = tile_sums + b * tiles_per_row;
+    const int lane = threadIdx.x & 63;
+
+    double mine = 0.0;
+    for (long t = lane; t < ntiles; t += 64)
+        mine += static_cast<double>(ts[t]);
+    double S = mine;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        S += __shfl_xor(S, off, 64);
 
     int token;
-    if (!s_fallback) {
-        long c0, c1;
-        split_range(groups, nsplit, s_cstar, &c0, &c1);
-        token = scan_range<DT, VEC>(prow, qrow, bonus, inv_t, cp, cq, c0, c1, s_P, s_tau, scan_lds);
+    if (S > 0.0) {
+        const double tau = static_cast<double>(st.u_res) * S;
+        double P;
+        const long tile = locate_tile(ts, ntiles, tau, &P);
+        token = scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
     } else {
-        // Empty residual (possible only through rounding when p and q agree
-        // to within fp32): draw from p at the same position instead.
-        const double Sp = range_sum<DT, VEC, U>(prow, prow, true, inv_t, cp, cp, 0, groups, lds_d);
-        const double tau = static_cast<double>(st.u_res) * Sp;
-        token = scan_range<DT, VEC>(prow, prow, true, inv_t, cp, cp, 0, groups, 0.0, tau, scan_lds);
+        // Empty residual (possible only through rounding when p and q agree to
+        // within fp32): draw from p at the same position instead. Slow path:
+        // this wavefront streams the row twice.
+        s.p_only = true;
+        double sp = 0.0;
+        for (long t = 0; t < ntiles; ++t)
+            sp += tile_sum_of<DT, VEC, NT>(s, t, groups);
+        const double tau = static_cast<double>(st.u_res) * sp;
+        double P = 0.0;
+        long tile = -1;
+        for (long t = 0; t < ntiles && tile < 0; ++t) {
+            const double tsum = tile_sum_of<DT, VEC, NT>(s, t, groups);
+            if (tsum > 0.0 && P + tsum > tau)
+                tile = t;
+            else
+                P += tsum;
+        }
+        if (tile < 0) {
+            tile = ntiles - 1;
+            P = -1.0;
+        }
+        token = scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
     }
-    if (token <= -2)
-        token = -2 - token;  // the range ended first: its last positive element
-    if (threadIdx.x == 0)
+    if (lane == 0)
         out_tok[b * (G + 1) + k] = token;
 }
 
 template <int DT, bool VEC>
-hipError_t launch_typed(const Shape& sh, int nsplit, const void* draft, const void* target,
-                        const float* temperature, const SeqState* seq, const RowNorm* rn,
-                        double* chunk_sums, int* tickets, int32_t* out_tok, hipStream_t stream) {
-    constexpr int U = VEC ? 2 : 8;
+hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const void* draft,
+                        const void* target, const float* temperature, const SeqState* seq,
+                        const RowNorm* rn, float* tile_sums, int32_t* out_tok, hipStream_t stream) {
+    constexpr int U = VEC ? 4 : 8;
+    constexpr bool NT = VEC;
     const long blocks = static_cast<long>(sh.batch) * nsplit;
     if (blocks == 0)
         return hipSuccess;
-    residual_kernel<DT, VEC, U><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream>>>(
-        draft, target, temperature, sh.gamma, sh.vocab, nsplit, seq, rn, chunk_sums, tickets, out_tok);
+    residual_tiles_kernel<DT, VEC, U, NT><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream>>>(
+        draft, target, temperature, sh.gamma, sh.vocab, nsplit, tiles_per_row, seq, rn, tile_sums);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    residual_locate_kernel<DT, VEC, NT><<<dim3(static_cast<unsigned>(sh.batch)), dim3(64), 0, stream>>>(
+        draft, target, temperature, sh.gamma, sh.vocab, tiles_per_row, seq, rn, tile_sums, out_tok);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int residual_tiles_per_row(int vocab) { return (vocab + kTile - 1) / kTile; }
+
 hipError_t launch_residual(const Shape& s, bool vec, int nsplit, const void* draft,
                            const void* target, const float* temperature, const SeqState* seq,
-                           const RowNorm* rn, double* chunk_sums, int* tickets,
-                           int32_t* out_tok, hipStream_t stream) {
+                           const RowNorm* rn, float* tile_sums, int32_t* out_tok,
+                           hipStream_t stream) {
     if (nsplit < 1 || nsplit > kMaxSplit)
         return hipErrorInvalidValue;
+    // Tile sums are laid out with the element-path tile count, which bounds the
+    // 16-byte-group tile count.
+    const int tiles = residual_tiles_per_row(s.vocab);
     if (s.dtype == kBF16)
-        return vec ? launch_typed<kBF16, true>(s, nsplit, draft, target, temperature, seq, rn,
-                                               chunk_sums, tickets, out_tok, stream)
-                   : launch_typed<kBF16, false>(s, nsplit, draft, target, temperature, seq, rn,
-                                                chunk_sums, tickets, out_tok, stream);
-    return vec ? launch_typed<kF32, true>(s, nsplit, draft, target, temperature, seq, rn, chunk_sums,
-                                          tickets, out_tok, stream)
-               : launch_typed<kF32, false>(s, nsplit, draft, target, temperature, seq, rn,
-                                           chunk_sums, tickets, out_tok, stream);
+        return vec ? launch_typed<kBF16, true>(s, nsplit, tiles, draft, target, temperature, seq, rn,
+                                               tile_sums, out_tok, stream)
+                   : launch_typed<kBF16, false>(s, nsplit, tiles, draft, target, temperature, seq,
+                                                rn, tile_sums, out_tok, stream);
+    return vec ? launch_typed<kF32, true>(s, nsplit, tiles, draft, target, temperature, seq, rn,
+                                          tile_sums, out_tok, stream)
+               : launch_typed<kF32, false>(s, nsplit, tiles, draft, target, temperature, seq, rn,
+                                           tile_sums, out_tok, stream);
 }
 
 }  // namespace specv

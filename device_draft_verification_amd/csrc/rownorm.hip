@@ -53,7 +53,7 @@ __device__ inline void online_add(const float (&x)[N], float& m, double& s) {
     m = mn;
 }
 
-template <int DT, bool VEC, int U>
+template <int DT, bool VEC, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void row_norm_kernel(
     const void* __restrict__ draft, const void* __restrict__ target,
     const float* __restrict__ temperature, int gamma, int vocab, int nsplit,
@@ -90,9 +90,28 @@ __global__ __launch_bounds__(kBlock) void row_norm_kernel(
         // lowest index of equal values.
         float bv = -__builtin_huge_valf();
         int bi = 0x7fffffff;
-        for (long g = g0 + threadIdx.x; g < g1; g += kBlock) {
+        long g = g0 + threadIdx.x;
+        for (; g + static_cast<long>(U - 1) * kBlock < g1; g += static_cast<long>(U) * kBlock) {
+            typename Ld::raw_t q[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                q[u] = Ld::template load_as<NT>(rp, g + static_cast<long>(u) * kBlock);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float z[W];
+                Ld::unpack(q[u], z);
+#pragma unroll
+                for (int e = 0; e < W; ++e) {
+                    if (z[e] > bv) {
+                        bv = z[e];
+                        bi = static_cast<int>((g + static_cast<long>(u) * kBlock) * W + e);
+                    }
+                }
+            }
+        }
+        for (; g < g1; g += kBlock) {
             float z[W];
-            Ld::unpack(Ld::load(rp, g), z);
+            Ld::unpack(Ld::template load_as<NT>(rp, g), z);
 #pragma unroll
             for (int e = 0; e < W; ++e) {
                 if (z[e] > bv) {
@@ -135,7 +154,7 @@ __global__ __launch_bounds__(kBlock) void row_norm_kernel(
         typename Ld::raw_t q[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            q[u] = Ld::load(rp, g + static_cast<long>(u) * kBlock);
+            q[u] = Ld::template load_as<NT>(rp, g + static_cast<long>(u) * kBlock);
         float x[U * W];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -149,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void row_norm_kernel(
     }
     for (; g < g1; g += kBlock) {
         float z[W], x[W];
-        Ld::unpack(Ld::load(rp, g), z);
+        Ld::unpack(Ld::template load_as<NT>(rp, g), z);
 #pragma unroll
         for (int e = 0; e < W; ++e)
             x[e] = scale_logit(z[e], inv_t);
@@ -163,29 +182,50 @@ __global__ __launch_bounds__(kBlock) void row_norm_kernel(
         part[blk] = Partial{bm, -1, bs};
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int U, bool NT>
 hipError_t launch_typed(const Shape& sh, int nsplit, const void* draft, const void* target,
                         const float* temperature, Partial* part, hipStream_t stream) {
-    constexpr int U = VEC ? (DT == kBF16 ? 4 : 4) : 8;
     const long rows = static_cast<long>(sh.batch) * (2 * sh.gamma + 1);
     const long blocks = rows * nsplit;
     if (blocks == 0)
         return hipSuccess;
-    row_norm_kernel<DT, VEC, U><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream>>>(
+    row_norm_kernel<DT, VEC, U, NT><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream>>>(
         draft, target, temperature, sh.gamma, sh.vocab, nsplit, part);
     return hipGetLastError();
 }
 
+template <int DT, bool VEC>
+hipError_t launch_unroll(const Shape& sh, const RowTuning& tu, const void* draft,
+                         const void* target, const float* temperature, Partial* part,
+                         hipStream_t stream) {
+    if constexpr (!VEC) {
+        return launch_typed<DT, false, 8, false>(sh, tu.nsplit, draft, target, temperature, part, stream);
+    } else {
+        if (tu.nontemporal) {
+            switch (tu.unroll) {
+            case 2: return launch_typed<DT, true, 2, true>(sh, tu.nsplit, draft, target, temperature, part, stream);
+            case 8: return launch_typed<DT, true, 8, true>(sh, tu.nsplit, draft, target, temperature, part, stream);
+            default: return launch_typed<DT, true, 4, true>(sh, tu.nsplit, draft, target, temperature, part, stream);
+            }
+        }
+        switch (tu.unroll) {
+        case 2: return launch_typed<DT, true, 2, false>(sh, tu.nsplit, draft, target, temperature, part, stream);
+        case 8: return launch_typed<DT, true, 8, false>(sh, tu.nsplit, draft, target, temperature, part, stream);
+        default: return launch_typed<DT, true, 4, false>(sh, tu.nsplit, draft, target, temperature, part, stream);
+        }
+    }
+}
+
 }  // namespace
 
-hipError_t launch_row_norm(const Shape& s, bool vec, int nsplit, const void* draft,
+hipError_t launch_row_norm(const Shape& s, bool vec, const RowTuning& tu, const void* draft,
                            const void* target, const float* temperature, Partial* part,
                            hipStream_t stream) {
     if (s.dtype == kBF16)
-        return vec ? launch_typed<kBF16, true>(s, nsplit, draft, target, temperature, part, stream)
-                   : launch_typed<kBF16, false>(s, nsplit, draft, target, temperature, part, stream);
-    return vec ? launch_typed<kF32, true>(s, nsplit, draft, target, temperature, part, stream)
-               : launch_typed<kF32, false>(s, nsplit, draft, target, temperature, part, stream);
+        return vec ? launch_unroll<kBF16, true>(s, tu, draft, target, temperature, part, stream)
+                   : launch_unroll<kBF16, false>(s, tu, draft, target, temperature, part, stream);
+    return vec ? launch_unroll<kF32, true>(s, tu, draft, target, temperature, part, stream)
+               : launch_unroll<kF32, false>(s, tu, draft, target, temperature, part, stream);
 }
 
 }  // namespace specv
