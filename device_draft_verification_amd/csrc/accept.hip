@@ -1,9 +1,10 @@
 // Accept kernel: one 64-lane wavefront per sequence, lane i <-> draft position i.
 //
 // Per lane: merge the vocabulary splits of draft row i and target row i into
-// their log-normalisers, gather the two log-probabilities of draft token t_i
-// (FlashSpec technical summary, Methodology section 1: two log-probability
-// scalars per candidate, one per model), draw the Philox block of (b, i) and
+// their log-normalisers, form the two log-probabilities of draft token t_i from
+// the raw logits the row kernel recorded (FlashSpec technical summary,
+// Methodology section 1: two log-probability scalars per candidate, one per
+// model), draw the Philox block of (b, i) and
 // run the log-space test log u < log p - log q in fp64. The first rejection is
 // one ballot and a count of trailing zeros. The kernel writes the accepted
 // prefix and the accept length, and leaves (k, u_res) for the residual kernel.
@@ -32,8 +33,9 @@ __device__ inline bool merge_sampled(const Partial* p, int nsplit, RowNorm* out)
         m = fmaxf(m, p[c].m);
     double s = 0.0;
     for (int c = 0; c < nsplit; ++c) {
-        const double f = (p[c].m == m) ? 1.0 : exp2(static_cast<double>(p[c].m) - static_cast<double>(m));
-        s = __builtin_fma(p[c].s, f, s);
+        // exact 1 for the splits holding the max; a 1-ulp fp32 factor otherwise
+        const float f = (p[c].m == m) ? 1.0f : fast_exp2(p[c].m - m);
+        s = __builtin_fma(p[c].s, static_cast<double>(f), s);
     }
     *out = RowNorm{m, -1, s};
     return s > 0.0;  // false: the row has no finite logit
@@ -57,7 +59,8 @@ __global__ __launch_bounds__(64) void accept_kernel(
     const void* __restrict__ draft, const void* __restrict__ target,
     const int32_t* __restrict__ tokens, const float* __restrict__ temperature, int gamma,
     int vocab, int nsplit, uint64_t seed, uint64_t offset, const Partial* __restrict__ part,
-    RowNorm* __restrict__ rn, double* __restrict__ lse_out, SeqState* __restrict__ seq,
+    const float* __restrict__ gathered, RowNorm* __restrict__ rn, double* __restrict__ lse_out,
+    SeqState* __restrict__ seq,
     int32_t* __restrict__ out_len, int32_t* __restrict__ out_tok) {
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
@@ -91,11 +94,11 @@ __global__ __launch_bounds__(64) void accept_kernel(
         }
         bool reject = false;
         if (mode == 1 && has_target) {
-            // gathers first: their latency overlaps the split merges
+            // raw logits of the draft token, recorded by the row kernel
             float zq = 0.0f, zp = 0.0f;
             if (t_ok) {
-                zq = load_logit(row_ptr(draft, DT, static_cast<size_t>(b) * G + i, vocab), DT, t);
-                zp = load_logit(row_ptr(target, DT, static_cast<size_t>(b) * (G + 1) + i, vocab), DT, t);
+                zq = gathered[row0 + i];
+                zp = gathered[row0 + G + i];
             }
             RowNorm rq{}, rp;
             if (has_draft) {
@@ -207,18 +210,19 @@ __global__ __launch_bounds__(256) void philox_words_kernel(int batch, int gamma,
 
 hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const void* target,
                          const int32_t* tokens, const float* temperature, uint64_t seed,
-                         uint64_t offset, const Partial* part, RowNorm* rn, double* lse_out,
-                         SeqState* seq, int32_t* out_len, int32_t* out_tok, hipStream_t stream) {
+                         uint64_t offset, const Partial* part, const float* gathered, RowNorm* rn,
+                         double* lse_out, SeqState* seq, int32_t* out_len, int32_t* out_tok,
+                         hipStream_t stream) {
     if (s.batch == 0)
         return hipSuccess;
     if (s.dtype == kBF16)
         accept_kernel<kBF16><<<dim3(s.batch), dim3(64), 0, stream>>>(
-            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, part, rn,
-            lse_out, seq, out_len, out_tok);
+            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, part,
+            gathered, rn, lse_out, seq, out_len, out_tok);
     else
         accept_kernel<kF32><<<dim3(s.batch), dim3(64), 0, stream>>>(
-            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, part, rn,
-            lse_out, seq, out_len, out_tok);
+            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, part,
+            gathered, rn, lse_out, seq, out_len, out_tok);
     return hipGetLastError();
 }
 

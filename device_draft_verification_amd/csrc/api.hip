@@ -20,12 +20,13 @@ struct spec_verify_ctx {
     hipStream_t stream = nullptr;
     int device = 0;
     int nsplit_rows = 1;      // vocabulary splits of the row-normaliser kernel
-    int row_unroll = 4;       // 16-byte groups in flight per thread in that kernel
+    int row_unroll = 8;       // 16-byte groups in flight per thread in that kernel
     bool row_nontemporal = true;
     int nsplit_residual = 1;  // vocabulary splits of the residual kernel
 
     void* ws = nullptr;
     Partial* part = nullptr;
+    float* gathered = nullptr;
     RowNorm* rn = nullptr;
     double* lse = nullptr;
     SeqState* seq = nullptr;
@@ -42,7 +43,7 @@ namespace {
 // Workgroup counts per launch: the row kernel wants several waves of
 // workgroups over the 256 CUs so the last wave is short; the residual kernel's
 // workgroups are short-lived, so fewer, longer ones.
-constexpr long kRowTargetBlocks = 16384;
+constexpr long kRowTargetBlocks = 12288;
 constexpr long kResidualTargetBlocks = 4096;
 
 int env_int(const char* name, int fallback) {
@@ -130,6 +131,7 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     size_t off = 0;
     const size_t o_part = off; off = align_up(off + n_part * sizeof(Partial), 256);
     const size_t o_rn = off;   off = align_up(off + rows * sizeof(RowNorm), 256);
+    const size_t o_ga = off;   off = align_up(off + rows * sizeof(float), 256);
     const size_t o_lse = off;  off = align_up(off + rows * sizeof(double), 256);
     const size_t o_seq = off;  off = align_up(off + static_cast<size_t>(batch) * sizeof(SeqState), 256);
     const size_t o_ts = off;   off = align_up(off + static_cast<size_t>(batch) * residual_tiles_per_row(vocab) * sizeof(float), 256);
@@ -141,6 +143,7 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     char* base = static_cast<char*>(ctx->ws);
     ctx->part = reinterpret_cast<Partial*>(base + o_part);
     ctx->rn = reinterpret_cast<RowNorm*>(base + o_rn);
+    ctx->gathered = reinterpret_cast<float*>(base + o_ga);
     ctx->lse = reinterpret_cast<double*>(base + o_lse);
     ctx->seq = reinterpret_cast<SeqState*>(base + o_seq);
     ctx->tile_sums = reinterpret_cast<float*>(base + o_ts);
@@ -194,14 +197,14 @@ int spec_verify(spec_verify_ctx* ctx, const void* logits_draft, const void* logi
     if (ev && hipEventRecord(ev[0], st) != hipSuccess)
         return SPEC_EHIP;
     const RowTuning tu{ctx->nsplit_rows, ctx->row_unroll, ctx->row_nontemporal};
-    if (launch_row_norm(s, vec, tu, logits_draft, logits_target, temperature, ctx->part, st) !=
-        hipSuccess)
+    if (launch_row_norm(s, vec, tu, logits_draft, logits_target, temperature, draft_tokens,
+                        ctx->part, ctx->gathered, st) != hipSuccess)
         return SPEC_EHIP;
     if (ev && hipEventRecord(ev[1], st) != hipSuccess)
         return SPEC_EHIP;
     if (launch_accept(s, ctx->nsplit_rows, logits_draft, logits_target, draft_tokens, temperature,
-                      seed, offset, ctx->part, ctx->rn, ctx->lse, ctx->seq, out_accept_len,
-                      out_tokens, st) != hipSuccess)
+                      seed, offset, ctx->part, ctx->gathered, ctx->rn, ctx->lse, ctx->seq,
+                      out_accept_len, out_tokens, st) != hipSuccess)
         return SPEC_EHIP;
     if (ev && hipEventRecord(ev[2], st) != hipSuccess)
         return SPEC_EHIP;

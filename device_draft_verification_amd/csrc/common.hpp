@@ -72,6 +72,18 @@ struct Loader {
         }
     }
 
+    // A group of -inf logits (the identity of max and of sum-of-exp).
+    __device__ static inline raw_t neg_inf() {
+        if constexpr (VEC) {
+            const unsigned w = DT == kBF16 ? 0xFF80FF80u : 0xFF800000u;
+            return make_uint4(w, w, w, w);
+        } else if constexpr (DT == kBF16) {
+            return static_cast<uint16_t>(0xFF80u);
+        } else {
+            return -__builtin_huge_valf();
+        }
+    }
+
     template <bool NT>
     __device__ static inline raw_t load_as(const void* row, long g) {
         if constexpr (NT)

@@ -35,16 +35,19 @@ struct RowTuning {
 };
 
 // Row normalisers: grid = B * (2G+1) * nsplit workgroups of kBlock threads.
+// Also records, per row of a position i < G, the raw logit of draft token t_i
+// in gathered[row] (rows of invalid tokens are left untouched).
 hipError_t launch_row_norm(const Shape& s, bool vec, const RowTuning& tu, const void* draft,
-                           const void* target, const float* temperature, Partial* part,
-                           hipStream_t stream);
+                           const void* target, const float* temperature, const int32_t* tokens,
+                           Partial* part, float* gathered, hipStream_t stream);
 
 // Split merge, gather, accept test, first rejection and the emitted prefix:
 // one 64-lane wavefront per sequence.
 hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const void* target,
                          const int32_t* tokens, const float* temperature, uint64_t seed,
-                         uint64_t offset, const Partial* part, RowNorm* rn, double* lse_out,
-                         SeqState* seq, int32_t* out_len, int32_t* out_tok, hipStream_t stream);
+                         uint64_t offset, const Partial* part, const float* gathered, RowNorm* rn,
+                         double* lse_out, SeqState* seq, int32_t* out_len, int32_t* out_tok,
+                         hipStream_t stream);
 
 // Residual / bonus draw at the first rejection: per-tile sums (B * nsplit
 // workgroups), then one locating wavefront per sequence. tile_sums holds

@@ -14,7 +14,7 @@
 //     wavefront streams whole tiles (lane l reads group 64*t + l of both rows,
 //     so one load instruction covers 1 KiB of consecutive memory), and stores
 //     one fp32 sum per tile: the groups' pairwise fp32 sums reduced by a fixed
-//     xor butterfly.
+//     DPP butterfly across the wavefront.
 //   residual_locate: one wavefront per sequence prefix-sums the tile sums in
 //     fp64, finds the tile holding u_res * S, recomputes that tile's group sums
 //     with the same arithmetic, scans them in fp64 to find the group and walks
@@ -22,9 +22,13 @@
 // The kernel boundary makes the tile sums visible to every XCD; all sums have
 // a fixed order, so the result is bitwise reproducible.
 //
-// p and q are recomputed from the row normalisers of the row kernel:
-// p_v = 2^(fma(x_v, log2e, -m)) / s, which sums to one under the same
-// normaliser the accept test used.
+// p and q are recomputed from the row normalisers (m, s) of the row kernel,
+// p_v = 2^(fma(x_v, log2e, -m_p)) / s_p and the same for q, i.e. under the
+// normalisers the accept test used. The kernels work with the residual scaled
+// by the constant s_q, r'_v = max(0, fma(p'_v, s_q / s_p, -q'_v)) with
+// p' = 2^(fma(x, log2e, -m)), which the inversion does not see (u * S scales
+// with it) and which costs one fused multiply-add per logit pair. The bonus
+// row uses p' itself.
 #include "launch.hpp"
 
 namespace specv {
@@ -32,36 +36,47 @@ namespace {
 
 constexpr int kTile = 64;  // groups per tile = lanes per wavefront
 
-struct RowCoef {
-    float m;      // base-2 reference of the row
-    float inv_s;  // 1 / s
-};
-
 // The one or two rows of a sequence at its first rejection.
 struct SeqRows {
     const void* prow;
     const void* qrow;
-    bool p_only;  // bonus row (or the empty-residual fallback): r = p
+    bool p_only;  // bonus row (or the empty-residual fallback): r' = p'
     float inv_t;
-    RowCoef cp, cq;
+    float mp, mq;   // base-2 references of the rows
+    float ratio;    // s_q / s_p
 };
+
+// Row pointers of sequence b at position k (needs only the accept outcome).
+template <int DT>
+__device__ inline void seq_row_ptrs(SeqRows& s, const void* draft, const void* target, int G,
+                                    int vocab, int b, int k) {
+    s.p_only = k == G;
+    s.prow = row_ptr(target, DT, static_cast<size_t>(b) * (G + 1) + k, vocab);
+    s.qrow = s.p_only ? s.prow : row_ptr(draft, DT, static_cast<size_t>(b) * G + k, vocab);
+}
+
+// Scaling coefficients of those rows from the row normalisers.
+__device__ inline void seq_row_coefs(SeqRows& s, const float* temperature, int G, int b, int k,
+                                     const RowNorm* rn) {
+    temperature_mode(temperature[b], &s.inv_t);
+    const size_t row0 = static_cast<size_t>(b) * (2 * G + 1);
+    const RowNorm np = rn[row0 + G + k];
+    s.mp = np.m;
+    s.mq = 0.0f;
+    s.ratio = 1.0f;
+    if (!s.p_only) {
+        const RowNorm nq = rn[row0 + k];
+        s.mq = nq.m;
+        s.ratio = static_cast<float>(nq.s / np.s);
+    }
+}
 
 template <int DT>
 __device__ inline SeqRows seq_rows(const void* draft, const void* target, const float* temperature,
-                                   int G, int vocab, long b, int k, const RowNorm* rn) {
+                                   int G, int vocab, int b, int k, const RowNorm* rn) {
     SeqRows s;
-    temperature_mode(temperature[b], &s.inv_t);
-    s.p_only = k == G;
-    const size_t row0 = static_cast<size_t>(b) * (2 * G + 1);
-    s.prow = row_ptr(target, DT, static_cast<size_t>(b) * (G + 1) + k, vocab);
-    s.qrow = s.p_only ? s.prow : row_ptr(draft, DT, static_cast<size_t>(b) * G + k, vocab);
-    const RowNorm np = rn[row0 + G + k];
-    s.cp = RowCoef{np.m, static_cast<float>(1.0 / np.s)};
-    s.cq = RowCoef{0.0f, 0.0f};
-    if (!s.p_only) {
-        const RowNorm nq = rn[row0 + k];
-        s.cq = RowCoef{nq.m, static_cast<float>(1.0 / nq.s)};
-    }
+    seq_row_ptrs<DT>(s, draft, target, G, vocab, b, k);
+    seq_row_coefs(s, temperature, G, b, k, rn);
     return s;
 }
 
@@ -71,29 +86,29 @@ struct GroupIO {
     static constexpr int W = Ld::W;
     typename Ld::raw_t p, q;
 
-    __device__ inline void load(const SeqRows& s, long g) {
+    __device__ inline void load(const SeqRows& s, int g) {
         p = Ld::template load_as<NT>(s.prow, g);
         if (!s.p_only)
             q = Ld::template load_as<NT>(s.qrow, g);
     }
 
-    // r of the group's elements, in index order.
+    // r' of the group's elements, in index order.
     __device__ inline void residual(const SeqRows& s, float (&r)[W]) const {
         float zp[W];
         Ld::unpack(p, zp);
         if (s.p_only) {
 #pragma unroll
             for (int e = 0; e < W; ++e)
-                r[e] = fast_exp2(__builtin_fmaf(scale_logit(zp[e], s.inv_t), kLog2e, -s.cp.m)) * s.cp.inv_s;
+                r[e] = fast_exp2(__builtin_fmaf(scale_logit(zp[e], s.inv_t), kLog2e, -s.mp));
             return;
         }
         float zq[W];
         Ld::unpack(q, zq);
 #pragma unroll
         for (int e = 0; e < W; ++e) {
-            const float pv = fast_exp2(__builtin_fmaf(scale_logit(zp[e], s.inv_t), kLog2e, -s.cp.m)) * s.cp.inv_s;
-            const float qv = fast_exp2(__builtin_fmaf(scale_logit(zq[e], s.inv_t), kLog2e, -s.cq.m)) * s.cq.inv_s;
-            r[e] = fmaxf(pv - qv, 0.0f);
+            const float pv = fast_exp2(__builtin_fmaf(scale_logit(zp[e], s.inv_t), kLog2e, -s.mp));
+            const float qv = fast_exp2(__builtin_fmaf(scale_logit(zq[e], s.inv_t), kLog2e, -s.mq));
+            r[e] = fmaxf(__builtin_fmaf(pv, s.ratio, -qv), 0.0f);
         }
     }
 };
@@ -113,12 +128,23 @@ __device__ inline float pairwise(const float (&r)[N]) {
     return t[0];
 }
 
-// Tile sum: fixed xor butterfly over the 64 lanes' group sums (all lanes get it).
+// Tile sum of the 64 lanes' group sums, in a fixed order: DPP butterfly
+// within each row of 16 lanes, then the row broadcasts, then lane 63 holds the
+// total, which is returned to every lane.
+template <int CTRL, int ROW_MASK>
+__device__ inline float add_dpp(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+    return v + __int_as_float(t);
+}
+
 __device__ inline float tile_reduce(float v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1)
-        v += __shfl_xor(v, off, 64);
-    return v;
+    v = add_dpp<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = add_dpp<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = add_dpp<0x141, 0xF>(v);  // row_half_mirror
+    v = add_dpp<0x140, 0xF>(v);  // row_mirror: every lane holds its row's sum
+    v = add_dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = add_dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3: lane 63 = total
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 template <int DT, bool VEC, int U, bool NT>
@@ -129,34 +155,45 @@ __global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
     float* __restrict__ tile_sums) {
     using IO = GroupIO<DT, VEC, NT>;
     constexpr int W = IO::W;
-    const long blk = blockIdx.x;
-    const int c = static_cast<int>(blk % nsplit);
-    const long b = blk / nsplit;
+    const int blk = blockIdx.x;
+    const int c = blk % nsplit;
+    const int b = blk / nsplit;
     const SeqState st = seq[b];
     if (st.mode != 1)
         return;  // greedy or rejected sequence: nothing to draw
-    const SeqRows s = seq_rows<DT>(draft, target, temperature, gamma, vocab, b, st.k, rn);
-    const long groups = vocab / W;
-    const long ntiles = (groups + kTile - 1) / kTile;
-    long t0, t1;
-    split_range(ntiles, nsplit, c, &t0, &t1);
+    const int groups = vocab / W;
+    const int ntiles = (groups + kTile - 1) / kTile;
+    long lt0, lt1;
+    split_range(ntiles, nsplit, c, &lt0, &lt1);
+    const int t0 = static_cast<int>(lt0), t1 = static_cast<int>(lt1);
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    float* out = tile_sums + b * tiles_per_row;
+    float* out = tile_sums + static_cast<size_t>(b) * tiles_per_row;
 
-    for (long t = t0 + wid; t < t1; t += static_cast<long>(kWaves) * U) {
-        IO io[U];
+    // The first batch of loads needs only the row pointers; issue it before
+    // the normaliser loads so the two latencies overlap.
+    SeqRows s;
+    seq_row_ptrs<DT>(s, draft, target, gamma, vocab, b, st.k);
+    IO io[U];
+    auto load_batch = [&](int t) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const long g = (t + static_cast<long>(u) * kWaves) * kTile + lane;
+            const int g = (t + u * kWaves) * kTile + lane;
             if (t + u * kWaves < t1 && g < groups)
                 io[u].load(s, g);
         }
+    };
+    int t = t0 + wid;
+    if (t < t1)
+        load_batch(t);
+    seq_row_coefs(s, temperature, gamma, b, st.k, rn);
+
+    while (t < t1) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const long tt = t + static_cast<long>(u) * kWaves;
+            const int tt = t + u * kWaves;
             if (tt >= t1)
                 break;  // wave-uniform
-            const long g = tt * kTile + lane;
+            const int g = tt * kTile + lane;
             float gs = 0.0f;
             if (g < groups) {
                 float r[W];
@@ -167,6 +204,9 @@ __global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
             if (lane == 0)
                 out[tt] = ts;
         }
+        t += kWaves * U;
+        if (t < t1)
+            load_batch(t);
     }
 }
 
@@ -201,28 +241,28 @@ __device__ inline int wave_max_int(int v) {
 // and the lane whose run crosses tau walks it. Returns the tile and writes the
 // fp64 prefix before it; when tau lies beyond the total (rounding only),
 // returns the last tile with mass and writes -1 (take its last positive element).
-__device__ inline long locate_tile(const float* ts, long ntiles, double tau, double* P_out) {
+__device__ inline int locate_tile(const float* ts, int ntiles, double tau, double* P_out) {
     const int lane = threadIdx.x & 63;
-    const long per = (ntiles + 63) / 64;
-    const long a0 = lane * per;
-    const long a1 = a0 + per < ntiles ? a0 + per : ntiles;
+    const int per = (ntiles + 63) / 64;
+    const int a0 = lane * per;
+    const int a1 = a0 + per < ntiles ? a0 + per : ntiles;
     double mine = 0.0;
     int last_pos = -1;
-    for (long t = a0; t < a1; ++t) {
+    for (int t = a0; t < a1; ++t) {
         const float v = ts[t];
         mine += static_cast<double>(v);
         if (v > 0.0f)
-            last_pos = static_cast<int>(t);
+            last_pos = t;
     }
     const double excl = wave_inclusive_scan(mine) - mine;
     int hit = -1;
     double before = 0.0;
     double acc = excl;
-    for (long t = a0; t < a1 && hit < 0; ++t) {
+    for (int t = a0; t < a1 && hit < 0; ++t) {
         const float v = ts[t];
         const double next = acc + static_cast<double>(v);
         if (v > 0.0f && next > tau) {
-            hit = static_cast<int>(t);
+            hit = t;
             before = acc;
         }
         acc = next;
@@ -241,11 +281,11 @@ __device__ inline long locate_tile(const float* ts, long ntiles, double tau, dou
 // first lane whose elements carry the running prefix past tau names the token.
 // P < 0 asks for the tile's last positive element.
 template <int DT, bool VEC, bool NT>
-__device__ inline int scan_tile(const SeqRows& s, long tile, long groups, double P, double tau) {
+__device__ inline int scan_tile(const SeqRows& s, int tile, int groups, double P, double tau) {
     using IO = GroupIO<DT, VEC, NT>;
     constexpr int W = IO::W;
     const int lane = threadIdx.x & 63;
-    const long g = tile * kTile + lane;
+    const int g = tile * kTile + lane;
     float r[W];
     float gs = 0.0f;
     if (g < groups) {
@@ -286,10 +326,10 @@ __device__ inline int scan_tile(const SeqRows& s, long tile, long groups, double
 }
 
 template <int DT, bool VEC, bool NT>
-__device__ inline double tile_sum_of(const SeqRows& s, long t, long groups) {
+__device__ inline double tile_sum_of(const SeqRows& s, int t, int groups) {
     using IO = GroupIO<DT, VEC, NT>;
     constexpr int W = IO::W;
-    const long g = t * kTile + (threadIdx.x & 63);
+    const int g = t * kTile + (threadIdx.x & 63);
     float gs = 0.0f;
     if (g < groups) {
         IO io;
@@ -308,19 +348,19 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
     const SeqState* __restrict__ seq, const RowNorm* __restrict__ rn,
     const float* __restrict__ tile_sums, int32_t* __restrict__ out_tok) {
     constexpr int W = Group<DT, VEC>::W;
-    const long b = blockIdx.x;
+    const int b = blockIdx.x;
     const SeqState st = seq[b];
     if (st.mode != 1)
         return;
     const int G = gamma, k = st.k;
     SeqRows s = seq_rows<DT>(draft, target, temperature, G, vocab, b, k, rn);
-    const long groups = vocab / W;
-    const long ntiles = (groups + kTile - 1) / kTile;
-    const float* ts = tile_sums + b * tiles_per_row;
+    const int groups = vocab / W;
+    const int ntiles = (groups + kTile - 1) / kTile;
+    const float* ts = tile_sums + static_cast<size_t>(b) * tiles_per_row;
     const int lane = threadIdx.x & 63;
 
     double mine = 0.0;
-    for (long t = lane; t < ntiles; t += 64)
+    for (int t = lane; t < ntiles; t += 64)
         mine += static_cast<double>(ts[t]);
     double S = mine;
 #pragma unroll
@@ -331,7 +371,7 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
     if (S > 0.0) {
         const double tau = static_cast<double>(st.u_res) * S;
         double P;
-        const long tile = locate_tile(ts, ntiles, tau, &P);
+        const int tile = locate_tile(ts, ntiles, tau, &P);
         token = scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
     } else {
         // Empty residual (possible only through rounding when p and q agree to
@@ -339,12 +379,12 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
         // this wavefront streams the row twice.
         s.p_only = true;
         double sp = 0.0;
-        for (long t = 0; t < ntiles; ++t)
+        for (int t = 0; t < ntiles; ++t)
             sp += tile_sum_of<DT, VEC, NT>(s, t, groups);
         const double tau = static_cast<double>(st.u_res) * sp;
         double P = 0.0;
-        long tile = -1;
-        for (long t = 0; t < ntiles && tile < 0; ++t) {
+        int tile = -1;
+        for (int t = 0; t < ntiles && tile < 0; ++t) {
             const double tsum = tile_sum_of<DT, VEC, NT>(s, t, groups);
             if (tsum > 0.0 && P + tsum > tau)
                 tile = t;
@@ -358,7 +398,7 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
         token = scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
     }
     if (lane == 0)
-        out_tok[b * (G + 1) + k] = token;
+        out_tok[static_cast<size_t>(b) * (G + 1) + k] = token;
 }
 
 template <int DT, bool VEC>
