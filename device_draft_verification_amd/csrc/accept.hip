@@ -80,6 +80,9 @@ __global__ __launch_bounds__(64) void accept_kernel(
     // entries of rows i and G + i in rn and lse_out. Decisions made for a
     // sequence that turns out to be invalid are discarded below.
     int k = G;
+    // coefficients of position k, broadcast from its lane once k is known
+    float k_mp = 0.0f, k_mq = 0.0f, k_ratio = 1.0f;
+    bool k_done = false;
     for (int i0 = 0; i0 <= G; i0 += 64) {
         const int i = i0 + lane;
         const bool has_draft = i < G;
@@ -93,6 +96,7 @@ __global__ __launch_bounds__(64) void accept_kernel(
                 bad = true;
         }
         bool reject = false;
+        RowNorm rq{0.0f, -1, 1.0}, rp{0.0f, -1, 1.0};
         if (mode == 1 && has_target) {
             // raw logits of the draft token, recorded by the row kernel
             float zq = 0.0f, zp = 0.0f;
@@ -100,7 +104,6 @@ __global__ __launch_bounds__(64) void accept_kernel(
                 zq = gathered[row0 + i];
                 zp = gathered[row0 + G + i];
             }
-            RowNorm rq{}, rp;
             if (has_draft) {
                 if (!merge_sampled(part + (row0 + i) * nsplit, nsplit, &rq))
                     bad = true;
@@ -138,6 +141,16 @@ __global__ __launch_bounds__(64) void accept_kernel(
         const unsigned long long mask = __ballot(reject);
         if (mask && k == G)
             k = i0 + __ffsll(static_cast<long long>(mask)) - 1;
+        // position k lies in this pass: first rejection here, or no rejection
+        // at all and this is the pass holding position G (wave-uniform test)
+        if (!k_done && k >= i0 && k < i0 + 64 && (k < G || G < i0 + 64)) {
+            const int src = k - i0;
+            k_mp = __shfl(rp.m, src, 64);
+            k_mq = __shfl(rq.m, src, 64);
+            const double sp = __shfl(rp.s, src, 64), sq = __shfl(rq.s, src, 64);
+            k_ratio = k < G ? static_cast<float>(sq / sp) : 1.0f;
+            k_done = true;
+        }
     }
     bad = __ballot(bad) != 0ull;
 
@@ -150,7 +163,7 @@ __global__ __launch_bounds__(64) void accept_kernel(
         }
         if (lane == 0) {
             out_len[b] = -1;
-            seq[b] = SeqState{0, 0, 0.0f, 0};
+            seq[b] = SeqState{0, 0, 0.0f, 0.0f, 0.0f, 0.0f, 1.0f, 0};
         }
         return;
     }
@@ -169,7 +182,7 @@ __global__ __launch_bounds__(64) void accept_kernel(
     if (lane == 0) {
         out_len[b] = k;
         const Words4 w = verify_block(seed, offset, static_cast<uint32_t>(b), static_cast<uint32_t>(k));
-        seq[b] = SeqState{k, mode == 1 ? 1 : 0, uniform24(w.w1), 0};
+        seq[b] = SeqState{k, mode == 1 ? 1 : 0, uniform24(w.w1), inv_t, k_mp, k_mq, k_ratio, 0};
     }
 }
 

@@ -23,6 +23,7 @@ struct spec_verify_ctx {
     int row_unroll = 8;       // 16-byte groups in flight per thread in that kernel
     bool row_nontemporal = true;
     int nsplit_residual = 1;  // vocabulary splits of the residual kernel
+    int residual_unroll = 4;  // tiles per batch per wavefront in that kernel
 
     void* ws = nullptr;
     Partial* part = nullptr;
@@ -118,6 +119,9 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     if (ou == 2 || ou == 4 || ou == 8)
         ctx->row_unroll = ou;
     ctx->row_nontemporal = env_int("SPEC_VERIFY_ROW_NT", ctx->row_nontemporal ? 1 : 0) != 0;
+    const int ru = env_int("SPEC_VERIFY_RESIDUAL_UNROLL", 0);
+    if (ru == 2 || ru == 4)
+        ctx->residual_unroll = ru;
     // A dispatch holds fewer than 2^32 work-items.
     const long long limit = 1LL << 32;
     if (static_cast<long long>(rows) * ctx->nsplit_rows * kBlock >= limit ||
@@ -208,8 +212,8 @@ int spec_verify(spec_verify_ctx* ctx, const void* logits_draft, const void* logi
         return SPEC_EHIP;
     if (ev && hipEventRecord(ev[2], st) != hipSuccess)
         return SPEC_EHIP;
-    if (launch_residual(s, vec, ctx->nsplit_residual, logits_draft, logits_target, temperature,
-                        ctx->seq, ctx->rn, ctx->tile_sums, out_tokens, st) != hipSuccess)
+    if (launch_residual(s, vec, ctx->nsplit_residual, ctx->residual_unroll, logits_draft,
+                        logits_target, ctx->seq, ctx->tile_sums, out_tokens, st) != hipSuccess)
         return SPEC_EHIP;
     if (ev && hipEventRecord(ev[3], st) != hipSuccess)
         return SPEC_EHIP;

@@ -34,11 +34,16 @@ struct RowNorm {
     double s;
 };
 
-// What the accept kernel leaves for the residual kernel, per sequence.
+// What the accept kernel leaves for the residual kernels, per sequence: the
+// outcome and every coefficient they need, so their prologue is one load.
 struct SeqState {
     int k;        // first rejected position, or gamma
     int mode;     // 1: draw the extra token from the residual / bonus row
     float u_res;  // resample uniform of position k
+    float inv_t;  // fl32(1 / T)
+    float mp;     // base-2 reference of target row k
+    float mq;     // base-2 reference of draft row k (k < gamma)
+    float ratio;  // s_q / s_p of those rows (k < gamma), else 1
     int pad;
 };
 

@@ -50,13 +50,13 @@ hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const vo
                          hipStream_t stream);
 
 // Residual / bonus draw at the first rejection: per-tile sums (B * nsplit
-// workgroups), then one locating wavefront per sequence. tile_sums holds
+// workgroups, `unroll` tiles per batch per wavefront: 2 or 4), then one
+// locating wavefront per sequence. tile_sums holds
 // B * residual_tiles_per_row(vocab) floats.
 int residual_tiles_per_row(int vocab);
-hipError_t launch_residual(const Shape& s, bool vec, int nsplit, const void* draft,
-                           const void* target, const float* temperature, const SeqState* seq,
-                           const RowNorm* rn, float* tile_sums, int32_t* out_tok,
-                           hipStream_t stream);
+hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, const void* draft,
+                           const void* target, const SeqState* seq, float* tile_sums,
+                           int32_t* out_tok, hipStream_t stream);
 
 // Scalar-only accept on gathered log-probability pairs.
 hipError_t launch_accept_scalar(int batch, int gamma, const float* logprobs, uint64_t seed,

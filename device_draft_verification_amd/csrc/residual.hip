@@ -55,29 +55,12 @@ __device__ inline void seq_row_ptrs(SeqRows& s, const void* draft, const void* t
     s.qrow = s.p_only ? s.prow : row_ptr(draft, DT, static_cast<size_t>(b) * G + k, vocab);
 }
 
-// Scaling coefficients of those rows from the row normalisers.
-__device__ inline void seq_row_coefs(SeqRows& s, const float* temperature, int G, int b, int k,
-                                     const RowNorm* rn) {
-    temperature_mode(temperature[b], &s.inv_t);
-    const size_t row0 = static_cast<size_t>(b) * (2 * G + 1);
-    const RowNorm np = rn[row0 + G + k];
-    s.mp = np.m;
-    s.mq = 0.0f;
-    s.ratio = 1.0f;
-    if (!s.p_only) {
-        const RowNorm nq = rn[row0 + k];
-        s.mq = nq.m;
-        s.ratio = static_cast<float>(nq.s / np.s);
-    }
-}
-
-template <int DT>
-__device__ inline SeqRows seq_rows(const void* draft, const void* target, const float* temperature,
-                                   int G, int vocab, int b, int k, const RowNorm* rn) {
-    SeqRows s;
-    seq_row_ptrs<DT>(s, draft, target, G, vocab, b, k);
-    seq_row_coefs(s, temperature, G, b, k, rn);
-    return s;
+// Scaling coefficients of those rows, as the accept kernel left them.
+__device__ inline void seq_row_coefs(SeqRows& s, const SeqState& st) {
+    s.inv_t = st.inv_t;
+    s.mp = st.mp;
+    s.mq = st.mq;
+    s.ratio = st.ratio;
 }
 
 template <int DT, bool VEC, bool NT>
@@ -149,32 +132,27 @@ __device__ inline float tile_reduce(float v) {
 
 template <int DT, bool VEC, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
-    const void* __restrict__ draft, const void* __restrict__ target,
-    const float* __restrict__ temperature, int gamma, int vocab, int nsplit, int tiles_per_row,
-    const SeqState* __restrict__ seq, const RowNorm* __restrict__ rn,
+    const void* __restrict__ draft, const void* __restrict__ target, int gamma, int vocab,
+    int ntiles, int tiles_per_split, int tiles_per_row, const SeqState* __restrict__ seq,
     float* __restrict__ tile_sums) {
     using IO = GroupIO<DT, VEC, NT>;
     constexpr int W = IO::W;
-    const int blk = blockIdx.x;
-    const int c = blk % nsplit;
-    const int b = blk / nsplit;
+    // grid: x = sequence, y = vocabulary split
+    const int b = blockIdx.x;
     const SeqState st = seq[b];
     if (st.mode != 1)
         return;  // greedy or rejected sequence: nothing to draw
     const int groups = vocab / W;
-    const int ntiles = (groups + kTile - 1) / kTile;
-    long lt0, lt1;
-    split_range(ntiles, nsplit, c, &lt0, &lt1);
-    const int t0 = static_cast<int>(lt0), t1 = static_cast<int>(lt1);
+    const int t0 = blockIdx.y * tiles_per_split;
+    const int t1 = t0 + tiles_per_split < ntiles ? t0 + tiles_per_split : ntiles;
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     float* out = tile_sums + static_cast<size_t>(b) * tiles_per_row;
 
-    // The first batch of loads needs only the row pointers; issue it before
-    // the normaliser loads so the two latencies overlap.
+    // Double-buffered: the loads of the next batch are in flight while this
+    // batch is reduced.
     SeqRows s;
     seq_row_ptrs<DT>(s, draft, target, gamma, vocab, b, st.k);
-    IO io[U];
-    auto load_batch = [&](int t) {
+    auto load_batch = [&](IO (&io)[U], int t) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int g = (t + u * kWaves) * kTile + lane;
@@ -182,12 +160,7 @@ __global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
                 io[u].load(s, g);
         }
     };
-    int t = t0 + wid;
-    if (t < t1)
-        load_batch(t);
-    seq_row_coefs(s, temperature, gamma, b, st.k, rn);
-
-    while (t < t1) {
+    auto reduce_batch = [&](const IO (&io)[U], int t) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int tt = t + u * kWaves;
@@ -204,9 +177,24 @@ __global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
             if (lane == 0)
                 out[tt] = ts;
         }
-        t += kWaves * U;
-        if (t < t1)
-            load_batch(t);
+    };
+    constexpr int kStep = kWaves * U;
+    IO buf_a[U], buf_b[U];
+    int t = t0 + wid;
+    if (t < t1)
+        load_batch(buf_a, t);
+    seq_row_coefs(s, st);
+    while (t < t1) {
+        if (t + kStep < t1)
+            load_batch(buf_b, t + kStep);
+        reduce_batch(buf_a, t);
+        t += kStep;
+        if (t >= t1)
+            break;
+        if (t + kStep < t1)
+            load_batch(buf_a, t + kStep);
+        reduce_batch(buf_b, t);
+        t += kStep;
     }
 }
 
@@ -343,9 +331,8 @@ __device__ inline double tile_sum_of(const SeqRows& s, int t, int groups) {
 
 template <int DT, bool VEC, bool NT>
 __global__ __launch_bounds__(64) void residual_locate_kernel(
-    const void* __restrict__ draft, const void* __restrict__ target,
-    const float* __restrict__ temperature, int gamma, int vocab, int tiles_per_row,
-    const SeqState* __restrict__ seq, const RowNorm* __restrict__ rn,
+    const void* __restrict__ draft, const void* __restrict__ target, int gamma, int vocab,
+    int ntiles, int tiles_per_row, const SeqState* __restrict__ seq,
     const float* __restrict__ tile_sums, int32_t* __restrict__ out_tok) {
     constexpr int W = Group<DT, VEC>::W;
     const int b = blockIdx.x;
@@ -353,9 +340,10 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
     if (st.mode != 1)
         return;
     const int G = gamma, k = st.k;
-    SeqRows s = seq_rows<DT>(draft, target, temperature, G, vocab, b, k, rn);
+    SeqRows s;
+    seq_row_ptrs<DT>(s, draft, target, G, vocab, b, k);
+    seq_row_coefs(s, st);
     const int groups = vocab / W;
-    const int ntiles = (groups + kTile - 1) / kTile;
     const float* ts = tile_sums + static_cast<size_t>(b) * tiles_per_row;
     const int lane = threadIdx.x & 63;
 
@@ -401,47 +389,60 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
         out_tok[static_cast<size_t>(b) * (G + 1) + k] = token;
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int U>
 hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const void* draft,
-                        const void* target, const float* temperature, const SeqState* seq,
-                        const RowNorm* rn, float* tile_sums, int32_t* out_tok, hipStream_t stream) {
-    constexpr int U = VEC ? 4 : 8;
+                        const void* target, const SeqState* seq, float* tile_sums,
+                        int32_t* out_tok, hipStream_t stream) {
     constexpr bool NT = VEC;
-    const long blocks = static_cast<long>(sh.batch) * nsplit;
-    if (blocks == 0)
+    constexpr int W = Group<DT, VEC>::W;
+    if (sh.batch == 0)
         return hipSuccess;
-    residual_tiles_kernel<DT, VEC, U, NT><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream>>>(
-        draft, target, temperature, sh.gamma, sh.vocab, nsplit, tiles_per_row, seq, rn, tile_sums);
+    const int groups = sh.vocab / W;
+    const int ntiles = (groups + kTile - 1) / kTile;
+    const int per = (ntiles + nsplit - 1) / nsplit;
+    residual_tiles_kernel<DT, VEC, U, NT><<<dim3(static_cast<unsigned>(sh.batch), static_cast<unsigned>(nsplit)),
+                                            dim3(kBlock), 0, stream>>>(
+        draft, target, sh.gamma, sh.vocab, ntiles, per, tiles_per_row, seq, tile_sums);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     residual_locate_kernel<DT, VEC, NT><<<dim3(static_cast<unsigned>(sh.batch)), dim3(64), 0, stream>>>(
-        draft, target, temperature, sh.gamma, sh.vocab, tiles_per_row, seq, rn, tile_sums, out_tok);
+        draft, target, sh.gamma, sh.vocab, ntiles, tiles_per_row, seq, tile_sums, out_tok);
     return hipGetLastError();
+}
+
+template <int DT, bool VEC>
+hipError_t launch_unroll(const Shape& sh, int nsplit, int unroll, int tiles_per_row,
+                         const void* draft, const void* target, const SeqState* seq,
+                         float* tile_sums, int32_t* out_tok, hipStream_t stream) {
+    if (unroll == 2)
+        return launch_typed<DT, VEC, 2>(sh, nsplit, tiles_per_row, draft, target, seq, tile_sums,
+                                        out_tok, stream);
+    return launch_typed<DT, VEC, 4>(sh, nsplit, tiles_per_row, draft, target, seq, tile_sums,
+                                    out_tok, stream);
 }
 
 }  // namespace
 
 int residual_tiles_per_row(int vocab) { return (vocab + kTile - 1) / kTile; }
 
-hipError_t launch_residual(const Shape& s, bool vec, int nsplit, const void* draft,
-                           const void* target, const float* temperature, const SeqState* seq,
-                           const RowNorm* rn, float* tile_sums, int32_t* out_tok,
-                           hipStream_t stream) {
+hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, const void* draft,
+                           const void* target, const SeqState* seq, float* tile_sums,
+                           int32_t* out_tok, hipStream_t stream) {
     if (nsplit < 1 || nsplit > kMaxSplit)
         return hipErrorInvalidValue;
     // Tile sums are laid out with the element-path tile count, which bounds the
     // 16-byte-group tile count.
     const int tiles = residual_tiles_per_row(s.vocab);
     if (s.dtype == kBF16)
-        return vec ? launch_typed<kBF16, true>(s, nsplit, tiles, draft, target, temperature, seq, rn,
-                                               tile_sums, out_tok, stream)
-                   : launch_typed<kBF16, false>(s, nsplit, tiles, draft, target, temperature, seq,
-                                                rn, tile_sums, out_tok, stream);
-    return vec ? launch_typed<kF32, true>(s, nsplit, tiles, draft, target, temperature, seq, rn,
-                                          tile_sums, out_tok, stream)
-               : launch_typed<kF32, false>(s, nsplit, tiles, draft, target, temperature, seq, rn,
-                                           tile_sums, out_tok, stream);
+        return vec ? launch_unroll<kBF16, true>(s, nsplit, unroll, tiles, draft, target, seq,
+                                                tile_sums, out_tok, stream)
+                   : launch_unroll<kBF16, false>(s, nsplit, unroll, tiles, draft, target, seq,
+                                                 tile_sums, out_tok, stream);
+    return vec ? launch_unroll<kF32, true>(s, nsplit, unroll, tiles, draft, target, seq, tile_sums,
+                                           out_tok, stream)
+               : launch_unroll<kF32, false>(s, nsplit, unroll, tiles, draft, target, seq,
+                                            tile_sums, out_tok, stream);
 }
 
 }  // namespace specv

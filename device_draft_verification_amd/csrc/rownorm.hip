@@ -37,20 +37,49 @@ __device__ inline float pairwise_sum(float (&t)[N]) {
     return t[0];
 }
 
-// Adds a batch of N scaled logits to the running (m, s), moving the reference m
-// to the batch max first: max(m, fl32(max x * log2e)).
-template <int N>
-__device__ inline void online_add(const float (&x)[N], float& m, double& s) {
-    float gm = x[0];
+// Batch helpers on the raw loads of U groups (W logits each). Sums are formed
+// per group by a pairwise tree and then by a pairwise tree over the groups,
+// i.e. a pairwise tree over the batch in index-within-batch order.
+
+// Largest scaled logit of the batch.
+template <class Ld, int U>
+__device__ inline float batch_max(const typename Ld::raw_t (&q)[U], float inv_t) {
+    float gm = -__builtin_huge_valf();
 #pragma unroll
-    for (int e = 1; e < N; ++e)
-        gm = fmaxf(gm, x[e]);
-    const float mn = fmaxf(m, gm * kLog2e);
-    float t[N];
+    for (int u = 0; u < U; ++u) {
+        float z[Ld::W];
+        Ld::unpack(q[u], z);
 #pragma unroll
-    for (int e = 0; e < N; ++e)
-        t[e] = fast_exp2(__builtin_fmaf(x[e], kLog2e, -mn));
-    const float g = pairwise_sum(t);
+        for (int e = 0; e < Ld::W; ++e)
+            gm = fmaxf(gm, scale_logit(z[e], inv_t));
+    }
+    return gm;
+}
+
+// sum over the batch of 2^(fma(x, log2e, -m)), x = fl32(z * inv_t)
+template <class Ld, int U>
+__device__ inline float batch_sum(const typename Ld::raw_t (&q)[U], float inv_t, float m) {
+    float gs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float z[Ld::W];
+        Ld::unpack(q[u], z);
+        float t[Ld::W];
+#pragma unroll
+        for (int e = 0; e < Ld::W; ++e)
+            t[e] = fast_exp2(__builtin_fmaf(scale_logit(z[e], inv_t), kLog2e, -m));
+        gs[u] = pairwise_sum(t);
+    }
+    return pairwise_sum(gs);
+}
+
+// Adds a batch to the running (m, s), first moving the reference m to
+// max(m, fl32(batch max * log2e)) and rescaling s by 2^(m_old - m_new).
+template <class Ld, int U>
+__device__ inline void online_add(const typename Ld::raw_t (&q)[U], float inv_t, float& m,
+                                  double& s) {
+    const float mn = fmaxf(m, batch_max<Ld, U>(q, inv_t) * kLog2e);
+    const float g = batch_sum<Ld, U>(q, inv_t, mn);
     const float sc = (mn == m) ? 1.0f : fast_exp2(m - mn);
     s = __builtin_fma(s, static_cast<double>(sc), static_cast<double>(g));
     m = mn;
@@ -58,21 +87,19 @@ __device__ inline void online_add(const float (&x)[N], float& m, double& s) {
 
 // The same with a lazy reference: the batch is summed against the current m,
 // and only a batch whose sum leaves [0, 2^64] (a term above 2^64: the
-// reference is far below the batch max, or no finite reference yet) is redone
-// with online_add. Terms up to 2^64 are exact in fp32 range, so the result is
-// a valid (m, s) pair; m may sit below the row max by up to 64 in base-2 units.
-template <int N>
-__device__ inline void lazy_add(const float (&x)[N], float& m, double& s) {
-    float t[N];
-#pragma unroll
-    for (int e = 0; e < N; ++e)
-        t[e] = fast_exp2(__builtin_fmaf(x[e], kLog2e, -m));
-    const float g = pairwise_sum(t);
+// reference is far below the batch max, or there is no finite reference yet)
+// is redone with online_add. Terms up to 2^64 are well inside the fp32 range,
+// so the result is a valid (m, s) pair; m may sit below the row max by up to
+// 64 in base-2 units.
+template <class Ld, int U>
+__device__ inline void lazy_add(const typename Ld::raw_t (&q)[U], float inv_t, float& m,
+                                double& s) {
+    const float g = batch_sum<Ld, U>(q, inv_t, m);
     if (g <= 18446744073709551616.0f) {
         s += static_cast<double>(g);
         return;
     }
-    online_add(x, m, s);
+    online_add<Ld, U>(q, inv_t, m, s);
 }
 
 template <int DT, bool VEC, int U, bool NT>
@@ -98,13 +125,33 @@ __global__ __launch_bounds__(kBlock) void row_norm_kernel(
         ? row_ptr(draft, DT, static_cast<size_t>(b) * gamma + j, vocab)
         : row_ptr(target, DT, static_cast<size_t>(b) * (gamma + 1) + (j - gamma), vocab);
 
-    const long groups = vocab / W;
-    long g0, g1;
-    split_range(groups, nsplit, c, &g0, &g1);
+    // Splits are whole multiples of a batch stride (U groups per thread), so
+    // only the row's last split ends in a partial batch.
+    const int groups = vocab / W;
+    constexpr int kStride = U * kBlock;
+    const int strides = (groups + kStride - 1) / kStride;
+    const int per = (strides + nsplit - 1) / nsplit * kStride;
+    const int g0 = c * per < groups ? c * per : groups;
+    const int g1 = g0 + per < groups ? g0 + per : groups;
+    // g < full_end: all U groups of the batch lie inside the split
+    const int full_end = g1 - (U - 1) * kBlock;
 
     __shared__ float lds_f[kWaves];
     __shared__ double lds_d[kWaves];
     __shared__ int lds_i[kWaves];
+
+    auto load_batch = [&](int g, typename Ld::raw_t (&q)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            q[u] = Ld::template load_as<NT>(rp, g + u * kBlock);
+    };
+    auto load_batch_tail = [&](int g, typename Ld::raw_t (&q)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = g + u * kBlock;
+            q[u] = idx < g1 ? Ld::template load_as<NT>(rp, idx) : Ld::neg_inf();
+        }
+    };
 
     if (mode == 0) {
         // Greedy row: largest raw logit, lowest index on ties. Each thread
@@ -112,13 +159,7 @@ __global__ __launch_bounds__(kBlock) void row_norm_kernel(
         // lowest index of equal values.
         float bv = -__builtin_huge_valf();
         int bi = 0x7fffffff;
-        for (long g = g0 + threadIdx.x; g < g1; g += static_cast<long>(U) * kBlock) {
-            typename Ld::raw_t q[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const long idx = g + static_cast<long>(u) * kBlock;
-                q[u] = idx < g1 ? Ld::template load_as<NT>(rp, idx) : Ld::neg_inf();
-            }
+        auto scan = [&](int g, const typename Ld::raw_t (&q)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float z[W];
@@ -127,10 +168,21 @@ __global__ __launch_bounds__(kBlock) void row_norm_kernel(
                 for (int e = 0; e < W; ++e) {
                     if (z[e] > bv) {
                         bv = z[e];
-                        bi = static_cast<int>((g + static_cast<long>(u) * kBlock) * W + e);
+                        bi = (g + u * kBlock) * W + e;
                     }
                 }
             }
+        };
+        int g = g0 + threadIdx.x;
+        for (; g < full_end; g += U * kBlock) {
+            typename Ld::raw_t q[U];
+            load_batch(g, q);
+            scan(g, q);
+        }
+        if (g < g1) {
+            typename Ld::raw_t q[U];
+            load_batch_tail(g, q);
+            scan(g, q);
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
@@ -159,62 +211,63 @@ __global__ __launch_bounds__(kBlock) void row_norm_kernel(
         return;
     }
 
-    // The draft token scored by this row (rows of position i < G): the thread
-    // whose batch holds its group records the raw logit for the accept kernel,
-    // which then needs no gather of its own.
+    // The draft token scored by this row (rows of position i < G): the one
+    // thread whose groups include the token's group records its raw logit for
+    // the accept kernel, which then needs no gather of its own. Thread t visits
+    // groups g0 + t + n * kBlock, n = 0, 1, ..., in batches of U.
     const int pos = is_draft ? j : j - gamma;
-    long tg = -1;
-    int te = 0;
+    int cap_batch = -1, cap_u = 0, cap_e = 0;
     if (pos < gamma) {
         const int t = tokens[static_cast<size_t>(b) * gamma + pos];
         if (t >= 0 && t < vocab) {
-            tg = t / W;
-            te = t % W;
+            const int tg = t / W;
+            if (tg >= g0 && tg < g1 && (tg - g0) % kBlock == static_cast<int>(threadIdx.x)) {
+                const int n = (tg - g0) / kBlock;
+                cap_batch = n / U;
+                cap_u = n % U;
+                cap_e = t % W;
+            }
         }
     }
-
-    // Every batch is U groups wide; groups past the split's end read as -inf,
-    // which adds nothing, so the split's tail keeps U loads in flight too.
-    float m = kNegMax;
-    double s = 0.0;
-    bool first = true;
-    for (long g = g0 + threadIdx.x; g < g1; g += static_cast<long>(U) * kBlock) {
-        typename Ld::raw_t q[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const long idx = g + static_cast<long>(u) * kBlock;
-            q[u] = idx < g1 ? Ld::template load_as<NT>(rp, idx) : Ld::neg_inf();
-        }
-        // (only inside this split: groups past g1 were not loaded here)
-        if (tg >= g && tg < g1 && tg < g + static_cast<long>(U) * kBlock && (tg - g) % kBlock == 0) {
-            const int uu = static_cast<int>((tg - g) / kBlock);
-            float zt = 0.0f;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float z[W];
-                Ld::unpack(q[u], z);
-#pragma unroll
-                for (int e = 0; e < W; ++e)
-                    zt = (u == uu && e == te) ? z[e] : zt;
-            }
-            gathered[row] = zt;
-        }
-        float x[U * W];
+    auto capture = [&](const typename Ld::raw_t (&q)[U]) {
+        float zt = 0.0f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float z[W];
             Ld::unpack(q[u], z);
 #pragma unroll
             for (int e = 0; e < W; ++e)
-                x[u * W + e] = scale_logit(z[e], inv_t);
+                zt = (u == cap_u && e == cap_e) ? z[e] : zt;
         }
+        gathered[row] = zt;
+    };
+
+    // (m, s) accumulation. Full batches load without predication; the split's
+    // last partial batch reads groups past its end as -inf, which adds nothing.
+    float m = kNegMax;
+    double s = 0.0;
+    auto accumulate = [&](const typename Ld::raw_t (&q)[U], bool first) {
         // the first batch sets the reference; later batches rarely move it
-        if (first) {
-            online_add(x, m, s);
-            first = false;
-        } else {
-            lazy_add(x, m, s);
-        }
+        if (first)
+            online_add<Ld, U>(q, inv_t, m, s);
+        else
+            lazy_add<Ld, U>(q, inv_t, m, s);
+    };
+    int g = g0 + threadIdx.x;
+    int batch = 0;
+    for (; g < full_end; g += U * kBlock, ++batch) {
+        typename Ld::raw_t q[U];
+        load_batch(g, q);
+        if (batch == cap_batch)
+            capture(q);
+        accumulate(q, batch == 0);
+    }
+    if (g < g1) {
+        typename Ld::raw_t q[U];
+        load_batch_tail(g, q);
+        if (batch == cap_batch)
+            capture(q);
+        accumulate(q, batch == 0);
     }
 
     const float bm = block_max(m, lds_f);
