@@ -155,6 +155,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=WORKLOAD_CONFIG, choices=[1, 2, 3, 4, 5],
+                    help="which of the five workloads to time (default: the B=256 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (counter calibration)")
@@ -176,23 +178,25 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     sv.load_library()
     dev = torch.device("cuda:0")
-    rec = specgen.config(WORKLOAD_CONFIG)
+    rec = specgen.config(args.workload)
     B, G, V = rec.batch, rec.gamma, rec.vocab
     t0 = time.perf_counter()
     d = specgen.generate(rec)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
 
-    def bf16(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
 
-    draft0, target0 = bf16(d["logits_draft"]), bf16(d["logits_target"])
+    draft0, target0 = to_dev(d["logits_draft"]), to_dev(d["logits_target"])
     copies = [(draft0, target0)] + [(draft0.clone(), target0.clone()) for _ in range(args.copies - 1)]
     tokens = torch.from_numpy(d["draft_tokens"]).to(dev)
     temp = torch.from_numpy(d["temperature"]).to(dev)
     alen = torch.empty(B, dtype=torch.int32, device=dev)
     toks = torch.empty(B, G + 1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
-    ctx = sv.spec_verify_init(B, G, V, torch.bfloat16, stream=stream)
+    ctx = sv.spec_verify_init(B, G, V, target0.dtype, stream=stream)
     geo = sv.spec_verify_get_geometry(ctx)
 
     def step(i):
@@ -220,6 +224,23 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+
+    # Scalar-only mode at B = 512, gamma = 4 (the [512, 4, 2] fp32 pairs the
+    # B=512 workload specifies); the pair values do not change the work.
+    sc_b, sc_g = 512, 4
+    sc_ctx = sv.spec_verify_init(sc_b, sc_g, 8, torch.float32, stream=stream)
+    sc_lp = torch.randn(sc_b, sc_g, 2, device=dev) - 2.0
+    sc_out = torch.empty(sc_b, dtype=torch.int32, device=dev)
+    for i in range(args.warmup):
+        sv.spec_accept_logprobs(sc_ctx, sc_lp, 0, i, sc_out)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        sv.spec_accept_logprobs(sc_ctx, sc_lp, 0, i, sc_out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    scalar_us = start.elapsed_time(end) * 1e3 / args.steps
+    sv.spec_verify_destroy(sc_ctx)
 
     # The same K steps again with the library's per-kernel HIP events, recorded
     # on the stream the kernels are launched on (each event adds a few us
@@ -253,7 +274,7 @@ def main() -> int:
         f"accept {k2_ms * 1e3:.1f} us, residual {k3_ms * 1e3:.1f} us ({k3_gbs:.0f} GB/s); "
         f"whole call {call_gbs:.0f} GB/s")
 
-    traffic = load_traffic(int(k1_bytes))
+    traffic = load_traffic(int(k1_bytes)) if args.workload == WORKLOAD_CONFIG else None
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -265,10 +286,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if rec.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": rec.name, "batch": B, "gamma": G, "vocab": V,
-                   "logits": "bf16", "greedy_fraction": 0.1, "parallelism": "none"},
+                   "logits": rec.dtype,
+                   "greedy_fraction": round(float((d["temperature"] == 0).mean()), 3),
+                   "parallelism": "none"},
         "hbm_gbs_whole_call": round(call_gbs, 1),
         "hbm_frac_whole_call": round(call_gbs / HBM_PEAK_GBS, 4),
         "kernels": {
@@ -280,6 +303,9 @@ def main() -> int:
                          "gbs": round(k3_gbs, 1), "frac": round(k3_gbs / HBM_PEAK_GBS, 4),
                          "splits": geo["residual_splits"]},
         },
+        "scalar_mode": {"us_per_call": round(scalar_us, 2), "batch": sc_b, "gamma": sc_g,
+                        "bytes": sc_b * sc_g * 8 + sc_b * 4,
+                        "sequences_per_s": round(sc_b / (scalar_us * 1e-6), 1)},
         "roofline": {"bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "row_norm_kernel"},

@@ -118,6 +118,13 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     const int ou = env_int("SPEC_VERIFY_ROW_UNROLL", 0);
     if (ou == 2 || ou == 4 || ou == 8)
         ctx->row_unroll = ou;
+    // Row splits are whole batch strides (unroll x kBlock groups): more splits
+    // than strides would only add empty splits for the accept kernel to merge.
+    {
+        const long stride = static_cast<long>(ctx->row_unroll) * kBlock;
+        const long strides = std::max(1L, (vocab / group_width(dtype) + stride - 1) / stride);
+        ctx->nsplit_rows = static_cast<int>(std::min<long>(ctx->nsplit_rows, strides));
+    }
     ctx->row_nontemporal = env_int("SPEC_VERIFY_ROW_NT", ctx->row_nontemporal ? 1 : 0) != 0;
     const int ru = env_int("SPEC_VERIFY_RESIDUAL_UNROLL", 0);
     if (ru == 2 || ru == 4)

@@ -69,10 +69,12 @@ struct GroupIO {
     static constexpr int W = Ld::W;
     typename Ld::raw_t p, q;
 
+    // Both rows are always loaded (for a bonus row qrow == prow), so a batch
+    // of loads has no branches and the compiler can wait for each group's
+    // loads alone instead of for everything in flight.
     __device__ inline void load(const SeqRows& s, int g) {
         p = Ld::template load_as<NT>(s.prow, g);
-        if (!s.p_only)
-            q = Ld::template load_as<NT>(s.qrow, g);
+        q = Ld::template load_as<NT>(s.qrow, g);
     }
 
     // r' of the group's elements, in index order.
@@ -145,19 +147,22 @@ __global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
     const int groups = vocab / W;
     const int t0 = blockIdx.y * tiles_per_split;
     const int t1 = t0 + tiles_per_split < ntiles ? t0 + tiles_per_split : ntiles;
-    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
     float* out = tile_sums + static_cast<size_t>(b) * tiles_per_row;
 
     // Double-buffered: the loads of the next batch are in flight while this
     // batch is reduced.
     SeqRows s;
     seq_row_ptrs<DT>(s, draft, target, gamma, vocab, b, st.k);
+    // Loads are unconditional: a group past the split or the row reads group 0
+    // of the row instead (always in bounds) and is not used.
     auto load_batch = [&](IO (&io)[U], int t) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int g = (t + u * kWaves) * kTile + lane;
-            if (t + u * kWaves < t1 && g < groups)
-                io[u].load(s, g);
+            const bool used = t + u * kWaves < t1 && g < groups;
+            io[u].load(s, used ? g : 0);
         }
     };
     auto reduce_batch = [&](const IO (&io)[U], int t) {
@@ -181,18 +186,18 @@ __global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
     constexpr int kStep = kWaves * U;
     IO buf_a[U], buf_b[U];
     int t = t0 + wid;
-    if (t < t1)
-        load_batch(buf_a, t);
+    load_batch(buf_a, t);
     seq_row_coefs(s, st);
+    // The next batch is loaded unconditionally (a batch past the split reads
+    // group 0, which is in cache, and is never reduced): with no branch around
+    // the loads the compiler waits for exactly the group being reduced.
     while (t < t1) {
-        if (t + kStep < t1)
-            load_batch(buf_b, t + kStep);
+        load_batch(buf_b, t + kStep);
         reduce_batch(buf_a, t);
         t += kStep;
         if (t >= t1)
             break;
-        if (t + kStep < t1)
-            load_batch(buf_a, t + kStep);
+        load_batch(buf_a, t + kStep);
         reduce_batch(buf_b, t);
         t += kStep;
     }

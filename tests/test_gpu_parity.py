@@ -109,7 +109,7 @@ def big(request):
     torch.cuda.empty_cache()
 
 
-def _sample_rows(rec, d, n=14):
+def _sample_rows(rec, d, n=44):
     rng = np.random.default_rng(1000 + rec.seed)
     rows = set(rng.choice(rec.batch, size=min(n, rec.batch), replace=False).tolist())
     greedy = np.nonzero(d["temperature"] == 0)[0]
@@ -311,3 +311,64 @@ def test_argument_errors_on_device():
         sv.spec_verify(ctx, ok, ok, alen, alen, 0, 0, alen, alen)
     with pytest.raises(sv.SpecVerifyError):
         sv.spec_verify_copy_lse(ctx, torch.empty((4, 5), dtype=torch.float64, device="cuda"))
+
+
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_misaligned_base_pointers_take_the_element_path(cfg):
+    """Logit buffers whose base is not 16-byte aligned (one element in) run the
+    element-load path even though V is a multiple of the 16-byte group."""
+    rec = specgen.config(cfg).replace(batch=6, vocab=4096, gamma=3)
+    d = specgen.generate(rec)
+    t = to_device(d)
+    for key in ("logits_draft", "logits_target"):
+        x = t[key]
+        buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)
+        view = buf[1:].view(x.shape)
+        view.copy_(x)
+        assert view.data_ptr() % 16 != 0
+        t[key] = view
+    gpu = run_gpu(t)
+    rep = compare(gpu, _oracle(d), d["temperature"])
+    _report(f"misaligned {rec.name}", rep)
+    assert_parity(rep, "misaligned")
+
+
+def _scalar_compare(lp, seed, offset):
+    B, G, _ = lp.shape
+    ctx = sv.spec_verify_init(B, G, 8, torch.float32)
+    out = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    sv.spec_accept_logprobs(ctx, torch.from_numpy(lp).cuda(), seed, offset, out)
+    got = out.cpu().numpy()
+    ref = oracle.accept_logprobs(lp, seed=seed, offset=offset)
+    for b in np.nonzero(got != ref["accept_len"])[0]:
+        k = min(got[b], ref["accept_len"][b])
+        m = np.abs(ref["acc_margin"][b, :k + 1])
+        assert np.nanmin(m) < 1e-5, (b, got[b], ref["accept_len"][b])
+    return got, ref["accept_len"]
+
+
+def test_scalar_mode_edge_values():
+    rng = np.random.default_rng(17)
+    B, G = 64, 5
+    lp = rng.normal(-3, 2, size=(B, G, 2)).astype(np.float32)
+    lp[0, 0, 1] = np.nan           # NaN target log-prob: reject
+    lp[1, 0, 0] = np.nan           # NaN draft log-prob: reject
+    lp[2, 0, 1] = -np.inf          # p = 0: reject
+    lp[3, 0, 0] = -np.inf          # q = 0 with p > 0: accept
+    lp[4, :, :] = -np.inf          # both zero: NaN difference, reject
+    lp[5, :, 1] = lp[5, :, 0]      # p = q: always accept
+    got, ref = _scalar_compare(lp, 5, 9)
+    assert list(got[:3]) == [0, 0, 0]
+    assert got[3] >= 1
+    assert got[4] == 0
+    assert got[5] == G
+    assert np.array_equal(got, ref)
+
+
+def test_scalar_mode_gamma_zero_and_large_gamma():
+    got, _ = _scalar_compare(np.zeros((7, 0, 2), np.float32), 1, 2)
+    assert np.all(got == 0)
+    rng = np.random.default_rng(18)
+    lp = rng.normal(-2, 0.3, size=(300, 70, 2)).astype(np.float32)
+    got, ref = _scalar_compare(lp, 123, 456)
+    assert got.max() <= 70

@@ -1,0 +1,106 @@
+"""The oracle's pins have teeth: each test plants one plausible mistake in a
+copy of the oracle's C source, builds it, swaps it in, and checks that a pin
+fails. Mistakes are planted on the CPU only, in a temporary copy; the real
+oracle is restored after each case."""
+import contextlib
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+import test_oracle_stats as stats
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "spec_oracle.c")
+
+
+@contextlib.contextmanager
+def mutated_oracle(old: str, new: str):
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    d = tempfile.mkdtemp(prefix="oracle_mut_")
+    src = os.path.join(d, "m.c")
+    lib = os.path.join(d, "libm_oracle.so")
+    with open(src, "w") as f:
+        f.write(text.replace(old, new))
+    subprocess.run(["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off", "-o", lib,
+                    src, "-lm"], check=True, capture_output=True)
+    saved_lib, saved_path = oracle._lib, oracle.LIB_PATH
+    oracle._lib = None
+    oracle.LIB_PATH = lib
+    try:
+        oracle._load()
+        yield
+    finally:
+        oracle._lib, oracle.LIB_PATH = saved_lib, saved_path
+        shutil.rmtree(d, ignore_errors=True)
+
+
+def fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_residual_without_the_max_is_caught():
+    with mutated_oracle("r[v] = p - q > 0.0 ? p - q : 0.0;", "r[v] = p;"):
+        fails(pins.test_residual_distribution_exact_sweep, 1.0)
+
+
+def test_flipped_accept_ratio_is_caught():
+    with mutated_oracle("int accept = log_u < (lp - lq);", "int accept = log_u < (lq - lp);"):
+        fails(pins.test_accept_probability_exact_sweep, 1.0)
+
+
+def test_temperature_ignored_is_caught():
+    with mutated_oracle("float x = z * inv_t;", "float x = z;"):
+        fails(pins.test_row_lse_matches_scipy, "f32", 0.7)
+
+
+def test_philox_constant_typo_is_caught(torch_philox_exe):
+    with mutated_oracle("const uint32_t M0 = 0xD2511F53u", "const uint32_t M0 = 0xD2511F55u"):
+        fails(pins.test_philox_matches_library_engine, torch_philox_exe)
+
+
+def test_philox_round_count_is_caught(torch_philox_exe):
+    with mutated_oracle("round < 10; ++round", "round < 7; ++round"):
+        fails(pins.test_philox_matches_library_engine, torch_philox_exe)
+
+
+def test_inclusive_bin_edge_is_caught():
+    with mutated_oracle("if (prefix > tau) {", "if (prefix >= tau) {"):
+        fails(pins.test_inverse_cdf_worked_margins)
+
+
+def test_lse_without_max_shift_is_caught():
+    with mutated_oracle("s += exp(x - m);\n    }\n    return m + log(s);",
+                        "s += exp(x - m + 1e-3);\n    }\n    return m + log(s);"):
+        fails(pins.test_row_lse_closed_forms)
+
+
+def test_last_index_on_ties_is_caught():
+    with mutated_oracle("if (z > best_z) {", "if (z >= best_z) {"):
+        fails(pins.test_row_argmax_first_index_on_ties)
+
+
+def test_bonus_from_the_wrong_row_is_caught():
+    # the bonus (all accepted) draws from target row G; use row G-1 instead
+    with mutated_oracle("double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)k * V + v), inv_t);\n        double p = exp(xp - lse_p[k]);",
+                        "int kk = k == G && k > 0 ? k - 1 : k;\n        double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)kk * V + v), inv_t);\n        double p = exp(xp - lse_p[kk]);"):
+        fails(pins.test_bonus_distribution_exact_sweep)
+
+
+def test_marginal_gate_catches_a_biased_residual():
+    """The statistical gate alone (chi-square over 10,000 draws) also catches
+    drawing the correction from p instead of the residual."""
+    with mutated_oracle("r[v] = p - q > 0.0 ? p - q : 0.0;", "r[v] = p;"):
+        fails(stats.test_gate_output_marginal_is_target, stats.build_gate_case())
+
+
+@pytest.fixture(scope="module")
+def torch_philox_exe():
+    d = tempfile.mkdtemp(prefix="philox_mut_")
+    yield pins.build_torch_philox_exe(d)
+    shutil.rmtree(d, ignore_errors=True)

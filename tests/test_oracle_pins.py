@@ -66,18 +66,23 @@ int main(int argc, char** argv) {
 """
 
 
-@pytest.fixture(scope="module")
-def torch_philox_exe():
+def build_torch_philox_exe(d):
+    """Compile the library-engine Philox program into directory d; its path."""
     if TORCH_INCLUDE is None or shutil.which("g++") is None:
         pytest.skip("PyTorch C++ headers or g++ not available")
-    d = tempfile.mkdtemp(prefix="philox_pin_")
     src = os.path.join(d, "p.cpp")
     exe = os.path.join(d, "p")
     with open(src, "w") as f:
         f.write(_PHILOX_PROG)
     subprocess.run(["g++", "-std=c++17", "-O1", "-I", TORCH_INCLUDE, src, "-o", exe],
                    check=True, capture_output=True)
-    yield exe
+    return exe
+
+
+@pytest.fixture(scope="module")
+def torch_philox_exe():
+    d = tempfile.mkdtemp(prefix="philox_pin_")
+    yield build_torch_philox_exe(d)
     shutil.rmtree(d, ignore_errors=True)
 
 

@@ -65,8 +65,7 @@ def chi2_ok(samples, probs):
     return chisquare(counts[keep], exp).pvalue > ALPHA
 
 
-@pytest.fixture(scope="module")
-def gate_case():
+def build_gate_case():
     rng = np.random.default_rng(1234)
     G, V = 3, 8
     base = rng.normal(0, 1.2, size=(G + 1, V))
@@ -76,6 +75,11 @@ def gate_case():
     draft, target, toks, temp = make_batch(zq, zp, T, N_DRAWS, seed=99)
     out = oracle.verify(draft, target, toks, temp, seed=2024, offset=7)
     return dict(zq=zq, zp=zp, T=T, toks=toks, out=out, G=G, V=V)
+
+
+@pytest.fixture(scope="module")
+def gate_case():
+    return build_gate_case()
 
 
 def test_gate_acceptance_rate_closed_form(gate_case):
