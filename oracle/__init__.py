@@ -19,6 +19,12 @@ is stated at the top of ``spec_oracle.c``. Parity status of each function:
   disjoint support, greedy).
 * ``accept_logprobs`` -- pinned by agreement with ``verify`` on the gathered
   pairs and by the closed-form acceptance probability min(1, p/q).
+* ``gamma_sample`` / ``beta_sample`` (``bandit_oracle.c``) -- pinned by
+  Kolmogorov-Smirnov tests against ``scipy.stats.gamma`` / ``scipy.stats.beta``.
+* ``bandit_step`` -- UCB1 pinned by its opening round robin and by the regret
+  bound of Auer, Cesa-Bianchi and Fischer (2002, Theorem 1); Thompson sampling by
+  logarithmic regret growth; both by the output-marginal gate with the bandit
+  choosing the draft distribution every step (the pages' Theorem 1).
 """
 from __future__ import annotations
 
@@ -29,7 +35,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "spec_oracle.c")
+_SRCS = [os.path.join(_HERE, "spec_oracle.c"), os.path.join(_HERE, "bandit_oracle.c")]
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
@@ -40,7 +46,7 @@ def build() -> str:
     """Compile the oracle with gcc: -O2, no fast-math, no FP contraction."""
     tmp = LIB_PATH + ".tmp"
     cmd = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, *_SRCS, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
@@ -80,6 +86,16 @@ def _load():
     lib.oracle_accept_logprobs.restype = None
     lib.oracle_gather_logprobs.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
     lib.oracle_gather_logprobs.restype = None
+    lib.oracle_gamma_mt.argtypes = [f64, u64, u64, i32, i32, i32, P]
+    lib.oracle_gamma_mt.restype = f64
+    lib.oracle_beta_sample.argtypes = [f64, f64, u64, u64, i32, i32, P]
+    lib.oracle_beta_sample.restype = f64
+    lib.oracle_ucb1_select.argtypes = [i32, P, P, P]
+    lib.oracle_ucb1_select.restype = i32
+    lib.oracle_thompson_select.argtypes = [i32, P, P, u64, u64, i32, P]
+    lib.oracle_thompson_select.restype = i32
+    lib.oracle_bandit_step.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, u64, u64, P, P]
+    lib.oracle_bandit_step.restype = None
     _lib = lib
     return lib
 
@@ -223,3 +239,48 @@ def gather_logprobs(logits_draft, logits_target, draft_tokens, temperature):
     _load().oracle_gather_logprobs(B, G, V, dt, _ptr(zq), _ptr(zp), _ptr(tok), _ptr(temp),
                                    _ptr(out))
     return out
+
+
+UCB1 = 0
+THOMPSON = 1
+
+
+def gamma_sample(shape: float, seed: int, offset: int, group: int = 0, arm: int = 0,
+                 which: int = 0) -> tuple[float, float]:
+    """One Gamma(shape, 1) variate (shape >= 1) and the smallest decision margin."""
+    m = ctypes.c_double(np.inf)
+    x = _load().oracle_gamma_mt(float(shape), seed, offset, group, arm, which, ctypes.byref(m))
+    return x, m.value
+
+
+def beta_sample(a: float, b: float, seed: int, offset: int, group: int = 0,
+                arm: int = 0) -> tuple[float, float]:
+    m = ctypes.c_double(np.inf)
+    x = _load().oracle_beta_sample(float(a), float(b), seed, offset, group, arm, ctypes.byref(m))
+    return x, m.value
+
+
+class Bandit:
+    """G independent K-armed bandits over groups of B/G consecutive sequences.
+    ``counts`` [G, K] uint32 and ``sums`` [G, K] float64 are the whole state."""
+
+    def __init__(self, policy: int, groups: int, arms: int, batch: int, gamma: int):
+        assert policy in (UCB1, THOMPSON) and 1 <= arms <= 64 and gamma >= 1
+        assert groups >= 1 and batch % groups == 0
+        self.policy, self.G, self.K, self.B, self.gamma = policy, groups, arms, batch, gamma
+        self.counts = np.zeros((groups, arms), dtype=np.uint32)
+        self.sums = np.zeros((groups, arms), dtype=np.float64)
+
+    def step(self, accept_len=None, arm_played=None, seed: int = 0, offset: int = 0):
+        """Fold in ``accept_len`` [B] for ``arm_played`` [G] (if given), then choose.
+        Returns (next arm [G] int32, decision margin [G] float64)."""
+        al = ap = None
+        if accept_len is not None:
+            al = np.ascontiguousarray(accept_len, dtype=np.int32).reshape(self.B)
+            ap = np.ascontiguousarray(arm_played, dtype=np.int32).reshape(self.G)
+        out = np.zeros(self.G, dtype=np.int32)
+        mg = np.zeros(self.G, dtype=np.float64)
+        _load().oracle_bandit_step(self.policy, self.G, self.K, self.B, self.gamma,
+                                   _ptr(self.counts), _ptr(self.sums), _ptr(al), _ptr(ap),
+                                   seed, offset, _ptr(out), _ptr(mg))
+        return out, mg

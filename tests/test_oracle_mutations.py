@@ -11,23 +11,31 @@ import tempfile
 import pytest
 
 import oracle
+import test_bandit_oracle as bandit
 import test_oracle_pins as pins
 import test_oracle_stats as stats
 
-SRC = os.path.join(os.path.dirname(oracle.__file__), "spec_oracle.c")
+ORACLE_DIR = os.path.dirname(oracle.__file__)
+SRC = os.path.join(ORACLE_DIR, "spec_oracle.c")
+BANDIT_SRC = os.path.join(ORACLE_DIR, "bandit_oracle.c")
 
 
 @contextlib.contextmanager
-def mutated_oracle(old: str, new: str):
-    text = open(SRC).read()
+def mutated_oracle(old: str, new: str, target: str = SRC):
+    """Build the oracle library with one mistake planted in ``target``."""
+    text = open(target).read()
     assert text.count(old) >= 1, f"mutation anchor not found: {old!r}"
     d = tempfile.mkdtemp(prefix="oracle_mut_")
-    src = os.path.join(d, "m.c")
+    srcs = []
+    for path in (SRC, BANDIT_SRC):
+        out = os.path.join(d, os.path.basename(path))
+        body = open(path).read()
+        with open(out, "w") as f:
+            f.write(body.replace(old, new) if path == target else body)
+        srcs.append(out)
     lib = os.path.join(d, "libm_oracle.so")
-    with open(src, "w") as f:
-        f.write(text.replace(old, new))
     subprocess.run(["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off", "-o", lib,
-                    src, "-lm"], check=True, capture_output=True)
+                    *srcs, "-lm"], check=True, capture_output=True)
     saved_lib, saved_path = oracle._lib, oracle.LIB_PATH
     oracle._lib = None
     oracle.LIB_PATH = lib
@@ -97,6 +105,58 @@ def test_marginal_gate_catches_a_biased_residual():
     drawing the correction from p instead of the residual."""
     with mutated_oracle("r[v] = p - q > 0.0 ? p - q : 0.0;", "r[v] = p;"):
         fails(stats.test_gate_output_marginal_is_target, stats.build_gate_case())
+
+
+def ucb1_pins():
+    run = bandit.run_bandits(oracle.UCB1, seeds=24, rounds=10_000, snapshot=1_000)
+    bandit.test_ucb1_regret_within_auer_bound(run)
+    bandit.test_ucb1_regret_grows_logarithmically(run)
+
+
+def thompson_pins():
+    bandit.test_gamma_sampler_matches_scipy()
+    bandit.test_beta_sampler_matches_scipy()
+    bandit.test_thompson_choice_probabilities_match_the_posterior()
+    run = bandit.run_bandits(oracle.THOMPSON, seeds=24, rounds=10_000, snapshot=1_000)
+    bandit.test_thompson_regret_logarithmic_and_below_ucb1_bound(run)
+
+
+def test_ucb1_bonus_with_the_wrong_sign_is_caught():
+    with mutated_oracle("score[j] = mean + bonus;", "score[j] = mean - bonus;", BANDIT_SRC):
+        fails(ucb1_pins)
+
+
+def test_ucb1_sum_in_place_of_mean_is_caught():
+    with mutated_oracle("double mean = sums[j] / nj;", "double mean = sums[j];", BANDIT_SRC):
+        fails(ucb1_pins)
+
+
+def test_ucb1_without_log_of_plays_is_caught():
+    with mutated_oracle("sqrt(2.0 * log((double)n) / nj)", "sqrt(2.0 / nj)", BANDIT_SRC):
+        fails(ucb1_pins)
+
+
+def test_marsaglia_tsang_without_the_third_is_caught():
+    with mutated_oracle("const double d = shape - 1.0 / 3.0;", "const double d = shape;",
+                        BANDIT_SRC):
+        fails(thompson_pins)
+
+
+def test_box_muller_reusing_a_uniform_is_caught():
+    with mutated_oracle("cos(two_pi * u2)", "cos(two_pi * u1)", BANDIT_SRC):
+        fails(thompson_pins)
+
+
+def test_thompson_failures_counted_as_plays_is_caught():
+    with mutated_oracle("double b = 1.0 + ((double)counts[j] - sums[j]);",
+                        "double b = 1.0 + (double)counts[j];", BANDIT_SRC):
+        fails(thompson_pins)
+
+
+def test_reward_not_divided_by_gamma_is_caught():
+    with mutated_oracle("double r = (double)ksum / ((double)gamma * (double)m);",
+                        "double r = (double)ksum / (double)m;", BANDIT_SRC):
+        fails(bandit.test_bandit_skips_invalid_rows_and_bad_arms)
 
 
 @pytest.fixture(scope="module")
