@@ -242,6 +242,29 @@ def main() -> int:
     scalar_us = start.elapsed_time(end) * 1e3 / args.steps
     sv.spec_verify_destroy(sc_ctx)
 
+    # Online draft selection (K = 3 draft models): one spec_bandit_step per
+    # decoding step, reading the last call's accept lengths on the device.
+    # Launch-latency bound (a few hundred bytes); reported in us per step.
+    step(0)
+    bandit_us = {}
+    for pol_name, pol in (("ucb1", sv.SPEC_BANDIT_UCB1), ("thompson", sv.SPEC_BANDIT_THOMPSON)):
+        for groups in (1, B):
+            bctx = sv.spec_bandit_init(groups, 3, B, G, pol, stream=stream) if G > 0 else None
+            if bctx is None:
+                continue
+            arm = torch.zeros(groups, dtype=torch.int32, device=dev)
+            sv.spec_bandit_step(bctx, None, None, 1, 0, arm)
+            for i in range(args.warmup):
+                sv.spec_bandit_step(bctx, alen, arm, 1, i + 1, arm)
+            torch.cuda.synchronize()
+            start.record(stream)
+            for i in range(args.steps):
+                sv.spec_bandit_step(bctx, alen, arm, 1, args.warmup + i + 1, arm)
+            end.record(stream)
+            torch.cuda.synchronize()
+            bandit_us[f"{pol_name}_groups{groups}"] = round(start.elapsed_time(end) * 1e3 / args.steps, 2)
+            sv.spec_bandit_destroy(bctx)
+
     # The same K steps again with the library's per-kernel HIP events, recorded
     # on the stream the kernels are launched on (each event adds a few us
     # between kernels, so the step time above is taken without them).
@@ -306,6 +329,7 @@ def main() -> int:
         "scalar_mode": {"us_per_call": round(scalar_us, 2), "batch": sc_b, "gamma": sc_g,
                         "bytes": sc_b * sc_g * 8 + sc_b * 4,
                         "sequences_per_s": round(sc_b / (scalar_us * 1e-6), 1)},
+        "bandit": {"arms": 3, "us_per_step": bandit_us},
         "roofline": {"bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "row_norm_kernel"},

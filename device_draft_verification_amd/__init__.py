@@ -1,7 +1,8 @@
 """Batched speculative-sampling verification on AMD Instinct MI355X (gfx950).
 
 The work is done by hand-written HIP kernels in ``libspecverify.so`` behind the
-C ABI of ``include/spec_verify.h``; this package is a thin ctypes binding with
+C ABI of ``include/spec_verify.h`` (verification) and ``include/spec_bandit.h``
+(online draft selection); this package is a thin ctypes binding with
 the same function names (``binding``) and the build script (``build``).
 """
 from .binding import (  # noqa: F401
@@ -10,4 +11,7 @@ from .binding import (  # noqa: F401
     spec_verify_destroy, spec_verify_enable_timing, spec_verify_get_geometry,
     spec_verify_init, spec_verify_philox_words, spec_verify_read_timing,
     spec_verify_set_stream, spec_verify_strerror,
+    SPEC_BANDIT_MAX_ARMS, SPEC_BANDIT_THOMPSON, SPEC_BANDIT_UCB1, BanditContext,
+    spec_bandit_destroy, spec_bandit_get_state, spec_bandit_init, spec_bandit_set_state,
+    spec_bandit_set_stream, spec_bandit_step,
 )

@@ -28,7 +28,13 @@ EXPORTED = (
     "spec_verify_copy_lse", "spec_verify_philox_words", "spec_verify_enable_timing",
     "spec_verify_read_timing", "spec_verify_get_geometry", "spec_verify_destroy",
     "spec_verify_strerror",
+    "spec_bandit_init", "spec_bandit_set_stream", "spec_bandit_step", "spec_bandit_get_state",
+    "spec_bandit_set_state", "spec_bandit_destroy",
 )
+
+SPEC_BANDIT_UCB1 = 0
+SPEC_BANDIT_THOMPSON = 1
+SPEC_BANDIT_MAX_ARMS = 64
 
 
 class SpecVerifyError(RuntimeError):
@@ -61,6 +67,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_verify_get_geometry": ([P, P], i32),
         "spec_verify_destroy": ([P], i32),
         "spec_verify_strerror": ([i32], ctypes.c_char_p),
+        "spec_bandit_init": ([i32, i32, i32, i32, i32, P, ctypes.POINTER(P)], i32),
+        "spec_bandit_set_stream": ([P, P], i32),
+        "spec_bandit_step": ([P, P, P, u64, u64, P], i32),
+        "spec_bandit_get_state": ([P, P, P], i32),
+        "spec_bandit_set_state": ([P, P, P], i32),
+        "spec_bandit_destroy": ([P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -210,3 +222,75 @@ def spec_verify_destroy(ctx: Context) -> None:
 
 def spec_verify_strerror(code: int) -> str:
     return _strerror(code)
+
+
+class BanditContext:
+    """Owns a spec_bandit_ctx*; destroyed with spec_bandit_destroy."""
+
+    def __init__(self, handle: ctypes.c_void_p, groups: int, arms: int, batch: int, gamma: int,
+                 policy: int):
+        self.handle = handle
+        self.groups, self.arms, self.batch, self.gamma, self.policy = groups, arms, batch, gamma, policy
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                load_library().spec_bandit_destroy(self.handle)
+            except Exception:
+                pass
+            self.handle = None
+
+
+def spec_bandit_init(groups: int, arms: int, batch: int, gamma: int, policy: int,
+                     stream=None) -> BanditContext:
+    h = ctypes.c_void_p()
+    _check("spec_bandit_init", load_library().spec_bandit_init(
+        groups, arms, batch, gamma, policy, _stream_handle(stream), ctypes.byref(h)))
+    return BanditContext(h, groups, arms, batch, gamma, policy)
+
+
+def spec_bandit_set_stream(ctx: BanditContext, stream=None) -> None:
+    _check("spec_bandit_set_stream",
+           load_library().spec_bandit_set_stream(ctx.handle, _stream_handle(stream)))
+
+
+def spec_bandit_step(ctx: BanditContext, accept_len, arm_played, seed: int, offset: int,
+                     out_arm) -> None:
+    """accept_len [B] / arm_played [G] int32 device tensors (both None for the
+    first choice); out_arm [G] int32 device tensor (may be arm_played)."""
+    if accept_len is not None:
+        _expect(accept_len, (ctx.batch,), torch.int32, "accept_len")
+        _expect(arm_played, (ctx.groups,), torch.int32, "arm_played")
+    _expect(out_arm, (ctx.groups,), torch.int32, "out_arm")
+    _check("spec_bandit_step", load_library().spec_bandit_step(
+        ctx.handle, _ptr(accept_len), _ptr(arm_played) if accept_len is not None else None,
+        seed, offset, _ptr(out_arm)))
+
+
+def spec_bandit_get_state(ctx: BanditContext):
+    """(counts [G, K] uint32, sums [G, K] float64) as host numpy arrays."""
+    import numpy as np
+    counts = np.zeros((ctx.groups, ctx.arms), np.uint32)
+    sums = np.zeros((ctx.groups, ctx.arms), np.float64)
+    _check("spec_bandit_get_state", load_library().spec_bandit_get_state(
+        ctx.handle, counts.ctypes.data, sums.ctypes.data))
+    return counts, sums
+
+
+def spec_bandit_set_state(ctx: BanditContext, counts=None, sums=None) -> None:
+    """Restore a saved state (host arrays [G, K]); no arguments resets to zero."""
+    import numpy as np
+    if counts is None and sums is None:
+        _check("spec_bandit_set_state", load_library().spec_bandit_set_state(ctx.handle, None, None))
+        return
+    c = np.ascontiguousarray(counts, np.uint32).reshape(ctx.groups, ctx.arms)
+    s = np.ascontiguousarray(sums, np.float64).reshape(ctx.groups, ctx.arms)
+    _check("spec_bandit_set_state", load_library().spec_bandit_set_state(
+        ctx.handle, c.ctypes.data, s.ctypes.data))
+
+
+def spec_bandit_destroy(ctx: BanditContext) -> None:
+    if ctx.handle:
+        rc = load_library().spec_bandit_destroy(ctx.handle)
+        ctx.handle = None
+        _check("spec_bandit_destroy", rc)

@@ -1,5 +1,5 @@
 """The C ABI library without a GPU: it loads, exports every function that
-include/spec_verify.h declares, and rejects bad arguments on the host before
+the headers in include/ declare, and rejects bad arguments on the host before
 touching the device."""
 import ctypes
 import os
@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("spec_verify_init", "spec_verify", "spec_accept_logprobs", "spec_verify_destroy"):
+    for n in ("spec_verify_init", "spec_verify", "spec_accept_logprobs", "spec_verify_destroy",
+              "spec_bandit_init", "spec_bandit_step", "spec_bandit_destroy"):
         assert n in names
     assert set(names) == set(sv.EXPORTED)
 
@@ -66,6 +67,24 @@ def test_host_argument_checks(lib):
     assert lib.spec_verify_destroy(None) == sv.binding.SPEC_EINVAL
     assert lib.spec_verify_enable_timing(None, 4) == sv.binding.SPEC_EINVAL
     assert lib.spec_verify_get_geometry(None, None) == sv.binding.SPEC_EINVAL
+
+
+def test_bandit_host_argument_checks(lib):
+    E = sv.binding.SPEC_EINVAL
+    h = ctypes.c_void_p()
+    assert lib.spec_bandit_init(1, 3, 8, 4, 0, None, None) == E
+    assert lib.spec_bandit_init(0, 3, 8, 4, 0, None, ctypes.byref(h)) == E  # no groups
+    assert lib.spec_bandit_init(1, 0, 8, 4, 0, None, ctypes.byref(h)) == E  # no arms
+    assert lib.spec_bandit_init(1, 65, 8, 4, 0, None, ctypes.byref(h)) == E  # > 64 arms
+    assert lib.spec_bandit_init(3, 3, 8, 4, 0, None, ctypes.byref(h)) == E  # 8 % 3 != 0
+    assert lib.spec_bandit_init(1, 3, 8, 0, 0, None, ctypes.byref(h)) == E  # gamma 0
+    assert lib.spec_bandit_init(1, 3, 8, 4, 2, None, ctypes.byref(h)) == E  # policy
+    assert not h.value
+    assert lib.spec_bandit_step(None, None, None, 0, 0, None) == E
+    assert lib.spec_bandit_get_state(None, None, None) == E
+    assert lib.spec_bandit_set_state(None, None, None) == E
+    assert lib.spec_bandit_set_stream(None, None) == E
+    assert lib.spec_bandit_destroy(None) == E
 
 
 def test_binding_refuses_missing_library(tmp_path, lib):
