@@ -86,6 +86,8 @@ def _load():
     lib.oracle_accept_logprobs.restype = None
     lib.oracle_gather_logprobs.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
     lib.oracle_gather_logprobs.restype = None
+    lib.oracle_outcomes.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, P, P, P, P, P, P]
+    lib.oracle_outcomes.restype = None
     lib.oracle_gamma_mt.argtypes = [f64, u64, u64, i32, i32, i32, P]
     lib.oracle_gamma_mt.restype = f64
     lib.oracle_beta_sample.argtypes = [f64, f64, u64, u64, i32, i32, P]
@@ -238,6 +240,39 @@ def gather_logprobs(logits_draft, logits_target, draft_tokens, temperature):
     out = np.zeros((B, G, 2), dtype=np.float64)
     _load().oracle_gather_logprobs(B, G, V, dt, _ptr(zq), _ptr(zp), _ptr(tok), _ptr(temp),
                                    _ptr(out))
+    return out
+
+
+def outcomes(logits_draft, logits_target, draft_tokens, temperature, F: int,
+             with_dist: bool = False):
+    """Distribution of each sequence's verification outcome given its drafts:
+    per length i in [0, G] the F most likely extra tokens and their
+    probabilities, P(k = i | drafts) and the residual mass S_i. With
+    ``with_dist`` also the whole distribution and the (p + q) / S magnitudes
+    ([B, G+1, V] float64 each)."""
+    zp, dt = _logits(logits_target)
+    B, G1, V = zp.shape
+    G = G1 - 1
+    if G > 0:
+        zq, dq = _logits(logits_draft)
+        assert dq == dt and zq.shape == (B, G, V)
+        tok = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    else:
+        zq = np.zeros((1,), dtype=zp.dtype)
+        tok = np.zeros((1,), dtype=np.int32)
+    temp = np.ascontiguousarray(temperature, dtype=np.float32).reshape(B)
+    out_tok = np.zeros((B, G + 1, F), np.int32)
+    out_prob = np.zeros((B, G + 1, F), np.float64)
+    pk = np.zeros((B, G + 1), np.float64)
+    mass = np.zeros((B, G + 1), np.float64)
+    dist = np.zeros((B, G + 1, V), np.float64) if with_dist else None
+    scale = np.zeros((B, G + 1, V), np.float64) if with_dist else None
+    _load().oracle_outcomes(B, G, V, dt, _ptr(zq), _ptr(zp), _ptr(tok), _ptr(temp), F,
+                            _ptr(out_tok), _ptr(out_prob), _ptr(pk), _ptr(mass), _ptr(dist),
+                            _ptr(scale))
+    out = dict(tokens=out_tok, probs=out_prob, pk=pk, mass=mass)
+    if with_dist:
+        out.update(dist=dist, scale=scale)
     return out
 
 

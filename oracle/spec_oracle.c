@@ -470,3 +470,187 @@ void oracle_gather_logprobs(int batch, int gamma, int vocab, int dtype,
         }
     }
 }
+
+/* ----------------------------------------------- verification outcomes -- */
+
+/*
+ * The distribution of one verification's outcome, given the drafted tokens.
+ * The outcome of a verification is the pair (accepted count k, extra token)
+ * that speculative speculative decoding predicts and keys its speculation
+ * cache on; its Saguaro algorithm spends the cache on the most likely lengths
+ * and, per length, on the F most likely extra tokens of the residual
+ * distribution (Speculative Speculative Decoding summary, section 2: central
+ * concept items 1-3; Saguaro challenge 1, fan-out over likely lengths;
+ * challenge 2, the top-F tokens of the residual the bonus token is drawn from).
+ * Under the rule of this file, with the drafts t fixed:
+ *   beta_j = min(1, p_j(t_j) / q_j(t_j)), evaluated as min(1, exp(lp_j - lq_j))
+ *            (0 when lp_j - lq_j is NaN, the reject case of the test);
+ *   P(k = i | t) = prod_{j<i} beta_j * (1 - beta_i) for i < gamma,
+ *   P(k = gamma | t) = prod_{j<gamma} beta_j;
+ *   extra token | k = i  ~  r_i / S_i, r_i = max(0, p_i - q_i) for i < gamma,
+ *                           r_gamma = p_gamma; r_i = p_i when S_i == 0 (R8).
+ * Readings: R21 the list for length i holds the F tokens of largest r_i(v),
+ *   ties to the lowest index, padded with token -1 / probability 0 when V < F;
+ *   R22 greedy sequences (T == 0) have a deterministic outcome: the list holds
+ *   the F largest raw target logits (argmax first) with probabilities 1, 0, ...
+ *   and P(k = i | t) is 0 or 1;
+ *   R23 out_mass[i] = S_i = sum_v max(0, p_i - q_i), the total-variation
+ *   distance of p_i and q_i (so 1 - S_i is the acceptance probability of
+ *   position i averaged over the draft token); 1 at i = gamma; 0 for greedy;
+ *   sentinel sequences (as in the verification) get tokens -1 and zeros.
+ *
+ * Shapes: out_tok / out_prob [B][G+1][F], out_pk / out_mass [B][G+1];
+ * out_dist and out_scale [B][G+1][V] may be NULL: when given they receive the
+ * whole distribution r_i / S_i and the magnitude (p_i + q_i) / S_i of the two
+ * terms behind each entry (p_i / S_i at i = gamma, 0 for greedy).
+ */
+void oracle_outcomes(int batch, int gamma, int vocab, int dtype,
+                     const void *logits_draft, const void *logits_target,
+                     const int32_t *draft_tokens, const float *temperature, int F,
+                     int32_t *out_tok, double *out_prob, double *out_pk, double *out_mass,
+                     double *out_dist, double *out_scale)
+{
+    const int G = gamma, V = vocab;
+    double *r = (double *)malloc(sizeof(double) * (size_t)V);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)V);
+    double *lse_q = (double *)malloc(sizeof(double) * (size_t)(G + 1));
+    double *lse_p = (double *)malloc(sizeof(double) * (size_t)(G + 1));
+    double *beta = (double *)malloc(sizeof(double) * (size_t)(G + 1));
+    char *taken = (char *)malloc((size_t)V);
+    for (int b = 0; b < batch; ++b) {
+        const size_t q_row0 = (size_t)b * G * V, p_row0 = (size_t)b * (G + 1) * V;
+        const int32_t *t = draft_tokens + (size_t)b * G;
+        int32_t *tok_b = out_tok + (size_t)b * (G + 1) * F;
+        double *prob_b = out_prob + (size_t)b * (G + 1) * F;
+        double *pk_b = out_pk + (size_t)b * (G + 1);
+        double *mass_b = out_mass + (size_t)b * (G + 1);
+        for (int i = 0; i < (G + 1) * F; ++i) {
+            tok_b[i] = -1;
+            prob_b[i] = 0.0;
+        }
+        for (int i = 0; i <= G; ++i) {
+            pk_b[i] = 0.0;
+            mass_b[i] = 0.0;
+        }
+        if (out_dist)
+            memset(out_dist + (size_t)b * (G + 1) * V, 0, sizeof(double) * (size_t)(G + 1) * V);
+        if (out_scale)
+            memset(out_scale + (size_t)b * (G + 1) * V, 0, sizeof(double) * (size_t)(G + 1) * V);
+
+        /* validity, as in the verification (sentinel rule) */
+        float inv_t = 0.0f;
+        int ok = temperature_valid(temperature[b], &inv_t);
+        for (int i = 0; ok && i < G; ++i)
+            if (t[i] < 0 || t[i] >= V)
+                ok = 0;
+        const int greedy = ok && temperature[b] == 0.0f;
+        if (ok && greedy) {
+            for (int i = 0; i <= G && ok; ++i)
+                if (oracle_row_argmax(logits_target, dtype, p_row0 + (size_t)i * V, V) < 0)
+                    ok = 0;
+        } else if (ok) {
+            for (int i = 0; i < G; ++i)
+                lse_q[i] = oracle_row_lse(logits_draft, dtype, q_row0 + (size_t)i * V, V, inv_t);
+            for (int i = 0; i <= G; ++i)
+                lse_p[i] = oracle_row_lse(logits_target, dtype, p_row0 + (size_t)i * V, V, inv_t);
+            for (int i = 0; i < G; ++i)
+                if (!(lse_q[i] > -INFINITY))
+                    ok = 0;
+            for (int i = 0; i <= G; ++i)
+                if (!(lse_p[i] > -INFINITY))
+                    ok = 0;
+        }
+        if (!ok)
+            continue;
+
+        /* per-position acceptance probability of the drafted token */
+        for (int j = 0; j < G; ++j) {
+            if (greedy) {
+                beta[j] = t[j] == oracle_row_argmax(logits_target, dtype,
+                                                    p_row0 + (size_t)j * V, V) ? 1.0 : 0.0;
+            } else {
+                double xq = scaled(raw_logit(logits_draft, dtype, q_row0 + (size_t)j * V + t[j]), inv_t);
+                double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)j * V + t[j]), inv_t);
+                double d = (xp - lse_p[j]) - (xq - lse_q[j]);
+                beta[j] = d >= 0.0 ? 1.0 : (d < 0.0 ? exp(d) : 0.0);
+            }
+        }
+        double reach = 1.0; /* P(k >= i | t) */
+        for (int i = 0; i <= G; ++i) {
+            pk_b[i] = i < G ? reach * (1.0 - beta[i]) : reach;
+            if (i < G)
+                reach *= beta[i];
+        }
+
+        for (int i = 0; i <= G; ++i) {
+            /* the distribution of the extra token at length i */
+            double S = 0.0;
+            if (greedy) {
+                for (int v = 0; v < V; ++v) {
+                    r[v] = raw_logit(logits_target, dtype, p_row0 + (size_t)i * V + v);
+                    sc[v] = 0.0;
+                }
+            } else {
+                for (int v = 0; v < V; ++v) {
+                    double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)i * V + v), inv_t);
+                    double p = exp(xp - lse_p[i]);
+                    if (i < G) {
+                        double xq = scaled(raw_logit(logits_draft, dtype, q_row0 + (size_t)i * V + v), inv_t);
+                        double q = exp(xq - lse_q[i]);
+                        r[v] = p - q > 0.0 ? p - q : 0.0;
+                        sc[v] = p + q;
+                    } else {
+                        r[v] = p;
+                        sc[v] = p;
+                    }
+                    S += r[v];
+                }
+                mass_b[i] = i < G ? S : 1.0;
+                if (!(S > 0.0)) {
+                    /* R8: an empty residual means the draw comes from p_i */
+                    S = 0.0;
+                    for (int v = 0; v < V; ++v) {
+                        double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)i * V + v), inv_t);
+                        r[v] = exp(xp - lse_p[i]);
+                        sc[v] = r[v];
+                        S += r[v];
+                    }
+                }
+            }
+            /* the F largest entries, lowest index first among equals */
+            memset(taken, 0, (size_t)V);
+            int n = F < V ? F : V;
+            for (int j = 0; j < n; ++j) {
+                int best = -1;
+                for (int v = 0; v < V; ++v) {
+                    if (taken[v])
+                        continue;
+                    if (best < 0 || r[v] > r[best])
+                        best = v;
+                }
+                taken[best] = 1;
+                tok_b[(size_t)i * F + j] = best;
+                prob_b[(size_t)i * F + j] = greedy ? (j == 0 ? 1.0 : 0.0) : r[best] / S;
+            }
+            if (out_dist) {
+                double *dd = out_dist + ((size_t)b * (G + 1) + i) * V;
+                double *ss = out_scale ? out_scale + ((size_t)b * (G + 1) + i) * V : NULL;
+                if (greedy) {
+                    dd[tok_b[(size_t)i * F]] = 1.0;
+                } else {
+                    for (int v = 0; v < V; ++v) {
+                        dd[v] = r[v] / S;
+                        if (ss)
+                            ss[v] = sc[v] / S;
+                    }
+                }
+            }
+        }
+    }
+    free(r);
+    free(sc);
+    free(lse_q);
+    free(lse_p);
+    free(beta);
+    free(taken);
+}

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_bandit_oracle as bandit
+import test_oracle_outcomes as outcomes
 import test_oracle_pins as pins
 import test_oracle_stats as stats
 
@@ -105,6 +106,29 @@ def test_marginal_gate_catches_a_biased_residual():
     drawing the correction from p instead of the residual."""
     with mutated_oracle("r[v] = p - q > 0.0 ? p - q : 0.0;", "r[v] = p;"):
         fails(stats.test_gate_output_marginal_is_target, stats.build_gate_case())
+
+
+def test_outcome_length_law_without_the_reject_factor_is_caught():
+    with mutated_oracle("pk_b[i] = i < G ? reach * (1.0 - beta[i]) : reach;",
+                        "pk_b[i] = reach;"):
+        fails(outcomes.test_outcome_law_matches_the_verification_oracle, (0.6, 0.6, 0.6))
+
+
+def test_outcome_acceptance_without_the_cap_is_caught():
+    with mutated_oracle("beta[j] = d >= 0.0 ? 1.0 : (d < 0.0 ? exp(d) : 0.0);",
+                        "beta[j] = d == d ? exp(d) : 0.0;"):
+        fails(outcomes.test_outcome_law_matches_the_verification_oracle, (0.6, 1.8, 0.4))
+
+
+def test_outcome_top_f_last_index_on_ties_is_caught():
+    with mutated_oracle("if (best < 0 || r[v] > r[best])", "if (best < 0 || r[v] >= r[best])"):
+        fails(outcomes.test_top_f_is_the_stable_sort_of_the_distribution)
+
+
+def test_outcome_residual_without_the_max_is_caught():
+    with mutated_oracle("r[v] = p - q > 0.0 ? p - q : 0.0;\n                        sc[v] = p + q;",
+                        "r[v] = p - q;\n                        sc[v] = p + q;"):
+        fails(outcomes.test_residual_mass_is_total_variation)
 
 
 def ucb1_pins():
