@@ -27,11 +27,12 @@ EXPORTED = (
     "spec_verify_init", "spec_verify_set_stream", "spec_verify", "spec_accept_logprobs",
     "spec_verify_copy_lse", "spec_verify_philox_words", "spec_verify_enable_timing",
     "spec_verify_read_timing", "spec_verify_get_geometry", "spec_verify_destroy",
-    "spec_verify_strerror",
+    "spec_verify_strerror", "spec_verify_outcomes",
     "spec_bandit_init", "spec_bandit_set_stream", "spec_bandit_step", "spec_bandit_get_state",
     "spec_bandit_set_state", "spec_bandit_destroy",
 )
 
+SPEC_OUTCOME_MAX_F = 64
 SPEC_BANDIT_UCB1 = 0
 SPEC_BANDIT_THOMPSON = 1
 SPEC_BANDIT_MAX_ARMS = 64
@@ -67,6 +68,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_verify_get_geometry": ([P, P], i32),
         "spec_verify_destroy": ([P], i32),
         "spec_verify_strerror": ([i32], ctypes.c_char_p),
+        "spec_verify_outcomes": ([P, P, P, P, i32, P, P, P, P], i32),
         "spec_bandit_init": ([i32, i32, i32, i32, i32, P, ctypes.POINTER(P)], i32),
         "spec_bandit_set_stream": ([P, P], i32),
         "spec_bandit_step": ([P, P, P, u64, u64, P], i32),
@@ -182,6 +184,27 @@ def spec_accept_logprobs(ctx: Context, logprobs, seed: int, offset: int, out_acc
     _expect(out_accept_len, (B,), torch.int32, "out_accept_len")
     _check("spec_accept_logprobs", load_library().spec_accept_logprobs(
         ctx.handle, _ptr(logprobs), seed, offset, _ptr(out_accept_len)))
+
+
+def spec_verify_outcomes(ctx: Context, logits_draft, logits_target, draft_tokens, top_f: int,
+                         out_tokens, out_probs, out_pk, out_mass=None) -> None:
+    """Law of the last verification's outcome (call after spec_verify with the
+    same inputs): out_tokens [B, G+1, F] int32, out_probs [B, G+1, F] float32,
+    out_pk [B, G+1] float32, out_mass [B, G+1] float32 or None."""
+    B, G, V = ctx.batch, ctx.gamma, ctx.vocab
+    ldt = torch.bfloat16 if ctx.dtype == SPEC_BF16 else torch.float32
+    if G > 0:
+        _expect(logits_draft, (B, G, V), ldt, "logits_draft")
+        _expect(draft_tokens, (B, G), torch.int32, "draft_tokens")
+    _expect(logits_target, (B, G + 1, V), ldt, "logits_target")
+    _expect(out_tokens, (B, G + 1, top_f), torch.int32, "out_tokens")
+    _expect(out_probs, (B, G + 1, top_f), torch.float32, "out_probs")
+    _expect(out_pk, (B, G + 1), torch.float32, "out_pk")
+    _expect(out_mass, (B, G + 1), torch.float32, "out_mass")
+    _check("spec_verify_outcomes", load_library().spec_verify_outcomes(
+        ctx.handle, _ptr(logits_draft) if G > 0 else None, _ptr(logits_target),
+        _ptr(draft_tokens) if G > 0 else None, top_f, _ptr(out_tokens), _ptr(out_probs),
+        _ptr(out_pk), _ptr(out_mass)))
 
 
 def spec_verify_copy_lse(ctx: Context, out_lse) -> None:

@@ -163,7 +163,8 @@ __global__ __launch_bounds__(64) void accept_kernel(
         }
         if (lane == 0) {
             out_len[b] = -1;
-            seq[b] = SeqState{0, 0, 0.0f, 0.0f, 0.0f, 0.0f, 1.0f, 0};
+            // mode -1 marks a sentinel sequence for the kernels that follow
+            seq[b] = SeqState{0, -1, 0.0f, 0.0f, 0.0f, 0.0f, 1.0f, 0};
         }
         return;
     }

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "launch.hpp"
+#include "outcome.hpp"
 #include "spec_verify.h"
 
 using namespace specv;
@@ -24,6 +25,7 @@ struct spec_verify_ctx {
     bool row_nontemporal = true;
     int nsplit_residual = 1;  // vocabulary splits of the residual kernel
     int residual_unroll = 4;  // tiles per batch per wavefront in that kernel
+    int nsplit_outcome = 1;   // vocabulary splits of the outcome kernel
 
     void* ws = nullptr;
     Partial* part = nullptr;
@@ -32,6 +34,7 @@ struct spec_verify_ctx {
     double* lse = nullptr;
     SeqState* seq = nullptr;
     float* tile_sums = nullptr;
+    OutcomeWork outcome{};
     bool have_verified = false;
 
     int timing_slots = 0;
@@ -46,6 +49,7 @@ namespace {
 // workgroups are short-lived, so fewer, longer ones.
 constexpr long kRowTargetBlocks = 12288;
 constexpr long kResidualTargetBlocks = 4096;
+constexpr long kOutcomeTargetBlocks = 8192;
 
 int env_int(const char* name, int fallback) {
     const char* v = std::getenv(name);
@@ -110,6 +114,9 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     }
     ctx->nsplit_rows = choose_split(rows, vocab, dtype, kRowTargetBlocks, 4L * kBlock);
     ctx->nsplit_residual = choose_split(batch, vocab, dtype, kResidualTargetBlocks, 16L * 64);
+    const long pairs = static_cast<long>(batch) * (gamma + 1);
+    ctx->nsplit_outcome = std::min(kOutcomeMaxSplit,
+                                   choose_split(pairs, vocab, dtype, kOutcomeTargetBlocks, 16L * 64));
     const int o1 = env_int("SPEC_VERIFY_ROW_SPLIT", 0), o3 = env_int("SPEC_VERIFY_RESIDUAL_SPLIT", 0);
     if (o1 > 0)
         ctx->nsplit_rows = std::min(o1, kMaxSplit);
@@ -132,7 +139,8 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     // A dispatch holds fewer than 2^32 work-items.
     const long long limit = 1LL << 32;
     if (static_cast<long long>(rows) * ctx->nsplit_rows * kBlock >= limit ||
-        static_cast<long long>(batch) * ctx->nsplit_residual * kBlock >= limit) {
+        static_cast<long long>(batch) * ctx->nsplit_residual * kBlock >= limit ||
+        static_cast<long long>(pairs) * ctx->nsplit_outcome * kBlock >= limit) {
         delete ctx;
         return SPEC_EINVAL;
     }
@@ -146,6 +154,9 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     const size_t o_lse = off;  off = align_up(off + rows * sizeof(double), 256);
     const size_t o_seq = off;  off = align_up(off + static_cast<size_t>(batch) * sizeof(SeqState), 256);
     const size_t o_ts = off;   off = align_up(off + static_cast<size_t>(batch) * residual_tiles_per_row(vocab) * sizeof(float), 256);
+    const size_t n_oc = static_cast<size_t>(pairs) * ctx->nsplit_outcome;
+    const size_t o_oc = off;   off = align_up(off + n_oc * kOutcomeMaxF * sizeof(Cand), 256);
+    const size_t o_os = off;   off = align_up(off + n_oc * sizeof(double), 256);
     const size_t total = std::max<size_t>(off, 256);
     if (hipMalloc(&ctx->ws, total) != hipSuccess) {
         delete ctx;
@@ -158,6 +169,8 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     ctx->lse = reinterpret_cast<double*>(base + o_lse);
     ctx->seq = reinterpret_cast<SeqState*>(base + o_seq);
     ctx->tile_sums = reinterpret_cast<float*>(base + o_ts);
+    ctx->outcome.cand = reinterpret_cast<Cand*>(base + o_oc);
+    ctx->outcome.sums = reinterpret_cast<double*>(base + o_os);
     // Defined contents before the first call (every entry is rewritten by it).
     if (hipMemset(ctx->ws, 0, total) != hipSuccess) {
         (void)hipFree(ctx->ws);
@@ -241,6 +254,38 @@ int spec_accept_logprobs(spec_verify_ctx* ctx, const float* logprobs, uint64_t s
         return SPEC_EINVAL;
     if (launch_accept_scalar(s.batch, s.gamma, logprobs, seed, offset, out_accept_len,
                              ctx->stream) != hipSuccess)
+        return SPEC_EHIP;
+    return SPEC_OK;
+}
+
+int spec_verify_outcomes(spec_verify_ctx* ctx, const void* logits_draft,
+                         const void* logits_target, const int32_t* draft_tokens, int top_f,
+                         int32_t* out_tokens, float* out_probs, float* out_pk, float* out_mass) {
+    if (!ctx)
+        return SPEC_EINVAL;
+    const Shape& s = ctx->shape;
+    if (top_f < 1 || top_f > SPEC_OUTCOME_MAX_F)
+        return SPEC_EINVAL;
+    if (s.batch == 0)
+        return SPEC_OK;
+    const size_t esz = s.dtype == SPEC_BF16 ? 2 : 4;
+    if (!logits_target || !out_tokens || !out_probs || !out_pk)
+        return SPEC_EINVAL;
+    if (s.gamma > 0 && (!logits_draft || !draft_tokens))
+        return SPEC_EINVAL;
+    if (!aligned(logits_target, esz) || (logits_draft && !aligned(logits_draft, esz)) ||
+        !aligned(out_tokens, 4) || !aligned(out_probs, 4) || !aligned(out_pk, 4) ||
+        (out_mass && !aligned(out_mass, 4)) || (draft_tokens && !aligned(draft_tokens, 4)))
+        return SPEC_EINVAL;
+    if (!ctx->have_verified)
+        return SPEC_ESTATE;
+    if (s.gamma == 0)
+        logits_draft = logits_target;
+    const bool vec = (s.vocab % group_width(s.dtype)) == 0 && aligned(logits_target, 16) &&
+                     aligned(logits_draft, 16);
+    if (launch_outcomes(s, vec, ctx->nsplit_outcome, top_f, logits_draft, logits_target,
+                        draft_tokens, ctx->seq, ctx->rn, ctx->lse, ctx->gathered, ctx->outcome,
+                        out_tokens, out_probs, out_pk, out_mass, ctx->stream) != hipSuccess)
         return SPEC_EHIP;
     return SPEC_OK;
 }

@@ -1,0 +1,502 @@
+// Verification-outcome kernels: for every sequence and every possible accept
+// length i in [0, G], the F most likely extra tokens with their probabilities,
+// the residual mass S_i, and the probability of that length given the drafts.
+//
+// The outcome of a verification -- accepted count plus extra token -- is what
+// speculative speculative decoding predicts and keys its speculation cache on;
+// Saguaro spends the cache on likely lengths and, per length, on the top-F
+// tokens of the residual distribution the extra token is drawn from
+// (Speculative Speculative Decoding summary, section 2: central concept, and
+// Saguaro challenges 1 and 2). With the drafts fixed the law is exact:
+//   beta_j = min(1, p_j(t_j) / q_j(t_j)),
+//   P(k = i) = prod_{j<i} beta_j * (1 - beta_i), P(k = G) = prod_j beta_j,
+//   extra | k = i ~ max(0, p_i - q_i) / S_i (i < G), p_G (i = G), p_i if S_i = 0;
+// greedy sequences have a deterministic outcome (lists by raw target logit).
+//
+// Work layout.
+//   outcome_topf: grid = B * (G+1) * nsplit workgroups of four wavefronts; a
+//     workgroup streams one vocabulary split of target row i and draft row i
+//     (lane l reads group 64 t + l of a tile t, so a load instruction covers
+//     1 KiB of consecutive memory) and evaluates the scaled residual
+//     r' = max(0, p' * s_q / s_p - q') with p' = 2^(x log2e - m_p), the same
+//     arithmetic as the residual draw. Each wavefront keeps a candidate list
+//     in LDS behind a threshold key that only rises: an element is appended
+//     (ballot + mbcnt, no atomics) only if it beats the F-th best key known,
+//     so after the first tile almost nothing is written. The threshold is
+//     seeded from the first tile by a 64-lane bitonic sort of the lanes'
+//     maxima (the F-th largest lane maximum is a lower bound of the F-th
+//     largest element); the list is cut back to its best F when it fills.
+//     The four wavefront lists are merged by wavefront 0 into F candidates
+//     and one fp64 partial sum per split.
+//   outcome_merge: one wavefront per (sequence, length) merges the splits,
+//     normalises, and forms P(k = i) from the accept test's log-probabilities.
+// Keys order by value, then by lower vocabulary index, so the lists are those
+// of a stable descending sort.
+#include <math.h>
+
+#include "outcome.hpp"
+
+namespace specv {
+namespace {
+
+constexpr int kCap = 1024;   // candidate slots per wavefront
+constexpr int kIdxNone = 0x7fffffff;
+
+__device__ inline bool key_gt(float v, int i, float tv, int ti) {
+    return v > tv || (v == tv && i < ti);
+}
+
+__device__ inline bool key_ge(float v, int i, float tv, int ti) {
+    return v > tv || (v == tv && i <= ti);
+}
+
+__device__ inline int lane_id() { return threadIdx.x & 63; }
+
+// Bitonic sort of one key per lane across the wavefront, largest key first.
+__device__ inline void wave_sort_desc(float& v, int& i) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const float ov = __shfl_xor(v, j, 64);
+            const int oi = __shfl_xor(i, j, 64);
+            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+            const bool take = keep_max ? key_gt(ov, oi, v, i) : key_gt(v, i, ov, oi);
+            if (take) {
+                v = ov;
+                i = oi;
+            }
+        }
+    }
+}
+
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1)
+        v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ inline double wave_prod_f64(double v) {
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1)
+        v *= __shfl_xor(v, m, 64);
+    return v;
+}
+
+// A wavefront's candidate list in LDS and its threshold key (wave-uniform).
+struct WaveList {
+    Cand* buf;
+    int count;
+    float tv;
+    int ti;
+};
+
+// Append the lanes whose `ok` is set, in lane order.
+__device__ inline void append(WaveList& L, bool ok, float v, int idx) {
+    const unsigned long long m = __ballot(ok);
+    if (m) {
+        const int below = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
+        if (ok)
+            L.buf[L.count + below] = Cand{v, idx};
+        L.count += __popcll(m);
+    }
+}
+
+// Keep the F best candidates of the list, sorted, at its front; when F were
+// found the threshold becomes the F-th key. Slots with index -1 are empty.
+// Returns the number kept (at most F). Every lane returns the same value.
+__device__ int select_top(WaveList& L, int F) {
+    const int lane = lane_id();
+    float mine_v = -__builtin_huge_valf();
+    int mine_i = -1;
+    int n = 0;
+    for (; n < F; ++n) {
+        float bv = -__builtin_huge_valf();
+        int bi = kIdxNone;
+        int bs = -1;
+        for (int s = lane; s < L.count; s += 64) {
+            const Cand c = L.buf[s];
+            if (c.i >= 0 && (bs < 0 || key_gt(c.v, c.i, bv, bi))) {
+                bv = c.v;
+                bi = c.i;
+                bs = s;
+            }
+        }
+#pragma unroll
+        for (int m = 32; m > 0; m >>= 1) {
+            const float ov = __shfl_xor(bv, m, 64);
+            const int oi = __shfl_xor(bi, m, 64);
+            const int os = __shfl_xor(bs, m, 64);
+            if (os >= 0 && (bs < 0 || key_gt(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+                bs = os;
+            }
+        }
+        if (bs < 0)
+            break;  // wave-uniform: the list is exhausted
+        if (lane == n) {
+            mine_v = bv;
+            mine_i = bi;
+        }
+        if (lane == 0)
+            L.buf[bs].i = -1;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    }
+    if (lane < n)
+        L.buf[lane] = Cand{mine_v, mine_i};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    L.count = n;
+    if (n == F && F > 0) {
+        L.tv = __shfl(mine_v, F - 1, 64);
+        L.ti = __shfl(mine_i, F - 1, 64);
+    }
+    return n;
+}
+
+// Values of one group whose ranking decides the list: the scaled residual, p'
+// alone (bonus row, or the empty-residual fallback), or the raw target logit
+// (greedy sequences).
+struct RowCoefs {
+    const void* prow;
+    const void* qrow;
+    int kind;  // 0: raw logit, 1: p', 2: residual
+    float inv_t, mp, mq, ratio;
+};
+
+template <int DT, bool VEC>
+__device__ inline void group_values(const RowCoefs& rc, const typename Loader<DT, VEC>::raw_t& p,
+                                    const typename Loader<DT, VEC>::raw_t& q,
+                                    float (&val)[Loader<DT, VEC>::W]) {
+    using Ld = Loader<DT, VEC>;
+    constexpr int W = Ld::W;
+    float zp[W];
+    Ld::unpack(p, zp);
+    if (rc.kind == 0) {
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            val[e] = zp[e];
+        return;
+    }
+    if (rc.kind == 1) {
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            val[e] = fast_exp2(__builtin_fmaf(scale_logit(zp[e], rc.inv_t), kLog2e, -rc.mp));
+        return;
+    }
+    float zq[W];
+    Ld::unpack(q, zq);
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+        const float pv = fast_exp2(__builtin_fmaf(scale_logit(zp[e], rc.inv_t), kLog2e, -rc.mp));
+        const float qv = fast_exp2(__builtin_fmaf(scale_logit(zq[e], rc.inv_t), kLog2e, -rc.mq));
+        val[e] = fmaxf(__builtin_fmaf(pv, rc.ratio, -qv), 0.0f);
+    }
+}
+
+template <int N>
+__device__ inline float pairwise_sum(const float (&r)[N]) {
+    float t[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        t[e] = r[e];
+#pragma unroll
+    for (int w = 1; w < N; w <<= 1) {
+#pragma unroll
+        for (int i = 0; i + w < N; i += 2 * w)
+            t[i] += t[i + w];
+    }
+    return t[0];
+}
+
+// One wavefront streams tiles [t_begin, t_end) with stride `t_step` of a row
+// pair into its list, and returns its fp64 sum of the values (kind > 0).
+// U tiles are loaded before any is consumed.
+template <int DT, bool VEC, bool NT, int U>
+__device__ double stream_tiles(const RowCoefs& rc, int groups, int t_begin, int t_end, int t_step,
+                               int F, WaveList& L) {
+    using Ld = Loader<DT, VEC>;
+    constexpr int W = Ld::W;
+    const int lane = lane_id();
+    double sum = 0.0;
+    bool seeded = false;
+    for (int t = t_begin; t < t_end; t += U * t_step) {
+        typename Ld::raw_t p[U], q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tt = t + u * t_step;
+            const int g = tt * 64 + lane;
+            const bool used = tt < t_end && g < groups;
+            p[u] = Ld::template load_as<NT>(rc.prow, used ? g : 0);
+            q[u] = Ld::template load_as<NT>(rc.qrow, used ? g : 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tt = t + u * t_step;
+            if (tt >= t_end)
+                break;  // wave-uniform
+            const int g = tt * 64 + lane;
+            const bool used = g < groups;
+            float val[W];
+            group_values<DT, VEC>(rc, p[u], q[u], val);
+            if (rc.kind != 0 && used)
+                sum += static_cast<double>(pairwise_sum(val));
+            if (!seeded) {
+                // threshold seed: the F-th largest of the lanes' best keys
+                float mv = -__builtin_huge_valf();
+                int mi = kIdxNone;
+                if (used) {
+#pragma unroll
+                    for (int e = 0; e < W; ++e)
+                        if (key_gt(val[e], g * W + e, mv, mi)) {
+                            mv = val[e];
+                            mi = g * W + e;
+                        }
+                }
+                wave_sort_desc(mv, mi);
+                L.tv = __shfl(mv, F - 1, 64);
+                L.ti = __shfl(mi, F - 1, 64);
+                seeded = true;
+            }
+#pragma unroll
+            for (int e = 0; e < W; ++e)
+                append(L, used && key_ge(val[e], g * W + e, L.tv, L.ti), val[e], g * W + e);
+            if (L.count > kCap - 64 * W)
+                select_top(L, F);
+        }
+    }
+    return sum;
+}
+
+// Coefficients of row pair (b, i): target row i and, for a residual, draft row i.
+template <int DT>
+__device__ inline RowCoefs pair_coefs(const void* draft, const void* target, int G, int vocab,
+                                      int b, int i, const SeqState& st, const RowNorm* rn) {
+    RowCoefs rc;
+    const size_t row0 = static_cast<size_t>(b) * (2 * G + 1);
+    rc.prow = row_ptr(target, DT, static_cast<size_t>(b) * (G + 1) + i, vocab);
+    rc.qrow = rc.prow;
+    rc.inv_t = st.inv_t;
+    rc.mp = rc.mq = 0.0f;
+    rc.ratio = 1.0f;
+    if (st.mode == 0) {
+        rc.kind = 0;
+        return rc;
+    }
+    const RowNorm rp = rn[row0 + G + i];
+    rc.mp = rp.m;
+    if (i == G) {
+        rc.kind = 1;
+        return rc;
+    }
+    const RowNorm rq = rn[row0 + i];
+    rc.kind = 2;
+    rc.qrow = row_ptr(draft, DT, static_cast<size_t>(b) * G + i, vocab);
+    rc.mq = rq.m;
+    rc.ratio = static_cast<float>(rq.s / rp.s);
+    return rc;
+}
+
+template <int DT, bool VEC, bool NT>
+__global__ __launch_bounds__(kBlock) void outcome_topf_kernel(
+    const void* __restrict__ draft, const void* __restrict__ target, int gamma, int vocab,
+    int nsplit, int tiles_per_split, int F, const SeqState* __restrict__ seq,
+    const RowNorm* __restrict__ rn, Cand* __restrict__ cand_out, double* __restrict__ sum_out) {
+    constexpr int W = Loader<DT, VEC>::W;
+    __shared__ Cand lds[kWaves][kCap];
+    __shared__ double lds_sum[kWaves];
+    __shared__ int lds_n[kWaves];
+    const int pair = blockIdx.x / nsplit;
+    const int c = blockIdx.x - pair * nsplit;
+    const int G = gamma;
+    const int b = pair / (G + 1);
+    const int i = pair - b * (G + 1);
+    const SeqState st = seq[b];
+    if (st.mode < 0)
+        return;  // sentinel sequence: the merge kernel writes its outputs
+    const RowCoefs rc = pair_coefs<DT>(draft, target, G, vocab, b, i, st, rn);
+    const int groups = vocab / W;
+    const int ntiles = (groups + 63) / 64;
+    const int t0 = c * tiles_per_split;
+    const int t1 = t0 + tiles_per_split < ntiles ? t0 + tiles_per_split : ntiles;
+    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int lane = lane_id();
+
+    WaveList L{lds[wid], 0, -__builtin_huge_valf(), kIdxNone};
+    double sum = stream_tiles<DT, VEC, NT, 2>(rc, groups, t0 + wid, t1, kWaves, F, L);
+    select_top(L, F);
+    sum = wave_sum_f64(sum);
+    if (lane == 0) {
+        lds_sum[wid] = sum;
+        lds_n[wid] = L.count;
+    }
+    __syncthreads();
+    if (wid != 0)
+        return;
+    int total = lds_n[0];
+    for (int w = 1; w < kWaves; ++w) {
+        const int n = lds_n[w];
+        if (lane < n)
+            L.buf[total + lane] = lds[w][lane];
+        total += n;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    L.count = total;
+    const int n = select_top(L, F);
+    Cand* out = cand_out + (static_cast<size_t>(pair) * nsplit + c) * F;
+    if (lane < F)
+        out[lane] = lane < n ? L.buf[lane] : Cand{-__builtin_huge_valf(), -1};
+    if (lane == 0)
+        sum_out[static_cast<size_t>(pair) * nsplit + c] =
+            ((lds_sum[0] + lds_sum[1]) + lds_sum[2]) + lds_sum[3];
+}
+
+// beta_j = min(1, p_j(t_j) / q_j(t_j)) from the accept test's log-probabilities
+// (0 when the difference is NaN); for greedy sequences 1 iff t_j is the argmax.
+__device__ inline double accept_prob(int j, int b, int G, int mode, float inv_t,
+                                     const int32_t* tokens, const RowNorm* rn, const double* lse,
+                                     const float* gathered) {
+    const size_t row0 = static_cast<size_t>(b) * (2 * G + 1);
+    if (mode == 0)
+        return tokens[static_cast<size_t>(b) * G + j] == rn[row0 + G + j].idx ? 1.0 : 0.0;
+    const double lq = static_cast<double>(scale_logit(gathered[row0 + j], inv_t)) - lse[row0 + j];
+    const double lp = static_cast<double>(scale_logit(gathered[row0 + G + j], inv_t)) - lse[row0 + G + j];
+    const double d = lp - lq;
+    return d >= 0.0 ? 1.0 : (d < 0.0 ? exp(d) : 0.0);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(64) void outcome_merge_kernel(
+    const void* __restrict__ draft, const void* __restrict__ target,
+    const int32_t* __restrict__ tokens, int gamma, int vocab, int nsplit, int F,
+    const SeqState* __restrict__ seq, const RowNorm* __restrict__ rn,
+    const double* __restrict__ lse, const float* __restrict__ gathered,
+    const Cand* __restrict__ cand, const double* __restrict__ sums, int32_t* __restrict__ out_tok,
+    float* __restrict__ out_prob, float* __restrict__ out_pk, float* __restrict__ out_mass) {
+    constexpr int W = Loader<DT, VEC>::W;
+    __shared__ Cand buf[kCap];
+    const int pair = blockIdx.x;
+    const int G = gamma;
+    const int b = pair / (G + 1);
+    const int i = pair - b * (G + 1);
+    const int lane = lane_id();
+    const SeqState st = seq[b];
+    int32_t* tok = out_tok + static_cast<size_t>(pair) * F;
+    float* prob = out_prob + static_cast<size_t>(pair) * F;
+    if (st.mode < 0) {
+        for (int j = lane; j < F; j += 64) {
+            tok[j] = -1;
+            prob[j] = 0.0f;
+        }
+        if (lane == 0) {
+            out_pk[pair] = 0.0f;
+            if (out_mass)
+                out_mass[pair] = 0.0f;
+        }
+        return;
+    }
+
+    // Probability of length i: prod_{j<i} beta_j, times (1 - beta_i) below G.
+    double reach = 1.0;
+    for (int j0 = 0; j0 < i; j0 += 64) {
+        const int j = j0 + lane;
+        const double beta = j < i ? accept_prob(j, b, G, st.mode, st.inv_t, tokens, rn, lse, gathered)
+                                  : 1.0;
+        reach *= wave_prod_f64(beta);
+    }
+    const double pk = i < G ? reach * (1.0 - accept_prob(i, b, G, st.mode, st.inv_t, tokens, rn,
+                                                         lse, gathered))
+                            : reach;
+
+    // Merge the splits' lists and sums (fixed order).
+    const int total = nsplit * F;
+    const Cand* src = cand + static_cast<size_t>(pair) * total;
+    for (int s = lane; s < total; s += 64)
+        buf[s] = src[s];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    double S = 0.0;
+    for (int c = 0; c < nsplit; ++c)
+        S += sums[static_cast<size_t>(pair) * nsplit + c];
+    WaveList L{buf, total, -__builtin_huge_valf(), kIdxNone};
+    double mass = 0.0;
+    if (st.mode == 1) {
+        const size_t row0 = static_cast<size_t>(b) * (2 * G + 1);
+        mass = i < G ? S / rn[row0 + i].s : 1.0;
+        if (i < G && !(S > 0.0)) {
+            // Empty residual: the extra token would be drawn from p_i; rank p'.
+            RowCoefs rc = pair_coefs<DT>(draft, target, G, vocab, b, i, st, rn);
+            rc.kind = 1;
+            rc.qrow = rc.prow;
+            L.count = 0;
+            L.tv = -__builtin_huge_valf();
+            L.ti = kIdxNone;
+            const int groups = vocab / W;
+            S = wave_sum_f64(stream_tiles<DT, VEC, false, 1>(rc, groups, 0, (groups + 63) / 64, 1,
+                                                              F, L));
+        }
+    }
+    const int n = select_top(L, F);
+    for (int j = lane; j < F; j += 64) {
+        const bool have = j < n;
+        tok[j] = have ? L.buf[j].i : -1;
+        float pr = 0.0f;
+        if (have)
+            pr = st.mode == 0 ? (j == 0 ? 1.0f : 0.0f)
+                              : static_cast<float>(static_cast<double>(L.buf[j].v) / S);
+        prob[j] = pr;
+    }
+    if (lane == 0) {
+        out_pk[pair] = static_cast<float>(pk);
+        if (out_mass)
+            out_mass[pair] = static_cast<float>(mass);
+    }
+}
+
+template <int DT, bool VEC>
+hipError_t launch_typed(const Shape& s, int nsplit, int F, const void* draft, const void* target,
+                        const int32_t* tokens, const SeqState* seq, const RowNorm* rn,
+                        const double* lse, const float* gathered, OutcomeWork work,
+                        int32_t* out_tok, float* out_prob, float* out_pk, float* out_mass,
+                        hipStream_t stream) {
+    constexpr int W = Loader<DT, VEC>::W;
+    const long pairs = static_cast<long>(s.batch) * (s.gamma + 1);
+    const int groups = s.vocab / W;
+    const int ntiles = (groups + 63) / 64;
+    const int per = (ntiles + nsplit - 1) / nsplit;
+    const int nsplit_eff = (ntiles + per - 1) / per;
+    outcome_topf_kernel<DT, VEC, true><<<dim3(static_cast<unsigned>(pairs * nsplit_eff)),
+                                         dim3(kBlock), 0, stream>>>(
+        draft, target, s.gamma, s.vocab, nsplit_eff, per, F, seq, rn, work.cand, work.sums);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    outcome_merge_kernel<DT, VEC><<<dim3(static_cast<unsigned>(pairs)), dim3(64), 0, stream>>>(
+        draft, target, tokens, s.gamma, s.vocab, nsplit_eff, F, seq, rn, lse, gathered, work.cand,
+        work.sums, out_tok, out_prob, out_pk, out_mass);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_outcomes(const Shape& s, bool vec, int nsplit, int top_f, const void* draft,
+                           const void* target, const int32_t* tokens, const SeqState* seq,
+                           const RowNorm* rn, const double* lse, const float* gathered,
+                           OutcomeWork work, int32_t* out_tok, float* out_prob, float* out_pk,
+                           float* out_mass, hipStream_t stream) {
+    if (s.batch == 0)
+        return hipSuccess;
+    if (s.dtype == kBF16)
+        return vec ? launch_typed<kBF16, true>(s, nsplit, top_f, draft, target, tokens, seq, rn, lse,
+                                               gathered, work, out_tok, out_prob, out_pk, out_mass, stream)
+                   : launch_typed<kBF16, false>(s, nsplit, top_f, draft, target, tokens, seq, rn, lse,
+                                                gathered, work, out_tok, out_prob, out_pk, out_mass, stream);
+    return vec ? launch_typed<kF32, true>(s, nsplit, top_f, draft, target, tokens, seq, rn, lse,
+                                          gathered, work, out_tok, out_prob, out_pk, out_mass, stream)
+               : launch_typed<kF32, false>(s, nsplit, top_f, draft, target, tokens, seq, rn, lse,
+                                           gathered, work, out_tok, out_prob, out_pk, out_mass, stream);
+}
+
+}  // namespace specv

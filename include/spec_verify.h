@@ -130,6 +130,48 @@ int spec_verify(spec_verify_ctx *ctx, const void *logits_draft,
 int spec_accept_logprobs(spec_verify_ctx *ctx, const float *logprobs, uint64_t seed,
                          uint64_t offset, int32_t *out_accept_len);
 
+/* Longest top-F list of spec_verify_outcomes. */
+#define SPEC_OUTCOME_MAX_F 64
+
+/*
+ * The law of the last verification's outcome given its drafts: the pair
+ * (accepted count k, extra token) that speculative speculative decoding
+ * predicts and keys its speculation cache on, spending the cache on likely
+ * lengths and, per length, on the top-F tokens of the residual distribution
+ * (Speculative Speculative Decoding summary, section 2: central concept,
+ * Saguaro challenges 1 and 2). For every sequence b and length i in [0, G]:
+ *   out_pk[b,i]   = P(k = i | drafts): prod_{j<i} beta_j * (1 - beta_i) for
+ *                   i < G and prod_{j<G} beta_j for i = G, with beta_j =
+ *                   min(1, p_j(t_j) / q_j(t_j)) from the accept test's
+ *                   log-probabilities (0 when their difference is NaN);
+ *   out_tokens[b,i,:F], out_probs[b,i,:F] = the F most likely extra tokens
+ *                   at length i and their probabilities, largest first, the
+ *                   lower index first among equal values: the residual
+ *                   max(0, p_i - q_i) / S_i for i < G, p_G for i = G, p_i when
+ *                   S_i = 0; token -1 and probability 0 past the vocabulary;
+ *   out_mass[b,i] = S_i = sum_v max(0, p_i - q_i) (the total-variation
+ *                   distance of p_i and q_i) for i < G, 1 for i = G.
+ * Greedy sequences (T == 0) have a deterministic outcome: lists by raw target
+ * logit with probabilities 1, 0, ..., P(k = i) in {0, 1}, mass 0. Sentinel
+ * sequences get tokens -1 and zeros. Probabilities use the row normalisers
+ * and the arithmetic of the verification (binary32 exp2 of the scaled
+ * logits), so they carry a relative error of a few 1e-6.
+ *
+ * Must follow a spec_verify call on the same context with the same logits,
+ * draft tokens and temperatures: it reuses that call's row normalisers,
+ * gathered logits and per-sequence state (SPEC_ESTATE if there was none).
+ * Reads the logits once more. Device pointers:
+ *   logits_draft [B, G, V], logits_target [B, G+1, V], draft_tokens [B, G]
+ *   (as given to spec_verify; draft pointers may be NULL iff G == 0);
+ *   out_tokens [B, G+1, F] int32, out_probs [B, G+1, F] float32,
+ *   out_pk [B, G+1] float32, out_mass [B, G+1] float32 (may be NULL);
+ *   1 <= top_f <= SPEC_OUTCOME_MAX_F.
+ */
+int spec_verify_outcomes(spec_verify_ctx *ctx, const void *logits_draft,
+                         const void *logits_target, const int32_t *draft_tokens, int top_f,
+                         int32_t *out_tokens, float *out_probs, float *out_pk,
+                         float *out_mass);
+
 /*
  * Test hook: copy the row log-normalisers of the last spec_verify call into
  * out_lse [B, 2G+1] float64 (device): draft rows 0..G-1, then target rows

@@ -67,6 +67,8 @@ def test_host_argument_checks(lib):
     assert lib.spec_verify_destroy(None) == sv.binding.SPEC_EINVAL
     assert lib.spec_verify_enable_timing(None, 4) == sv.binding.SPEC_EINVAL
     assert lib.spec_verify_get_geometry(None, None) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify_outcomes(None, None, None, None, 4, None, None, None, None) == \
+        sv.binding.SPEC_EINVAL
 
 
 def test_bandit_host_argument_checks(lib):
