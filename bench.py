@@ -289,6 +289,32 @@ def main() -> int:
     k2_bytes /= args.steps
     k3_bytes /= args.steps
     k1_ms, k2_ms, k3_ms = per_kernel.mean(axis=0)
+
+    # Verification-outcome law with F = 16 tokens per length, after a call on
+    # input copy 0: one more pass over the same logits the row kernel reads.
+    F_OUT = 16
+    o_tok = torch.empty(B, G + 1, F_OUT, dtype=torch.int32, device=dev)
+    o_prob = torch.empty(B, G + 1, F_OUT, dtype=torch.float32, device=dev)
+    o_pk = torch.empty(B, G + 1, dtype=torch.float32, device=dev)
+    o_mass = torch.empty(B, G + 1, dtype=torch.float32, device=dev)
+    step(0)
+    zq0, zp0 = copies[0]
+
+    def outcomes():
+        sv.spec_verify_outcomes(ctx, zq0 if G else None, zp0, tokens if G else None, F_OUT,
+                                o_tok, o_prob, o_pk, o_mass)
+
+    for _ in range(args.warmup):
+        outcomes()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        outcomes()
+    end.record(stream)
+    torch.cuda.synchronize()
+    outcome_ms = start.elapsed_time(end) / args.steps
+    outcome_bytes = algorithmic_bytes(rec, d["temperature"], alen.cpu().numpy())["row_norm"]
+    outcome_gbs = outcome_bytes / (outcome_ms * 1e-3) / 1e9
     k1_gbs = k1_bytes / (k1_ms * 1e-3) / 1e9
     k3_gbs = k3_bytes / (k3_ms * 1e-3) / 1e9
     call_gbs = (k1_bytes + k2_bytes + k3_bytes) / (ms_per_step * 1e-3) / 1e9
@@ -330,6 +356,9 @@ def main() -> int:
                         "bytes": sc_b * sc_g * 8 + sc_b * 4,
                         "sequences_per_s": round(sc_b / (scalar_us * 1e-6), 1)},
         "bandit": {"arms": 3, "us_per_step": bandit_us},
+        "outcomes": {"top_f": F_OUT, "us_per_call": round(outcome_ms * 1e3, 2),
+                     "bytes": int(outcome_bytes), "gbs": round(outcome_gbs, 1),
+                     "frac": round(outcome_gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "row_norm_kernel"},

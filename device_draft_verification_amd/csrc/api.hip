@@ -49,7 +49,7 @@ namespace {
 // workgroups are short-lived, so fewer, longer ones.
 constexpr long kRowTargetBlocks = 12288;
 constexpr long kResidualTargetBlocks = 4096;
-constexpr long kOutcomeTargetBlocks = 8192;
+constexpr long kOutcomeTargetBlocks = 2048;
 
 int env_int(const char* name, int fallback) {
     const char* v = std::getenv(name);
@@ -117,6 +117,9 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     const long pairs = static_cast<long>(batch) * (gamma + 1);
     ctx->nsplit_outcome = std::min(kOutcomeMaxSplit,
                                    choose_split(pairs, vocab, dtype, kOutcomeTargetBlocks, 16L * 64));
+    const int oo = env_int("SPEC_VERIFY_OUTCOME_SPLIT", 0);
+    if (oo > 0)
+        ctx->nsplit_outcome = std::min(oo, kOutcomeMaxSplit);
     const int o1 = env_int("SPEC_VERIFY_ROW_SPLIT", 0), o3 = env_int("SPEC_VERIFY_RESIDUAL_SPLIT", 0);
     if (o1 > 0)
         ctx->nsplit_rows = std::min(o1, kMaxSplit);

@@ -39,21 +39,24 @@
 namespace specv {
 namespace {
 
-constexpr int kCap = 1024;   // candidate slots per wavefront
+constexpr int kCap = 640;    // candidate slots per wavefront: kTightenAt + one tile
+constexpr int kTightenAt = 128;  // the list is cut back to F once it holds more
+// the merge kernel's list: every split's F candidates
+constexpr int kMergeCap = kOutcomeMaxSplit * kOutcomeMaxF;
 constexpr int kIdxNone = 0x7fffffff;
 
-__device__ inline bool key_gt(float v, int i, float tv, int ti) {
+__device__ __forceinline__ bool key_gt(float v, int i, float tv, int ti) {
     return v > tv || (v == tv && i < ti);
 }
 
-__device__ inline bool key_ge(float v, int i, float tv, int ti) {
+__device__ __forceinline__ bool key_ge(float v, int i, float tv, int ti) {
     return v > tv || (v == tv && i <= ti);
 }
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
 // Bitonic sort of one key per lane across the wavefront, largest key first.
-__device__ inline void wave_sort_desc(float& v, int& i) {
+__device__ __forceinline__ void wave_sort_desc(float& v, int& i) {
     const int lane = lane_id();
 #pragma unroll
     for (int k = 2; k <= 64; k <<= 1) {
@@ -94,7 +97,7 @@ struct WaveList {
 };
 
 // Append the lanes whose `ok` is set, in lane order.
-__device__ inline void append(WaveList& L, bool ok, float v, int idx) {
+__device__ __forceinline__ void append(WaveList& L, bool ok, float v, int idx) {
     const unsigned long long m = __ballot(ok);
     if (m) {
         const int below = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
@@ -105,69 +108,211 @@ __device__ inline void append(WaveList& L, bool ok, float v, int idx) {
     }
 }
 
-// Keep the F best candidates of the list, sorted, at its front; when F were
-// found the threshold becomes the F-th key. Slots with index -1 are empty.
-// Returns the number kept (at most F). Every lane returns the same value.
-__device__ int select_top(WaveList& L, int F) {
+// Keys as 64-bit unsigned integers that order like (value, then lower index):
+// the value's bits mapped to an order-preserving code in the high word, the
+// complemented index in the low word. -0 is coded as +0, so the codes agree
+// with floating-point equality. 0 is below every real key.
+__device__ __forceinline__ uint64_t key_code(float v, int idx) {
+    uint32_t u = __float_as_uint(v);
+    if ((u << 1) == 0)
+        u = 0;
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx));
+}
+
+__device__ __forceinline__ void key_decode(uint64_t k, float* v, int* idx) {
+    const uint32_t o = static_cast<uint32_t>(k >> 32);
+    const uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+    *v = __uint_as_float(u);
+    *idx = static_cast<int>(~static_cast<uint32_t>(k));
+}
+
+// Cut the list to its F best candidates (unordered) and raise the threshold
+// to the F-th best key. The F-th best is found by binary searches over the key
+// bits with ballot counts, so no data moves between lanes: first over the
+// value code (the largest h with at least F keys of value code >= h), then,
+// only if several candidates share that value and not all of them fit, over
+// the index among those. Fewer than F candidates: all are kept.
+// Slots are read S per lane from registers when the list fits 64 * S slots,
+// else from LDS on every step (a rare path: lists are cut once they pass 64).
+template <int S>
+struct SlotKeys {
+    uint32_t hi[S], lo[S];
+};
+
+template <int S>
+__device__ __forceinline__ void load_keys(const WaveList& L, SlotKeys<S>& K) {
     const int lane = lane_id();
-    float mine_v = -__builtin_huge_valf();
-    int mine_i = -1;
-    int n = 0;
-    for (; n < F; ++n) {
-        float bv = -__builtin_huge_valf();
-        int bi = kIdxNone;
-        int bs = -1;
-        for (int s = lane; s < L.count; s += 64) {
-            const Cand c = L.buf[s];
-            if (c.i >= 0 && (bs < 0 || key_gt(c.v, c.i, bv, bi))) {
-                bv = c.v;
-                bi = c.i;
-                bs = s;
-            }
-        }
 #pragma unroll
-        for (int m = 32; m > 0; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, 64);
-            const int oi = __shfl_xor(bi, m, 64);
-            const int os = __shfl_xor(bs, m, 64);
-            if (os >= 0 && (bs < 0 || key_gt(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
-                bs = os;
+    for (int s = 0; s < S; ++s) {
+        const int slot = s * 64 + lane;
+        K.hi[s] = 0;
+        K.lo[s] = 0;
+        if (slot < L.count) {
+            const Cand c = L.buf[slot];
+            if (c.i >= 0) {
+                const uint64_t k = key_code(c.v, c.i);
+                K.hi[s] = static_cast<uint32_t>(k >> 32);
+                K.lo[s] = static_cast<uint32_t>(k);
             }
         }
-        if (bs < 0)
-            break;  // wave-uniform: the list is exhausted
-        if (lane == n) {
-            mine_v = bv;
-            mine_i = bi;
-        }
-        if (lane == 0)
-            L.buf[bs].i = -1;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     }
-    if (lane < n)
-        L.buf[lane] = Cand{mine_v, mine_i};
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    L.count = n;
-    if (n == F && F > 0) {
-        L.tv = __shfl(mine_v, F - 1, 64);
-        L.ti = __shfl(mine_i, F - 1, 64);
+}
+
+// count of slots with (hi > h) or (hi == h and lo >= l); `eq_only` counts only hi == h
+template <int S>
+__device__ __forceinline__ int count_ge(const SlotKeys<S>& K, uint32_t h, uint32_t l, bool eq_only) {
+    int n = 0;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const bool ge = eq_only ? (K.hi[s] == h && K.lo[s] >= l)
+                                : (K.hi[s] > h || (K.hi[s] == h && K.lo[s] >= l));
+        n += __popcll(__ballot(ge));
     }
     return n;
 }
 
-// Values of one group whose ranking decides the list: the scaled residual, p'
-// alone (bonus row, or the empty-residual fallback), or the raw target logit
-// (greedy sequences).
+__device__ __forceinline__ int count_ge_lds(const WaveList& L, uint32_t h, uint32_t l, bool eq_only) {
+    const int lane = lane_id();
+    int n = 0;
+    for (int base = 0; base < L.count; base += 64) {
+        const int slot = base + lane;
+        bool ge = false;
+        if (slot < L.count) {
+            const Cand c = L.buf[slot];
+            if (c.i >= 0) {
+                const uint64_t k = key_code(c.v, c.i);
+                const uint32_t kh = static_cast<uint32_t>(k >> 32), kl = static_cast<uint32_t>(k);
+                ge = eq_only ? (kh == h && kl >= l) : (kh > h || (kh == h && kl >= l));
+            }
+        }
+        n += __popcll(__ballot(ge));
+    }
+    return n;
+}
+
+template <int S, typename KT>
+__device__ __forceinline__ int count_keys(const WaveList& L, const KT& K, uint32_t h,
+                                          uint32_t l, bool eq_only) {
+    if constexpr (S > 0)
+        return count_ge(K, h, l, eq_only);
+    else
+        return count_ge_lds(L, h, l, eq_only);
+}
+
+template <int S>
+__device__ __forceinline__ void tighten_s(WaveList& L, int F) {
+    SlotKeys<(S > 0 ? S : 1)> K;
+    if constexpr (S > 0)
+        load_keys(L, K);
+    // value code of the F-th best
+    uint32_t h = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = h | (1u << bit);
+        if (count_keys<S>(L, K, c, 0u, false) >= F)
+            h = c;
+    }
+    uint32_t l = 0;      // keep (hi, lo) >= (h, l)
+    bool exact = false;  // the threshold index is the F-th's own
+    if (h != 0) {
+        const int n_ge = count_keys<S>(L, K, h, 0u, false);
+        if (n_ge > F) {
+            // more candidates share value h than fit: search their index word
+            const int n_gt = n_ge - count_keys<S>(L, K, h, 0u, true);
+            const int need = F - n_gt;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t c = l | (1u << bit);
+                if (count_keys<S>(L, K, h, c, true) >= need)
+                    l = c;
+            }
+            exact = true;
+        }
+    } else {
+        h = 0;
+        l = 1;  // fewer than F candidates: keep every real key
+    }
+    // Compact the kept slots to the front, in slot order. A slot is written at
+    // or below its own position, and every lane reads its slot of a row before
+    // any lane writes in that row, so nothing unread is overwritten.
+    const int lane = lane_id();
+    int n = 0;
+    const int count = L.count;
+    for (int base = 0; base < count; base += 64) {
+        const int slot = base + lane;
+        Cand c{0.0f, -1};
+        bool keep = false;
+        if (slot < count) {
+            c = L.buf[slot];
+            if (c.i >= 0) {
+                const uint64_t k = key_code(c.v, c.i);
+                const uint32_t kh = static_cast<uint32_t>(k >> 32), kl = static_cast<uint32_t>(k);
+                keep = kh > h || (kh == h && kl >= l);
+            }
+        }
+        const unsigned long long m = __ballot(keep);
+        __builtin_amdgcn_wave_barrier();
+        if (keep) {
+            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
+            L.buf[n + below] = c;
+        }
+        n += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    L.count = n;
+    if (h != 0 && n >= F) {
+        // threshold: the F-th key itself, or the lowest key of its value
+        key_decode((static_cast<uint64_t>(h) << 32) | (exact ? l : 0u), &L.tv, &L.ti);
+        if (!exact)
+            L.ti = kIdxNone;
+    }
+}
+
+template <int SMAX>
+__device__ __forceinline__ void tighten(WaveList& L, int F) {
+    if (L.count <= F)
+        return;
+    if (L.count <= 64)
+        tighten_s<1>(L, F);
+    else if (L.count <= 256)
+        tighten_s<4>(L, F);
+    else
+        tighten_s<0>(L, F);
+}
+
+// The list (at most 64 entries after tighten) sorted by key, largest first,
+// one entry per lane: lane j holds entry j, or (-inf, -1) past the end.
+__device__ __forceinline__ void sorted_entries(const WaveList& L, float* v, int* i) {
+    const int lane = lane_id();
+    float vv = -__builtin_huge_valf();
+    int ii = kIdxNone;
+    if (lane < L.count) {
+        const Cand c = L.buf[lane];
+        if (c.i >= 0) {
+            vv = c.v;
+            ii = c.i;
+        }
+    }
+    wave_sort_desc(vv, ii);
+    if (ii == kIdxNone)
+        ii = -1;
+    *v = vv;
+    *i = ii;
+}
+
+// What ranks the entries of a row pair: the raw target logit (greedy
+// sequences), p' alone (bonus row, or the empty-residual fallback), or the
+// scaled residual.
+enum Kind { kRaw = 0, kP = 1, kResidual = 2 };
+
 struct RowCoefs {
     const void* prow;
     const void* qrow;
-    int kind;  // 0: raw logit, 1: p', 2: residual
+    int kind;
     float inv_t, mp, mq, ratio;
 };
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int KIND>
 __device__ inline void group_values(const RowCoefs& rc, const typename Loader<DT, VEC>::raw_t& p,
                                     const typename Loader<DT, VEC>::raw_t& q,
                                     float (&val)[Loader<DT, VEC>::W]) {
@@ -175,25 +320,23 @@ __device__ inline void group_values(const RowCoefs& rc, const typename Loader<DT
     constexpr int W = Ld::W;
     float zp[W];
     Ld::unpack(p, zp);
-    if (rc.kind == 0) {
+    if constexpr (KIND == kRaw) {
 #pragma unroll
         for (int e = 0; e < W; ++e)
             val[e] = zp[e];
-        return;
-    }
-    if (rc.kind == 1) {
+    } else if constexpr (KIND == kP) {
 #pragma unroll
         for (int e = 0; e < W; ++e)
             val[e] = fast_exp2(__builtin_fmaf(scale_logit(zp[e], rc.inv_t), kLog2e, -rc.mp));
-        return;
-    }
-    float zq[W];
-    Ld::unpack(q, zq);
+    } else {
+        float zq[W];
+        Ld::unpack(q, zq);
 #pragma unroll
-    for (int e = 0; e < W; ++e) {
-        const float pv = fast_exp2(__builtin_fmaf(scale_logit(zp[e], rc.inv_t), kLog2e, -rc.mp));
-        const float qv = fast_exp2(__builtin_fmaf(scale_logit(zq[e], rc.inv_t), kLog2e, -rc.mq));
-        val[e] = fmaxf(__builtin_fmaf(pv, rc.ratio, -qv), 0.0f);
+        for (int e = 0; e < W; ++e) {
+            const float pv = fast_exp2(__builtin_fmaf(scale_logit(zp[e], rc.inv_t), kLog2e, -rc.mp));
+            const float qv = fast_exp2(__builtin_fmaf(scale_logit(zq[e], rc.inv_t), kLog2e, -rc.mq));
+            val[e] = fmaxf(__builtin_fmaf(pv, rc.ratio, -qv), 0.0f);
+        }
     }
 }
 
@@ -212,63 +355,123 @@ __device__ inline float pairwise_sum(const float (&r)[N]) {
     return t[0];
 }
 
-// One wavefront streams tiles [t_begin, t_end) with stride `t_step` of a row
-// pair into its list, and returns its fp64 sum of the values (kind > 0).
-// U tiles are loaded before any is consumed.
-template <int DT, bool VEC, bool NT, int U>
-__device__ double stream_tiles(const RowCoefs& rc, int groups, int t_begin, int t_end, int t_step,
+template <int N>
+__device__ inline float group_max(const float (&r)[N]) {
+    float m = r[0];
+#pragma unroll
+    for (int e = 1; e < N; ++e)
+        m = fmaxf(m, r[e]);
+    return m;
+}
+
+// One wavefront streams tiles t_begin, t_begin + t_step, ... (< t_end) of a
+// row pair into its list and returns its fp64 sum of the values (KIND > kRaw).
+// Double-buffered: the U tiles of the next batch are loaded, unconditionally
+// (past the end they read group 0, which is in cache, and are never used),
+// before the current batch is consumed, so the compiler waits for exactly the
+// group being consumed. A group enters the list only if its largest value
+// reaches the threshold, which is one compare per group in the common case.
+template <int DT, bool VEC, bool NT, int KIND, int U>
+__device__ __forceinline__ double stream_tiles(const RowCoefs& rc, int groups, int t_begin, int t_end, int t_step,
                                int F, WaveList& L) {
     using Ld = Loader<DT, VEC>;
+    using raw_t = typename Ld::raw_t;
     constexpr int W = Ld::W;
     const int lane = lane_id();
     double sum = 0.0;
     bool seeded = false;
-    for (int t = t_begin; t < t_end; t += U * t_step) {
-        typename Ld::raw_t p[U], q[U];
+    auto load_batch = [&](raw_t (&p)[U], raw_t (&q)[U], int t) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int tt = t + u * t_step;
             const int g = tt * 64 + lane;
             const bool used = tt < t_end && g < groups;
             p[u] = Ld::template load_as<NT>(rc.prow, used ? g : 0);
-            q[u] = Ld::template load_as<NT>(rc.qrow, used ? g : 0);
+            if constexpr (KIND == kResidual)
+                q[u] = Ld::template load_as<NT>(rc.qrow, used ? g : 0);
+        }
+    };
+    auto consume = [&](const raw_t (&p)[U], const raw_t (&q)[U], int t) {
+        float val[U][W];
+        bool used[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            group_values<DT, VEC, KIND>(rc, p[u], q[u], val[u]);
+            const int tt = t + u * t_step;
+            used[u] = tt < t_end && tt * 64 + lane < groups;
+        }
+        if constexpr (KIND != kRaw) {
+            float bs = 0.0f;  // one batch of one lane: at most 32 values
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (used[u])
+                    bs += pairwise_sum(val[u]);
+            sum += static_cast<double>(bs);
+        }
+        if (!seeded) {
+            // Threshold seed from the first batch: the F-th largest of the
+            // lanes' best values is a lower bound of the F-th largest element.
+            uint32_t best = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (used[u]) {
+                    const uint32_t c = static_cast<uint32_t>(key_code(group_max(val[u]), 0) >> 32);
+                    best = c > best ? c : best;
+                }
+            uint32_t h = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t c = h | (1u << bit);
+                if (__popcll(__ballot(best >= c)) >= F)
+                    h = c;
+            }
+            if (h != 0) {
+                key_decode(static_cast<uint64_t>(h) << 32, &L.tv, &L.ti);
+                L.ti = kIdxNone;  // the lowest key of that value
+            }
+            seeded = true;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int tt = t + u * t_step;
-            if (tt >= t_end)
-                break;  // wave-uniform
-            const int g = tt * 64 + lane;
-            const bool used = g < groups;
-            float val[W];
-            group_values<DT, VEC>(rc, p[u], q[u], val);
-            if (rc.kind != 0 && used)
-                sum += static_cast<double>(pairwise_sum(val));
-            if (!seeded) {
-                // threshold seed: the F-th largest of the lanes' best keys
-                float mv = -__builtin_huge_valf();
-                int mi = kIdxNone;
-                if (used) {
+            if (__ballot(used[u] && group_max(val[u]) >= L.tv)) {
+                const int g = (t + u * t_step) * 64 + lane;
 #pragma unroll
-                    for (int e = 0; e < W; ++e)
-                        if (key_gt(val[e], g * W + e, mv, mi)) {
-                            mv = val[e];
-                            mi = g * W + e;
-                        }
-                }
-                wave_sort_desc(mv, mi);
-                L.tv = __shfl(mv, F - 1, 64);
-                L.ti = __shfl(mi, F - 1, 64);
-                seeded = true;
+                for (int e = 0; e < W; ++e)
+                    append(L, used[u] && key_ge(val[u][e], g * W + e, L.tv, L.ti), val[u][e],
+                           g * W + e);
+                if (L.count > kTightenAt)
+                    tighten<kCap / 64>(L, F);
             }
-#pragma unroll
-            for (int e = 0; e < W; ++e)
-                append(L, used && key_ge(val[e], g * W + e, L.tv, L.ti), val[e], g * W + e);
-            if (L.count > kCap - 64 * W)
-                select_top(L, F);
         }
+    };
+    raw_t pa[U], qa[U], pb[U], qb[U];
+    const int step = U * t_step;
+    int t = t_begin;
+    if (t >= t_end)
+        return sum;
+    load_batch(pa, qa, t);
+    while (true) {
+        load_batch(pb, qb, t + step);
+        consume(pa, qa, t);
+        t += step;
+        if (t >= t_end)
+            break;
+        load_batch(pa, qa, t + step);
+        consume(pb, qb, t);
+        t += step;
+        if (t >= t_end)
+            break;
     }
     return sum;
+}
+
+template <int DT, bool VEC, bool NT, int U>
+__device__ __forceinline__ double stream_pair(const RowCoefs& rc, int groups, int t_begin, int t_end,
+                                     int t_step, int F, WaveList& L) {
+    if (rc.kind == kResidual)
+        return stream_tiles<DT, VEC, NT, kResidual, U>(rc, groups, t_begin, t_end, t_step, F, L);
+    if (rc.kind == kP)
+        return stream_tiles<DT, VEC, NT, kP, U>(rc, groups, t_begin, t_end, t_step, F, L);
+    return stream_tiles<DT, VEC, NT, kRaw, U>(rc, groups, t_begin, t_end, t_step, F, L);
 }
 
 // Coefficients of row pair (b, i): target row i and, for a residual, draft row i.
@@ -283,17 +486,17 @@ __device__ inline RowCoefs pair_coefs(const void* draft, const void* target, int
     rc.mp = rc.mq = 0.0f;
     rc.ratio = 1.0f;
     if (st.mode == 0) {
-        rc.kind = 0;
+        rc.kind = kRaw;
         return rc;
     }
     const RowNorm rp = rn[row0 + G + i];
     rc.mp = rp.m;
     if (i == G) {
-        rc.kind = 1;
+        rc.kind = kP;
         return rc;
     }
     const RowNorm rq = rn[row0 + i];
-    rc.kind = 2;
+    rc.kind = kResidual;
     rc.qrow = row_ptr(draft, DT, static_cast<size_t>(b) * G + i, vocab);
     rc.mq = rq.m;
     rc.ratio = static_cast<float>(rq.s / rp.s);
@@ -326,8 +529,8 @@ __global__ __launch_bounds__(kBlock) void outcome_topf_kernel(
     const int lane = lane_id();
 
     WaveList L{lds[wid], 0, -__builtin_huge_valf(), kIdxNone};
-    double sum = stream_tiles<DT, VEC, NT, 2>(rc, groups, t0 + wid, t1, kWaves, F, L);
-    select_top(L, F);
+    double sum = stream_pair<DT, VEC, NT, 4>(rc, groups, t0 + wid, t1, kWaves, F, L);
+    tighten<kCap / 64>(L, F);
     sum = wave_sum_f64(sum);
     if (lane == 0) {
         lds_sum[wid] = sum;
@@ -343,9 +546,10 @@ __global__ __launch_bounds__(kBlock) void outcome_topf_kernel(
             L.buf[total + lane] = lds[w][lane];
         total += n;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     L.count = total;
-    const int n = select_top(L, F);
+    tighten<kCap / 64>(L, F);
+    const int n = L.count;
     Cand* out = cand_out + (static_cast<size_t>(pair) * nsplit + c) * F;
     if (lane < F)
         out[lane] = lane < n ? L.buf[lane] : Cand{-__builtin_huge_valf(), -1};
@@ -377,7 +581,7 @@ __global__ __launch_bounds__(64) void outcome_merge_kernel(
     const Cand* __restrict__ cand, const double* __restrict__ sums, int32_t* __restrict__ out_tok,
     float* __restrict__ out_prob, float* __restrict__ out_pk, float* __restrict__ out_mass) {
     constexpr int W = Loader<DT, VEC>::W;
-    __shared__ Cand buf[kCap];
+    __shared__ Cand buf[kMergeCap];
     const int pair = blockIdx.x;
     const int G = gamma;
     const int b = pair / (G + 1);
@@ -416,7 +620,7 @@ __global__ __launch_bounds__(64) void outcome_merge_kernel(
     const Cand* src = cand + static_cast<size_t>(pair) * total;
     for (int s = lane; s < total; s += 64)
         buf[s] = src[s];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     double S = 0.0;
     for (int c = 0; c < nsplit; ++c)
         S += sums[static_cast<size_t>(pair) * nsplit + c];
@@ -428,25 +632,27 @@ __global__ __launch_bounds__(64) void outcome_merge_kernel(
         if (i < G && !(S > 0.0)) {
             // Empty residual: the extra token would be drawn from p_i; rank p'.
             RowCoefs rc = pair_coefs<DT>(draft, target, G, vocab, b, i, st, rn);
-            rc.kind = 1;
+            rc.kind = kP;
             rc.qrow = rc.prow;
             L.count = 0;
             L.tv = -__builtin_huge_valf();
             L.ti = kIdxNone;
             const int groups = vocab / W;
-            S = wave_sum_f64(stream_tiles<DT, VEC, false, 1>(rc, groups, 0, (groups + 63) / 64, 1,
-                                                              F, L));
+            S = wave_sum_f64(stream_tiles<DT, VEC, false, kP, 1>(rc, groups, 0, (groups + 63) / 64,
+                                                                  1, F, L));
         }
     }
-    const int n = select_top(L, F);
-    for (int j = lane; j < F; j += 64) {
-        const bool have = j < n;
-        tok[j] = have ? L.buf[j].i : -1;
+    tighten<kMergeCap / 64>(L, F);
+    float v;
+    int idx;
+    sorted_entries(L, &v, &idx);
+    if (lane < F) {
+        tok[lane] = idx;
         float pr = 0.0f;
-        if (have)
-            pr = st.mode == 0 ? (j == 0 ? 1.0f : 0.0f)
-                              : static_cast<float>(static_cast<double>(L.buf[j].v) / S);
-        prob[j] = pr;
+        if (idx >= 0)
+            pr = st.mode == 0 ? (lane == 0 ? 1.0f : 0.0f)
+                              : static_cast<float>(static_cast<double>(v) / S);
+        prob[lane] = pr;
     }
     if (lane == 0) {
         out_pk[pair] = static_cast<float>(pk);
