@@ -50,6 +50,7 @@ namespace {
 constexpr long kRowTargetBlocks = 12288;
 constexpr long kResidualTargetBlocks = 4096;
 constexpr long kOutcomeTargetBlocks = 2048;
+constexpr int kResidualFusedMinBatch = 128;
 
 int env_int(const char* name, int fallback) {
     const char* v = std::getenv(name);
@@ -139,10 +140,17 @@ int spec_verify_init(int batch, int gamma, int vocab, int dtype, void* hip_strea
     const int ru = env_int("SPEC_VERIFY_RESIDUAL_UNROLL", 0);
     if (ru == 2 || ru == 4)
         ctx->residual_unroll = ru;
+    // With at least half as many sequences as CUs, one workgroup per sequence
+    // (the fused residual kernel) fills the GPU by itself.
+    const bool fused_fits = residual_tiles_per_row(vocab) <= residual_fused_max_tiles();
+    int fused = batch >= kResidualFusedMinBatch && fused_fits ? 1 : 0;
+    fused = env_int("SPEC_VERIFY_RESIDUAL_FUSED", fused);
+    if (fused && fused_fits && o3 <= 0)
+        ctx->nsplit_residual = 0;
     // A dispatch holds fewer than 2^32 work-items.
     const long long limit = 1LL << 32;
     if (static_cast<long long>(rows) * ctx->nsplit_rows * kBlock >= limit ||
-        static_cast<long long>(batch) * ctx->nsplit_residual * kBlock >= limit ||
+        static_cast<long long>(batch) * std::max(ctx->nsplit_residual, 1) * kBlock >= limit ||
         static_cast<long long>(pairs) * ctx->nsplit_outcome * kBlock >= limit) {
         delete ctx;
         return SPEC_EINVAL;

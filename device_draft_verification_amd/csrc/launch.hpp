@@ -52,8 +52,11 @@ hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const vo
 // Residual / bonus draw at the first rejection: per-tile sums (B * nsplit
 // workgroups, `unroll` tiles per batch per wavefront: 2 or 4), then one
 // locating wavefront per sequence. tile_sums holds
-// B * residual_tiles_per_row(vocab) floats.
+// B * residual_tiles_per_row(vocab) floats. nsplit == 0 selects the fused
+// kernel instead (one workgroup per sequence, tile sums in LDS, one launch),
+// for rows of at most residual_fused_max_tiles() tiles.
 int residual_tiles_per_row(int vocab);
+int residual_fused_max_tiles();
 hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, const void* draft,
                            const void* target, const SeqState* seq, float* tile_sums,
                            int32_t* out_tok, hipStream_t stream);

@@ -35,6 +35,7 @@ namespace specv {
 namespace {
 
 constexpr int kTile = 64;  // groups per tile = lanes per wavefront
+constexpr int kResidualFusedMaxTiles = 16384;  // LDS tile sums of the fused kernel (64 KiB)
 
 // The one or two rows of a sequence at its first rejection.
 struct SeqRows {
@@ -334,24 +335,13 @@ __device__ inline double tile_sum_of(const SeqRows& s, int t, int groups) {
     return static_cast<double>(tile_reduce(gs));
 }
 
+// The draw of one sequence from its tile sums `ts` (global memory or LDS), by
+// one wavefront: total S, the tile holding tau = u_res * S, then the token
+// inside it; the empty-residual fallback streams p at position k.
 template <int DT, bool VEC, bool NT>
-__global__ __launch_bounds__(64) void residual_locate_kernel(
-    const void* __restrict__ draft, const void* __restrict__ target, int gamma, int vocab,
-    int ntiles, int tiles_per_row, const SeqState* __restrict__ seq,
-    const float* __restrict__ tile_sums, int32_t* __restrict__ out_tok) {
-    constexpr int W = Group<DT, VEC>::W;
-    const int b = blockIdx.x;
-    const SeqState st = seq[b];
-    if (st.mode != 1)
-        return;
-    const int G = gamma, k = st.k;
-    SeqRows s;
-    seq_row_ptrs<DT>(s, draft, target, G, vocab, b, k);
-    seq_row_coefs(s, st);
-    const int groups = vocab / W;
-    const float* ts = tile_sums + static_cast<size_t>(b) * tiles_per_row;
+__device__ inline void locate_emit(SeqRows& s, const SeqState& st, const float* ts, int ntiles,
+                                   int groups, int G, int b, int32_t* out_tok) {
     const int lane = threadIdx.x & 63;
-
     double mine = 0.0;
     for (int t = lane; t < ntiles; t += 64)
         mine += static_cast<double>(ts[t]);
@@ -391,7 +381,97 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
         token = scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
     }
     if (lane == 0)
-        out_tok[static_cast<size_t>(b) * (G + 1) + k] = token;
+        out_tok[static_cast<size_t>(b) * (G + 1) + st.k] = token;
+}
+
+template <int DT, bool VEC, bool NT>
+__global__ __launch_bounds__(64) void residual_locate_kernel(
+    const void* __restrict__ draft, const void* __restrict__ target, int gamma, int vocab,
+    int ntiles, int tiles_per_row, const SeqState* __restrict__ seq,
+    const float* __restrict__ tile_sums, int32_t* __restrict__ out_tok) {
+    constexpr int W = Group<DT, VEC>::W;
+    const int b = blockIdx.x;
+    const SeqState st = seq[b];
+    if (st.mode != 1)
+        return;
+    SeqRows s;
+    seq_row_ptrs<DT>(s, draft, target, gamma, vocab, b, st.k);
+    seq_row_coefs(s, st);
+    locate_emit<DT, VEC, NT>(s, st, tile_sums + static_cast<size_t>(b) * tiles_per_row, ntiles,
+                             vocab / W, gamma, b, out_tok);
+}
+
+// One workgroup of 16 wavefronts per sequence: the wavefronts stream the
+// sequence's tiles (wavefront w takes tiles w, w + 16, ..., U at a time,
+// double-buffered as in residual_tiles_kernel, with the same arithmetic and
+// the same per-tile sums), keep the tile sums in LDS, and after one barrier
+// wavefront 0 draws the token. Used when there are enough sequences to give
+// every CU a workgroup; it saves the second launch and the round trip of the
+// tile sums through memory.
+constexpr int kFusedBlock = 1024;
+
+template <int DT, bool VEC, int U, bool NT, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
+    const void* __restrict__ draft, const void* __restrict__ target, int gamma, int vocab,
+    int ntiles, const SeqState* __restrict__ seq, int32_t* __restrict__ out_tok) {
+    using IO = GroupIO<DT, VEC, NT>;
+    constexpr int W = IO::W;
+    constexpr int kFusedWaves = BLOCK / 64;
+    extern __shared__ float lds_ts[];
+    const int b = blockIdx.x;
+    const SeqState st = seq[b];
+    if (st.mode != 1)
+        return;  // greedy or rejected sequence: nothing to draw
+    const int groups = vocab / W;
+    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
+    SeqRows s;
+    seq_row_ptrs<DT>(s, draft, target, gamma, vocab, b, st.k);
+    auto load_batch = [&](IO (&io)[U], int t) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int g = (t + u * kFusedWaves) * kTile + lane;
+            const bool used = t + u * kFusedWaves < ntiles && g < groups;
+            io[u].load(s, used ? g : 0);
+        }
+    };
+    auto reduce_batch = [&](const IO (&io)[U], int t) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tt = t + u * kFusedWaves;
+            if (tt >= ntiles)
+                break;  // wave-uniform
+            const int g = tt * kTile + lane;
+            float gs = 0.0f;
+            if (g < groups) {
+                float r[W];
+                io[u].residual(s, r);
+                gs = pairwise(r);
+            }
+            const float ts = tile_reduce(gs);
+            if (lane == 0)
+                lds_ts[tt] = ts;
+        }
+    };
+    constexpr int kStep = kFusedWaves * U;
+    IO buf_a[U], buf_b[U];
+    int t = wid;
+    load_batch(buf_a, t);
+    seq_row_coefs(s, st);
+    while (t < ntiles) {
+        load_batch(buf_b, t + kStep);
+        reduce_batch(buf_a, t);
+        t += kStep;
+        if (t >= ntiles)
+            break;
+        load_batch(buf_a, t + kStep);
+        reduce_batch(buf_b, t);
+        t += kStep;
+    }
+    __syncthreads();
+    if (wid != 0)
+        return;
+    locate_emit<DT, VEC, NT>(s, st, lds_ts, ntiles, groups, gamma, b, out_tok);
 }
 
 template <int DT, bool VEC, int U>
@@ -404,6 +484,16 @@ hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const vo
         return hipSuccess;
     const int groups = sh.vocab / W;
     const int ntiles = (groups + kTile - 1) / kTile;
+    if (nsplit == 0) {
+        // One tile in flight per wavefront (double-buffered) measured best:
+        // 16 wavefronts already keep 32 KiB per row in flight per workgroup.
+        residual_fused_kernel<DT, VEC, 1, NT, kFusedBlock><<<dim3(static_cast<unsigned>(sh.batch)),
+                                                           dim3(kFusedBlock),
+                                                           static_cast<size_t>(ntiles) * sizeof(float),
+                                                           stream>>>(
+            draft, target, sh.gamma, sh.vocab, ntiles, seq, out_tok);
+        return hipGetLastError();
+    }
     const int per = (ntiles + nsplit - 1) / nsplit;
     residual_tiles_kernel<DT, VEC, U, NT><<<dim3(static_cast<unsigned>(sh.batch), static_cast<unsigned>(nsplit)),
                                             dim3(kBlock), 0, stream>>>(
@@ -431,10 +521,14 @@ hipError_t launch_unroll(const Shape& sh, int nsplit, int unroll, int tiles_per_
 
 int residual_tiles_per_row(int vocab) { return (vocab + kTile - 1) / kTile; }
 
+int residual_fused_max_tiles() { return kResidualFusedMaxTiles; }
+
 hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, const void* draft,
                            const void* target, const SeqState* seq, float* tile_sums,
                            int32_t* out_tok, hipStream_t stream) {
-    if (nsplit < 1 || nsplit > kMaxSplit)
+    if (nsplit < 0 || nsplit > kMaxSplit)
+        return hipErrorInvalidValue;
+    if (nsplit == 0 && residual_tiles_per_row(s.vocab) > kResidualFusedMaxTiles)
         return hipErrorInvalidValue;
     // Tile sums are laid out with the element-path tile count, which bounds the
     // 16-byte-group tile count.

@@ -200,7 +200,9 @@ int spec_verify_enable_timing(spec_verify_ctx *ctx, int max_calls);
 int spec_verify_read_timing(spec_verify_ctx *ctx, float *out_ms, int max_calls);
 
 /* Launch geometry chosen at init: vocabulary splits of the row-normaliser and
- * residual kernels, and threads per workgroup. Host memory out[3]. */
+ * residual kernels (0 for the residual: one workgroup per sequence, the tile
+ * sums kept in LDS), and threads per workgroup of the vocabulary kernels.
+ * Host memory out[3]. */
 int spec_verify_get_geometry(spec_verify_ctx *ctx, int *out);
 
 /* Free the workspace and the context (waits for the context's stream). */

@@ -95,6 +95,30 @@ def test_small_shapes_parity(cfg, over):
         assert_parity(rep, str(over))
 
 
+@pytest.mark.parametrize("cfg,over", [CASES[i] for i in (0, 1, 2, 4, 5, 8, 9)])
+@pytest.mark.parametrize("fused", [1, 0], ids=["fused", "split"])
+def test_residual_kernel_choice_parity(cfg, over, fused, monkeypatch):
+    """Both residual paths on the same inputs: the fused one-workgroup-per-
+    sequence kernel (chosen by default from B = 128) and the split kernels
+    (forced), each against the oracle, and against each other bit for bit."""
+    monkeypatch.setenv("SPEC_VERIFY_RESIDUAL_FUSED", str(fused))
+    rec = specgen.config(cfg).replace(**over)
+    d = specgen.generate(rec)
+    t = to_device(d)
+    ctx = sv.spec_verify_init(rec.batch, rec.gamma, rec.vocab, t["logits_target"].dtype)
+    geo = sv.spec_verify_get_geometry(ctx)
+    assert (geo["residual_splits"] == 0) == bool(fused)
+    gpu = run_gpu(t, seed=7, offset=1, ctx=ctx)
+    ref = _oracle(d, seed=7, offset=1)
+    rep = compare(gpu, ref, d["temperature"])
+    _report(f"{rec.name} {over} fused={fused}", rep)
+    assert_parity(rep, str(over))
+    monkeypatch.setenv("SPEC_VERIFY_RESIDUAL_FUSED", str(1 - fused))
+    other = run_gpu(t, seed=7, offset=1)
+    assert np.array_equal(other["tokens"], gpu["tokens"])
+    assert np.array_equal(other["accept_len"], gpu["accept_len"])
+
+
 # ------------------------------------------- full-size large configs, sampled --
 
 @pytest.fixture(scope="module", params=[3, 4, 5])
