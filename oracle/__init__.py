@@ -21,6 +21,10 @@ is stated at the top of ``spec_oracle.c``. Parity status of each function:
   pairs and by the closed-form acceptance probability min(1, p/q).
 * ``gamma_sample`` / ``beta_sample`` (``bandit_oracle.c``) -- pinned by
   Kolmogorov-Smirnov tests against ``scipy.stats.gamma`` / ``scipy.stats.beta``.
+* ``lowrank_head`` -- pinned against numpy's float64 matrix products, the
+  bfloat16 rounding against PyTorch's float32 -> bfloat16 conversion and
+  hand-made ties, the normaliser against ``scipy.special.logsumexp``, and the
+  rank-one closed form.
 * ``bandit_step`` -- UCB1 pinned by its opening round robin and by the regret
   bound of Auer, Cesa-Bianchi and Fischer (2002, Theorem 1); Thompson sampling by
   logarithmic regret growth; both by the output-marginal gate with the bandit
@@ -88,6 +92,8 @@ def _load():
     lib.oracle_gather_logprobs.restype = None
     lib.oracle_outcomes.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, P, P, P, P, P, P]
     lib.oracle_outcomes.restype = None
+    lib.oracle_lowrank_head.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_lowrank_head.restype = None
     lib.oracle_gamma_mt.argtypes = [f64, u64, u64, i32, i32, i32, P]
     lib.oracle_gamma_mt.restype = f64
     lib.oracle_beta_sample.argtypes = [f64, f64, u64, u64, i32, i32, P]
@@ -273,6 +279,31 @@ def outcomes(logits_draft, logits_target, draft_tokens, temperature, F: int,
     out = dict(tokens=out_tok, probs=out_prob, pk=pk, mass=mass)
     if with_dist:
         out.update(dist=dist, scale=scale)
+    return out
+
+
+def lowrank_head(h, w_down, w_up, temperature, rows=None):
+    """z = W_up (W_down h) with bfloat16 inputs (uint16 bit patterns), the
+    rank-r activation and the logits rounded to bfloat16, and the logits' row
+    log-normaliser at the row's temperature. h [N, d], w_down [r, d],
+    w_up [V, r], temperature [N]; ``rows`` restricts the work to some rows."""
+    h = np.ascontiguousarray(h, np.uint16)
+    w_down = np.ascontiguousarray(w_down, np.uint16)
+    w_up = np.ascontiguousarray(w_up, np.uint16)
+    N, d = h.shape
+    r, d2 = w_down.shape
+    V, r2 = w_up.shape
+    assert d2 == d and r2 == r
+    temp = np.ascontiguousarray(temperature, np.float32).reshape(N)
+    idx = None if rows is None else np.ascontiguousarray(rows, np.int32)
+    n = N if idx is None else idx.size
+    out = dict(u_exact=np.zeros((n, r)), u=np.zeros((n, r), np.uint16), u_abs=np.zeros((n, r)),
+               z_exact=np.zeros((n, V)), z=np.zeros((n, V), np.uint16), z_abs=np.zeros((n, V)),
+               lse=np.zeros(n))
+    _load().oracle_lowrank_head(n, d, r, V, _ptr(h), _ptr(w_down), _ptr(w_up), _ptr(temp),
+                                _ptr(idx), _ptr(out["u_exact"]), _ptr(out["u"]), _ptr(out["u_abs"]),
+                                _ptr(out["z_exact"]), _ptr(out["z"]), _ptr(out["z_abs"]),
+                                _ptr(out["lse"]))
     return out
 
 

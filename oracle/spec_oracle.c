@@ -654,3 +654,101 @@ void oracle_outcomes(int batch, int gamma, int vocab, int dtype,
     free(beta);
     free(taken);
 }
+
+/* ------------------------------------------------ low-rank draft head -- */
+
+/* binary32 -> bfloat16, round to nearest even (finite inputs). */
+static uint16_t oracle_bf16_rne(double x)
+{
+    float f = (float)x; /* a first guess only: bf16_nearest checks it */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* The bfloat16 nearest to x (ties to even), decided in double: the two
+ * neighbours of x on the bfloat16 grid are compared by their distance. */
+static uint16_t bf16_nearest(double x)
+{
+    uint16_t c = oracle_bf16_rne(x); /* a candidate within one step */
+    double best = (double)bf16_bits_to_float(c);
+    uint16_t out = c;
+    for (int d = -1; d <= 1; d += 2) {
+        uint16_t n = (uint16_t)(c + d);
+        double v = (double)bf16_bits_to_float(n);
+        double e0 = fabs(best - x), e1 = fabs(v - x);
+        if (e1 < e0 || (e1 == e0 && (n & 1u) == 0u)) {
+            best = v;
+            out = n;
+        }
+    }
+    return out;
+}
+
+/*
+ * The low-rank draft LM head and the normaliser of its logits. The SlimSpec
+ * summary (Methodology, architecture) replaces the draft's full projection
+ * z = W_full h by z = W_up W_down h with W_down in R^{r x d}, W_up in
+ * R^{V x r}, r << d, computed with dense matrix products. Readings:
+ *   SL1 h, W_down and W_up are bfloat16; the rank-r activation u = W_down h is
+ *       a bfloat16 tensor (the output of a bf16 linear layer, rounded to
+ *       nearest even), and the logits z = W_up u are rounded to bfloat16 (the
+ *       dtype the verifier reads);
+ *   SL2 the normaliser is that of the verifier's draft rows (R3):
+ *       lse = log sum_v exp(fl32(z_v * fl32(1/T))), NaN when T is not > 0 or
+ *       the reciprocal overflows.
+ * Products and sums are exact up to the rounding of double (each product of
+ * two bfloat16 values is exact; sums of at most 2^16 terms of such products
+ * carry a relative error below 2^-37 of their magnitude), so the roundings to
+ * bfloat16 are those of the exact values except within that margin.
+ *
+ * Outputs (row-major): u_exact [N][r], u [N][r] (bf16 bits), u_abs [N][r]
+ * = sum_k |W_down[j][k] h[k]|; z_exact [N][V] = W_up u (from the rounded u),
+ * z [N][V] (bf16 bits), z_abs [N][V] = sum_j |W_up[v][j] u[j]|; lse [N].
+ * rows restricts the work to a subset of rows (NULL = all): row i of the
+ * outputs is input row rows[i].
+ */
+void oracle_lowrank_head(int n_rows, int d, int r, int V, const uint16_t *h,
+                         const uint16_t *w_down, const uint16_t *w_up, const float *temperature,
+                         const int32_t *rows, double *u_exact, uint16_t *u, double *u_abs,
+                         double *z_exact, uint16_t *z, double *z_abs, double *lse)
+{
+    double *uu = (double *)malloc(sizeof(double) * (size_t)r);
+    for (int i = 0; i < n_rows; ++i) {
+        const int row = rows ? rows[i] : i;
+        const uint16_t *hr = h + (size_t)row * d;
+        for (int j = 0; j < r; ++j) {
+            double s = 0.0, a = 0.0;
+            for (int k = 0; k < d; ++k) {
+                double t = (double)bf16_bits_to_float(w_down[(size_t)j * d + k]) *
+                           (double)bf16_bits_to_float(hr[k]);
+                s += t;
+                a += fabs(t);
+            }
+            u_exact[(size_t)i * r + j] = s;
+            u_abs[(size_t)i * r + j] = a;
+            u[(size_t)i * r + j] = bf16_nearest(s);
+            uu[j] = (double)bf16_bits_to_float(u[(size_t)i * r + j]);
+        }
+        for (int v = 0; v < V; ++v) {
+            double s = 0.0, a = 0.0;
+            for (int j = 0; j < r; ++j) {
+                double t = (double)bf16_bits_to_float(w_up[(size_t)v * r + j]) * uu[j];
+                s += t;
+                a += fabs(t);
+            }
+            z_exact[(size_t)i * V + v] = s;
+            z_abs[(size_t)i * V + v] = a;
+            z[(size_t)i * V + v] = bf16_nearest(s);
+        }
+        float inv_t = 0.0f;
+        if (!temperature_valid(temperature[row], &inv_t) || temperature[row] == 0.0f) {
+            lse[i] = NAN;
+            continue;
+        }
+        lse[i] = oracle_row_lse(z + (size_t)i * V, ORACLE_BF16, 0, V, inv_t);
+    }
+    free(uu);
+}

@@ -40,7 +40,7 @@ import os
 import numpy as np
 
 __all__ = ["Recipe", "CONFIGS", "config", "generate", "f32_to_bf16_bits",
-           "bf16_bits_to_f32", "gumbel_max_tokens"]
+           "bf16_bits_to_f32", "gumbel_max_tokens", "lowrank_head_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -184,3 +184,29 @@ def generate(recipe: Recipe, seq_ids=None, threads: int | None = None) -> dict:
     return dict(logits_draft=draft, logits_target=target, draft_tokens=tokens,
                 temperature=temps_all[ids].copy(), seq_ids=ids.astype(np.int64),
                 recipe=recipe)
+
+
+def lowrank_head_inputs(rows: int, hidden: int, rank: int, vocab: int, seed: int = 0,
+                        logit_std: float = 2.5, greedy_fraction: float = 0.1):
+    """Synthetic inputs of a low-rank draft LM head z = W_up (W_down h), as
+    bfloat16 bit patterns: h [rows, hidden] ~ N(0, 1), W_down [rank, hidden]
+    ~ N(0, 1/hidden) (so W_down h ~ N(0, 1)), W_up [vocab, rank] ~ N(0,
+    logit_std^2 / rank) (so the logits have standard deviation about
+    logit_std, that of the B=256 workload's draft rows); temperatures
+    U[0.3, 1.5] per row with round(greedy_fraction * rows) rows at 0. Random
+    weights stand in for a trained head; no dataset is involved."""
+    rng = np.random.default_rng([seed, 7919])
+    h = rng.standard_normal((rows, hidden), dtype=np.float32)
+    w_down = rng.standard_normal((rank, hidden), dtype=np.float32) * np.float32(1.0 / np.sqrt(hidden))
+    w_up = np.empty((vocab, rank), dtype=np.uint16)
+    scale = np.float32(logit_std / np.sqrt(rank))
+    step = 16384
+    for v0 in range(0, vocab, step):   # in slices, to bound the float32 temporaries
+        v1 = min(vocab, v0 + step)
+        w_up[v0:v1] = f32_to_bf16_bits(rng.standard_normal((v1 - v0, rank), dtype=np.float32) * scale)
+    temp = rng.uniform(0.3, 1.5, size=rows).astype(np.float32)
+    n_greedy = int(round(greedy_fraction * rows))
+    if n_greedy:
+        temp[rng.choice(rows, size=n_greedy, replace=False)] = 0.0
+    return dict(h=f32_to_bf16_bits(h), w_down=f32_to_bf16_bits(w_down), w_up=w_up,
+                temperature=temp)

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_bandit_oracle as bandit
+import test_oracle_lowrank as lowrank
 import test_oracle_outcomes as outcomes
 import test_oracle_pins as pins
 import test_oracle_stats as stats
@@ -129,6 +130,28 @@ def test_outcome_residual_without_the_max_is_caught():
     with mutated_oracle("r[v] = p - q > 0.0 ? p - q : 0.0;\n                        sc[v] = p + q;",
                         "r[v] = p - q;\n                        sc[v] = p + q;"):
         fails(outcomes.test_residual_mass_is_total_variation)
+
+
+def test_head_up_projection_transposed_is_caught():
+    with mutated_oracle("double t = (double)bf16_bits_to_float(w_up[(size_t)v * r + j]) * uu[j];",
+                        "double t = (double)bf16_bits_to_float(w_up[(size_t)j * V + v]) * uu[j];"):
+        fails(lowrank.test_products_match_numpy)
+
+
+def test_head_activation_not_rounded_is_caught():
+    with mutated_oracle("uu[j] = (double)bf16_bits_to_float(u[(size_t)i * r + j]);", "uu[j] = s;"):
+        fails(lowrank.test_products_match_numpy)
+
+
+def test_head_normaliser_without_temperature_is_caught():
+    with mutated_oracle("lse[i] = oracle_row_lse(z + (size_t)i * V, ORACLE_BF16, 0, V, inv_t);",
+                        "lse[i] = oracle_row_lse(z + (size_t)i * V, ORACLE_BF16, 0, V, 1.0f);"):
+        fails(lowrank.test_lse_matches_scipy)
+
+
+def test_head_ties_to_odd_are_caught():
+    with mutated_oracle("(e1 == e0 && (n & 1u) == 0u)", "(e1 == e0 && (n & 1u) == 1u)"):
+        fails(lowrank.test_bf16_rounding_matches_torch_and_ties_go_to_even)
 
 
 def ucb1_pins():
