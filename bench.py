@@ -315,6 +315,32 @@ def main() -> int:
     outcome_ms = start.elapsed_time(end) / args.steps
     outcome_bytes = algorithmic_bytes(rec, d["temperature"], alen.cpu().numpy())["row_norm"]
     outcome_gbs = outcome_bytes / (outcome_ms * 1e-3) / 1e9
+
+    # Low-rank draft head for one draft step of this batch: N = B rows,
+    # hidden d = 4096, rank r = d / 8 = 512 (the pages' example ratio), this
+    # workload's vocabulary; random bf16 weights made on the device.
+    hd, hr = 4096, 512
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    hh = torch.randn(B, hd, device=dev, generator=gen).to(torch.bfloat16)
+    wd = (torch.randn(hr, hd, device=dev, generator=gen) / hd ** 0.5).to(torch.bfloat16)
+    wu = (torch.randn(V, hr, device=dev, generator=gen) * (2.5 / hr ** 0.5)).to(torch.bfloat16)
+    hz = torch.empty(B, V, dtype=torch.bfloat16, device=dev)
+    hl = torch.empty(B, dtype=torch.float64, device=dev)
+    hctx = sv.spec_lowrank_head_init(B, hd, hr, V, stream=stream)
+    for _ in range(args.warmup):
+        sv.spec_lowrank_head(hctx, hh, wd, wu, temp, hz, hl)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        sv.spec_lowrank_head(hctx, hh, wd, wu, temp, hz, hl)
+    end.record(stream)
+    torch.cuda.synchronize()
+    head_ms = start.elapsed_time(end) / args.steps
+    head_bytes = 2 * (V * hr + B * V + hr * hd + B * hd)
+    head_flops = 2 * B * (hd * hr + hr * V)
+    sv.spec_lowrank_head_destroy(hctx)
+    del hh, wd, wu, hz
     k1_gbs = k1_bytes / (k1_ms * 1e-3) / 1e9
     k3_gbs = k3_bytes / (k3_ms * 1e-3) / 1e9
     call_gbs = (k1_bytes + k2_bytes + k3_bytes) / (ms_per_step * 1e-3) / 1e9
@@ -356,6 +382,11 @@ def main() -> int:
                         "bytes": sc_b * sc_g * 8 + sc_b * 4,
                         "sequences_per_s": round(sc_b / (scalar_us * 1e-6), 1)},
         "bandit": {"arms": 3, "us_per_step": bandit_us},
+        "lowrank_head": {"rows": B, "hidden": hd, "rank": hr, "vocab": V,
+                         "us_per_call": round(head_ms * 1e3, 2), "bytes": int(head_bytes),
+                         "gbs": round(head_bytes / (head_ms * 1e-3) / 1e9, 1),
+                         "tflops": round(head_flops / (head_ms * 1e-3) / 1e12, 1),
+                         "frac_hbm": round(head_bytes / (head_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "outcomes": {"top_f": F_OUT, "us_per_call": round(outcome_ms * 1e3, 2),
                      "bytes": int(outcome_bytes), "gbs": round(outcome_gbs, 1),
                      "frac": round(outcome_gbs / HBM_PEAK_GBS, 4)},

@@ -1,8 +1,9 @@
 """Batched speculative-sampling verification on AMD Instinct MI355X (gfx950).
 
 The work is done by hand-written HIP kernels in ``libspecverify.so`` behind the
-C ABI of ``include/spec_verify.h`` (verification) and ``include/spec_bandit.h``
-(online draft selection); this package is a thin ctypes binding with
+C ABI of ``include/spec_verify.h`` (verification), ``include/spec_bandit.h``
+(online draft selection) and ``include/spec_head.h`` (low-rank draft head with
+its fused normaliser); this package is a thin ctypes binding with
 the same function names (``binding``) and the build script (``build``).
 """
 from .binding import (  # noqa: F401
@@ -14,4 +15,6 @@ from .binding import (  # noqa: F401
     SPEC_BANDIT_MAX_ARMS, SPEC_BANDIT_THOMPSON, SPEC_BANDIT_UCB1, BanditContext,
     spec_bandit_destroy, spec_bandit_get_state, spec_bandit_init, spec_bandit_set_state,
     spec_bandit_set_stream, spec_bandit_step,
+    HeadContext, spec_lowrank_head, spec_lowrank_head_copy_activation, spec_lowrank_head_destroy,
+    spec_lowrank_head_init, spec_lowrank_head_set_stream,
 )

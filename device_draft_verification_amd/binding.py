@@ -30,6 +30,8 @@ EXPORTED = (
     "spec_verify_strerror", "spec_verify_outcomes",
     "spec_bandit_init", "spec_bandit_set_stream", "spec_bandit_step", "spec_bandit_get_state",
     "spec_bandit_set_state", "spec_bandit_destroy",
+    "spec_lowrank_head_init", "spec_lowrank_head_set_stream", "spec_lowrank_head",
+    "spec_lowrank_head_copy_activation", "spec_lowrank_head_destroy",
 )
 
 SPEC_OUTCOME_MAX_F = 64
@@ -75,6 +77,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_bandit_get_state": ([P, P, P], i32),
         "spec_bandit_set_state": ([P, P, P], i32),
         "spec_bandit_destroy": ([P], i32),
+        "spec_lowrank_head_init": ([i32, i32, i32, i32, P, ctypes.POINTER(P)], i32),
+        "spec_lowrank_head_set_stream": ([P, P], i32),
+        "spec_lowrank_head": ([P, P, P, P, P, P, P], i32),
+        "spec_lowrank_head_copy_activation": ([P, P], i32),
+        "spec_lowrank_head_destroy": ([P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -317,3 +324,71 @@ def spec_bandit_destroy(ctx: BanditContext) -> None:
         rc = load_library().spec_bandit_destroy(ctx.handle)
         ctx.handle = None
         _check("spec_bandit_destroy", rc)
+
+
+class HeadContext:
+    """Owns a spec_head_ctx*; destroyed with spec_lowrank_head_destroy."""
+
+    def __init__(self, handle: ctypes.c_void_p, rows: int, hidden: int, rank: int, vocab: int):
+        self.handle = handle
+        self.rows, self.hidden, self.rank, self.vocab = rows, hidden, rank, vocab
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                load_library().spec_lowrank_head_destroy(self.handle)
+            except Exception:
+                pass
+            self.handle = None
+
+
+def _bf16_like(t, shape, name):
+    """bf16 tensors may be passed as torch.bfloat16 or as their int16 bits."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype not in (torch.bfloat16, torch.int16):
+        raise TypeError(f"{name}: dtype {t.dtype}, expected bfloat16 (or int16 bits)")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def spec_lowrank_head_init(rows: int, hidden: int, rank: int, vocab: int, stream=None) -> HeadContext:
+    h = ctypes.c_void_p()
+    _check("spec_lowrank_head_init", load_library().spec_lowrank_head_init(
+        rows, hidden, rank, vocab, _stream_handle(stream), ctypes.byref(h)))
+    return HeadContext(h, rows, hidden, rank, vocab)
+
+
+def spec_lowrank_head_set_stream(ctx: HeadContext, stream=None) -> None:
+    _check("spec_lowrank_head_set_stream",
+           load_library().spec_lowrank_head_set_stream(ctx.handle, _stream_handle(stream)))
+
+
+def spec_lowrank_head(ctx: HeadContext, hidden, w_down, w_up, temperature, out_logits, out_lse) -> None:
+    """hidden [N, d], w_down [r, d], w_up [V, r], out_logits [N, V] bf16;
+    temperature [N] float32; out_lse [N] float64."""
+    N, d, r, V = ctx.rows, ctx.hidden, ctx.rank, ctx.vocab
+    _bf16_like(hidden, (N, d), "hidden")
+    _bf16_like(w_down, (r, d), "w_down")
+    _bf16_like(w_up, (V, r), "w_up")
+    _bf16_like(out_logits, (N, V), "out_logits")
+    _expect(temperature, (N,), torch.float32, "temperature")
+    _expect(out_lse, (N,), torch.float64, "out_lse")
+    _check("spec_lowrank_head", load_library().spec_lowrank_head(
+        ctx.handle, _ptr(hidden), _ptr(w_down), _ptr(w_up), _ptr(temperature),
+        _ptr(out_logits), _ptr(out_lse)))
+
+
+def spec_lowrank_head_copy_activation(ctx: HeadContext, out_u) -> None:
+    _bf16_like(out_u, (ctx.rows, ctx.rank), "out_u")
+    _check("spec_lowrank_head_copy_activation",
+           load_library().spec_lowrank_head_copy_activation(ctx.handle, _ptr(out_u)))
+
+
+def spec_lowrank_head_destroy(ctx: HeadContext) -> None:
+    if ctx.handle:
+        rc = load_library().spec_lowrank_head_destroy(ctx.handle)
+        ctx.handle = None
+        _check("spec_lowrank_head_destroy", rc)

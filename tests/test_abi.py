@@ -89,6 +89,21 @@ def test_bandit_host_argument_checks(lib):
     assert lib.spec_bandit_destroy(None) == E
 
 
+def test_head_host_argument_checks(lib):
+    E = sv.binding.SPEC_EINVAL
+    h = ctypes.c_void_p()
+    assert lib.spec_lowrank_head_init(8, 128, 64, 296, None, None) == E
+    assert lib.spec_lowrank_head_init(0, 128, 64, 296, None, ctypes.byref(h)) == E   # no rows
+    assert lib.spec_lowrank_head_init(8, 96, 64, 296, None, ctypes.byref(h)) == E    # d % 64
+    assert lib.spec_lowrank_head_init(8, 128, 32, 296, None, ctypes.byref(h)) == E   # r % 64
+    assert lib.spec_lowrank_head_init(8, 128, 64, 300, None, ctypes.byref(h)) == E   # V % 8
+    assert not h.value
+    assert lib.spec_lowrank_head(None, None, None, None, None, None, None) == E
+    assert lib.spec_lowrank_head_copy_activation(None, None) == E
+    assert lib.spec_lowrank_head_set_stream(None, None) == E
+    assert lib.spec_lowrank_head_destroy(None) == E
+
+
 def test_binding_refuses_missing_library(tmp_path, lib):
     saved = sv.binding._lib
     sv.binding._lib = None
