@@ -25,6 +25,9 @@ is stated at the top of ``spec_oracle.c``. Parity status of each function:
   bfloat16 rounding against PyTorch's float32 -> bfloat16 conversion and
   hand-made ties, the normaliser against ``scipy.special.logsumexp``, and the
   rank-one closed form.
+* ``tree_prune`` / ``tree_verify_greedy`` -- pinned by brute force over the
+  paths of small trees (path scores summed root to leaf, selection by sorting)
+  and, for chains, by the verification oracle's greedy outcome.
 * ``bandit_step`` -- UCB1 pinned by its opening round robin and by the regret
   bound of Auer, Cesa-Bianchi and Fischer (2002, Theorem 1); Thompson sampling by
   logarithmic regret growth; both by the output-marginal gate with the bandit
@@ -94,6 +97,10 @@ def _load():
     lib.oracle_outcomes.restype = None
     lib.oracle_lowrank_head.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.oracle_lowrank_head.restype = None
+    lib.oracle_tree_prune.argtypes = [i32, i32, P, P, f64, i32, P, P, P, P]
+    lib.oracle_tree_prune.restype = None
+    lib.oracle_tree_verify_greedy.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P]
+    lib.oracle_tree_verify_greedy.restype = None
     lib.oracle_gamma_mt.argtypes = [f64, u64, u64, i32, i32, i32, P]
     lib.oracle_gamma_mt.restype = f64
     lib.oracle_beta_sample.argtypes = [f64, f64, u64, u64, i32, i32, P]
@@ -304,6 +311,36 @@ def lowrank_head(h, w_down, w_up, temperature, rows=None):
                                 _ptr(idx), _ptr(out["u_exact"]), _ptr(out["u"]), _ptr(out["u_abs"]),
                                 _ptr(out["z_exact"]), _ptr(out["z"]), _ptr(out["z_abs"]),
                                 _ptr(out["lse"]))
+    return out
+
+
+def tree_prune(parent, logq, tau: float, budget: int):
+    """Cumulative path log-probabilities of draft trees and their pruning by a
+    threshold and a node budget. parent [B, M] int32 (parent[:, 0] = -1),
+    logq [B, M] float32 (logq[:, 0] ignored)."""
+    par = np.ascontiguousarray(parent, np.int32)
+    lq = np.ascontiguousarray(logq, np.float32)
+    B, M = par.shape
+    out = dict(cum=np.zeros((B, M)), new_index=np.zeros((B, M), np.int32),
+               new_parent=np.zeros((B, M), np.int32), count=np.zeros(B, np.int32))
+    _load().oracle_tree_prune(B, M, _ptr(par), _ptr(lq), float(tau), int(budget),
+                              _ptr(out["cum"]), _ptr(out["new_index"]), _ptr(out["new_parent"]),
+                              _ptr(out["count"]))
+    return out
+
+
+def tree_verify_greedy(parent, token, n_nodes, target):
+    """Greedy verification of draft trees: parent, token [B, M] int32,
+    n_nodes [B], target logits [B, M, V] (float32 or bf16 bits)."""
+    zt, dt = _logits(target)
+    B, M, V = zt.shape
+    par = np.ascontiguousarray(parent, np.int32)
+    tok = np.ascontiguousarray(token, np.int32)
+    nn = np.ascontiguousarray(n_nodes, np.int32).reshape(B)
+    out = dict(length=np.zeros(B, np.int32), path=np.zeros((B, M), np.int32),
+               extra=np.zeros(B, np.int32))
+    _load().oracle_tree_verify_greedy(B, M, V, dt, _ptr(par), _ptr(tok), _ptr(nn), _ptr(zt),
+                                      _ptr(out["length"]), _ptr(out["path"]), _ptr(out["extra"]))
     return out
 
 

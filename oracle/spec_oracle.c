@@ -752,3 +752,135 @@ void oracle_lowrank_head(int n_rows, int d, int r, int V, const uint16_t *h,
     }
     free(uu);
 }
+
+/* ------------------------------------------------------------ draft trees -- */
+
+/*
+ * Confidence-guided pruning of a batch of draft trees (SpecLA summary,
+ * Methodology section 3, target-aligned drafting: low-probability paths are
+ * pruned by their cumulative log-probability before verification).
+ * Tree b has M nodes in topological order: node 0 is the root (the last
+ * verified token, no draft token), and node i >= 1 hangs under parent[i] in
+ * [0, i) with its draft token's log-probability logq[i] <= 0 given its path.
+ * Readings:
+ *   TR1 the path score is c(0) = 0, c(i) = c(parent(i)) + logq(i), added from
+ *       the root down in double;
+ *   TR2 a node is kept iff c(i) >= tau and it is among the K nodes with the
+ *       largest c (ties to the lower index). Both sets are closed under
+ *       ancestors because scores never rise along a path, so every kept node's
+ *       path is kept; the root is always kept (K >= 1, tau <= 0);
+ *   TR3 a tree whose parent array is not topological, or with a log-probability
+ *       that is NaN or positive, is a sentinel: count -1, nothing kept.
+ * Outputs: cum [B][M] (NaN for sentinel trees), new_index [B][M] (position of
+ * the node among the kept ones in index order, -1 if pruned), new_parent
+ * [B][M] (by new position: the parent's new index, -1 for the root and for
+ * unused slots), count [B].
+ */
+void oracle_tree_prune(int B, int M, const int32_t *parent, const float *logq, double tau,
+                       int K, double *cum, int32_t *new_index, int32_t *new_parent,
+                       int32_t *count)
+{
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parent + (size_t)b * M;
+        const float *lq = logq + (size_t)b * M;
+        double *c = cum + (size_t)b * M;
+        int32_t *ni = new_index + (size_t)b * M;
+        int32_t *np = new_parent + (size_t)b * M;
+        int ok = par[0] == -1;
+        for (int i = 1; i < M && ok; ++i)
+            if (par[i] < 0 || par[i] >= i || isnan(lq[i]) || lq[i] > 0.0f)
+                ok = 0;
+        for (int i = 0; i < M; ++i) {
+            ni[i] = -1;
+            np[i] = -1;
+            c[i] = NAN;
+        }
+        if (!ok) {
+            count[b] = -1;
+            continue;
+        }
+        c[0] = 0.0;
+        for (int i = 1; i < M; ++i)
+            c[i] = c[par[i]] + (double)lq[i];
+        int n = 0;
+        for (int i = 0; i < M; ++i) {
+            /* rank of node i: how many nodes score higher (ties: lower index) */
+            int rank = 0;
+            for (int j = 0; j < M; ++j)
+                if (c[j] > c[i] || (c[j] == c[i] && j < i))
+                    ++rank;
+            if (c[i] >= tau && rank < K)
+                ni[i] = n++;
+        }
+        for (int i = 0; i < M; ++i)
+            if (ni[i] >= 0)
+                np[ni[i]] = i == 0 ? -1 : ni[par[i]];
+        count[b] = n;
+    }
+}
+
+/*
+ * Greedy verification of a batch of (pruned) draft trees: at T = 0 a draft
+ * token is accepted when it equals the target's argmax after its parent, and a
+ * tree is accepted along the path that keeps matching (the exact-match rule of
+ * token-tree speculative decoding, e.g. Miao et al., SpecInfer, ASPLOS 2024;
+ * on a chain it is the greedy rule R4 of the verifier). Readings:
+ *   TR4 the target's logits are given for every node, row i holding the
+ *       distribution of the token that follows node i's path; a[i] is its
+ *       argmax over raw logits, lowest index on ties;
+ *   TR5 from the root, step to the lowest-index child whose token is a[x] while
+ *       there is one; the extra token is a[last node];
+ *   TR6 trees with n nodes < 1 or > M, a parent outside [0, i), a token
+ *       outside [0, V), or a row of a reached node with no finite logit get
+ *       length -1, path -1, extra token -1.
+ * Shapes: parent, token [B][M] (node 0's token is ignored), n_nodes [B],
+ * target [B][M][V]; outputs length [B], path [B][M] (accepted nodes in order,
+ * -1 padded), extra [B].
+ */
+void oracle_tree_verify_greedy(int B, int M, int V, int dtype, const int32_t *parent,
+                               const int32_t *token, const int32_t *n_nodes, const void *target,
+                               int32_t *length, int32_t *path, int32_t *extra)
+{
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parent + (size_t)b * M;
+        const int32_t *tk = token + (size_t)b * M;
+        int32_t *pa = path + (size_t)b * M;
+        const int n = n_nodes[b];
+        for (int i = 0; i < M; ++i)
+            pa[i] = -1;
+        length[b] = -1;
+        extra[b] = -1;
+        int ok = n >= 1 && n <= M && par[0] == -1;
+        for (int i = 1; i < n && ok; ++i)
+            if (par[i] < 0 || par[i] >= i || tk[i] < 0 || tk[i] >= V)
+                ok = 0;
+        if (!ok)
+            continue;
+        int x = 0, L = 0;
+        for (;;) {
+            int a = oracle_row_argmax(target, dtype, ((size_t)b * M + x) * V, V);
+            if (a < 0) {
+                L = -1;
+                break;
+            }
+            int next = -1;
+            for (int j = 1; j < n; ++j)
+                if (par[j] == x && tk[j] == a) {
+                    next = j;
+                    break;
+                }
+            if (next < 0) {
+                extra[b] = a;
+                break;
+            }
+            pa[L++] = next;
+            x = next;
+        }
+        if (L < 0) {
+            for (int i = 0; i < M; ++i)
+                pa[i] = -1;
+            continue;
+        }
+        length[b] = L;
+    }
+}

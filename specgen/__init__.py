@@ -40,7 +40,8 @@ import os
 import numpy as np
 
 __all__ = ["Recipe", "CONFIGS", "config", "generate", "f32_to_bf16_bits",
-           "bf16_bits_to_f32", "gumbel_max_tokens", "lowrank_head_inputs"]
+           "bf16_bits_to_f32", "gumbel_max_tokens", "lowrank_head_inputs", "draft_trees",
+           "tree_target_logits"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -210,3 +211,59 @@ def lowrank_head_inputs(rows: int, hidden: int, rank: int, vocab: int, seed: int
         temp[rng.choice(rows, size=n_greedy, replace=False)] = 0.0
     return dict(h=f32_to_bf16_bits(h), w_down=f32_to_bf16_bits(w_down), w_up=w_up,
                 temperature=temp)
+
+
+def draft_trees(batch: int, nodes: int, vocab: int, seed: int = 0, max_children: int = 3,
+                chain_bias: float = 0.6):
+    """Seeded draft trees in topological order, as a tree-drafting proposer
+    would emit them: node 0 is the root; node i >= 1 hangs under node i - 1
+    with probability chain_bias (when it has room), else under a uniformly
+    chosen earlier node with fewer than max_children children. Each node's
+    children split a Dirichlet(1, ..., 1) draft mass with one extra "other"
+    share, so logq (the draft log-probability of a node's token) is <= 0 and
+    the children's probabilities sum to less than one. Tokens are uniform in
+    [0, vocab). Returns parent [B, M] int32 (parent[:, 0] = -1), token [B, M]
+    int32 (token[:, 0] = 0), logq [B, M] float32 (logq[:, 0] = 0)."""
+    parent = np.full((batch, nodes), -1, np.int32)
+    token = np.zeros((batch, nodes), np.int32)
+    logq = np.zeros((batch, nodes), np.float32)
+    for b in range(batch):
+        rng = np.random.default_rng([seed, b, 104729])
+        kids = [[] for _ in range(nodes)]
+        for i in range(1, nodes):
+            if len(kids[i - 1]) < max_children and rng.random() < chain_bias:
+                p = i - 1
+            else:
+                free = [j for j in range(i) if len(kids[j]) < max_children]
+                p = int(free[rng.integers(len(free))])
+            parent[b, i] = p
+            kids[p].append(i)
+            token[b, i] = rng.integers(vocab)
+        for j in range(nodes):
+            if kids[j]:
+                w = rng.dirichlet(np.ones(len(kids[j]) + 1))
+                for k, c in enumerate(kids[j]):
+                    logq[b, c] = np.float32(np.log(w[k]))
+    return dict(parent=parent, token=token, logq=logq)
+
+
+def tree_target_logits(trees: dict, vocab: int, seed: int = 0, follow: float = 0.7,
+                       std: float = 2.5, dtype: str = "bf16") -> np.ndarray:
+    """Target logits [B, M, V] for draft trees: N(0, std^2) per entry; for each
+    node with children, with probability `follow` the token of its first
+    child gets +4 std added, so that greedy paths often continue into the
+    tree (the input construction adds a bump; it computes no argmax)."""
+    parent, token = trees["parent"], trees["token"]
+    B, M = parent.shape
+    out = np.empty((B, M, vocab), np.uint16 if dtype == "bf16" else np.float32)
+    for b in range(B):
+        rng = np.random.default_rng([seed, b, 15485863])
+        z = rng.standard_normal((M, vocab), dtype=np.float32) * np.float32(std)
+        first = {}
+        for i in range(1, M):
+            first.setdefault(int(parent[b, i]), i)
+        for x, c in first.items():
+            if rng.random() < follow:
+                z[x, token[b, c]] += np.float32(4 * std)
+        out[b] = f32_to_bf16_bits(z) if dtype == "bf16" else z
+    return out

@@ -13,6 +13,7 @@ import pytest
 import oracle
 import test_bandit_oracle as bandit
 import test_oracle_lowrank as lowrank
+import test_oracle_tree as tree
 import test_oracle_outcomes as outcomes
 import test_oracle_pins as pins
 import test_oracle_stats as stats
@@ -152,6 +153,31 @@ def test_head_normaliser_without_temperature_is_caught():
 def test_head_ties_to_odd_are_caught():
     with mutated_oracle("(e1 == e0 && (n & 1u) == 0u)", "(e1 == e0 && (n & 1u) == 1u)"):
         fails(lowrank.test_bf16_rounding_matches_torch_and_ties_go_to_even)
+
+
+def test_tree_score_without_the_path_is_caught():
+    with mutated_oracle("c[i] = c[par[i]] + (double)lq[i];", "c[i] = (double)lq[i];"):
+        fails(tree.test_path_scores_and_kept_set_by_brute_force)
+
+
+def test_tree_ties_to_the_higher_index_are_caught():
+    with mutated_oracle("if (c[j] > c[i] || (c[j] == c[i] && j < i))",
+                        "if (c[j] > c[i] || (c[j] == c[i] && j > i))"):
+        fails(tree.test_prune_ties_go_to_the_lower_index)
+
+
+def test_tree_walk_taking_the_last_match_is_caught():
+    with mutated_oracle("""                if (par[j] == x && tk[j] == a) {
+                    next = j;
+                    break;
+                }""", """                if (par[j] == x && tk[j] == a)
+                    next = j;"""):
+        fails(tree.test_greedy_tree_duplicate_siblings_take_the_lower_index)
+
+
+def test_tree_extra_token_from_the_root_is_caught():
+    with mutated_oracle("                extra[b] = a;\n", "                extra[b] = oracle_row_argmax(target, dtype, ((size_t)b * M) * V, V);\n"):
+        fails(tree.test_greedy_tree_on_chains_matches_the_verifier)
 
 
 def ucb1_pins():
