@@ -341,6 +341,51 @@ def main() -> int:
     head_flops = 2 * B * (hd * hr + hr * V)
     sv.spec_lowrank_head_destroy(hctx)
     del hh, wd, wu, hz
+
+    # Draft trees of this batch and vocabulary: pruning 64-node trees, and
+    # greedy verification of 16-node trees (target rows read once by the
+    # argmax pass; random bf16 logits made on the device).
+    tp = specgen.draft_trees(B, 64, V, seed=1)
+    t_par, t_lq = torch.from_numpy(tp["parent"]).to(dev), torch.from_numpy(tp["logq"]).to(dev)
+    p_cum = torch.empty(B, 64, dtype=torch.float64, device=dev)
+    p_ni = torch.empty(B, 64, dtype=torch.int32, device=dev)
+    p_np = torch.empty(B, 64, dtype=torch.int32, device=dev)
+    p_cnt = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def prune():
+        sv.spec_tree_prune(t_par, t_lq, float(np.log(1e-3)), 32, p_cum, p_ni, p_np, p_cnt,
+                           stream=stream)
+
+    for _ in range(args.warmup):
+        prune()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        prune()
+    end.record(stream)
+    torch.cuda.synchronize()
+    prune_us = start.elapsed_time(end) * 1e3 / args.steps
+    tm = 16
+    tv = specgen.draft_trees(B, tm, V, seed=2)
+    v_par, v_tok = torch.from_numpy(tv["parent"]).to(dev), torch.from_numpy(tv["token"]).to(dev)
+    v_n = torch.full((B,), tm, dtype=torch.int32, device=dev)
+    v_tgt = (torch.randn(B, tm, V, device=dev, generator=gen) * 2.5).to(torch.bfloat16)
+    v_len = torch.empty(B, dtype=torch.int32, device=dev)
+    v_path = torch.empty(B, tm, dtype=torch.int32, device=dev)
+    v_extra = torch.empty(B, dtype=torch.int32, device=dev)
+    tctx = sv.spec_tree_verify_init(B, tm, V, torch.bfloat16, stream=stream)
+    for _ in range(args.warmup):
+        sv.spec_tree_verify_greedy(tctx, v_par, v_tok, v_n, v_tgt, v_len, v_path, v_extra)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        sv.spec_tree_verify_greedy(tctx, v_par, v_tok, v_n, v_tgt, v_len, v_path, v_extra)
+    end.record(stream)
+    torch.cuda.synchronize()
+    tree_ms = start.elapsed_time(end) / args.steps
+    tree_bytes = B * tm * V * 2
+    sv.spec_tree_verify_destroy(tctx)
+    del v_tgt
     k1_gbs = k1_bytes / (k1_ms * 1e-3) / 1e9
     k3_gbs = k3_bytes / (k3_ms * 1e-3) / 1e9
     call_gbs = (k1_bytes + k2_bytes + k3_bytes) / (ms_per_step * 1e-3) / 1e9
@@ -382,6 +427,10 @@ def main() -> int:
                         "bytes": sc_b * sc_g * 8 + sc_b * 4,
                         "sequences_per_s": round(sc_b / (scalar_us * 1e-6), 1)},
         "bandit": {"arms": 3, "us_per_step": bandit_us},
+        "tree": {"prune_nodes": 64, "prune_us": round(prune_us, 2), "verify_nodes": tm,
+                 "verify_us": round(tree_ms * 1e3, 2), "verify_bytes": int(tree_bytes),
+                 "verify_gbs": round(tree_bytes / (tree_ms * 1e-3) / 1e9, 1),
+                 "verify_frac": round(tree_bytes / (tree_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "lowrank_head": {"rows": B, "hidden": hd, "rank": hr, "vocab": V,
                          "us_per_call": round(head_ms * 1e3, 2), "bytes": int(head_bytes),
                          "gbs": round(head_bytes / (head_ms * 1e-3) / 1e9, 1),

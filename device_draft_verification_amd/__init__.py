@@ -2,8 +2,9 @@
 
 The work is done by hand-written HIP kernels in ``libspecverify.so`` behind the
 C ABI of ``include/spec_verify.h`` (verification), ``include/spec_bandit.h``
-(online draft selection) and ``include/spec_head.h`` (low-rank draft head with
-its fused normaliser); this package is a thin ctypes binding with
+(online draft selection), ``include/spec_head.h`` (low-rank draft head with
+its fused normaliser) and ``include/spec_tree.h`` (draft-tree pruning and
+greedy tree verification); this package is a thin ctypes binding with
 the same function names (``binding``) and the build script (``build``).
 """
 from .binding import (  # noqa: F401
@@ -17,4 +18,6 @@ from .binding import (  # noqa: F401
     spec_bandit_set_stream, spec_bandit_step,
     HeadContext, spec_lowrank_head, spec_lowrank_head_copy_activation, spec_lowrank_head_destroy,
     spec_lowrank_head_init, spec_lowrank_head_set_stream,
+    SPEC_TREE_MAX_NODES, TreeContext, spec_tree_prune, spec_tree_verify_destroy,
+    spec_tree_verify_greedy, spec_tree_verify_init, spec_tree_verify_set_stream,
 )

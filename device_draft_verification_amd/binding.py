@@ -32,7 +32,11 @@ EXPORTED = (
     "spec_bandit_set_state", "spec_bandit_destroy",
     "spec_lowrank_head_init", "spec_lowrank_head_set_stream", "spec_lowrank_head",
     "spec_lowrank_head_copy_activation", "spec_lowrank_head_destroy",
+    "spec_tree_prune", "spec_tree_verify_init", "spec_tree_verify_set_stream",
+    "spec_tree_verify_greedy", "spec_tree_verify_destroy",
 )
+
+SPEC_TREE_MAX_NODES = 256
 
 SPEC_OUTCOME_MAX_F = 64
 SPEC_BANDIT_UCB1 = 0
@@ -82,6 +86,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_lowrank_head": ([P, P, P, P, P, P, P], i32),
         "spec_lowrank_head_copy_activation": ([P, P], i32),
         "spec_lowrank_head_destroy": ([P], i32),
+        "spec_tree_prune": ([i32, i32, P, P, ctypes.c_double, i32, P, P, P, P, P], i32),
+        "spec_tree_verify_init": ([i32, i32, i32, i32, P, ctypes.POINTER(P)], i32),
+        "spec_tree_verify_set_stream": ([P, P], i32),
+        "spec_tree_verify_greedy": ([P, P, P, P, P, P, P, P], i32),
+        "spec_tree_verify_destroy": ([P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -392,3 +401,71 @@ def spec_lowrank_head_destroy(ctx: HeadContext) -> None:
         rc = load_library().spec_lowrank_head_destroy(ctx.handle)
         ctx.handle = None
         _check("spec_lowrank_head_destroy", rc)
+
+
+def spec_tree_prune(parent, logq, tau: float, budget: int, out_cum, out_new_index, out_new_parent,
+                    out_count, stream=None) -> None:
+    """parent [B, M] int32, logq [B, M] float32; outputs out_cum [B, M] float64,
+    out_new_index / out_new_parent [B, M] int32, out_count [B] int32."""
+    B, M = parent.shape
+    _expect(parent, (B, M), torch.int32, "parent")
+    _expect(logq, (B, M), torch.float32, "logq")
+    _expect(out_cum, (B, M), torch.float64, "out_cum")
+    _expect(out_new_index, (B, M), torch.int32, "out_new_index")
+    _expect(out_new_parent, (B, M), torch.int32, "out_new_parent")
+    _expect(out_count, (B,), torch.int32, "out_count")
+    _check("spec_tree_prune", load_library().spec_tree_prune(
+        B, M, _ptr(parent), _ptr(logq), float(tau), int(budget), _ptr(out_cum),
+        _ptr(out_new_index), _ptr(out_new_parent), _ptr(out_count), _stream_handle(stream)))
+
+
+class TreeContext:
+    """Owns a spec_tree_ctx*; destroyed with spec_tree_verify_destroy."""
+
+    def __init__(self, handle: ctypes.c_void_p, batch: int, max_nodes: int, vocab: int, dtype: int):
+        self.handle = handle
+        self.batch, self.max_nodes, self.vocab, self.dtype = batch, max_nodes, vocab, dtype
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                load_library().spec_tree_verify_destroy(self.handle)
+            except Exception:
+                pass
+            self.handle = None
+
+
+def spec_tree_verify_init(batch: int, max_nodes: int, vocab: int, dtype, stream=None) -> TreeContext:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    h = ctypes.c_void_p()
+    _check("spec_tree_verify_init", load_library().spec_tree_verify_init(
+        batch, max_nodes, vocab, code, _stream_handle(stream), ctypes.byref(h)))
+    return TreeContext(h, batch, max_nodes, vocab, code)
+
+
+def spec_tree_verify_set_stream(ctx: TreeContext, stream=None) -> None:
+    _check("spec_tree_verify_set_stream",
+           load_library().spec_tree_verify_set_stream(ctx.handle, _stream_handle(stream)))
+
+
+def spec_tree_verify_greedy(ctx: TreeContext, parent, token, n_nodes, target, out_length,
+                            out_path, out_extra) -> None:
+    B, M, V = ctx.batch, ctx.max_nodes, ctx.vocab
+    ldt = torch.bfloat16 if ctx.dtype == SPEC_BF16 else torch.float32
+    _expect(parent, (B, M), torch.int32, "parent")
+    _expect(token, (B, M), torch.int32, "token")
+    _expect(n_nodes, (B,), torch.int32, "n_nodes")
+    _expect(target, (B, M, V), ldt, "target")
+    _expect(out_length, (B,), torch.int32, "out_length")
+    _expect(out_path, (B, M), torch.int32, "out_path")
+    _expect(out_extra, (B,), torch.int32, "out_extra")
+    _check("spec_tree_verify_greedy", load_library().spec_tree_verify_greedy(
+        ctx.handle, _ptr(parent), _ptr(token), _ptr(n_nodes), _ptr(target), _ptr(out_length),
+        _ptr(out_path), _ptr(out_extra)))
+
+
+def spec_tree_verify_destroy(ctx: TreeContext) -> None:
+    if ctx.handle:
+        rc = load_library().spec_tree_verify_destroy(ctx.handle)
+        ctx.handle = None
+        _check("spec_tree_verify_destroy", rc)

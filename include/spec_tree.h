@@ -1,0 +1,79 @@
+/*
+ * spec_tree.h -- C ABI for draft trees on AMD Instinct MI355X (gfx950):
+ * confidence-guided pruning and greedy tree verification.
+ *
+ * Pruning (SpecLA summary, Methodology section 3, target-aligned drafting):
+ * low-probability paths of a draft tree are cut by their cumulative draft
+ * log-probability before the target verifies them. Tree b has M nodes in
+ * topological order: node 0 is the root (the last verified token) and node
+ * i >= 1 hangs under parent[i] in [0, i), carrying logq[i] <= 0, its draft
+ * token's log-probability given its path. Definition:
+ *   c(0) = 0, c(i) = c(parent(i)) + (double)logq(i), summed from the root down;
+ *   node i is kept iff c(i) >= tau and fewer than `budget` nodes have a larger
+ *   c (ties to the lower index). Scores never rise along a path, so the kept
+ *   set contains every kept node's ancestors; kept nodes are renumbered in
+ *   index order.
+ * A tree whose parent array is not topological or with a NaN or positive
+ * logq is a sentinel: count -1, nothing kept, scores NaN.
+ *
+ * Greedy verification (T = 0; the exact-match rule of token-tree speculative
+ * decoding, Miao et al., SpecInfer, ASPLOS 2024; on a chain it is
+ * spec_verify's greedy rule): the target's logits are given for every node,
+ * row i holding the distribution of the token after node i's path; a(i) is
+ * its argmax over raw logits (lowest index on ties). From the root the walk
+ * steps to the lowest-index child whose token is a(x), while there is one;
+ * the result is the accepted nodes, their count, and the extra token a(last).
+ * Trees with n_nodes outside [1, M], a parent outside [0, i), a token outside
+ * [0, V), or a reached row with no finite logit get length -1, path -1 and
+ * extra token -1. The multi-branch rule for T > 0 is not defined here.
+ *
+ * Layouts: dense row-major DEVICE arrays owned by the caller; int32 indices,
+ * float32 logq, float64 scores; target logits [B, M, V] in the dtype of
+ * spec_verify.h (16-byte-aligned rows take the vector path). 1 <= M <=
+ * SPEC_TREE_MAX_NODES. Calls enqueue kernels on the given (or context's)
+ * stream and return; host-detectable errors return SPEC_EINVAL first.
+ */
+#ifndef SPEC_TREE_H
+#define SPEC_TREE_H
+
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_TREE_MAX_NODES 256
+
+/* Prune B trees of M nodes. Outputs: out_cum [B, M] float64, out_new_index
+ * [B, M] (new position or -1), out_new_parent [B, M] (by new position, -1 for
+ * the root and unused slots), out_count [B]. No workspace; hip_stream may be
+ * NULL. */
+int spec_tree_prune(int batch, int nodes, const int32_t* parent, const float* logq, double tau,
+                    int budget, double* out_cum, int32_t* out_new_index,
+                    int32_t* out_new_parent, int32_t* out_count, void* hip_stream);
+
+typedef struct spec_tree_ctx spec_tree_ctx;
+
+/* Workspace for greedy verification of B trees of at most M nodes over a
+ * vocabulary of V logits of the given dtype. */
+int spec_tree_verify_init(int batch, int max_nodes, int vocab, int dtype, void* hip_stream,
+                          spec_tree_ctx** out_ctx);
+
+int spec_tree_verify_set_stream(spec_tree_ctx* ctx, void* hip_stream);
+
+/* parent, token [B, M] int32 (token[b][0] ignored), n_nodes [B], target
+ * [B, M, V]; outputs out_length [B], out_path [B, M] (accepted node indices in
+ * order, -1 padded), out_extra [B]. Rows of nodes >= n_nodes are not read. */
+int spec_tree_verify_greedy(spec_tree_ctx* ctx, const int32_t* parent, const int32_t* token,
+                            const int32_t* n_nodes, const void* target, int32_t* out_length,
+                            int32_t* out_path, int32_t* out_extra);
+
+int spec_tree_verify_destroy(spec_tree_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_TREE_H */

@@ -104,6 +104,22 @@ def test_head_host_argument_checks(lib):
     assert lib.spec_lowrank_head_destroy(None) == E
 
 
+def test_tree_host_argument_checks(lib):
+    E = sv.binding.SPEC_EINVAL
+    D = ctypes.c_double
+    assert lib.spec_tree_prune(2, 0, None, None, D(0.0), 4, None, None, None, None, None) == E
+    assert lib.spec_tree_prune(2, 257, None, None, D(0.0), 4, None, None, None, None, None) == E
+    assert lib.spec_tree_prune(2, 8, None, None, D(0.5), 4, None, None, None, None, None) == E
+    assert lib.spec_tree_prune(2, 8, None, None, D(0.0), 0, None, None, None, None, None) == E
+    assert lib.spec_tree_prune(2, 8, None, None, D(0.0), 4, None, None, None, None, None) == E
+    h = ctypes.c_void_p()
+    assert lib.spec_tree_verify_init(2, 300, 100, 1, None, ctypes.byref(h)) == E
+    assert lib.spec_tree_verify_init(2, 8, 100, 5, None, ctypes.byref(h)) == E
+    assert not h.value
+    assert lib.spec_tree_verify_greedy(None, None, None, None, None, None, None, None) == E
+    assert lib.spec_tree_verify_destroy(None) == E
+
+
 def test_binding_refuses_missing_library(tmp_path, lib):
     saved = sv.binding._lib
     sv.binding._lib = None
