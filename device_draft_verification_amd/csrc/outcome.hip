@@ -448,19 +448,20 @@ __device__ __forceinline__ double stream_tiles(const RowCoefs& rc, int groups, i
     int t = t_begin;
     if (t >= t_end)
         return sum;
+    // Batches in pairs with no exit between the halves: at the loop head only
+    // the a-batch's loads are in flight, so the compiler waits for exactly the
+    // batch being consumed (a mid-loop exit makes it wait for everything).
+    const int nb = (t_end - t + step - 1) / step;
     load_batch(pa, qa, t);
-    while (true) {
+    for (int i = 0; i + 2 <= nb; i += 2) {
         load_batch(pb, qb, t + step);
         consume(pa, qa, t);
-        t += step;
-        if (t >= t_end)
-            break;
-        load_batch(pa, qa, t + step);
-        consume(pb, qb, t);
-        t += step;
-        if (t >= t_end)
-            break;
+        load_batch(pa, qa, t + 2 * step);
+        consume(pb, qb, t + step);
+        t += 2 * step;
     }
+    if (nb & 1)
+        consume(pa, qa, t);
     return sum;
 }
 

@@ -191,29 +191,51 @@ __global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
     seq_row_coefs(s, st);
     // The next batch is loaded unconditionally (a batch past the split reads
     // group 0, which is in cache, and is never reduced): with no branch around
-    // the loads the compiler waits for exactly the group being reduced.
-    while (t < t1) {
+    // the loads, and no loop exit between the two halves, the compiler waits
+    // for exactly the batch being reduced.
+    const int nb = t < t1 ? (t1 - t + kStep - 1) / kStep : 0;
+    for (int i = 0; i + 2 <= nb; i += 2) {
         load_batch(buf_b, t + kStep);
         reduce_batch(buf_a, t);
-        t += kStep;
-        if (t >= t1)
-            break;
-        load_batch(buf_a, t + kStep);
-        reduce_batch(buf_b, t);
-        t += kStep;
+        load_batch(buf_a, t + 2 * kStep);
+        reduce_batch(buf_b, t + kStep);
+        t += 2 * kStep;
     }
+    if (nb & 1)
+        reduce_batch(buf_a, t);
 }
 
-// Inclusive prefix over the 64 lanes in fp64 (lane order).
+// 64-bit DPP move: both halves take the same lane pattern; lanes whose source
+// lies outside the row, or whose row is not in ROW_MASK, read +0.0.
+template <int CTRL, int ROW_MASK>
+__device__ inline double dpp_f64(double v) {
+    const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(v));
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), CTRL, ROW_MASK,
+                                               0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, ROW_MASK, 0xF,
+                                               true);
+    return __longlong_as_double(static_cast<long long>(
+        (static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) | static_cast<unsigned>(lo)));
+}
+
+// Inclusive prefix over the 64 lanes in fp64 (lane order), in a fixed order:
+// shifts by 1, 2, 4 and 8 within each row of 16 lanes, then the row totals
+// are carried forward by the row broadcasts.
 __device__ inline double wave_inclusive_scan(double v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(v, off, 64);
-        if (lane >= off)
-            v += o;
-    }
+    v += dpp_f64<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_f64<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_f64<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_f64<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
+}
+
+__device__ inline double lane63_f64(double v) {
+    const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(v));
+    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffu), 63));
+    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), 63));
+    return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
 
 __device__ inline int first_lane(bool flag) {
@@ -230,29 +252,43 @@ __device__ inline int wave_max_int(int v) {
     return v;
 }
 
-// Locate the tile holding tau given the per-tile sums `ts` (fp32) of one row:
-// lane l sums a contiguous run of tiles, the wavefront scans the runs in fp64
-// and the lane whose run crosses tau walks it. Returns the tile and writes the
-// fp64 prefix before it; when tau lies beyond the total (rounding only),
-// returns the last tile with mass and writes -1 (take its last positive element).
-__device__ inline int locate_tile(const float* ts, int ntiles, double tau, double* P_out) {
+// The tile sums `ts` (fp32) of one row, cut into 64 contiguous runs: lane l
+// sums run l in fp64 and the wavefront scans the runs; the last lane's prefix
+// is the row total S.
+struct TileRuns {
+    int a0, a1;       // this lane's run [a0, a1)
+    int last_pos;     // its last tile with mass, or -1
+    double mine;      // its run's sum
+    double inc;       // inclusive prefix of the runs through this lane
+};
+
+__device__ inline TileRuns tile_runs(const float* ts, int ntiles) {
     const int lane = threadIdx.x & 63;
     const int per = (ntiles + 63) / 64;
-    const int a0 = lane * per;
-    const int a1 = a0 + per < ntiles ? a0 + per : ntiles;
-    double mine = 0.0;
-    int last_pos = -1;
-    for (int t = a0; t < a1; ++t) {
+    TileRuns tr;
+    tr.a0 = lane * per < ntiles ? lane * per : ntiles;
+    tr.a1 = tr.a0 + per < ntiles ? tr.a0 + per : ntiles;
+    tr.mine = 0.0;
+    tr.last_pos = -1;
+    for (int t = tr.a0; t < tr.a1; ++t) {
         const float v = ts[t];
-        mine += static_cast<double>(v);
+        tr.mine += static_cast<double>(v);
         if (v > 0.0f)
-            last_pos = t;
+            tr.last_pos = t;
     }
-    const double excl = wave_inclusive_scan(mine) - mine;
+    tr.inc = wave_inclusive_scan(tr.mine);
+    return tr;
+}
+
+// Locate the tile holding tau: the lane whose run crosses tau walks it.
+// Returns the tile and writes the fp64 prefix before it; when tau lies beyond
+// the total (rounding only), returns the last tile with mass and writes -1
+// (take its last positive element).
+__device__ inline int locate_tile(const float* ts, const TileRuns& tr, double tau, double* P_out) {
     int hit = -1;
     double before = 0.0;
-    double acc = excl;
-    for (int t = a0; t < a1 && hit < 0; ++t) {
+    double acc = tr.inc - tr.mine;
+    for (int t = tr.a0; t < tr.a1 && hit < 0; ++t) {
         const float v = ts[t];
         const double next = acc + static_cast<double>(v);
         if (v > 0.0f && next > tau) {
@@ -267,16 +303,16 @@ __device__ inline int locate_tile(const float* ts, int ntiles, double tau, doubl
         return __shfl(hit, fl, 64);
     }
     *P_out = -1.0;
-    return wave_max_int(last_pos);
+    return wave_max_int(tr.last_pos);
 }
 
 // Token inside one tile: lane l recomputes group 64*tile + l exactly as the
-// tile kernel did, the wavefront scans the group sums in fp64 from P, and the
-// first lane whose elements carry the running prefix past tau names the token.
-// P < 0 asks for the tile's last positive element.
+// tile kernel did (a cached re-read), the wavefront scans the group sums in
+// fp64 from P, and the first lane whose elements carry the running prefix past
+// tau names the token. P < 0 asks for the tile's last positive element.
 template <int DT, bool VEC, bool NT>
 __device__ inline int scan_tile(const SeqRows& s, int tile, int groups, double P, double tau) {
-    using IO = GroupIO<DT, VEC, NT>;
+    using IO = GroupIO<DT, VEC, false>;
     constexpr int W = IO::W;
     const int lane = threadIdx.x & 63;
     const int g = tile * kTile + lane;
@@ -297,9 +333,8 @@ __device__ inline int scan_tile(const SeqRows& s, int tile, int groups, double P
     for (int e = 0; e < W; ++e)
         if (r[e] > 0.0f)
             my_last = static_cast<int>(g * W + e);
-    const int tile_last = wave_max_int(my_last);
     if (P < 0.0)
-        return tile_last;
+        return wave_max_int(my_last);
     const double inc = wave_inclusive_scan(static_cast<double>(gs));
     int hit = -1;
     double a = P + (inc - static_cast<double>(gs));
@@ -316,7 +351,7 @@ __device__ inline int scan_tile(const SeqRows& s, int tile, int groups, double P
     const int fl = first_lane(hit >= 0);
     if (fl < 64)
         return __shfl(hit, fl, 64);
-    return tile_last;
+    return wave_max_int(my_last);
 }
 
 template <int DT, bool VEC, bool NT>
@@ -342,19 +377,14 @@ template <int DT, bool VEC, bool NT>
 __device__ inline void locate_emit(SeqRows& s, const SeqState& st, const float* ts, int ntiles,
                                    int groups, int G, int b, int32_t* out_tok) {
     const int lane = threadIdx.x & 63;
-    double mine = 0.0;
-    for (int t = lane; t < ntiles; t += 64)
-        mine += static_cast<double>(ts[t]);
-    double S = mine;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        S += __shfl_xor(S, off, 64);
+    const TileRuns tr = tile_runs(ts, ntiles);
+    const double S = lane63_f64(tr.inc);
 
     int token;
     if (S > 0.0) {
         const double tau = static_cast<double>(st.u_res) * S;
         double P;
-        const int tile = locate_tile(ts, ntiles, tau, &P);
+        const int tile = locate_tile(ts, tr, tau, &P);
         token = scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
     } else {
         // Empty residual (possible only through rounding when p and q agree to
@@ -402,15 +432,16 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
 }
 
 // One workgroup of 16 wavefronts per sequence: the wavefronts stream the
-// sequence's tiles (wavefront w takes tiles w, w + 16, ..., U at a time,
-// double-buffered as in residual_tiles_kernel, with the same arithmetic and
-// the same per-tile sums), keep the tile sums in LDS, and after one barrier
-// wavefront 0 draws the token. Used when there are enough sequences to give
-// every CU a workgroup; it saves the second launch and the round trip of the
-// tile sums through memory.
+// sequence's tiles with the tile kernel's arithmetic and per-tile sums, keep
+// the tile sums in LDS, and after one barrier wavefront 0 draws the token.
+// Used when there are enough sequences to give every CU a workgroup; it saves
+// the second launch and the round trip of the tile sums through memory.
+// Tiles are handed out by an LDS counter (each wavefront holds two in flight
+// and asks for the next one a tile ahead), so wavefronts whose loads return
+// late take fewer tiles and all reach the barrier together.
 constexpr int kFusedBlock = 1024;
 
-template <int DT, bool VEC, int U, bool NT, int BLOCK>
+template <int DT, bool VEC, bool NT, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
     const void* __restrict__ draft, const void* __restrict__ target, int gamma, int vocab,
     int ntiles, const SeqState* __restrict__ seq, int32_t* __restrict__ out_tok) {
@@ -418,6 +449,7 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
     constexpr int W = IO::W;
     constexpr int kFusedWaves = BLOCK / 64;
     extern __shared__ float lds_ts[];
+    __shared__ int next_tile;
     const int b = blockIdx.x;
     const SeqState st = seq[b];
     if (st.mode != 1)
@@ -425,48 +457,56 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
     const int groups = vocab / W;
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane = threadIdx.x & 63;
+    if (threadIdx.x == 0)
+        next_tile = 2 * kFusedWaves;  // tiles below are dealt out statically
+    __syncthreads();
     SeqRows s;
     seq_row_ptrs<DT>(s, draft, target, gamma, vocab, b, st.k);
-    auto load_batch = [&](IO (&io)[U], int t) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int g = (t + u * kFusedWaves) * kTile + lane;
-            const bool used = t + u * kFusedWaves < ntiles && g < groups;
-            io[u].load(s, used ? g : 0);
-        }
+    // Loads are unconditional: a tile past the row reads group 0 instead and
+    // is not reduced.
+    auto load_tile = [&](IO& io, int t) {
+        const int g = t * kTile + lane;
+        io.load(s, t < ntiles && g < groups ? g : 0);
     };
-    auto reduce_batch = [&](const IO (&io)[U], int t) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int tt = t + u * kFusedWaves;
-            if (tt >= ntiles)
-                break;  // wave-uniform
-            const int g = tt * kTile + lane;
-            float gs = 0.0f;
-            if (g < groups) {
-                float r[W];
-                io[u].residual(s, r);
-                gs = pairwise(r);
-            }
-            const float ts = tile_reduce(gs);
-            if (lane == 0)
-                lds_ts[tt] = ts;
-        }
-    };
-    constexpr int kStep = kFusedWaves * U;
-    IO buf_a[U], buf_b[U];
-    int t = wid;
-    load_batch(buf_a, t);
-    seq_row_coefs(s, st);
-    while (t < ntiles) {
-        load_batch(buf_b, t + kStep);
-        reduce_batch(buf_a, t);
-        t += kStep;
+    auto reduce_tile = [&](const IO& io, int t) {
         if (t >= ntiles)
-            break;
-        load_batch(buf_a, t + kStep);
-        reduce_batch(buf_b, t);
-        t += kStep;
+            return;  // wave-uniform
+        const int g = t * kTile + lane;
+        float gs = 0.0f;
+        if (g < groups) {
+            float r[W];
+            io.residual(s, r);
+            gs = pairwise(r);
+        }
+        const float ts = tile_reduce(gs);
+        if (lane == 0)
+            lds_ts[t] = ts;
+    };
+    // The counter's answer stays in lane 0's register until the tile after
+    // next is loaded, so the LDS atomic completes behind a tile's arithmetic.
+    auto grab = [&]() {
+        int v = 0;
+        if (lane == 0)
+            v = atomicAdd(&next_tile, 1);
+        return v;
+    };
+    auto uniform = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    IO buf_a, buf_b;
+    int ta = wid, tb = wid + kFusedWaves;
+    load_tile(buf_a, ta);
+    seq_row_coefs(s, st);
+    int tn = grab();
+    // Counter values only grow, so once ta is past the row so is every later
+    // tile, and the single exit at the head leaves nothing in flight unused.
+    while (ta < ntiles) {
+        load_tile(buf_b, tb);
+        reduce_tile(buf_a, ta);
+        ta = uniform(tn);
+        tn = grab();
+        load_tile(buf_a, ta);
+        reduce_tile(buf_b, tb);
+        tb = uniform(tn);
+        tn = grab();
     }
     __syncthreads();
     if (wid != 0)
@@ -485,9 +525,9 @@ hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const vo
     const int groups = sh.vocab / W;
     const int ntiles = (groups + kTile - 1) / kTile;
     if (nsplit == 0) {
-        // One tile in flight per wavefront (double-buffered) measured best:
-        // 16 wavefronts already keep 32 KiB per row in flight per workgroup.
-        residual_fused_kernel<DT, VEC, 1, NT, kFusedBlock><<<dim3(static_cast<unsigned>(sh.batch)),
+        // Two tiles in flight per wavefront: 16 wavefronts keep 64 KiB in
+        // flight per workgroup.
+        residual_fused_kernel<DT, VEC, NT, kFusedBlock><<<dim3(static_cast<unsigned>(sh.batch)),
                                                            dim3(kFusedBlock),
                                                            static_cast<size_t>(ntiles) * sizeof(float),
                                                            stream>>>(
