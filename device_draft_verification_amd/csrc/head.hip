@@ -3,22 +3,24 @@
 // factored through rank r, computed with dense matrix products).
 //
 // Both products run on the matrix cores (v_mfma_f32_16x16x32_bf16: bf16
-// operands, binary32 accumulation). One tile routine serves both: C[m][n] =
-// sum_k A[m][k] B[n][k] with A and B row-major and K contiguous, a 128 x 128
-// output tile per 256-thread workgroup (2 x 2 wavefronts of 64 x 64, i.e. 4 x 4
-// MFMA tiles each), K in chunks of 64 staged through LDS with double
-// buffering (rows padded to 144 bytes) and two chunks in flight in registers.
+// operands, binary32 accumulation).
 //
 //   head_down: u = W_down h, split over K into fp32 partials (the activation
-//     is small, N x r, so the split gives the GPU enough workgroups);
+//     is small, N x r, so the split gives the GPU enough workgroups), with the
+//     tile routine below: C[m][n] = sum_k A[m][k] B[n][k], A and B row-major
+//     with K contiguous, 64 x 64 per wavefront, K in chunks of 64 staged
+//     through LDS with double buffering (rows padded to 144 bytes) and two
+//     chunks in flight in registers;
 //   head_down_reduce: u = bf16(sum of the partials, in split order);
-//   head_up: z = W_up u; the tile is rounded to bf16, staged in LDS, stored
-//     with 16-byte rows, and, while it is still on chip, reduced to one
-//     (m, s) pair per row: m = fl32(max x * log2e), s = sum 2^(fma(x, log2e,
-//     -m)) with x = fl32(z * fl32(1/T)), the row kernel's base-2 form;
+//   head_up_stream (rank 256 or 512): z^T = W_up u^T with the vocabulary on
+//     M, one workgroup per CU streaming its run of W_up through an LDS ring
+//     while the batch rows stay in registers; each block of logits is rounded
+//     to bf16, stored, and folded into per-row (m, s) pairs while still in
+//     registers: m = fl32(max x * log2e), s = sum 2^(fma(x, log2e, -m)) with
+//     x = fl32(z * fl32(1/T)), the row kernel's base-2 form;
+//   head_up (other ranks): the same product with the tile routine, 128
+//     vocabulary entries x 256 batch rows per workgroup;
 //   head_lse: merges a row's (m, s) pairs into its log-normaliser.
-// Workgroups of head_up are ordered row tile fastest, so the workgroups that
-// read one W_up tile run together and all but the first read it from cache.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -35,14 +37,21 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBK = 64;
 constexpr int kLdsK = kBK + 8;    // bf16 per LDS row of a K chunk (144 bytes)
 constexpr int kThreads = 256;
-constexpr int kOutLd = kBN + 8;   // bf16 per LDS row of the staged output tile
-constexpr int kLdsElems = 2 * (kBM + kBN) * kLdsK;
 constexpr float kHeadLog2e = 1.44269504088896340736f;
 
-static_assert(kBM * kOutLd <= kLdsElems, "output staging must fit the K-chunk buffers");
+// Tile shapes: the first product uses 128 x 128 tiles (rows x rank); the
+// second puts the vocabulary on M and all of a 256-row batch on N, so each
+// W_up slab is read once and every lane ends up holding four consecutive
+// logits of one row.
+constexpr int kDownBM = 128, kDownBN = 128;   // 2 x 2 wavefronts of 64 x 64
+constexpr int kUpBM = 128, kUpBN = 256;       // 2 x 4 wavefronts of 64 x 64
+constexpr int kUpThreads = 512;
+
+template <int BM, int BN>
+constexpr int lds_elems() { return 2 * (BM + BN) * kLdsK; }
 
 struct HeadPart {
     float m;
@@ -85,70 +94,89 @@ __device__ inline u32x4 load16(const uint16_t* base, long row, int ld, int k, bo
 }
 
 // acc[mt][nt] += the wavefront's 64 x 64 block of A[m0.., k] B[n0.., k]^T over
-// k in [k_begin, k_end) (a multiple of 64). Lane l of MFMA tile (mt, nt) ends
-// up holding C[row][col] for row = wm*64 + mt*16 + 4*(l/16) + j, j < 4, and
-// col = wn*64 + nt*16 + l%16. Rows or columns past M or Nc hold garbage
-// (finite: products of real rows) that the callers never store.
+// k in [k_begin, k_end) (a multiple of 64); the THREADS / 64 wavefronts form a
+// (BM / 64) x (BN / 64) grid, wavefront w at (wm, wn) = (w / (BN/64), w % (BN/64)).
+// Lane l of MFMA tile (mt, nt) ends up holding C[row][col] for
+// row = wm*64 + mt*16 + 4*(l/16) + j, j < 4, and col = wn*64 + nt*16 + l%16.
+// Rows or columns past M or Nc hold garbage (finite: products of real rows)
+// that the callers never store.
 // Pipeline: chunk c is multiplied out of LDS buffer c % 2 while chunks c + 1
 // and c + 2 are in registers; after the multiply, chunk c + 1 goes to the
 // other LDS buffer and its registers start loading chunk c + 3.
+template <int BM, int BN, int THREADS>
 struct ChunkRegs {
-    u32x4 a[4], b[4];
+    static constexpr int kA = BM * (kBK / 8) / THREADS;  // 16-byte pieces per thread
+    static constexpr int kB = BN * (kBK / 8) / THREADS;
+    u32x4 a[kA], b[kB];
 };
 
+template <int BM, int BN, int THREADS>
 __device__ inline void tile_mma(const TileArgs& t, int k_begin, int k_end, uint16_t* lds,
                                 f32x4 (&acc)[4][4]) {
+    static_assert((BM / 64) * (BN / 64) * 64 == THREADS, "one wavefront per 64 x 64 block");
+    using Regs = ChunkRegs<BM, BN, THREADS>;
+    constexpr int MT = 4, NT = 4;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / (BN / 64), wn = w % (BN / 64);
     uint16_t* la = lds;
-    uint16_t* lb = lds + 2 * kBM * kLdsK;
+    uint16_t* lb = lds + 2 * BM * kLdsK;
     const int nk = (k_end - k_begin) / kBK;
     // Chunks past the end reload the last one (never stored where it is read).
-    auto gload = [&](ChunkRegs& R, int c) {
+    auto gload = [&](Regs& R, int c) {
         const int k0 = k_begin + (c < nk ? c : nk - 1) * kBK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + kThreads * i;       // 1024 16-byte pieces per operand
+        for (int i = 0; i < Regs::kA; ++i) {
+            const int q = tid + THREADS * i;
             const int row = q >> 3, kc = (q & 7) * 8;
             R.a[i] = load16(t.A, t.m0 + row, t.K, k0 + kc, t.m0 + row < t.M);
+        }
+#pragma unroll
+        for (int i = 0; i < Regs::kB; ++i) {
+            const int q = tid + THREADS * i;
+            const int row = q >> 3, kc = (q & 7) * 8;
             R.b[i] = load16(t.B, t.n0 + row, t.K, k0 + kc, t.n0 + row < t.Nc);
         }
     };
-    auto lstore = [&](const ChunkRegs& R, int buf) {
+    auto lstore = [&](const Regs& R, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + kThreads * i;
+        for (int i = 0; i < Regs::kA; ++i) {
+            const int q = tid + THREADS * i;
             const int row = q >> 3, kc = (q & 7) * 8;
-            *reinterpret_cast<u32x4*>(la + (buf * kBM + row) * kLdsK + kc) = R.a[i];
-            *reinterpret_cast<u32x4*>(lb + (buf * kBN + row) * kLdsK + kc) = R.b[i];
+            *reinterpret_cast<u32x4*>(la + (buf * BM + row) * kLdsK + kc) = R.a[i];
+        }
+#pragma unroll
+        for (int i = 0; i < Regs::kB; ++i) {
+            const int q = tid + THREADS * i;
+            const int row = q >> 3, kc = (q & 7) * 8;
+            *reinterpret_cast<u32x4*>(lb + (buf * BN + row) * kLdsK + kc) = R.b[i];
         }
     };
     const int fr = lane & 15, fk = (lane >> 4) * 8;
     auto multiply = [&](int buf) {
-#pragma unroll
+#pragma unroll 1
         for (int ks = 0; ks < kBK; ks += 32) {
-            bf16x8 a[4], b[4];
+            bf16x8 a[MT], b[NT];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
                 a[mt] = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(
-                                la + (buf * kBM + wm * 64 + mt * 16 + fr) * kLdsK + ks + fk));
+                                la + (buf * BM + wm * 64 + mt * 16 + fr) * kLdsK + ks + fk));
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
                 b[nt] = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(
-                                lb + (buf * kBN + wn * 64 + nt * 16 + fr) * kLdsK + ks + fk));
+                                lb + (buf * BN + wn * 64 + nt * 16 + fr) * kLdsK + ks + fk));
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
                     acc[mt][nt] =
                         __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
         }
     };
     if (nk <= 0)
         return;
-    ChunkRegs r0, r1;
+    Regs r0, r1;
     gload(r0, 0);
     lstore(r0, 0);
     gload(r0, 1);
@@ -171,11 +199,12 @@ __device__ inline void tile_mma(const TileArgs& t, int k_begin, int k_end, uint1
     }
 }
 
-__device__ inline void zero(f32x4 (&acc)[4][4]) {
+template <int MT, int NT>
+__device__ inline void zero(f32x4 (&acc)[MT][NT]) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
             acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
@@ -184,14 +213,14 @@ __global__ __launch_bounds__(kThreads) void head_down_kernel(const uint16_t* __r
                                                              const uint16_t* __restrict__ w_down,
                                                              int N, int r, int d, int k_per_split,
                                                              float* __restrict__ partial) {
-    __shared__ __align__(16) uint16_t lds[kLdsElems];
-    const TileArgs t{h, w_down, N, r, d, static_cast<int>(blockIdx.x) * kBM,
-                     static_cast<int>(blockIdx.y) * kBN};
+    __shared__ __align__(16) uint16_t lds[lds_elems<kDownBM, kDownBN>()];
+    const TileArgs t{h, w_down, N, r, d, static_cast<int>(blockIdx.x) * kDownBM,
+                     static_cast<int>(blockIdx.y) * kDownBN};
     const int kb = static_cast<int>(blockIdx.z) * k_per_split;
     const int ke = kb + k_per_split < d ? kb + k_per_split : d;
     f32x4 acc[4][4];
     zero(acc);
-    tile_mma(t, kb, ke, lds, acc);
+    tile_mma<kDownBM, kDownBN, kThreads>(t, kb, ke, lds, acc);
     float* out = partial + static_cast<size_t>(blockIdx.z) * N * r;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1;
@@ -229,75 +258,320 @@ __global__ __launch_bounds__(256) void head_down_reduce_kernel(const float* __re
     }
 }
 
-// z = bf16(u w_up^T) for one 128-row x 128-vocabulary tile, and each row's
-// (m, s) over the tile's columns.
-__global__ __launch_bounds__(kThreads) void head_up_kernel(const uint16_t* __restrict__ u,
+// z^T = bf16(W_up u^T) for one 128-vocabulary x 256-row tile, and each row's
+// (m, s) over the tile's 128 vocabulary entries. Lane l of MFMA tile (mt, nt)
+// holds logits v0..v0+3 (v0 = 4 * (l / 16) + ...) of row n = ... + l % 16, so
+// the rounded logits go out as 8-byte stores of four consecutive entries, and
+// a row's reduction runs over the lane's 16 values, the four lanes l % 16 + 16i
+// (two shuffles) and the two wavefronts that share the row (through LDS).
+__global__ __launch_bounds__(kUpThreads) void head_up_kernel(const uint16_t* __restrict__ u,
                                                            const uint16_t* __restrict__ w_up,
                                                            const float* __restrict__ temperature,
                                                            int N, int V, int r,
                                                            uint16_t* __restrict__ z,
                                                            HeadPart* __restrict__ part, int ntn) {
-    __shared__ __align__(16) uint16_t lds[kLdsElems];
-    const TileArgs t{u, w_up, N, V, r, static_cast<int>(blockIdx.x) * kBM,
-                     static_cast<int>(blockIdx.y) * kBN};
-    f32x4 acc[4][4];
+    constexpr int MT = 4, NT = 4;
+    __shared__ __align__(16) uint16_t lds[lds_elems<kUpBM, kUpBN>()];
+    __shared__ float lds_max[2][kUpBN];
+    __shared__ double lds_sum[2][kUpBN];
+    const int vt = static_cast<int>(blockIdx.x);
+    const TileArgs t{w_up, u, V, N, r, vt * kUpBM, static_cast<int>(blockIdx.y) * kUpBN};
+    f32x4 acc[MT][NT];
     zero(acc);
-    tile_mma(t, 0, r, lds, acc);  // ends with a barrier: the LDS is free
+    tile_mma<kUpBM, kUpBN, kUpThreads>(t, 0, r, lds, acc);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
-    uint16_t* st = lds;  // [kBM][kOutLd]
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / (kUpBN / 64), wn = w % (kUpBN / 64);
+    const int vbase = t.m0 + wm * 64 + 4 * (lane >> 4);
+    const int nloc0 = wn * 64 + (lane & 15);  // row within the tile, + 16 nt
+    // Round to bf16, store, and keep the rounded values.
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int nt = 0; nt < NT; ++nt) {
+        const int n = t.n0 + nloc0 + nt * 16;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const int v0 = vbase + mt * 16;
+            uint16_t b[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = wm * 64 + mt * 16 + 4 * (lane >> 4) + j;
-                const int col = wn * 64 + nt * 16 + (lane & 15);
-                st[row * kOutLd + col] = bf16_rne(acc[mt][nt][j]);
+                b[j] = bf16_rne(acc[mt][nt][j]);
+                acc[mt][nt][j] = bf16_to_f32(b[j]);
             }
-    __syncthreads();
-
-    // 16-byte stores: a row of the tile is 16 chunks of 8 logits.
-#pragma unroll
-    for (int i = 0; i < (kBM * kBN / 8) / kThreads; ++i) {
-        const int c = tid + kThreads * i;
-        const int row = c >> 4, cc = (c & 15) * 8;
-        if (t.m0 + row < N && t.n0 + cc < V)
-            *reinterpret_cast<u32x4*>(z + static_cast<size_t>(t.m0 + row) * V + t.n0 + cc) =
-                *reinterpret_cast<const u32x4*>(st + row * kOutLd + cc);
-    }
-
-    // Row normaliser pieces: two threads per row, 64 columns each.
-    const int row = tid >> 1, half = tid & 1;
-    const int grow = t.m0 + row;
-    const int n_valid = V - t.n0 < kBN ? V - t.n0 : kBN;
-    float inv_t = 0.0f;
-    const bool active = grow < N && sampled_row(temperature[grow < N ? grow : 0], &inv_t);
-    const int c0 = half * 64;
-    const int c1 = c0 + 64 < n_valid ? c0 + 64 : n_valid;
-    float xmax = -__builtin_huge_valf();
-    if (active)
-        for (int c = c0; c < c1; ++c)
-            xmax = fmaxf(xmax, bf16_to_f32(st[row * kOutLd + c]) * inv_t);
-    xmax = fmaxf(xmax, __shfl_xor(xmax, 1, 64));
-    const float m = xmax * kHeadLog2e;
-    double s = 0.0;
-    if (active && xmax > -__builtin_huge_valf()) {
-        for (int c = c0; c < c1; c += 8) {
-            float g = 0.0f;  // eight terms in binary32, then binary64
-            const int ce = c + 8 < c1 ? c + 8 : c1;
-            for (int e = c; e < ce; ++e) {
-                const float x = bf16_to_f32(st[row * kOutLd + e]) * inv_t;
-                g += __builtin_amdgcn_exp2f(__builtin_fmaf(x, kHeadLog2e, -m));
-            }
-            s += static_cast<double>(g);
+            if (n < N && v0 < V)  // V % 8 == 0: v0 < V covers all four
+                *reinterpret_cast<uint2*>(z + static_cast<size_t>(n) * V + v0) =
+                    make_uint2(b[0] | (static_cast<uint32_t>(b[1]) << 16),
+                               b[2] | (static_cast<uint32_t>(b[3]) << 16));
         }
     }
-    s += __shfl_xor(s, 1, 64);
-    if (half == 0 && grow < N)
-        part[static_cast<size_t>(grow) * ntn + blockIdx.y] = HeadPart{m, 0, s};
+    // Row maxima of x = fl32(z * fl32(1/T)) over the tile's valid entries.
+    float inv_t[NT];
+    bool act[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int n = t.n0 + nloc0 + nt * 16;
+        inv_t[nt] = 0.0f;
+        act[nt] = n < N && sampled_row(temperature[n < N ? n : 0], &inv_t[nt]);
+        float xmax = -__builtin_huge_valf();
+        if (act[nt]) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                if (vbase + mt * 16 < V)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        xmax = fmaxf(xmax, acc[mt][nt][j] * inv_t[nt]);
+        }
+        xmax = fmaxf(xmax, __shfl_xor(xmax, 16, 64));
+        xmax = fmaxf(xmax, __shfl_xor(xmax, 32, 64));
+        if (lane < 16)
+            lds_max[wm][nloc0 + nt * 16] = xmax;
+    }
+    __syncthreads();
+    // s = sum 2^(fma(x, log2e, -m)) with m = fl32(max x * log2e): eight terms
+    // in binary32, then binary64.
+    float m[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int nl = nloc0 + nt * 16;
+        const float xmax = fmaxf(lds_max[0][nl], lds_max[1][nl]);
+        m[nt] = xmax * kHeadLog2e;
+        double sum = 0.0;
+        if (act[nt] && xmax > -__builtin_huge_valf()) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float g = 0.0f;
+#pragma unroll
+                for (int mt = 2 * half; mt < 2 * half + 2; ++mt)
+                    if (vbase + mt * 16 < V)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            g += __builtin_amdgcn_exp2f(
+                                __builtin_fmaf(acc[mt][nt][j] * inv_t[nt], kHeadLog2e, -m[nt]));
+                sum += static_cast<double>(g);
+            }
+        }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        if (lane < 16)
+            lds_sum[wm][nl] = sum;
+    }
+    __syncthreads();
+    if (wm == 0 && lane < 16) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int nl = nloc0 + nt * 16;
+            const int n = t.n0 + nl;
+            if (n < N)
+                part[static_cast<size_t>(n) * ntn + vt] =
+                    HeadPart{m[nt], 0, lds_sum[0][nl] + lds_sum[1][nl]};
+        }
+    }
+}
+
+// Streaming form of the second product for rank r = 32 * KS, KS in {8, 16}.
+// Each of the G workgroups (one per CU) owns a contiguous run of 16-row
+// blocks of W_up and all of a 256-row batch tile:
+// * every wavefront keeps the B fragments of its 32 batch rows (all of K) in
+//   registers for the whole run (each W_up fragment read from LDS feeds two
+//   matrix instructions; 64 rows per wavefront would halve the LDS reads but
+//   leave one wavefront per SIMD, which measured slower);
+// * blocks of W_up stream through a ring of kRing LDS slots, loaded straight
+//   into LDS in MFMA fragment order (fragment ks of a block is 1 KiB, lane l's
+//   16 bytes at offset 16 l), kRing - 1 blocks ahead;
+// * each block gives every wavefront a 16 x 32 piece of z^T, rounded and
+//   stored as 8-byte runs, and folded into per-row (m, s) pairs online: when a
+//   block raises a row's maximum the pair is rescaled by a binary32 exp2
+//   factor, and each block adds at most four binary32 terms to the binary64 s;
+// * a step multiplies block b out while it rounds, stores and folds block
+//   b - 1, so matrix and vector instructions interleave.
+// The pieces of the four lanes sharing a row are merged at the end into one
+// (m, s) per (row, workgroup).
+constexpr int kRing = 6;
+constexpr int kStreamWaves = 8;   // two per SIMD, so one's matrix work covers the other's waits
+constexpr int kStreamRows = 32;
+
+__device__ constexpr int vmcnt_imm(int n) {
+    // s_waitcnt operand: vmcnt n (bits 3:0 and 15:14), expcnt and lgkmcnt not waited
+    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+template <int KS>
+__global__ __launch_bounds__(kStreamWaves * 64) void head_up_stream_kernel(
+    const uint16_t* __restrict__ u, const uint16_t* __restrict__ w_up,
+    const float* __restrict__ temperature, int N, int V, uint16_t* __restrict__ z,
+    HeadPart* __restrict__ part, int nparts, uint2* __restrict__ sink) {
+    static_assert(KS % kStreamWaves == 0, "each wavefront loads KS / 8 fragments per block");
+    constexpr int NT = kStreamRows / 16;
+    constexpr int K = KS * 32;
+    constexpr int kLoadsPerBlock = KS / kStreamWaves;  // per wavefront
+    __shared__ __align__(16) uint16_t ring[kRing][KS * 512];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int g = blockIdx.x, G = gridDim.x;
+    const int nblk = (V + 15) / 16;
+    const int b0 = static_cast<int>(static_cast<long>(nblk) * g / G);
+    const int b1 = static_cast<int>(static_cast<long>(nblk) * (g + 1) / G);
+    const int n0 = static_cast<int>(blockIdx.y) * (kStreamWaves * kStreamRows) + wv * kStreamRows;
+
+    // Block b into slot (b - b0) % kRing. Blocks past the run reload the run's
+    // last block into a slot nobody reads again: every wavefront always issues
+    // kLoadsPerBlock loads per step, which the waits below count on.
+    auto issue = [&](int b) {
+        const int bb = b < b1 ? b : b1 - 1;
+        const int v = bb * 16 + (lane & 15);
+        const uint16_t* row = w_up + static_cast<size_t>(v < V ? v : V - 1) * K + (lane >> 4) * 8;
+        uint16_t* slot = ring[(b - b0) % kRing];
+#pragma unroll
+        for (int i = 0; i < kLoadsPerBlock; ++i) {
+            const int ks = wv + kStreamWaves * i;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(row + ks * 32),
+                                             slot + ks * 512, 16, 0, 0);
+        }
+    };
+    float inv_t[NT], mref[NT];
+    double sacc[NT];
+    bool act[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + nt * 16 + (lane & 15);
+        inv_t[nt] = 0.0f;
+        act[nt] = n < N && sampled_row(temperature[n < N ? n : 0], &inv_t[nt]);
+        mref[nt] = -__builtin_huge_valf();
+        sacc[nt] = 0.0;
+    }
+
+    // This wavefront's batch rows as B fragments (rows past N read row 0).
+    bf16x8 ub[NT][KS];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + nt * 16 + (lane & 15);
+        const uint16_t* urow = u + static_cast<size_t>(n < N ? n : 0) * K + (lane >> 4) * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            ub[nt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(urow + ks * 32));
+    }
+    // The first kRing - 1 blocks; the temperature and U loads above are
+    // older, so the step waits below cover them too.
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i)
+        issue(b0 + i);
+
+    // Step for block b: wait until it has landed, publish it, refill the ring
+    // and read its fragments. Loads complete in order, and kLoadsPerBlock *
+    // (kRing - 2) loads were issued after block b's: once at most that many
+    // are outstanding, block b is in LDS. The barrier then makes every
+    // wavefront's part of it visible and frees the slot read one step earlier.
+    auto fetch = [&](int b, bf16x8 (&a)[KS]) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerBlock * (kRing - 2)));
+        __syncthreads();
+        issue(b + kRing - 1);
+        const uint16_t* slot = ring[(b - b0) % kRing];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            a[ks] = __builtin_bit_cast(bf16x8,
+                                       *reinterpret_cast<const u32x4*>(slot + ks * 512 + lane * 8));
+    };
+    // A quarter of the block's K range.
+    auto mma = [&](const bf16x8 (&a)[KS], f32x4 (&acc)[NT], int q) {
+#pragma unroll
+        for (int ks = q * (KS / 4); ks < (q + 1) * (KS / 4); ++ks)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], ub[nt][ks], acc[nt], 0, 0, 0);
+    };
+    // Finishing block b: lane l holds logits v0..v0+3 of row n (V % 8 == 0:
+    // v0 < V covers all four). Part 2 nt rounds and scales row tile nt and
+    // moves its reference; part 2 nt + 1 adds its terms and stores it. Lanes
+    // outside the batch or the vocabulary store to their own word of a sink:
+    // no branch anywhere, so the parts can sit between matrix instructions.
+    float fx[NT][4], fscale[NT];
+    uint2 fpack[NT];
+    auto finish = [&](int b, const f32x4 (&acc)[NT], int part) {
+        const int nt = part >> 1;
+        const int v0 = b * 16 + 4 * (lane >> 4);
+        const bool on = act[nt] && v0 < V;
+        if ((part & 1) == 0) {
+            uint16_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h[j] = bf16_rne(acc[nt][j]);
+                fx[nt][j] = bf16_to_f32(h[j]) * inv_t[nt];
+            }
+            fpack[nt] = make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16),
+                                   h[2] | (static_cast<uint32_t>(h[3]) << 16));
+            const float bm = on ? fmaxf(fmaxf(fx[nt][0], fx[nt][1]), fmaxf(fx[nt][2], fx[nt][3]))
+                                : -__builtin_huge_valf();
+            const float m_new = fmaxf(mref[nt], bm * kHeadLog2e);  // fl32(max x * log2e)
+            fscale[nt] = mref[nt] == m_new ? 1.0f : __builtin_amdgcn_exp2f(mref[nt] - m_new);
+            mref[nt] = m_new;
+        } else {
+            const bool live = on && mref[nt] > -__builtin_huge_valf();
+            float gsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(fx[nt][j], kHeadLog2e, -mref[nt]));
+                gsum += live ? e : 0.0f;
+            }
+            sacc[nt] = sacc[nt] * static_cast<double>(fscale[nt]) + static_cast<double>(gsum);
+            const int n = n0 + nt * 16 + (lane & 15);
+            uint2* dst = n < N && v0 < V
+                             ? reinterpret_cast<uint2*>(z + static_cast<size_t>(n) * V + v0)
+                             : sink + lane;
+            *dst = fpack[nt];
+        }
+    };
+    static_assert(2 * NT == 4, "four finishing parts, one per quarter of K");
+    // Two-stage pipeline: block b is multiplied while block b - 1 is finished,
+    // a quarter of each at a time.
+    f32x4 acc_c[NT], acc_n[NT];
+    {
+        bf16x8 a[KS];
+        fetch(b0, a);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            acc_c[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            mma(a, acc_c, q);
+    }
+    for (int b = b0 + 1; b < b1; ++b) {
+        bf16x8 a[KS];
+        fetch(b, a);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            acc_n[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            mma(a, acc_n, q);
+            finish(b - 1, acc_c, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            acc_c[nt] = acc_n[nt];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        finish(b1 - 1, acc_c, q);
+    // Merge the four lanes of each row (l % 16 + 16 i), then one piece per row.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+            const float mo = __shfl_xor(mref[nt], off, 64);
+            const double so = __shfl_xor(sacc[nt], off, 64);
+            const float mn = fmaxf(mref[nt], mo);
+            const double a = sacc[nt] == 0.0 ? 0.0
+                             : mref[nt] == mn ? sacc[nt]
+                                              : sacc[nt] * static_cast<double>(__builtin_amdgcn_exp2f(mref[nt] - mn));
+            const double c = so == 0.0 ? 0.0
+                             : mo == mn ? so : so * static_cast<double>(__builtin_amdgcn_exp2f(mo - mn));
+            mref[nt] = mn;
+            sacc[nt] = a + c;
+        }
+        const int n = n0 + nt * 16 + lane;
+        if (lane < 16 && n < N)
+            part[static_cast<size_t>(n) * nparts + g] = HeadPart{mref[nt], 0, sacc[nt]};
+    }
 }
 
 // One 256-thread workgroup per row: each thread folds a few (m, s) pieces,
@@ -357,11 +631,13 @@ using namespace specv;
 struct spec_head_ctx {
     int N = 0, d = 0, r = 0, V = 0;
     int splits = 1, k_per_split = 0, ntn = 0;
+    int stream_groups = 0;  // > 0: the streaming second product with this many workgroups
     hipStream_t stream = nullptr;
     void* ws = nullptr;
     uint16_t* u = nullptr;
     float* partial = nullptr;
     HeadPart* part = nullptr;
+    uint2* sink = nullptr;  // 64 words the streaming kernel's idle lanes store to
 };
 
 extern "C" {
@@ -372,7 +648,7 @@ int spec_lowrank_head_init(int rows, int hidden, int rank, int vocab, void* hip_
         return SPEC_EINVAL;
     *out_ctx = nullptr;
     if (rows < 1 || hidden < kBK || hidden % kBK || rank < kBK || rank % kBK || vocab < 8 ||
-        vocab % 8 || (vocab + kBN - 1) / kBN > 65535)
+        vocab % 8 || (rows + kUpBN - 1) / kUpBN > 65535)
         return SPEC_EINVAL;
     spec_head_ctx* ctx = new (std::nothrow) spec_head_ctx();
     if (!ctx)
@@ -384,13 +660,25 @@ int spec_lowrank_head_init(int rows, int hidden, int rank, int vocab, void* hip_
     ctx->stream = static_cast<hipStream_t>(hip_stream);
     // Split the small first product over K until there are ~128 workgroups,
     // keeping at least 4 chunks per split.
-    const int tiles = ((rows + kBM - 1) / kBM) * ((rank + kBN - 1) / kBN);
+    const int tiles = ((rows + kDownBM - 1) / kDownBM) * ((rank + kDownBN - 1) / kDownBN);
     const int max_split = std::max(1, hidden / (4 * kBK));
     ctx->splits = std::max(1, std::min(max_split, (128 + tiles - 1) / tiles));
     const int chunks = hidden / kBK;
     ctx->k_per_split = ((chunks + ctx->splits - 1) / ctx->splits) * kBK;
     ctx->splits = (hidden + ctx->k_per_split - 1) / ctx->k_per_split;
-    ctx->ntn = (vocab + kBN - 1) / kBN;
+    ctx->ntn = (vocab + kUpBM - 1) / kUpBM;
+    if (rank == 256 || rank == 512) {
+        // One workgroup per CU, each with at least one 16-row block of W_up.
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1) {
+            delete ctx;
+            return SPEC_EHIP;
+        }
+        ctx->stream_groups = std::min(cus, (vocab + 15) / 16);
+        ctx->ntn = ctx->stream_groups;
+    }
     const size_t nr = static_cast<size_t>(rows) * rank;
     size_t off = 0;
     const size_t o_u = off;
@@ -399,6 +687,8 @@ int spec_lowrank_head_init(int rows, int hidden, int rank, int vocab, void* hip_
     off = align_up(off + nr * ctx->splits * sizeof(float), 256);
     const size_t o_h = off;
     off = align_up(off + static_cast<size_t>(rows) * ctx->ntn * sizeof(HeadPart), 256);
+    const size_t o_s = off;
+    off = align_up(off + 64 * sizeof(uint2), 256);
     if (hipMalloc(&ctx->ws, off) != hipSuccess) {
         delete ctx;
         return SPEC_ENOMEM;
@@ -407,6 +697,7 @@ int spec_lowrank_head_init(int rows, int hidden, int rank, int vocab, void* hip_
     ctx->u = reinterpret_cast<uint16_t*>(base + o_u);
     ctx->partial = reinterpret_cast<float*>(base + o_p);
     ctx->part = reinterpret_cast<HeadPart*>(base + o_h);
+    ctx->sink = reinterpret_cast<uint2*>(base + o_s);
     *out_ctx = ctx;
     return SPEC_OK;
 }
@@ -428,8 +719,8 @@ int spec_lowrank_head(spec_head_ctx* ctx, const void* hidden, const void* w_down
         return SPEC_EINVAL;
     const int N = ctx->N, d = ctx->d, r = ctx->r, V = ctx->V;
     hipStream_t s = ctx->stream;
-    const unsigned mt = static_cast<unsigned>((N + kBM - 1) / kBM);
-    head_down_kernel<<<dim3(mt, static_cast<unsigned>((r + kBN - 1) / kBN),
+    const unsigned mt = static_cast<unsigned>((N + kDownBM - 1) / kDownBM);
+    head_down_kernel<<<dim3(mt, static_cast<unsigned>((r + kDownBN - 1) / kDownBN),
                             static_cast<unsigned>(ctx->splits)),
                        dim3(kThreads), 0, s>>>(static_cast<const uint16_t*>(hidden),
                                               static_cast<const uint16_t*>(w_down), N, r, d,
@@ -441,9 +732,23 @@ int spec_lowrank_head(spec_head_ctx* ctx, const void* hidden, const void* w_down
     head_down_reduce_kernel<<<dim3(rb), dim3(256), 0, s>>>(ctx->partial, ctx->splits, nr, ctx->u);
     if (hipGetLastError() != hipSuccess)
         return SPEC_EHIP;
-    head_up_kernel<<<dim3(mt, static_cast<unsigned>(ctx->ntn)), dim3(kThreads), 0, s>>>(
-        ctx->u, static_cast<const uint16_t*>(w_up), temperature, N, V, r,
-        static_cast<uint16_t*>(out_logits), ctx->part, ctx->ntn);
+    if (ctx->stream_groups > 0) {
+        const dim3 grid(static_cast<unsigned>(ctx->stream_groups),
+                        static_cast<unsigned>((N + kStreamWaves * kStreamRows - 1) / (kStreamWaves * kStreamRows)));
+        if (r == 512)
+            head_up_stream_kernel<16><<<grid, dim3(kStreamWaves * 64), 0, s>>>(
+                ctx->u, static_cast<const uint16_t*>(w_up), temperature, N, V,
+                static_cast<uint16_t*>(out_logits), ctx->part, ctx->ntn, ctx->sink);
+        else
+            head_up_stream_kernel<8><<<grid, dim3(kStreamWaves * 64), 0, s>>>(
+                ctx->u, static_cast<const uint16_t*>(w_up), temperature, N, V,
+                static_cast<uint16_t*>(out_logits), ctx->part, ctx->ntn, ctx->sink);
+    } else {
+        head_up_kernel<<<dim3(static_cast<unsigned>(ctx->ntn), static_cast<unsigned>((N + kUpBN - 1) / kUpBN)),
+                         dim3(kUpThreads), 0, s>>>(
+            ctx->u, static_cast<const uint16_t*>(w_up), temperature, N, V, r,
+            static_cast<uint16_t*>(out_logits), ctx->part, ctx->ntn);
+    }
     if (hipGetLastError() != hipSuccess)
         return SPEC_EHIP;
     head_lse_kernel<<<dim3(static_cast<unsigned>(N)), dim3(256), 0, s>>>(ctx->part, ctx->ntn,

@@ -123,6 +123,10 @@ def check_rows(gpu, ref, x, rows):
     (8, 128, 64, 296),         # single tiles, ragged everywhere
     (130, 256, 64, 2056),      # two row tiles, ragged vocabulary tile, split K
     (64, 1024, 128, 8192),     # several K splits and vocabulary tiles
+    # the streaming second product (rank 256 or 512): W_up in 16-row blocks
+    (8, 128, 256, 296),        # 19 blocks, the last one half full, one per workgroup
+    (300, 256, 512, 2056),     # two 256-row batch tiles, ragged last block
+    (37, 512, 512, 65544),     # 4097 blocks over the CUs, rows not a multiple of 16
 ])
 def test_head_parity_small(N, d, r, V):
     x = specgen.lowrank_head_inputs(N, d, r, V, seed=N + d)
