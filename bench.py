@@ -87,7 +87,72 @@ def cpu_baseline(rec, d, budget_s: float = 10.0, cap_s: float = 30.0) -> dict:
     return {"value": round(n / dt, 3), "unit": "sequences/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} sequence verifications ({passes} passes over the {rec.batch} "
                       f"sequences of the {rec.name} workload, one oracle call per sequence), "
-                      f"{dt:.1f} s on one host core"}
+                      f"{dt:.1f} s on one host core",
+            "host_cpu": host_cpu_model(), "nproc": os.cpu_count()}
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_next_rows(rec, d, host: dict, F: int) -> dict:
+    """The oracle of each further row, single-threaded, on a bounded sample of
+    the same work the GPU lines above time (a few seconds each)."""
+    import oracle
+    oracle._load()
+    B, G = rec.batch, rec.gamma
+    res = {}
+
+    def timed(fn, reps=1):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        return (time.perf_counter() - t0) / reps
+
+    n_seq = min(2, B)
+    dt = timed(lambda: oracle.outcomes(d["logits_draft"][:n_seq], d["logits_target"][:n_seq],
+                                       d["draft_tokens"][:n_seq], d["temperature"][:n_seq], F))
+    res["outcomes"] = {"us_per_sequence": round(dt / n_seq * 1e6, 1),
+                       "sample": f"outcome law with F = {F} for {n_seq} sequences of the workload"}
+    if "head" in host:
+        hx = host["head"]
+        rows = [r for r in (0, 1) if r < hx["h"].shape[0]]
+        dt = timed(lambda: oracle.lowrank_head(hx["h"], hx["w_down"], hx["w_up"],
+                                               hx["temperature"], rows=rows))
+        res["lowrank_head"] = {"us_per_row": round(dt / len(rows) * 1e6, 1),
+                               "sample": f"{len(rows)} rows of the N = {hx['h'].shape[0]} head"}
+    if "tree" in host:
+        tr = host["tree"]
+        pr = tr["prune"]
+        dt = timed(lambda: oracle.tree_prune(pr["parent"], pr["logq"], float(np.log(1e-3)), 32), 3)
+        res["tree_prune"] = {"us_per_call": round(dt * 1e6, 1),
+                             "sample": f"{pr['parent'].shape[0]} trees of {pr['parent'].shape[1]} nodes"}
+        vt, nt = tr["verify"], tr["target"].shape[0]
+        n_nodes = np.full(nt, tr["n"], np.int32)
+        dt = timed(lambda: oracle.tree_verify_greedy(vt["parent"][:nt], vt["token"][:nt], n_nodes,
+                                                     tr["target"]))
+        res["tree_verify"] = {"us_per_tree": round(dt / nt * 1e6, 1),
+                              "sample": f"{nt} trees of {tr['n']} nodes"}
+    if G > 0:
+        al = np.minimum(np.arange(B, dtype=np.int32) % (G + 1), G)
+        for name, pol in (("ucb1", oracle.UCB1), ("thompson", oracle.THOMPSON)):
+            bd = oracle.Bandit(pol, B, 3, B, G)
+            arm, _ = bd.step(seed=1, offset=0)
+            reps = 200
+            t0 = time.perf_counter()
+            for i in range(reps):
+                arm, _ = bd.step(al, arm, seed=1, offset=i + 1)
+            res[f"bandit_{name}_groups{B}"] = {
+                "us_per_step": round((time.perf_counter() - t0) / reps * 1e6, 1),
+                "sample": f"{reps} steps, {B} groups of 3 arms"}
+    return res
 
 
 COPY_BYTES = 1 << 30
@@ -225,6 +290,16 @@ def main() -> int:
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
 
+    # Distribution of single calls: each bracketed by its own event pair.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(args.steps, 100))]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        step(args.warmup + i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    call_us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+
     # Scalar-only mode at B = 512, gamma = 4 (the [512, 4, 2] fp32 pairs the
     # B=512 workload specifies); the pair values do not change the work.
     sc_b, sc_g = 512, 4
@@ -340,6 +415,11 @@ def main() -> int:
     head_bytes = 2 * (V * hr + B * V + hr * hd + B * hd)
     head_flops = 2 * B * (hd * hr + hr * V)
     sv.spec_lowrank_head_destroy(hctx)
+    host = {}
+    if not args.no_cpu_baseline:
+        bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        host["head"] = dict(h=bits(hh), w_down=bits(wd), w_up=bits(wu),
+                            temperature=d["temperature"][:B].copy())
     del hh, wd, wu, hz
 
     # Draft trees of this batch and vocabulary: pruning 64-node trees, and
@@ -385,6 +465,9 @@ def main() -> int:
     tree_ms = start.elapsed_time(end) / args.steps
     tree_bytes = B * tm * V * 2
     sv.spec_tree_verify_destroy(tctx)
+    if not args.no_cpu_baseline:
+        host["tree"] = dict(prune=tp, verify=tv, n=tm,
+                            target=v_tgt[:4].view(torch.int16).cpu().numpy().view(np.uint16))
     del v_tgt
     k1_gbs = k1_bytes / (k1_ms * 1e-3) / 1e9
     k3_gbs = k3_bytes / (k3_ms * 1e-3) / 1e9
@@ -403,6 +486,9 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "call_us": {"median": round(float(np.median(call_us)), 2),
+                    "p10": round(float(np.percentile(call_us, 10)), 2),
+                    "p90": round(float(np.percentile(call_us, 90)), 2), "calls": int(call_us.size)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -445,6 +531,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(rec, d)
+        out["cpu_baseline"]["rows"] = cpu_next_rows(rec, d, host, F_OUT)
     sv.spec_verify_destroy(ctx)
     print(json.dumps(out), flush=True)
     return 0

@@ -303,6 +303,7 @@ def lowrank_head(h, w_down, w_up, temperature, rows=None):
     assert d2 == d and r2 == r
     temp = np.ascontiguousarray(temperature, np.float32).reshape(N)
     idx = None if rows is None else np.ascontiguousarray(rows, np.int32)
+    assert idx is None or (idx.size and idx.min() >= 0 and idx.max() < N), "rows outside [0, N)"
     n = N if idx is None else idx.size
     out = dict(u_exact=np.zeros((n, r)), u=np.zeros((n, r), np.uint16), u_abs=np.zeros((n, r)),
                z_exact=np.zeros((n, V)), z=np.zeros((n, V), np.uint16), z_abs=np.zeros((n, V)),
