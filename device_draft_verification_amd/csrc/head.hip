@@ -552,6 +552,9 @@ __global__ __launch_bounds__(kStreamWaves * 64) void head_up_stream_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         finish(b1 - 1, acc_c, q);
+    // The last steps' ring loads land in slots nobody reads; drain them so no
+    // write into this workgroup's LDS is pending when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     // Merge the four lanes of each row (l % 16 + 16 i), then one piece per row.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
