@@ -27,27 +27,48 @@ __device__ inline double lse_of(const RowNorm& r) {
     return (static_cast<double>(r.m) + log2(r.s)) / static_cast<double>(kLog2e);
 }
 
-__device__ inline bool merge_sampled(const Partial* p, int nsplit, RowNorm* out) {
+// The first kPre splits of a row are loaded up front with the kernel's other
+// loads (one round trip to memory); further splits, if any, in the loop.
+constexpr int kPre = 4;
+
+struct RowSplits {
+    Partial pre[kPre];
+    const Partial* p;
+    int nsplit;
+    __device__ inline Partial at(int c) const { return c < kPre ? pre[c] : p[c]; }
+};
+
+__device__ inline void load_splits(RowSplits& r, const Partial* p, int nsplit) {
+    r.p = p;
+    r.nsplit = nsplit;
+#pragma unroll
+    for (int c = 0; c < kPre; ++c)
+        r.pre[c] = p[c < nsplit ? c : nsplit - 1];  // unconditional, in range
+}
+
+__device__ inline bool merge_sampled(const RowSplits& r, RowNorm* out) {
     float m = kNegMax;
-    for (int c = 0; c < nsplit; ++c)
-        m = fmaxf(m, p[c].m);
+    for (int c = 0; c < r.nsplit; ++c)
+        m = fmaxf(m, r.at(c).m);
     double s = 0.0;
-    for (int c = 0; c < nsplit; ++c) {
+    for (int c = 0; c < r.nsplit; ++c) {
         // exact 1 for the splits holding the max; a 1-ulp fp32 factor otherwise
-        const float f = (p[c].m == m) ? 1.0f : fast_exp2(p[c].m - m);
-        s = __builtin_fma(p[c].s, static_cast<double>(f), s);
+        const Partial q = r.at(c);
+        const float f = (q.m == m) ? 1.0f : fast_exp2(q.m - m);
+        s = __builtin_fma(q.s, static_cast<double>(f), s);
     }
     *out = RowNorm{m, -1, s};
     return s > 0.0;  // false: the row has no finite logit
 }
 
-__device__ inline bool merge_greedy(const Partial* p, int nsplit, RowNorm* out) {
+__device__ inline bool merge_greedy(const RowSplits& r, RowNorm* out) {
     float bv = -__builtin_huge_valf();
     int bi = 0x7fffffff;
-    for (int c = 0; c < nsplit; ++c) {
-        if (p[c].m > bv || (p[c].m == bv && p[c].idx < bi)) {
-            bv = p[c].m;
-            bi = p[c].idx;
+    for (int c = 0; c < r.nsplit; ++c) {
+        const Partial q = r.at(c);
+        if (q.m > bv || (q.m == bv && q.idx < bi)) {
+            bv = q.m;
+            bi = q.idx;
         }
     }
     *out = RowNorm{bv, bi, 0.0};
@@ -87,10 +108,21 @@ __global__ __launch_bounds__(64) void accept_kernel(
         const int i = i0 + lane;
         const bool has_draft = i < G;
         const bool has_target = i <= G;
+        // Every load of this pass first, unconditional and clamped into range
+        // (lanes past the sequence read position 0 or G and use nothing), so
+        // they share one round trip instead of waiting on each other.
+        const int id = has_draft ? i : 0;
+        const int ip = has_target ? i : G;
+        const int t_raw = G > 0 ? tokens[static_cast<size_t>(b) * G + id] : 0;
+        const float zq_raw = gathered[row0 + id];
+        const float zp_raw = gathered[row0 + G + ip];
+        RowSplits sq, sp;
+        load_splits(sq, part + (row0 + id) * nsplit, nsplit);
+        load_splits(sp, part + (row0 + G + ip) * nsplit, nsplit);
         int t = 0;
         bool t_ok = false;
         if (has_draft) {
-            t = tokens[static_cast<size_t>(b) * G + i];
+            t = t_raw;
             t_ok = t >= 0 && t < vocab;
             if (!t_ok)
                 bad = true;
@@ -99,17 +131,14 @@ __global__ __launch_bounds__(64) void accept_kernel(
         RowNorm rq{0.0f, -1, 1.0}, rp{0.0f, -1, 1.0};
         if (mode == 1 && has_target) {
             // raw logits of the draft token, recorded by the row kernel
-            float zq = 0.0f, zp = 0.0f;
-            if (t_ok) {
-                zq = gathered[row0 + i];
-                zp = gathered[row0 + G + i];
-            }
+            const float zq = t_ok ? zq_raw : 0.0f;
+            const float zp = t_ok ? zp_raw : 0.0f;
             if (has_draft) {
-                if (!merge_sampled(part + (row0 + i) * nsplit, nsplit, &rq))
+                if (!merge_sampled(sq, &rq))
                     bad = true;
                 rn[row0 + i] = rq;
             }
-            if (!merge_sampled(part + (row0 + G + i) * nsplit, nsplit, &rp))
+            if (!merge_sampled(sp, &rp))
                 bad = true;
             rn[row0 + G + i] = rp;
             const double lse_p = lse_of(rp);
@@ -125,7 +154,7 @@ __global__ __launch_bounds__(64) void accept_kernel(
             }
         } else if (mode == 0 && has_target) {
             RowNorm rp;
-            if (!merge_greedy(part + (row0 + G + i) * nsplit, nsplit, &rp))
+            if (!merge_greedy(sp, &rp))
                 bad = true;
             rn[row0 + G + i] = rp;
             if (has_draft) {
