@@ -101,6 +101,9 @@ def _load():
     lib.oracle_tree_prune.restype = None
     lib.oracle_tree_verify_greedy.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P]
     lib.oracle_tree_verify_greedy.restype = None
+    lib.oracle_tree_verify_sample.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, u64, u64,
+                                              P, P, P, P, P, P]
+    lib.oracle_tree_verify_sample.restype = None
     lib.oracle_gamma_mt.argtypes = [f64, u64, u64, i32, i32, i32, P]
     lib.oracle_gamma_mt.restype = f64
     lib.oracle_beta_sample.argtypes = [f64, f64, u64, u64, i32, i32, P]
@@ -342,6 +345,31 @@ def tree_verify_greedy(parent, token, n_nodes, target):
                extra=np.zeros(B, np.int32))
     _load().oracle_tree_verify_greedy(B, M, V, dt, _ptr(par), _ptr(tok), _ptr(nn), _ptr(zt),
                                       _ptr(out["length"]), _ptr(out["path"]), _ptr(out["extra"]))
+    return out
+
+
+def tree_verify_sample(parent, token, n_nodes, draft, target, temperature, seed=0, offset=0,
+                       seq_ids=None):
+    """Sampled verification of draft trees (multi-step speculative sampling
+    with one draft distribution per node): parent, token [B, M] int32,
+    n_nodes [B], draft and target logits [B, M, V] (float32 or bf16 bits; draft
+    row u is the distribution u's children were drawn from), temperature [B];
+    seq_ids [B] are the b of the Philox counter (default 0..B-1)."""
+    zt, dt = _logits(target)
+    zq, dq = _logits(draft)
+    assert dq == dt and zq.shape == zt.shape
+    B, M, V = zt.shape
+    par = np.ascontiguousarray(parent, np.int32)
+    tok = np.ascontiguousarray(token, np.int32)
+    nn = np.ascontiguousarray(n_nodes, np.int32).reshape(B)
+    temp = np.ascontiguousarray(temperature, np.float32).reshape(B)
+    sid = None if seq_ids is None else np.ascontiguousarray(seq_ids, np.int64).reshape(B)
+    out = dict(length=np.zeros(B, np.int32), path=np.zeros((B, M), np.int32),
+               extra=np.zeros(B, np.int32), acc_margin=np.zeros(B), res_margin=np.zeros(B))
+    _load().oracle_tree_verify_sample(B, M, V, dt, _ptr(par), _ptr(tok), _ptr(nn), _ptr(zq),
+                                      _ptr(zt), _ptr(temp), seed, offset, _ptr(sid),
+                                      _ptr(out["length"]), _ptr(out["path"]), _ptr(out["extra"]),
+                                      _ptr(out["acc_margin"]), _ptr(out["res_margin"]))
     return out
 
 

@@ -884,3 +884,187 @@ void oracle_tree_verify_greedy(int B, int M, int V, int dtype, const int32_t *pa
         length[b] = L;
     }
 }
+
+/*
+ * Sampled verification of a batch of draft trees (T > 0): multi-step
+ * speculative sampling (Miao et al., SpecInfer, ASPLOS 2024, its tree
+ * verification with stochastic decoding), written here with one draft
+ * distribution per node: the children of node u are draft tokens drawn
+ * independently from q_u. The pages name tree drafting and pruning but give no
+ * multi-branch acceptance rule; this is the published one that keeps the
+ * target's output distribution. Readings:
+ *   TS1 rows: target row u holds the distribution of the token that follows
+ *       node u's path (p_u), draft row u the distribution u's children were
+ *       drawn from (q_u); x = fl32(z * fl32(1/T)) as in R3;
+ *   TS2 at node u with current target pi (pi = p_u on arrival), u's children
+ *       are tried in increasing node order; child s with token t is accepted
+ *       iff log u_acc(s) < log pi(t) - log q_u(t) (IEEE, as in R5); on
+ *       acceptance the walk moves to s with pi = p_s; on rejection
+ *       pi <- max(0, pi - q_u) / its sum, unless that sum is <= 0 (rounding
+ *       only), when pi stays (as in R8);
+ *   TS3 when u has no child left to try (all rejected, or none) the extra token
+ *       is drawn from pi by the inverse CDF of R7;
+ *   TS4 uniforms: Philox block (s - 1, b) word 0 is child s's accept uniform,
+ *       block (L, b) word 1 the draw's, L the number of accepted nodes; on a
+ *       chain (node i + 1 holding draft token i) these are the verifier's R6
+ *       uniforms, and the rule is the verifier's, so a chain gives the same
+ *       outcome as oracle_verify;
+ *   TS5 T == 0: the greedy rule TR5 (no uniforms);
+ *   TS6 sentinels: TR6's, a temperature R3 rejects, or a row the walk needs
+ *       with no finite logit: length -1, path -1, extra -1.
+ * Before any rejection at u, log pi(t) is x_p(t) - lse_p(u) and the residual
+ * weights are max(0, p - q) unnormalised, so on a chain every operation is
+ * oracle_verify_sequence's.
+ * Shapes: parent, token [B][M], n_nodes [B], draft and target [B][M][V],
+ * temperature [B], seq_ids [B] (NULL: 0..B-1, the b of the Philox counter);
+ * outputs length [B], path [B][M], extra [B], acc_margin [B] (smallest
+ * |(log pi - log q) - log u| over the tests made, +inf if none) and
+ * res_margin [B] (the draw's log-margin of R7), each may be NULL.
+ */
+static int load_row_prob(const void *base, int dtype, size_t row0, int V, float inv_t,
+                         double *lse_out, double *prob)
+{
+    double lse = oracle_row_lse(base, dtype, row0, V, inv_t);
+    *lse_out = lse;
+    if (!(lse > -INFINITY))
+        return 0;
+    for (int v = 0; v < V; ++v)
+        prob[v] = exp((double)scaled(raw_logit(base, dtype, row0 + (size_t)v), inv_t) - lse);
+    return 1;
+}
+
+void oracle_tree_verify_sample(int B, int M, int V, int dtype, const int32_t *parent,
+                               const int32_t *token, const int32_t *n_nodes, const void *draft,
+                               const void *target, const float *temperature, uint64_t seed,
+                               uint64_t offset, const int64_t *seq_ids, int32_t *length,
+                               int32_t *path, int32_t *extra, double *acc_margin,
+                               double *res_margin)
+{
+    double *pi = (double *)malloc(sizeof(double) * (size_t)V);
+    double *q = (double *)malloc(sizeof(double) * (size_t)V);
+    double *w = (double *)malloc(sizeof(double) * (size_t)V);
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parent + (size_t)b * M;
+        const int32_t *tk = token + (size_t)b * M;
+        int32_t *pa = path + (size_t)b * M;
+        const int n = n_nodes[b];
+        for (int i = 0; i < M; ++i)
+            pa[i] = -1;
+        length[b] = -1;
+        extra[b] = -1;
+        if (acc_margin)
+            acc_margin[b] = NAN;
+        if (res_margin)
+            res_margin[b] = NAN;
+        int ok = n >= 1 && n <= M && par[0] == -1;
+        for (int i = 1; i < n && ok; ++i)
+            if (par[i] < 0 || par[i] >= i || tk[i] < 0 || tk[i] >= V)
+                ok = 0;
+        float inv_t = 0.0f;
+        if (!ok || !temperature_valid(temperature[b], &inv_t))
+            continue;
+        if (temperature[b] == 0.0f) {
+            /* TS5 */
+            oracle_tree_verify_greedy(1, M, V, dtype, par, tk, &n_nodes[b],
+                                      (const char *)target + (size_t)b * M * V * (dtype == ORACLE_BF16 ? 2 : 4),
+                                      &length[b], pa, &extra[b]);
+            if (length[b] >= 0) {
+                if (acc_margin)
+                    acc_margin[b] = INFINITY;
+                if (res_margin)
+                    res_margin[b] = INFINITY;
+            }
+            continue;
+        }
+        const int64_t sid = seq_ids ? seq_ids[b] : b;
+        const size_t base = (size_t)b * M * V;
+        int u = 0, L = 0, bad = 0;
+        double amin = INFINITY;
+        double lse_p = 0.0, lse_q = 0.0;
+        if (!load_row_prob(target, dtype, base, V, inv_t, &lse_p, pi))
+            bad = 1;
+        /* weights of the current target: pi itself until a rejection, then
+         * the unnormalised residual w with sum wsum */
+        int residual = 0;
+        double wsum = 1.0;
+        while (!bad) {
+            int moved = 0, have_q = 0;
+            for (int s = 1; s < n && !bad; ++s) {
+                if (par[s] != u)
+                    continue;
+                if (!have_q) {
+                    if (!load_row_prob(draft, dtype, base + (size_t)u * V, V, inv_t, &lse_q, q)) {
+                        bad = 1;
+                        break;
+                    }
+                    have_q = 1;
+                }
+                const int t = tk[s];
+                uint32_t words[4];
+                oracle_philox_words(seed, offset, sid, s - 1, words);
+                const double log_u = log(oracle_uniform24(words[0]));
+                const double xq = scaled(raw_logit(draft, dtype, base + (size_t)u * V + t), inv_t);
+                const double lq = xq - lse_q;
+                double lpi;
+                if (!residual) {
+                    const double xp =
+                        scaled(raw_logit(target, dtype, base + (size_t)u * V + t), inv_t);
+                    lpi = xp - lse_p;
+                } else {
+                    lpi = log(w[t]) - log(wsum);
+                }
+                const double m = (lpi - lq) - log_u;
+                if (fabs(m) < amin)
+                    amin = fabs(m);
+                if (log_u < lpi - lq) {
+                    pa[L++] = s;
+                    u = s;
+                    moved = 1;
+                    residual = 0;
+                    wsum = 1.0;
+                    if (!load_row_prob(target, dtype, base + (size_t)u * V, V, inv_t, &lse_p, pi))
+                        bad = 1;
+                    break;
+                }
+                /* rejection: pi <- max(0, pi - q_u) / sum, pi being p_u or
+                 * w / wsum; the first pass only sums, so an empty residual
+                 * leaves pi as it was */
+                double sum = 0.0;
+                for (int v = 0; v < V; ++v) {
+                    const double cur = residual ? w[v] / wsum : pi[v];
+                    const double r = cur - q[v];
+                    sum += r > 0.0 ? r : 0.0;
+                }
+                if (sum > 0.0) {
+                    for (int v = 0; v < V; ++v) {
+                        const double cur = residual ? w[v] / wsum : pi[v];
+                        const double r = cur - q[v];
+                        w[v] = r > 0.0 ? r : 0.0;
+                    }
+                    wsum = sum;
+                    residual = 1;
+                }
+            }
+            if (!moved)
+                break;
+        }
+        if (bad) {
+            for (int i = 0; i < M; ++i)
+                pa[i] = -1;
+            continue;
+        }
+        uint32_t words[4];
+        oracle_philox_words(seed, offset, sid, L, words);
+        double margin = 0.0;
+        const int j = oracle_inverse_cdf(residual ? w : pi, V, oracle_uniform24(words[1]), &margin);
+        length[b] = L;
+        extra[b] = j;
+        if (acc_margin)
+            acc_margin[b] = amin;
+        if (res_margin)
+            res_margin[b] = margin;
+    }
+    free(pi);
+    free(q);
+    free(w);
+}

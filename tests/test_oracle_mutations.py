@@ -14,6 +14,7 @@ import oracle
 import test_bandit_oracle as bandit
 import test_oracle_lowrank as lowrank
 import test_oracle_tree as tree
+import test_oracle_tree_sample as tsample
 import test_oracle_outcomes as outcomes
 import test_oracle_pins as pins
 import test_oracle_stats as stats
@@ -237,3 +238,24 @@ def torch_philox_exe():
     d = tempfile.mkdtemp(prefix="philox_mut_")
     yield pins.build_torch_philox_exe(d)
     shutil.rmtree(d, ignore_errors=True)
+
+
+def test_tree_sampling_without_the_residual_update_is_caught():
+    # the next child is tested against p again instead of the residual
+    with mutated_oracle("""                    wsum = sum;
+                    residual = 1;""", """                    wsum = sum;
+                    residual = 0;"""):
+        fails(tsample.test_outputs_follow_the_target)
+
+
+def test_tree_sampling_residual_the_wrong_way_is_caught():
+    with mutated_oracle("""                        const double r = cur - q[v];
+                        w[v] = r > 0.0 ? r : 0.0;""", """                        const double r = q[v] - cur;
+                        w[v] = r > 0.0 ? r : 0.0;"""):
+        fails(tsample.test_outputs_follow_the_target)
+
+
+def test_tree_sampling_uniform_block_off_by_one_is_caught():
+    with mutated_oracle("oracle_philox_words(seed, offset, sid, s - 1, words);",
+                        "oracle_philox_words(seed, offset, sid, s, words);"):
+        fails(tsample.test_chain_is_the_verifier, 2, dict())
