@@ -19,5 +19,6 @@ from .binding import (  # noqa: F401
     HeadContext, spec_lowrank_head, spec_lowrank_head_copy_activation, spec_lowrank_head_destroy,
     spec_lowrank_head_init, spec_lowrank_head_set_stream,
     SPEC_TREE_MAX_NODES, TreeContext, spec_tree_prune, spec_tree_verify_destroy,
-    spec_tree_verify_greedy, spec_tree_verify_init, spec_tree_verify_set_stream,
+    spec_tree_verify_greedy, spec_tree_verify_init, spec_tree_verify_sample,
+    spec_tree_verify_set_stream,
 )

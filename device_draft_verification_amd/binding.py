@@ -33,7 +33,7 @@ EXPORTED = (
     "spec_lowrank_head_init", "spec_lowrank_head_set_stream", "spec_lowrank_head",
     "spec_lowrank_head_copy_activation", "spec_lowrank_head_destroy",
     "spec_tree_prune", "spec_tree_verify_init", "spec_tree_verify_set_stream",
-    "spec_tree_verify_greedy", "spec_tree_verify_destroy",
+    "spec_tree_verify_greedy", "spec_tree_verify_sample", "spec_tree_verify_destroy",
 )
 
 SPEC_TREE_MAX_NODES = 256
@@ -90,6 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_tree_verify_init": ([i32, i32, i32, i32, P, ctypes.POINTER(P)], i32),
         "spec_tree_verify_set_stream": ([P, P], i32),
         "spec_tree_verify_greedy": ([P, P, P, P, P, P, P, P], i32),
+        "spec_tree_verify_sample": ([P, P, P, P, P, P, P, u64, u64, P, P, P], i32),
         "spec_tree_verify_destroy": ([P], i32),
     }
     for name, (args, res) in sig.items():
@@ -462,6 +463,24 @@ def spec_tree_verify_greedy(ctx: TreeContext, parent, token, n_nodes, target, ou
     _check("spec_tree_verify_greedy", load_library().spec_tree_verify_greedy(
         ctx.handle, _ptr(parent), _ptr(token), _ptr(n_nodes), _ptr(target), _ptr(out_length),
         _ptr(out_path), _ptr(out_extra)))
+
+
+def spec_tree_verify_sample(ctx: TreeContext, parent, token, n_nodes, draft, target, temperature,
+                            seed: int, offset: int, out_length, out_path, out_extra) -> None:
+    B, M, V = ctx.batch, ctx.max_nodes, ctx.vocab
+    ldt = torch.bfloat16 if ctx.dtype == SPEC_BF16 else torch.float32
+    _expect(parent, (B, M), torch.int32, "parent")
+    _expect(token, (B, M), torch.int32, "token")
+    _expect(n_nodes, (B,), torch.int32, "n_nodes")
+    _expect(draft, (B, M, V), ldt, "draft")
+    _expect(target, (B, M, V), ldt, "target")
+    _expect(temperature, (B,), torch.float32, "temperature")
+    _expect(out_length, (B,), torch.int32, "out_length")
+    _expect(out_path, (B, M), torch.int32, "out_path")
+    _expect(out_extra, (B,), torch.int32, "out_extra")
+    _check("spec_tree_verify_sample", load_library().spec_tree_verify_sample(
+        ctx.handle, _ptr(parent), _ptr(token), _ptr(n_nodes), _ptr(draft), _ptr(target),
+        _ptr(temperature), seed, offset, _ptr(out_length), _ptr(out_path), _ptr(out_extra)))
 
 
 def spec_tree_verify_destroy(ctx: TreeContext) -> None:

@@ -61,6 +61,14 @@ hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, con
                            const void* target, const SeqState* seq, float* tile_sums,
                            int32_t* out_tok, hipStream_t stream);
 
+// Sampled verification of draft trees (spec_tree.h): one 1024-thread
+// workgroup per tree, dynamic LDS for the tile sums of one row.
+hipError_t launch_tree_sample(int batch, int max_nodes, int vocab, int dtype, bool vec,
+                              const int32_t* parent, const int32_t* token, const int32_t* n_nodes,
+                              const void* draft, const void* target, const float* temperature,
+                              uint64_t seed, uint64_t offset, int32_t* out_length,
+                              int32_t* out_path, int32_t* out_extra, hipStream_t stream);
+
 // Scalar-only accept on gathered log-probability pairs.
 hipError_t launch_accept_scalar(int batch, int gamma, const float* logprobs, uint64_t seed,
                                 uint64_t offset, int32_t* out_len, hipStream_t stream);

@@ -30,6 +30,7 @@
 // with it) and which costs one fused multiply-add per logit pair. The bonus
 // row uses p' itself.
 #include "launch.hpp"
+#include "philox.hpp"
 
 namespace specv {
 namespace {
@@ -370,47 +371,50 @@ __device__ inline double tile_sum_of(const SeqRows& s, int t, int groups) {
     return static_cast<double>(tile_reduce(gs));
 }
 
-// The draw of one sequence from its tile sums `ts` (global memory or LDS), by
-// one wavefront: total S, the tile holding tau = u_res * S, then the token
-// inside it; the empty-residual fallback streams p at position k.
+// The draw from the tile sums `ts` (global memory or LDS) of one row pair, by
+// one wavefront, with uniform u: total S, the tile holding tau = u * S, then
+// the token inside it; the empty-residual fallback streams p at the same
+// position. Every lane returns the token.
+template <int DT, bool VEC, bool NT>
+__device__ inline int draw_token(SeqRows& s, float u, const float* ts, int ntiles, int groups) {
+    const TileRuns tr = tile_runs(ts, ntiles);
+    const double S = lane63_f64(tr.inc);
+    if (S > 0.0) {
+        const double tau = static_cast<double>(u) * S;
+        double P;
+        const int tile = locate_tile(ts, tr, tau, &P);
+        return scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
+    }
+    // Empty residual (possible only through rounding when p and q agree to
+    // within fp32): draw from p at the same position instead. Slow path:
+    // this wavefront streams the row twice.
+    s.p_only = true;
+    double sp = 0.0;
+    for (int t = 0; t < ntiles; ++t)
+        sp += tile_sum_of<DT, VEC, NT>(s, t, groups);
+    const double tau = static_cast<double>(u) * sp;
+    double P = 0.0;
+    int tile = -1;
+    for (int t = 0; t < ntiles && tile < 0; ++t) {
+        const double tsum = tile_sum_of<DT, VEC, NT>(s, t, groups);
+        if (tsum > 0.0 && P + tsum > tau)
+            tile = t;
+        else
+            P += tsum;
+    }
+    if (tile < 0) {
+        tile = ntiles - 1;
+        P = -1.0;
+    }
+    return scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
+}
+
+// The draw of one sequence (one wavefront), written to its extra token.
 template <int DT, bool VEC, bool NT>
 __device__ inline void locate_emit(SeqRows& s, const SeqState& st, const float* ts, int ntiles,
                                    int groups, int G, int b, int32_t* out_tok) {
-    const int lane = threadIdx.x & 63;
-    const TileRuns tr = tile_runs(ts, ntiles);
-    const double S = lane63_f64(tr.inc);
-
-    int token;
-    if (S > 0.0) {
-        const double tau = static_cast<double>(st.u_res) * S;
-        double P;
-        const int tile = locate_tile(ts, tr, tau, &P);
-        token = scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
-    } else {
-        // Empty residual (possible only through rounding when p and q agree to
-        // within fp32): draw from p at the same position instead. Slow path:
-        // this wavefront streams the row twice.
-        s.p_only = true;
-        double sp = 0.0;
-        for (int t = 0; t < ntiles; ++t)
-            sp += tile_sum_of<DT, VEC, NT>(s, t, groups);
-        const double tau = static_cast<double>(st.u_res) * sp;
-        double P = 0.0;
-        int tile = -1;
-        for (int t = 0; t < ntiles && tile < 0; ++t) {
-            const double tsum = tile_sum_of<DT, VEC, NT>(s, t, groups);
-            if (tsum > 0.0 && P + tsum > tau)
-                tile = t;
-            else
-                P += tsum;
-        }
-        if (tile < 0) {
-            tile = ntiles - 1;
-            P = -1.0;
-        }
-        token = scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
-    }
-    if (lane == 0)
+    const int token = draw_token<DT, VEC, NT>(s, st.u_res, ts, ntiles, groups);
+    if ((threadIdx.x & 63) == 0)
         out_tok[static_cast<size_t>(b) * (G + 1) + st.k] = token;
 }
 
@@ -514,6 +518,401 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
     locate_emit<DT, VEC, NT>(s, st, lds_ts, ntiles, groups, gamma, b, out_tok);
 }
 
+// ----------------------------------------------- sampled draft trees ---
+//
+// Multi-step speculative sampling over a draft tree (SpecInfer, ASPLOS 2024,
+// stochastic tree verification, with one draft distribution per node): one
+// 1024-thread workgroup per tree walks it from the root. At node u the target
+// is pi = (p_u - c q_u)^+ / Z: c = 0, Z = 1 on arrival, and after a rejection
+// c <- c + Z, Z <- sum_v (p_u - c q_u)^+, which is norm(max(0, pi - q_u))
+// written in closed form. Each step that needs a whole row is one pass of the
+// workgroup over it:
+//   * arrival at u: (m, s) of target row u, and of draft row u before its
+//     first child is tried (the row kernel's online base-2 form);
+//   * a rejection: the tile sums of r' = max(0, fma(p', s_q / (c s_p), -q'))
+//     (the residual draw's arithmetic, r' = (s_q / c) (p - c q)^+), whose total
+//     gives Z;
+//   * the end: the same tile sums (p' alone when c = 0) and the residual
+//     draw's inversion with the uniform of block (L, b), word 1.
+// The accept test of child s is the verifier's, in fp64: log u < log pi(t) -
+// log q(t) with u from block (s - 1, b), word 0, and log pi(t) = x_p(t) -
+// lse_p while c = 0. At T = 0 the walk follows the raw-logit argmax instead.
+constexpr int kTreeBlock = 1024;
+constexpr int kTreeWaves = kTreeBlock / 64;
+
+struct TreeSampleArgs {
+    const int32_t* parent;
+    const int32_t* token;
+    const int32_t* n_nodes;
+    const void* draft;
+    const void* target;
+    const float* temperature;
+    int M, V;
+    uint64_t seed, offset;
+    int32_t* out_length;
+    int32_t* out_path;
+    int32_t* out_extra;
+};
+
+struct TreeShared {
+    int parent[256];
+    int token[256];
+    int path[256];
+    float red_f[kTreeWaves];
+    double red_d[kTreeWaves];
+    int red_i[kTreeWaves];
+    int flag;
+    int decision;
+};
+
+// Block-wide reductions of the tree workgroup (every thread gets the result).
+__device__ inline float tree_block_max(float v, TreeShared& sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, 64));
+    __syncthreads();
+    if (lane == 0)
+        sh.red_f[w] = v;
+    __syncthreads();
+    float m = sh.red_f[0];
+#pragma unroll
+    for (int i = 1; i < kTreeWaves; ++i)
+        m = fmaxf(m, sh.red_f[i]);
+    return m;
+}
+
+// Sum in a fixed order: lanes by a butterfly, then the wavefronts in order.
+__device__ inline double tree_block_sum(double v, TreeShared& sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    __syncthreads();
+    if (lane == 0)
+        sh.red_d[w] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < kTreeWaves; ++i)
+        t += sh.red_d[i];
+    return t;
+}
+
+// Largest raw logit, lowest index on ties.
+__device__ inline int tree_block_argmax(float v, int i, TreeShared& sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(v, off, 64);
+        const int oi = __shfl_xor(i, off, 64);
+        if (ov > v || (ov == v && oi < i)) {
+            v = ov;
+            i = oi;
+        }
+    }
+    __syncthreads();
+    if (lane == 0) {
+        sh.red_f[w] = v;
+        sh.red_i[w] = i;
+    }
+    __syncthreads();
+    float bv = sh.red_f[0];
+    int bi = sh.red_i[0];
+    for (int k = 1; k < kTreeWaves; ++k) {
+        if (sh.red_f[k] > bv || (sh.red_f[k] == bv && sh.red_i[k] < bi)) {
+            bv = sh.red_f[k];
+            bi = sh.red_i[k];
+        }
+    }
+    return bv > -__builtin_huge_valf() ? bi : -1;
+}
+
+// One pass over a row: groups of 64-group tiles w, w + 16, ... per wavefront,
+// two loads in flight (clamped into the row), f(group index, values).
+template <int DT, bool VEC, bool NT, class F>
+__device__ inline void tree_stream_row(const void* row, int groups, F&& f) {
+    using Ld = Loader<DT, VEC>;
+    constexpr int W = Ld::W;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int ntiles = (groups + kTile - 1) / kTile;
+    auto gi = [&](int t) { return t * kTile + lane; };
+    auto clampg = [&](int g) { return g < groups ? g : 0; };
+    int t = wid;
+    typename Ld::raw_t a = Ld::template load_as<NT>(row, clampg(gi(t)));
+    const int nb = t < ntiles ? (ntiles - t + kTreeWaves - 1) / kTreeWaves : 0;
+    for (int k = 0; k < nb; ++k) {
+        const typename Ld::raw_t cur = a;
+        a = Ld::template load_as<NT>(row, clampg(gi(t + kTreeWaves)));
+        const int g = gi(t);
+        if (g < groups) {
+            float z[W];
+            Ld::unpack(cur, z);
+            f(g, z);
+        }
+        t += kTreeWaves;
+    }
+}
+
+// (m, s) of one row in the row kernel's base-2 form, m = fl32(max x * log2e),
+// s = sum 2^(fma(x, log2e, -m)): per thread online, then merged.
+template <int DT, bool VEC, bool NT>
+__device__ inline void tree_row_norm(const void* row, int groups, float inv_t, TreeShared& sh,
+                                     float* m_out, double* s_out) {
+    constexpr int W = Group<DT, VEC>::W;
+    float m = kNegMax;
+    double sacc = 0.0;
+    tree_stream_row<DT, VEC, NT>(row, groups, [&](int, const float (&z)[W]) {
+        float x[W];
+        float gm = -__builtin_huge_valf();
+#pragma unroll
+        for (int e = 0; e < W; ++e) {
+            x[e] = scale_logit(z[e], inv_t);
+            gm = fmaxf(gm, x[e]);
+        }
+        const float mn = gm * kLog2e;
+        if (mn > m) {
+            sacc *= static_cast<double>(fast_exp2(m - mn));
+            m = mn;
+        }
+        float g = 0.0f;
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            g += fast_exp2(__builtin_fmaf(x[e], kLog2e, -m));
+        sacc += static_cast<double>(g);
+    });
+    const float M = tree_block_max(m, sh);
+    const double f = m == M ? 1.0 : static_cast<double>(fast_exp2(m - M));
+    *m_out = M;
+    *s_out = tree_block_sum(sacc > 0.0 ? sacc * f : 0.0, sh);
+}
+
+template <int DT, bool VEC, bool NT>
+__device__ inline int tree_row_argmax(const void* row, int groups, TreeShared& sh) {
+    constexpr int W = Group<DT, VEC>::W;
+    float bv = -__builtin_huge_valf();
+    int bi = 0x7fffffff;
+    tree_stream_row<DT, VEC, NT>(row, groups, [&](int g, const float (&z)[W]) {
+#pragma unroll
+        for (int e = 0; e < W; ++e)
+            if (z[e] > bv) {
+                bv = z[e];
+                bi = g * W + e;
+            }
+    });
+    return tree_block_argmax(bv, bi, sh);
+}
+
+// Tile sums of the row pair's weights into ts (LDS), as the residual kernels
+// form them, and their fp64 total (every thread).
+template <int DT, bool VEC, bool NT>
+__device__ inline double tree_tile_pass(const SeqRows& s, int ntiles, int groups, float* ts,
+                                        TreeShared& sh) {
+    using IO = GroupIO<DT, VEC, NT>;
+    constexpr int W = IO::W;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    IO a, nxt;
+    int t = wid;
+    auto load = [&](IO& io, int tt) {
+        const int g = tt * kTile + lane;
+        io.load(s, tt < ntiles && g < groups ? g : 0);
+    };
+    load(a, t);
+    const int nb = t < ntiles ? (ntiles - t + kTreeWaves - 1) / kTreeWaves : 0;
+    for (int k = 0; k < nb; ++k) {
+        load(nxt, t + kTreeWaves);
+        const int g = t * kTile + lane;
+        float gs = 0.0f;
+        if (g < groups) {
+            float r[W];
+            a.residual(s, r);
+            gs = pairwise(r);
+        }
+        const float tsum = tile_reduce(gs);
+        if (lane == 0)
+            ts[t] = tsum;
+        a = nxt;
+        t += kTreeWaves;
+    }
+    __syncthreads();
+    double part = 0.0;
+    for (int i = threadIdx.x; i < ntiles; i += kTreeBlock)
+        part += static_cast<double>(ts[i]);
+    return tree_block_sum(part, sh);
+}
+
+template <int DT, bool VEC, bool NT>
+__global__ __launch_bounds__(kTreeBlock) void tree_sample_kernel(TreeSampleArgs a) {
+    constexpr int W = Group<DT, VEC>::W;
+    extern __shared__ float lds_ts[];
+    __shared__ TreeShared sh;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int M = a.M, V = a.V;
+    const int groups = V / W;
+    const int ntiles = (groups + kTile - 1) / kTile;
+    const int n = a.n_nodes[b];
+    int32_t* path_out = a.out_path + static_cast<size_t>(b) * M;
+
+    // Structure, tokens and temperature.
+    if (tid == 0)
+        sh.flag = 0;
+    __syncthreads();
+    const bool n_ok = n >= 1 && n <= M;
+    if (n_ok && tid < n) {
+        const int pr = a.parent[static_cast<size_t>(b) * M + tid];
+        const int tk = a.token[static_cast<size_t>(b) * M + tid];
+        sh.parent[tid] = pr;
+        sh.token[tid] = tk;
+        const bool ok = tid == 0 ? pr == -1 : (pr >= 0 && pr < tid && tk >= 0 && tk < V);
+        if (!ok)
+            atomicOr(&sh.flag, 1);
+    }
+    float inv_t = 0.0f;
+    const int mode = temperature_mode(a.temperature[b], &inv_t);
+    __syncthreads();
+    bool bad = !n_ok || sh.flag != 0 || mode < 0;
+
+    const size_t row_base = static_cast<size_t>(b) * M;
+    auto prow = [&](int u) { return row_ptr(a.target, DT, row_base + u, V); };
+    auto qrow = [&](int u) { return row_ptr(a.draft, DT, row_base + u, V); };
+    auto xval = [&](const void* row, int t) { return scale_logit(load_logit(row, DT, t), inv_t); };
+    int u = 0, L = 0, extra = -1;
+    if (!bad && mode == 0) {
+        // T = 0: step to the lowest-index child holding the target argmax.
+        for (;;) {
+            const int am = tree_row_argmax<DT, VEC, NT>(prow(u), groups, sh);
+            if (am < 0) {
+                bad = true;
+                break;
+            }
+            int next = -1;
+            for (int s = 1; s < n; ++s)
+                if (sh.parent[s] == u && sh.token[s] == am) {
+                    next = s;
+                    break;
+                }
+            if (next < 0) {
+                extra = am;
+                break;
+            }
+            if (tid == 0)
+                sh.path[L] = next;
+            ++L;
+            u = next;
+        }
+    } else if (!bad) {
+        float mp = 0.0f, mq = 0.0f;
+        double sp = 0.0, sq = 0.0;
+        tree_row_norm<DT, VEC, NT>(prow(u), groups, inv_t, sh, &mp, &sp);
+        bad = !(sp > 0.0);
+        double c = 0.0, Z = 1.0;
+        bool have_q = false;
+        bool ts_current = false;  // lds_ts holds the tile sums of the current (c, Z)
+        int s = 1;
+        while (!bad) {
+            while (s < n && sh.parent[s] != u)
+                ++s;
+            if (s >= n)
+                break;  // no child left to try at u
+            if (!have_q) {
+                tree_row_norm<DT, VEC, NT>(qrow(u), groups, inv_t, sh, &mq, &sq);
+                if (!(sq > 0.0)) {
+                    bad = true;
+                    break;
+                }
+                have_q = true;
+            }
+            // The accept test of child s, in fp64 (every thread computes it).
+            const int t = sh.token[s];
+            const double lse_p = (static_cast<double>(mp) + log2(sp)) / static_cast<double>(kLog2e);
+            const double lse_q = (static_cast<double>(mq) + log2(sq)) / static_cast<double>(kLog2e);
+            const double lp = static_cast<double>(xval(prow(u), t)) - lse_p;
+            const double lq = static_cast<double>(xval(qrow(u), t)) - lse_q;
+            double lpi = lp;
+            if (c > 0.0) {
+                const double d = exp(lp) - c * exp(lq);
+                lpi = d > 0.0 ? log(d) - log(Z) : -__builtin_huge_val();
+            }
+            const Words4 w = verify_block(a.seed, a.offset, static_cast<uint32_t>(b),
+                                          static_cast<uint32_t>(s - 1));
+            const double log_u = log(static_cast<double>(uniform24(w.w0)));
+            if (log_u < lpi - lq) {
+                if (tid == 0)
+                    sh.path[L] = s;
+                ++L;
+                u = s;
+                s = 1;
+                c = 0.0;
+                Z = 1.0;
+                have_q = false;
+                ts_current = false;
+                tree_row_norm<DT, VEC, NT>(prow(u), groups, inv_t, sh, &mp, &sp);
+                bad = !(sp > 0.0);
+                continue;
+            }
+            // Rejected: the residual against q_u, in closed form.
+            const double c2 = c + Z;
+            SeqRows rows;
+            rows.prow = prow(u);
+            rows.qrow = qrow(u);
+            rows.p_only = false;
+            rows.inv_t = inv_t;
+            rows.mp = mp;
+            rows.mq = mq;
+            rows.ratio = static_cast<float>(sq / (c2 * sp));
+            const double tot = tree_tile_pass<DT, VEC, NT>(rows, ntiles, groups, lds_ts, sh);
+            const double Z2 = c2 / sq * tot;
+            if (Z2 > 0.0) {
+                c = c2;
+                Z = Z2;
+                ts_current = true;
+            } else {
+                ts_current = false;  // an empty residual (rounding): pi stays
+            }
+            ++s;
+        }
+        if (!bad) {
+            SeqRows rows;
+            rows.prow = prow(u);
+            rows.qrow = c > 0.0 ? qrow(u) : prow(u);
+            rows.p_only = !(c > 0.0);
+            rows.inv_t = inv_t;
+            rows.mp = mp;
+            rows.mq = mq;
+            rows.ratio = c > 0.0 ? static_cast<float>(sq / (c * sp)) : 1.0f;
+            if (!ts_current)
+                tree_tile_pass<DT, VEC, NT>(rows, ntiles, groups, lds_ts, sh);
+            const Words4 w = verify_block(a.seed, a.offset, static_cast<uint32_t>(b),
+                                          static_cast<uint32_t>(L));
+            if (tid < 64) {
+                const int tok = draw_token<DT, VEC, NT>(rows, uniform24(w.w1), lds_ts, ntiles, groups);
+                if (tid == 0)
+                    sh.decision = tok;
+            }
+            __syncthreads();
+            extra = sh.decision;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < M; i += kTreeBlock)
+        path_out[i] = !bad && i < L ? sh.path[i] : -1;
+    if (tid == 0) {
+        a.out_length[b] = bad ? -1 : L;
+        a.out_extra[b] = bad ? -1 : extra;
+    }
+}
+
+template <int DT, bool VEC>
+hipError_t launch_tree_sample_typed(int batch, const TreeSampleArgs& args, hipStream_t stream) {
+    constexpr bool NT = VEC;
+    constexpr int W = Group<DT, VEC>::W;
+    const int ntiles = (args.V / W + kTile - 1) / kTile;
+    tree_sample_kernel<DT, VEC, NT><<<dim3(static_cast<unsigned>(batch)), dim3(kTreeBlock),
+                                       static_cast<size_t>(ntiles) * sizeof(float), stream>>>(args);
+    return hipGetLastError();
+}
+
 template <int DT, bool VEC, int U>
 hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const void* draft,
                         const void* target, const SeqState* seq, float* tile_sums,
@@ -560,6 +959,22 @@ hipError_t launch_unroll(const Shape& sh, int nsplit, int unroll, int tiles_per_
 }  // namespace
 
 int residual_tiles_per_row(int vocab) { return (vocab + kTile - 1) / kTile; }
+
+hipError_t launch_tree_sample(int batch, int max_nodes, int vocab, int dtype, bool vec,
+                              const int32_t* parent, const int32_t* token, const int32_t* n_nodes,
+                              const void* draft, const void* target, const float* temperature,
+                              uint64_t seed, uint64_t offset, int32_t* out_length,
+                              int32_t* out_path, int32_t* out_extra, hipStream_t stream) {
+    if (batch == 0)
+        return hipSuccess;
+    const TreeSampleArgs args{parent, token, n_nodes, draft, target, temperature, max_nodes,
+                              vocab, seed, offset, out_length, out_path, out_extra};
+    if (dtype == kBF16)
+        return vec ? launch_tree_sample_typed<kBF16, true>(batch, args, stream)
+                   : launch_tree_sample_typed<kBF16, false>(batch, args, stream);
+    return vec ? launch_tree_sample_typed<kF32, true>(batch, args, stream)
+               : launch_tree_sample_typed<kF32, false>(batch, args, stream);
+}
 
 int residual_fused_max_tiles() { return kResidualFusedMaxTiles; }
 

@@ -355,6 +355,26 @@ int spec_tree_verify_greedy(spec_tree_ctx* ctx, const int32_t* parent, const int
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
+int spec_tree_verify_sample(spec_tree_ctx* ctx, const int32_t* parent, const int32_t* token,
+                            const int32_t* n_nodes, const void* draft, const void* target,
+                            const float* temperature, uint64_t seed, uint64_t offset,
+                            int32_t* out_length, int32_t* out_path, int32_t* out_extra) {
+    if (!ctx || !parent || !token || !n_nodes || !draft || !target || !temperature ||
+        !out_length || !out_path || !out_extra)
+        return SPEC_EINVAL;
+    const size_t esz = ctx->dtype == SPEC_BF16 ? 2 : 4;
+    if (!aligned(parent, 4) || !aligned(token, 4) || !aligned(n_nodes, 4) || !aligned(draft, esz) ||
+        !aligned(target, esz) || !aligned(temperature, 4) || !aligned(out_length, 4) ||
+        !aligned(out_path, 4) || !aligned(out_extra, 4))
+        return SPEC_EINVAL;
+    const int W = ctx->dtype == SPEC_BF16 ? 8 : 4;
+    const bool vec = ctx->V % W == 0 && aligned(draft, 16) && aligned(target, 16);
+    const hipError_t e = launch_tree_sample(ctx->B, ctx->M, ctx->V, ctx->dtype, vec, parent, token,
+                                            n_nodes, draft, target, temperature, seed, offset,
+                                            out_length, out_path, out_extra, ctx->stream);
+    return e == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
 int spec_tree_verify_destroy(spec_tree_ctx* ctx) {
     if (!ctx)
         return SPEC_EINVAL;

@@ -25,7 +25,27 @@
  * the result is the accepted nodes, their count, and the extra token a(last).
  * Trees with n_nodes outside [1, M], a parent outside [0, i), a token outside
  * [0, V), or a reached row with no finite logit get length -1, path -1 and
- * extra token -1. The multi-branch rule for T > 0 is not defined here.
+ * extra token -1.
+ *
+ * Sampled verification (T > 0): multi-step speculative sampling (Miao et al.,
+ * SpecInfer, ASPLOS 2024, stochastic tree verification), the published
+ * multi-branch rule that keeps the target's output distribution when the
+ * children of node u are draft tokens drawn independently from q_u. The
+ * pages name tree drafting but give no such rule. Draft row u is q_u, target
+ * row u is p_u (both as the verifier scales them, x = fl32(z * fl32(1/T))).
+ * At node u with current target pi (pi = p_u on arrival), u's children are
+ * tried in increasing node order: child s with token t is accepted iff
+ * log u_acc < log pi(t) - log q_u(t) (fp64), and the walk moves to s;
+ * otherwise pi <- norm(max(0, pi - q_u)) (kept when that mass is zero, which
+ * only rounding produces) and the next child is tried. When u has no child
+ * left, the extra token is drawn from pi by inversion in vocabulary order.
+ * Uniforms: Philox4x32-10 as in spec_verify.h, block (s - 1, b) word 0 for
+ * child s, block (L, b) word 1 for the draw (L accepted nodes), so a chain
+ * (node i + 1 holding draft token i) sees the verifier's uniforms and gives
+ * its outcome. T == 0 trees follow the greedy rule above; invalid
+ * temperatures are sentinels as in spec_verify.h. Outputs as for the greedy
+ * call. Cost: one pass over the two rows of each visited node, one per
+ * rejection, one for the draw, by one 1024-thread workgroup per tree.
  *
  * Layouts: dense row-major DEVICE arrays owned by the caller; int32 indices,
  * float32 logq, float64 scores; target logits [B, M, V] in the dtype of
@@ -69,6 +89,15 @@ int spec_tree_verify_set_stream(spec_tree_ctx* ctx, void* hip_stream);
 int spec_tree_verify_greedy(spec_tree_ctx* ctx, const int32_t* parent, const int32_t* token,
                             const int32_t* n_nodes, const void* target, int32_t* out_length,
                             int32_t* out_path, int32_t* out_extra);
+
+/* draft, target [B, M, V] in the context's dtype (draft row u: the
+ * distribution u's children were drawn from), temperature [B] fp32, seed and
+ * offset as in spec_verify.h; other arguments and outputs as for
+ * spec_tree_verify_greedy. No workspace. */
+int spec_tree_verify_sample(spec_tree_ctx* ctx, const int32_t* parent, const int32_t* token,
+                            const int32_t* n_nodes, const void* draft, const void* target,
+                            const float* temperature, uint64_t seed, uint64_t offset,
+                            int32_t* out_length, int32_t* out_path, int32_t* out_extra);
 
 int spec_tree_verify_destroy(spec_tree_ctx* ctx);
 

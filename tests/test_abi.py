@@ -117,6 +117,8 @@ def test_tree_host_argument_checks(lib):
     assert lib.spec_tree_verify_init(2, 8, 100, 5, None, ctypes.byref(h)) == E
     assert not h.value
     assert lib.spec_tree_verify_greedy(None, None, None, None, None, None, None, None) == E
+    assert lib.spec_tree_verify_sample(None, None, None, None, None, None, None, 0, 0, None, None,
+                                       None) == E
     assert lib.spec_tree_verify_destroy(None) == E
 
 

@@ -121,3 +121,121 @@ def test_greedy_tree_sentinels_and_no_finite_row():
     for key in ("length", "path", "extra"):
         assert np.array_equal(g[key], o[key]), key
     assert o["length"].tolist()[1:] == [-1, -1, -1, -1]
+
+
+# ------------------------------------------------- sampled verification ---
+#
+# Match rule: lengths, paths and extra tokens exact, except a tree whose
+# oracle takes an accept decision or the draw with a log-margin below 1e-5
+# (the verifier's rule), which is counted as flagged. Sentinels and T = 0
+# trees are exact.
+
+MARGIN = 1e-5
+
+
+def to_dev_logits(x, dtype):
+    if dtype == torch.bfloat16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return dev(x)
+
+
+def gpu_sample(parent, token, n_nodes, draft, target, temperature, dtype, seed=0, offset=0):
+    B, M = parent.shape
+    V = target.shape[-1]
+    ctx = sv.spec_tree_verify_init(B, M, V, dtype)
+    L = torch.empty(B, dtype=torch.int32, device="cuda")
+    path = torch.empty((B, M), dtype=torch.int32, device="cuda")
+    extra = torch.empty(B, dtype=torch.int32, device="cuda")
+    sv.spec_tree_verify_sample(ctx, dev(parent), dev(token), dev(n_nodes),
+                               to_dev_logits(draft, dtype), to_dev_logits(target, dtype),
+                               dev(np.asarray(temperature, np.float32)), seed, offset, L, path, extra)
+    torch.cuda.synchronize()
+    return dict(length=L.cpu().numpy(), path=path.cpu().numpy(), extra=extra.cpu().numpy())
+
+
+def check_sample(g, o, temperature, rows=None):
+    rows = np.arange(len(o["length"])) if rows is None else np.asarray(rows)
+    flagged = 0
+    for n, b in enumerate(rows):
+        near = o["length"][n] >= 0 and temperature[n] > 0 and (
+            o["acc_margin"][n] < MARGIN or o["res_margin"][n] < MARGIN)
+        same = (g["length"][b] == o["length"][n] and g["extra"][b] == o["extra"][n]
+                and np.array_equal(g["path"][b], o["path"][n]))
+        if near:
+            flagged += 1
+            continue
+        assert same, (b, g["length"][b], o["length"][n], g["extra"][b], o["extra"][n],
+                      g["path"][b][:6], o["path"][n][:6])
+    return flagged
+
+
+@pytest.mark.parametrize("cfg,over", [(1, dict()), (2, dict()), (3, dict(batch=6, vocab=4096)),
+                                      (4, dict(batch=40, vocab=3000)), (5, dict(batch=20, vocab=2048))])
+def test_sample_chains(cfg, over):
+    """Chain trees built from the verification workloads (node i + 1 holds draft
+    token i), including greedy and sentinel sequences."""
+    rec = specgen.config(cfg).replace(**over)
+    d = specgen.generate(rec)
+    zq, zt = d["logits_draft"], d["logits_target"]
+    B, G1, V = zt.shape
+    par = np.tile(np.arange(-1, G1 - 1, dtype=np.int32), (B, 1))
+    tok = np.zeros((B, G1), np.int32)
+    tok[:, 1:] = d["draft_tokens"]
+    q = np.zeros((B, G1, V), zq.dtype)
+    q[:, :G1 - 1] = zq
+    n = np.full(B, G1, np.int32)
+    dt = torch.bfloat16 if rec.dtype == "bf16" else torch.float32
+    print(f"\n[tree sample chains {rec.name} {over}]", flush=True)
+    for offset in (0, 5):
+        g = gpu_sample(par, tok, n, q, zt, d["temperature"], dt, seed=3, offset=offset)
+        o = oracle.tree_verify_sample(par, tok, n, q, zt, d["temperature"], seed=3, offset=offset)
+        f = check_sample(g, o, d["temperature"])
+        print(f"  offset {offset}: flagged {f}/{B}, mean length {g['length'].mean():.2f}", flush=True)
+
+
+@pytest.mark.parametrize("B,M,V,dt", [(16, 12, 1000, "f32"), (32, 20, 4099, "bf16"),
+                                      (8, 64, 32000, "bf16"), (4, 256, 777, "f32")])
+def test_sample_random_trees(B, M, V, dt):
+    trees = specgen.draft_trees(B, M, V, seed=M + V)
+    zt = specgen.tree_target_logits(trees, V, seed=1, dtype=dt)
+    zq = specgen.tree_target_logits(trees, V, seed=2, dtype=dt)
+    rng = np.random.default_rng(B + M)
+    temp = rng.uniform(0.3, 1.5, B).astype(np.float32)
+    temp[::5] = 0.0                                   # some greedy trees
+    n = np.full(B, M, np.int32)
+    n[1::4] = np.maximum(1, M // 2)
+    par, tok = trees["parent"].copy(), trees["token"].copy()
+    if B >= 8:
+        temp[2] = -1.0                                # sentinel temperature
+        tok[3, M - 1] = V                             # token out of range
+    torch_dt = torch.bfloat16 if dt == "bf16" else torch.float32
+    print(f"\n[tree sample B={B} M={M} V={V} {dt}]", flush=True)
+    g = gpu_sample(par, tok, n, zq, zt, temp, torch_dt, seed=9, offset=1)
+    o = oracle.tree_verify_sample(par, tok, n, zq, zt, temp, seed=9, offset=1)
+    f = check_sample(g, o, temp)
+    if B >= 8:
+        assert g["length"][2] == -1 and g["length"][3] == -1
+    print(f"  flagged {f}/{B}, lengths {g['length'].tolist()[:12]}", flush=True)
+    assert (o["length"] >= 1).any()
+
+
+def test_sample_full_workload_sampled():
+    """B = 256 trees of 16 nodes over V = 152064 bf16, temperatures drawn as in
+    the B=256 workload (U[0.3, 1.5], 10 % greedy); the oracle on 12 trees
+    (Philox indices kept)."""
+    B, M, V = 256, 16, 152064
+    trees = specgen.draft_trees(B, M, V, seed=31)
+    zt = specgen.tree_target_logits(trees, V, seed=5)
+    zq = specgen.tree_target_logits(trees, V, seed=6)
+    rng = np.random.default_rng(7)
+    temp = rng.uniform(0.3, 1.5, B).astype(np.float32)   # the workload's temperature recipe
+    temp[rng.random(B) < 0.1] = 0.0
+    n = np.full(B, M, np.int32)
+    print(f"\n[tree sample B={B} M={M} V={V}]", flush=True)
+    g = gpu_sample(trees["parent"], trees["token"], n, zq, zt, temp, torch.bfloat16, seed=2, offset=4)
+    rows = np.array([0, 1, 17, 64, 100, 128, 150, 199, 200, 230, 254, 255])
+    o = oracle.tree_verify_sample(trees["parent"][rows], trees["token"][rows], n[rows], zq[rows],
+                                  zt[rows], temp[rows], seed=2, offset=4, seq_ids=rows)
+    f = check_sample(g, o, temp[rows], rows=rows)
+    print(f"  flagged {f}/{rows.size}; GPU mean length {g['length'].mean():.2f}", flush=True)
+    assert (g["length"] >= 0).all()
