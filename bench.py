@@ -91,6 +91,34 @@ def cpu_baseline(rec, d, budget_s: float = 10.0, cap_s: float = 30.0) -> dict:
             "host_cpu": host_cpu_model(), "nproc": os.cpu_count()}
 
 
+def tree_sample_bytes(parent, M, length, path, temperature, row_bytes) -> int:
+    """Rows one sampled tree walk must read, from its outcome: at each visited
+    node the target row (its normaliser, or the argmax at T = 0) and, when it
+    has children, the draft row; two rows per rejected child (children are
+    tried in node order, so those before the accepted one, and all of the
+    last node's); one more row for the final draw when nothing was rejected at
+    the last node (a rejection leaves that draw's tile sums ready)."""
+    total = 0
+    for b in range(parent.shape[0]):
+        L = int(length[b])
+        if L < 0:
+            continue
+        nodes = [0] + [int(x) for x in path[b, :L]]
+        for i, u in enumerate(nodes):
+            kids = [s for s in range(1, M) if parent[b, s] == u]
+            total += row_bytes
+            if temperature[b] == 0:
+                continue
+            if kids:
+                total += row_bytes
+            nxt = nodes[i + 1] if i + 1 < len(nodes) else None
+            rejected = [s for s in kids if nxt is None or s < nxt]
+            total += 2 * row_bytes * len(rejected)
+            if nxt is None and not rejected:
+                total += row_bytes
+    return total
+
+
 def host_cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -135,6 +163,13 @@ def cpu_next_rows(rec, d, host: dict, F: int) -> dict:
         res["tree_prune"] = {"us_per_call": round(dt * 1e6, 1),
                              "sample": f"{pr['parent'].shape[0]} trees of {pr['parent'].shape[1]} nodes"}
         vt, nt = tr["verify"], tr["target"].shape[0]
+        if "draft" in tr:
+            temp4 = d["temperature"][:nt]
+            dt_s = timed(lambda: oracle.tree_verify_sample(vt["parent"][:nt], vt["token"][:nt],
+                                                           np.full(nt, tr["n"], np.int32),
+                                                           tr["draft"], tr["target"], temp4))
+            res["tree_sample"] = {"us_per_tree": round(dt_s / nt * 1e6, 1),
+                                  "sample": f"{nt} trees of {tr['n']} nodes, sampled rule"}
         n_nodes = np.full(nt, tr["n"], np.int32)
         dt = timed(lambda: oracle.tree_verify_greedy(vt["parent"][:nt], vt["token"][:nt], n_nodes,
                                                      tr["target"]))
@@ -464,10 +499,29 @@ def main() -> int:
     torch.cuda.synchronize()
     tree_ms = start.elapsed_time(end) / args.steps
     tree_bytes = B * tm * V * 2
+    # Sampled verification of the same trees (multi-step speculative
+    # sampling) at the workload's temperatures, with random bf16 draft rows.
+    v_q = (torch.randn(B, tm, V, device=dev, generator=gen) * 2.5).to(torch.bfloat16)
+    for i in range(args.warmup):
+        sv.spec_tree_verify_sample(tctx, v_par, v_tok, v_n, v_q, v_tgt, temp, 0, i, v_len, v_path,
+                                   v_extra)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        sv.spec_tree_verify_sample(tctx, v_par, v_tok, v_n, v_q, v_tgt, temp, 0, args.warmup + i,
+                                   v_len, v_path, v_extra)
+    end.record(stream)
+    torch.cuda.synchronize()
+    tree_s_ms = start.elapsed_time(end) / args.steps
+    tree_s_bytes = tree_sample_bytes(tv["parent"], tm, v_len.cpu().numpy(), v_path.cpu().numpy(),
+                                     d["temperature"], V * 2)
+    host_tree_draft = v_q[:4].view(torch.int16).cpu().numpy().view(np.uint16)
+    del v_q
     sv.spec_tree_verify_destroy(tctx)
     if not args.no_cpu_baseline:
         host["tree"] = dict(prune=tp, verify=tv, n=tm,
-                            target=v_tgt[:4].view(torch.int16).cpu().numpy().view(np.uint16))
+                            target=v_tgt[:4].view(torch.int16).cpu().numpy().view(np.uint16),
+                            draft=host_tree_draft)
     del v_tgt
     k1_gbs = k1_bytes / (k1_ms * 1e-3) / 1e9
     k3_gbs = k3_bytes / (k3_ms * 1e-3) / 1e9
@@ -516,7 +570,10 @@ def main() -> int:
         "tree": {"prune_nodes": 64, "prune_us": round(prune_us, 2), "verify_nodes": tm,
                  "verify_us": round(tree_ms * 1e3, 2), "verify_bytes": int(tree_bytes),
                  "verify_gbs": round(tree_bytes / (tree_ms * 1e-3) / 1e9, 1),
-                 "verify_frac": round(tree_bytes / (tree_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                 "verify_frac": round(tree_bytes / (tree_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "sample_us": round(tree_s_ms * 1e3, 2),
+                 "sample_bytes_last_call": int(tree_s_bytes),
+                 "sample_gbs": round(tree_s_bytes / (tree_s_ms * 1e-3) / 1e9, 1)},
         "lowrank_head": {"rows": B, "hidden": hd, "rank": hr, "vocab": V,
                          "us_per_call": round(head_ms * 1e3, 2), "bytes": int(head_bytes),
                          "gbs": round(head_bytes / (head_ms * 1e-3) / 1e9, 1),
