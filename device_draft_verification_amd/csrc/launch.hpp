@@ -61,13 +61,22 @@ hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, con
                            const void* target, const SeqState* seq, float* tile_sums,
                            int32_t* out_tok, hipStream_t stream);
 
-// Sampled verification of draft trees (spec_tree.h): one 1024-thread
-// workgroup per tree, dynamic LDS for the tile sums of one row.
+// Sampled verification of draft trees (spec_tree.h): each tree split over
+// tree_sample_parts() workgroups, n_groups trees at a time (at most
+// tree_sample_max_groups, which the device holds at once). shares holds
+// n_groups * tree_sample_group_bytes() bytes, zeroed once before the first
+// call; call numbers start at 1 and increase by one per launch on the same
+// workspace.
+int tree_sample_parts();
+size_t tree_sample_group_bytes();
+hipError_t tree_sample_max_groups(int dtype, int* out_groups);
+bool tree_sample_fits(int vocab, int dtype);
 hipError_t launch_tree_sample(int batch, int max_nodes, int vocab, int dtype, bool vec,
                               const int32_t* parent, const int32_t* token, const int32_t* n_nodes,
                               const void* draft, const void* target, const float* temperature,
                               uint64_t seed, uint64_t offset, int32_t* out_length,
-                              int32_t* out_path, int32_t* out_extra, hipStream_t stream);
+                              int32_t* out_path, int32_t* out_extra, uint64_t* shares,
+                              int n_groups, uint64_t call, hipStream_t stream);
 
 // Scalar-only accept on gathered log-probability pairs.
 hipError_t launch_accept_scalar(int batch, int gamma, const float* logprobs, uint64_t seed,

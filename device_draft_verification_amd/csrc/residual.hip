@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kTile = 64;  // groups per tile = lanes per wavefront
 constexpr int kResidualFusedMaxTiles = 16384;  // LDS tile sums of the fused kernel (64 KiB)
+constexpr size_t kTreeLdsBytes = 16384;       // LDS tile sums of one part of a tree (4096 tiles)
 
 // The one or two rows of a sequence at its first rejection.
 struct SeqRows {
@@ -376,6 +377,18 @@ __device__ inline double tile_sum_of(const SeqRows& s, int t, int groups) {
 // the token inside it; the empty-residual fallback streams p at the same
 // position. Every lane returns the token.
 template <int DT, bool VEC, bool NT>
+__device__ inline int draw_p_fallback(SeqRows& s, float u, int ntiles, int groups);
+
+// The token at position tau of the weights whose tile sums are ts.
+template <int DT, bool VEC, bool NT>
+__device__ inline int draw_at(const SeqRows& s, double tau, const float* ts, int ntiles, int groups) {
+    const TileRuns tr = tile_runs(ts, ntiles);
+    double P;
+    const int tile = locate_tile(ts, tr, tau, &P);
+    return scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
+}
+
+template <int DT, bool VEC, bool NT>
 __device__ inline int draw_token(SeqRows& s, float u, const float* ts, int ntiles, int groups) {
     const TileRuns tr = tile_runs(ts, ntiles);
     const double S = lane63_f64(tr.inc);
@@ -385,9 +398,14 @@ __device__ inline int draw_token(SeqRows& s, float u, const float* ts, int ntile
         const int tile = locate_tile(ts, tr, tau, &P);
         return scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
     }
-    // Empty residual (possible only through rounding when p and q agree to
-    // within fp32): draw from p at the same position instead. Slow path:
-    // this wavefront streams the row twice.
+    return draw_p_fallback<DT, VEC, NT>(s, u, ntiles, groups);
+}
+
+// Empty residual (possible only through rounding when p and q agree to within
+// fp32): draw from p at the same position instead. Slow path: the wavefront
+// streams the row twice.
+template <int DT, bool VEC, bool NT>
+__device__ inline int draw_p_fallback(SeqRows& s, float u, int ntiles, int groups) {
     s.p_only = true;
     double sp = 0.0;
     for (int t = 0; t < ntiles; ++t)
@@ -537,8 +555,62 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
 // The accept test of child s is the verifier's, in fp64: log u < log pi(t) -
 // log q(t) with u from block (s - 1, b), word 0, and log pi(t) = x_p(t) -
 // lse_p while c = 0. At T = 0 the walk follows the raw-logit argmax instead.
-constexpr int kTreeBlock = 1024;
+// ---------------------------------------------------------------------------
+// Sampled verification of draft trees (multi-step speculative sampling with
+// one draft distribution per node). The walk through one tree is sequential,
+// and one CU streams a row pair with exp2 on every logit at far below its
+// share of HBM, so a lone long walk would set the time of the whole call.
+// Each tree is therefore split over kTreeParts workgroups that each own a
+// contiguous run of whole tiles of the vocabulary. Every part runs the same
+// walk: after each pass it publishes its share (row maxima and sums, the
+// residual total, the argmax) and reads the other parts' shares; all parts
+// merge them in one fixed order, so they take identical decisions. The part
+// whose run holds the final draw position writes the extra token.
+//
+// Exchange: a share travels as 16-bit pieces, each in a 64-bit word whose
+// upper 48 bits carry the pass's tag, (call << 20) | pass. A part writes its
+// pieces with device-coherent 64-bit stores and polls its partners' pieces
+// with device-coherent loads until every tag matches, so one round trip both
+// signals and delivers. Pieces live in two slots by pass parity (a part
+// cannot run two passes ahead of a partner, so the slot it reads holds either
+// the partner's share of this pass or an older one). A tag from an earlier
+// call can only match after 2^28 calls that left the slot untouched. Release
+// and acquire fences are not used: at device scope they write back and
+// invalidate the whole L2 of an XCD, which a thousand workgroups exchanging
+// at once serialise. The grid never exceeds what the device holds at once, so
+// every part becomes resident; every wait is still bounded: a partner missing
+// for kTreeSpinLimit polls marks the tree invalid, and all parts finish.
+constexpr int kTreeParts = 4;
+constexpr int kTreeBlock = 256;
 constexpr int kTreeWaves = kTreeBlock / 64;
+constexpr int kTreeSpinLimit = 1 << 20;
+
+// One part's share of a pass, six 32-bit words: a norm pass puts the target
+// row's base-2 maximum in word 0 and its sum (fp64) in words 2-3, the draft
+// row's in word 1 and words 4-5; a tile pass its residual total (fp64) in
+// words 2-3; an argmax pass the best raw logit in word 0 and its token in 1.
+struct TreePart {
+    uint32_t w[6];
+};
+constexpr int kShareHalves = 12;  // 16-bit pieces of a share
+
+__device__ inline void part_set_f(TreePart& p, int i, float x) { p.w[i] = __float_as_uint(x); }
+__device__ inline void part_set_d(TreePart& p, int i, double x) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x));
+    p.w[i] = static_cast<uint32_t>(b);
+    p.w[i + 1] = static_cast<uint32_t>(b >> 32);
+}
+__device__ inline float part_f(const TreePart& p, int i) { return __uint_as_float(p.w[i]); }
+__device__ inline double part_d(const TreePart& p, int i) {
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(p.w[i + 1]) << 32) | p.w[i]));
+}
+__device__ inline TreePart part_zero() {
+    TreePart p;
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+        p.w[i] = 0;
+    return p;
+}
 
 struct TreeSampleArgs {
     const int32_t* parent;
@@ -547,11 +619,13 @@ struct TreeSampleArgs {
     const void* draft;
     const void* target;
     const float* temperature;
-    int M, V;
+    int B, M, V;
     uint64_t seed, offset;
     int32_t* out_length;
     int32_t* out_path;
     int32_t* out_extra;
+    uint64_t* shares;  // [groups][2][kTreeParts][kShareHalves] tagged pieces
+    uint64_t call;     // this call's number (>= 1), increasing per call
 };
 
 struct TreeShared {
@@ -561,8 +635,10 @@ struct TreeShared {
     float red_f[kTreeWaves];
     double red_d[kTreeWaves];
     int red_i[kTreeWaves];
+    TreePart xp[kTreeParts];
     int flag;
     int decision;
+    int ok;
 };
 
 // Block-wide reductions of the tree workgroup (every thread gets the result).
@@ -599,8 +675,9 @@ __device__ inline double tree_block_sum(double v, TreeShared& sh) {
     return t;
 }
 
-// Largest raw logit, lowest index on ties.
-__device__ inline int tree_block_argmax(float v, int i, TreeShared& sh) {
+// Largest raw logit, lowest index on ties (index 0x7fffffff when empty).
+__device__ inline void tree_block_argmax(float v, int i, TreeShared& sh, float* bv_out,
+                                         int* bi_out) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -625,44 +702,65 @@ __device__ inline int tree_block_argmax(float v, int i, TreeShared& sh) {
             bi = sh.red_i[k];
         }
     }
-    return bv > -__builtin_huge_valf() ? bi : -1;
+    *bv_out = bv;
+    *bi_out = bi;
 }
 
-// One pass over a row: groups of 64-group tiles w, w + 16, ... per wavefront,
-// two loads in flight (clamped into the row), f(group index, values).
-template <int DT, bool VEC, bool NT, class F>
-__device__ inline void tree_stream_row(const void* row, int groups, F&& f) {
+// One pass over R rows at once: 64-group tiles w, w + kTreeWaves, ... per
+// wavefront, D tiles of every row in flight in a register ring (loads past the
+// end are clamped onto group 0 and never used). f(group index, in range,
+// values of each row) is called by whole wavefronts; lanes past the last
+// group get in range = false (their values are group 0's). groups >= 1.
+template <int DT, bool VEC, bool NT, int R, int D, class F>
+__device__ inline void tree_stream(const void* const (&rows)[R], int groups, F&& f) {
     using Ld = Loader<DT, VEC>;
+    using raw_t = typename Ld::raw_t;
     constexpr int W = Ld::W;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int ntiles = (groups + kTile - 1) / kTile;
-    auto gi = [&](int t) { return t * kTile + lane; };
-    auto clampg = [&](int g) { return g < groups ? g : 0; };
-    int t = wid;
-    typename Ld::raw_t a = Ld::template load_as<NT>(row, clampg(gi(t)));
-    const int nb = t < ntiles ? (ntiles - t + kTreeWaves - 1) / kTreeWaves : 0;
-    for (int k = 0; k < nb; ++k) {
-        const typename Ld::raw_t cur = a;
-        a = Ld::template load_as<NT>(row, clampg(gi(t + kTreeWaves)));
-        const int g = gi(t);
-        if (g < groups) {
-            float z[W];
-            Ld::unpack(cur, z);
-            f(g, z);
+    auto addr = [&](int k) {
+        const int g = (wid + k * kTreeWaves) * kTile + lane;
+        return g < groups ? g : 0;
+    };
+    raw_t buf[D][R];
+    // Issue the first loads in slot order (the waits below count loads in
+    // flight, so a reordered prologue would make the first use wait for all).
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            buf[j][r] = Ld::template load_as<NT>(rows[r], addr(j));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const int nb = wid < ntiles ? (ntiles - wid + kTreeWaves - 1) / kTreeWaves : 0;
+    for (int k = 0; k < nb; k += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            // Use slot j, then refill it: each slot keeps its registers, so
+            // the ring needs no copies (which would wait for every load).
+            const int g = (wid + (k + j) * kTreeWaves) * kTile + lane;
+            if (k + j < nb) {
+                float z[R][W];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    Ld::unpack(buf[j][r], z[r]);
+                f(g, g < groups, z);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                buf[j][r] = Ld::template load_as<NT>(rows[r], addr(k + j + D));
         }
-        t += kTreeWaves;
     }
 }
 
-// (m, s) of one row in the row kernel's base-2 form, m = fl32(max x * log2e),
-// s = sum 2^(fma(x, log2e, -m)): per thread online, then merged.
-template <int DT, bool VEC, bool NT>
-__device__ inline void tree_row_norm(const void* row, int groups, float inv_t, TreeShared& sh,
-                                     float* m_out, double* s_out) {
-    constexpr int W = Group<DT, VEC>::W;
+// Online (m, s) of one row in the row kernel's base-2 form: m = fl32(max x *
+// log2e), s = sum 2^(fma(x, log2e, -m)).
+template <int W>
+struct OnlineNorm {
     float m = kNegMax;
-    double sacc = 0.0;
-    tree_stream_row<DT, VEC, NT>(row, groups, [&](int, const float (&z)[W]) {
+    double s = 0.0;
+
+    __device__ inline void add(const float (&z)[W], float inv_t) {
         float x[W];
         float gm = -__builtin_huge_valf();
 #pragma unroll
@@ -672,244 +770,517 @@ __device__ inline void tree_row_norm(const void* row, int groups, float inv_t, T
         }
         const float mn = gm * kLog2e;
         if (mn > m) {
-            sacc *= static_cast<double>(fast_exp2(m - mn));
+            s *= static_cast<double>(fast_exp2(m - mn));
             m = mn;
         }
         float g = 0.0f;
 #pragma unroll
         for (int e = 0; e < W; ++e)
             g += fast_exp2(__builtin_fmaf(x[e], kLog2e, -m));
-        sacc += static_cast<double>(g);
-    });
-    const float M = tree_block_max(m, sh);
-    const double f = m == M ? 1.0 : static_cast<double>(fast_exp2(m - M));
+        s += static_cast<double>(g);
+    }
+
+    // Merge over the workgroup (every thread gets the part's (m, s)).
+    __device__ inline void finish(TreeShared& sh, float* m_out, double* s_out) const {
+        const float M = tree_block_max(m, sh);
+        const double f = m == M ? 1.0 : static_cast<double>(fast_exp2(m - M));
+        *m_out = M;
+        *s_out = tree_block_sum(s > 0.0 ? s * f : 0.0, sh);
+    }
+};
+
+// (m, s) of the shares in sh.xp, in part order: the target row's, or the
+// draft row's when second.
+__device__ inline void merge_norm(const TreeShared& sh, bool second, float* m_out, double* s_out) {
+    float M = kNegMax;
+    for (int j = 0; j < kTreeParts; ++j)
+        M = fmaxf(M, part_f(sh.xp[j], second ? 1 : 0));
+    double S = 0.0;
+    for (int j = 0; j < kTreeParts; ++j) {
+        const float mj = part_f(sh.xp[j], second ? 1 : 0);
+        const double sj = part_d(sh.xp[j], second ? 4 : 2);
+        if (sj > 0.0)
+            S += mj == M ? sj : sj * static_cast<double>(fast_exp2(mj - M));
+    }
     *m_out = M;
-    *s_out = tree_block_sum(sacc > 0.0 ? sacc * f : 0.0, sh);
+    *s_out = S;
 }
 
-template <int DT, bool VEC, bool NT>
-__device__ inline int tree_row_argmax(const void* row, int groups, TreeShared& sh) {
-    constexpr int W = Group<DT, VEC>::W;
-    float bv = -__builtin_huge_valf();
-    int bi = 0x7fffffff;
-    tree_stream_row<DT, VEC, NT>(row, groups, [&](int g, const float (&z)[W]) {
+constexpr int kTreeDepth1 = 4;  // ring depth of a one-row pass
+constexpr int kTreeDepth2 = 2;  // ring depth of a two-row pass
+
+// A part's view of its tree: its run of the vocabulary and the exchange.
+struct TreePartView {
+    int part;        // 0 .. kTreeParts - 1
+    int g0, ng;      // first group and number of groups of the run (ng may be 0)
+    int nt;          // tiles of the run
+    int W;           // logits per group
+    int dt;          // dtype
+    uint64_t* shares;  // this group's two slots
+    uint64_t tag;      // last published tag
+    bool live;       // false once a partner went missing
+
+    __device__ inline const void* sub(const void* row) const {
+        const size_t esz = dt == kBF16 ? 2 : 4;
+        return static_cast<const char*>(row) + static_cast<size_t>(g0) * W * esz;
+    }
+};
+
+// Publish this part's share of the next pass and collect all shares into
+// sh.xp (part order). Returns false (for every thread) when a partner has not
+// published within the spin limit; the view then stops waiting altogether.
+__device__ inline bool tree_exchange(TreePartView& v, const TreePart mine, TreeShared& sh) {
+    constexpr int kPieces = kTreeParts * kShareHalves;
+    static_assert(kPieces <= 64, "one wavefront moves the shares");
+    v.tag += 1;
+    const uint64_t tag48 = v.tag & ((1ULL << 48) - 1);
+    __syncthreads();  // sh.xp of the previous exchange is no longer read
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        uint64_t* slot = v.shares + (v.tag & 1) * kPieces;
+        if (lane < kShareHalves) {
+            uint32_t w = mine.w[0];
 #pragma unroll
-        for (int e = 0; e < W; ++e)
-            if (z[e] > bv) {
-                bv = z[e];
-                bi = g * W + e;
-            }
-    });
-    return tree_block_argmax(bv, bi, sh);
-}
-
-// Tile sums of the row pair's weights into ts (LDS), as the residual kernels
-// form them, and their fp64 total (every thread).
-template <int DT, bool VEC, bool NT>
-__device__ inline double tree_tile_pass(const SeqRows& s, int ntiles, int groups, float* ts,
-                                        TreeShared& sh) {
-    using IO = GroupIO<DT, VEC, NT>;
-    constexpr int W = IO::W;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    IO a, nxt;
-    int t = wid;
-    auto load = [&](IO& io, int tt) {
-        const int g = tt * kTile + lane;
-        io.load(s, tt < ntiles && g < groups ? g : 0);
-    };
-    load(a, t);
-    const int nb = t < ntiles ? (ntiles - t + kTreeWaves - 1) / kTreeWaves : 0;
-    for (int k = 0; k < nb; ++k) {
-        load(nxt, t + kTreeWaves);
-        const int g = t * kTile + lane;
-        float gs = 0.0f;
-        if (g < groups) {
-            float r[W];
-            a.residual(s, r);
-            gs = pairwise(r);
+            for (int i = 1; i < 6; ++i)
+                w = (lane >> 1) == i ? mine.w[i] : w;
+            const uint64_t piece = (w >> ((lane & 1) * 16)) & 0xFFFFu;
+            __hip_atomic_store(slot + v.part * kShareHalves + lane, (tag48 << 16) | piece,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        const float tsum = tile_reduce(gs);
+        bool ok = v.live;
+        bool have = lane >= kPieces;
+        uint32_t got = 0;
+        int polls = 0;
+        while (ok) {
+            if (!have) {
+                const uint64_t x = __hip_atomic_load(slot + lane, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                if ((x >> 16) == tag48) {
+                    got = static_cast<uint32_t>(x & 0xFFFFu);
+                    have = true;
+                }
+            }
+            if (__ballot(!have) == 0)
+                break;
+            if (++polls > kTreeSpinLimit)
+                ok = false;
+            else
+                __builtin_amdgcn_s_sleep(1);
+        }
+        if (ok && lane < kPieces)
+            reinterpret_cast<uint16_t*>(sh.xp)[lane] = static_cast<uint16_t>(got);
         if (lane == 0)
-            ts[t] = tsum;
-        a = nxt;
-        t += kTreeWaves;
+            sh.ok = ok ? 1 : 0;
     }
     __syncthreads();
-    double part = 0.0;
-    for (int i = threadIdx.x; i < ntiles; i += kTreeBlock)
-        part += static_cast<double>(ts[i]);
-    return tree_block_sum(part, sh);
+    const bool ok = sh.ok != 0;
+    v.live = v.live && ok;
+    return ok;
+}
+
+// Row normaliser(s) of one node over the whole vocabulary: target row, and
+// the draft row too when two_rows (one pass over both).
+template <int DT, bool VEC, bool NT>
+__device__ inline bool tree_norms(TreePartView& v, const void* prow, const void* qrow,
+                                  bool two_rows, float inv_t, TreeShared& sh, float* mp,
+                                  double* sp, float* mq, double* sq) {
+    constexpr int W = Group<DT, VEC>::W;
+    TreePart mine = part_zero();
+    part_set_f(mine, 0, kNegMax);
+    part_set_f(mine, 1, kNegMax);
+    if (v.ng > 0) {
+        OnlineNorm<W> np, nq;
+        if (two_rows) {
+            const void* const rows[2] = {v.sub(prow), v.sub(qrow)};
+            tree_stream<DT, VEC, NT, 2, kTreeDepth2>(rows, v.ng, [&](int, bool in, const float (&z)[2][W]) {
+                if (in) {
+                    np.add(z[0], inv_t);
+                    nq.add(z[1], inv_t);
+                }
+            });
+            float m;
+            double sum;
+            nq.finish(sh, &m, &sum);
+            part_set_f(mine, 1, m);
+            part_set_d(mine, 4, sum);
+        } else {
+            const void* const rows[1] = {v.sub(prow)};
+            tree_stream<DT, VEC, NT, 1, kTreeDepth1>(rows, v.ng, [&](int, bool in, const float (&z)[1][W]) {
+                if (in)
+                    np.add(z[0], inv_t);
+            });
+        }
+        float m;
+        double sum;
+        np.finish(sh, &m, &sum);
+        part_set_f(mine, 0, m);
+        part_set_d(mine, 2, sum);
+    }
+    if (!tree_exchange(v, mine, sh))
+        return false;
+    merge_norm(sh, false, mp, sp);
+    if (two_rows)
+        merge_norm(sh, true, mq, sq);
+    return true;
+}
+
+// Target argmax over the whole vocabulary (lowest index on ties); -1 when the
+// row has no finite maximum, -2 when a partner went missing.
+template <int DT, bool VEC, bool NT>
+__device__ inline int tree_argmax(TreePartView& v, const void* row, TreeShared& sh) {
+    constexpr int W = Group<DT, VEC>::W;
+    TreePart mine = part_zero();
+    part_set_f(mine, 0, -__builtin_huge_valf());
+    mine.w[1] = 0x7fffffffu;
+    if (v.ng > 0) {
+        float bv = -__builtin_huge_valf();
+        int bi = 0x7fffffff;
+        const void* const rows[1] = {v.sub(row)};
+        const int base = v.g0 * W;
+        tree_stream<DT, VEC, NT, 1, kTreeDepth1>(rows, v.ng, [&](int g, bool in, const float (&z)[1][W]) {
+#pragma unroll
+            for (int e = 0; e < W; ++e)
+                if (in && z[0][e] > bv) {
+                    bv = z[0][e];
+                    bi = base + g * W + e;
+                }
+        });
+        float av;
+        int ai;
+        tree_block_argmax(bv, bi, sh, &av, &ai);
+        part_set_f(mine, 0, av);
+        mine.w[1] = static_cast<uint32_t>(ai);
+    }
+    if (!tree_exchange(v, mine, sh))
+        return -2;
+    float bv = part_f(sh.xp[0], 0);
+    int bi = static_cast<int>(sh.xp[0].w[1]);
+    for (int j = 1; j < kTreeParts; ++j) {
+        const float av = part_f(sh.xp[j], 0);
+        const int ai = static_cast<int>(sh.xp[j].w[1]);
+        if (av > bv || (av == bv && ai < bi)) {
+            bv = av;
+            bi = ai;
+        }
+    }
+    return bv > -__builtin_huge_valf() ? bi : -1;
+}
+
+// Tile sums of the row pair's weights over this part's run into ts (LDS), as
+// the residual kernels form them, and the shares' totals in sh.xp (words 2-3).
+// Returns false when a partner went missing.
+template <int DT, bool VEC, bool NT>
+__device__ inline bool tree_tile_pass(TreePartView& v, const SeqRows& s, float* ts, TreeShared& sh) {
+    constexpr int W = Group<DT, VEC>::W;
+    const int lane = threadIdx.x & 63;
+    TreePart mine = part_zero();
+    if (v.ng > 0) {
+        const void* const rows[2] = {v.sub(s.prow), v.sub(s.qrow)};
+        tree_stream<DT, VEC, NT, 2, kTreeDepth2>(rows, v.ng, [&](int g, bool in, const float (&z)[2][W]) {
+            float r[W];
+            if (!in) {
+#pragma unroll
+                for (int e = 0; e < W; ++e)
+                    r[e] = 0.0f;
+            } else if (s.p_only) {
+#pragma unroll
+                for (int e = 0; e < W; ++e)
+                    r[e] = fast_exp2(__builtin_fmaf(scale_logit(z[0][e], s.inv_t), kLog2e, -s.mp));
+            } else {
+#pragma unroll
+                for (int e = 0; e < W; ++e) {
+                    const float pv = fast_exp2(__builtin_fmaf(scale_logit(z[0][e], s.inv_t), kLog2e, -s.mp));
+                    const float qv = fast_exp2(__builtin_fmaf(scale_logit(z[1][e], s.inv_t), kLog2e, -s.mq));
+                    r[e] = fmaxf(__builtin_fmaf(pv, s.ratio, -qv), 0.0f);
+                }
+            }
+            const float tsum = tile_reduce(pairwise(r));
+            if (lane == 0)
+                ts[g / kTile] = tsum;
+        });
+        __syncthreads();
+        double part = 0.0;
+        for (int i = threadIdx.x; i < v.nt; i += kTreeBlock)
+            part += static_cast<double>(ts[i]);
+        part_set_d(mine, 2, tree_block_sum(part, sh));
+    }
+    return tree_exchange(v, mine, sh);
 }
 
 template <int DT, bool VEC, bool NT>
-__global__ __launch_bounds__(kTreeBlock) void tree_sample_kernel(TreeSampleArgs a) {
+__global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleArgs a) {
     constexpr int W = Group<DT, VEC>::W;
     extern __shared__ float lds_ts[];
     __shared__ TreeShared sh;
-    const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int M = a.M, V = a.V;
     const int groups = V / W;
     const int ntiles = (groups + kTile - 1) / kTile;
-    const int n = a.n_nodes[b];
-    int32_t* path_out = a.out_path + static_cast<size_t>(b) * M;
+    const int n_grp = gridDim.x / kTreeParts;
+    const int grp = blockIdx.x / kTreeParts;
 
-    // Structure, tokens and temperature.
-    if (tid == 0)
-        sh.flag = 0;
-    __syncthreads();
-    const bool n_ok = n >= 1 && n <= M;
-    if (n_ok && tid < n) {
-        const int pr = a.parent[static_cast<size_t>(b) * M + tid];
-        const int tk = a.token[static_cast<size_t>(b) * M + tid];
-        sh.parent[tid] = pr;
-        sh.token[tid] = tk;
-        const bool ok = tid == 0 ? pr == -1 : (pr >= 0 && pr < tid && tk >= 0 && tk < V);
-        if (!ok)
-            atomicOr(&sh.flag, 1);
+    TreePartView v;
+    v.part = blockIdx.x % kTreeParts;
+    {
+        const int t0 = static_cast<int>(static_cast<long>(ntiles) * v.part / kTreeParts);
+        const int t1 = static_cast<int>(static_cast<long>(ntiles) * (v.part + 1) / kTreeParts);
+        v.g0 = t0 * kTile;
+        v.ng = t1 > t0 ? min(t1 * kTile, groups) - v.g0 : 0;
+        v.nt = t1 - t0;
     }
-    float inv_t = 0.0f;
-    const int mode = temperature_mode(a.temperature[b], &inv_t);
-    __syncthreads();
-    bool bad = !n_ok || sh.flag != 0 || mode < 0;
+    v.W = W;
+    v.dt = DT;
+    v.shares = a.shares + static_cast<size_t>(grp) * 2 * kTreeParts * kShareHalves;
+    v.tag = a.call << 20;
+    v.live = true;
 
-    const size_t row_base = static_cast<size_t>(b) * M;
-    auto prow = [&](int u) { return row_ptr(a.target, DT, row_base + u, V); };
-    auto qrow = [&](int u) { return row_ptr(a.draft, DT, row_base + u, V); };
-    auto xval = [&](const void* row, int t) { return scale_logit(load_logit(row, DT, t), inv_t); };
-    int u = 0, L = 0, extra = -1;
-    if (!bad && mode == 0) {
-        // T = 0: step to the lowest-index child holding the target argmax.
-        for (;;) {
-            const int am = tree_row_argmax<DT, VEC, NT>(prow(u), groups, sh);
-            if (am < 0) {
-                bad = true;
-                break;
-            }
-            int next = -1;
-            for (int s = 1; s < n; ++s)
-                if (sh.parent[s] == u && sh.token[s] == am) {
-                    next = s;
-                    break;
-                }
-            if (next < 0) {
-                extra = am;
-                break;
-            }
-            if (tid == 0)
-                sh.path[L] = next;
-            ++L;
-            u = next;
+    for (int b = grp; b < a.B; b += n_grp) {
+        const int n = a.n_nodes[b];
+        // Structure, tokens and temperature (every part reads them).
+        if (tid == 0)
+            sh.flag = 0;
+        __syncthreads();
+        const bool n_ok = n >= 1 && n <= M;
+        if (n_ok && tid < n) {
+            const int pr = a.parent[static_cast<size_t>(b) * M + tid];
+            const int tk = a.token[static_cast<size_t>(b) * M + tid];
+            sh.parent[tid] = pr;
+            sh.token[tid] = tk;
+            const bool ok = tid == 0 ? pr == -1 : (pr >= 0 && pr < tid && tk >= 0 && tk < V);
+            if (!ok)
+                atomicOr(&sh.flag, 1);
         }
-    } else if (!bad) {
-        float mp = 0.0f, mq = 0.0f;
-        double sp = 0.0, sq = 0.0;
-        tree_row_norm<DT, VEC, NT>(prow(u), groups, inv_t, sh, &mp, &sp);
-        bad = !(sp > 0.0);
-        double c = 0.0, Z = 1.0;
-        bool have_q = false;
-        bool ts_current = false;  // lds_ts holds the tile sums of the current (c, Z)
-        int s = 1;
-        while (!bad) {
-            while (s < n && sh.parent[s] != u)
-                ++s;
-            if (s >= n)
-                break;  // no child left to try at u
-            if (!have_q) {
-                tree_row_norm<DT, VEC, NT>(qrow(u), groups, inv_t, sh, &mq, &sq);
-                if (!(sq > 0.0)) {
+        float inv_t = 0.0f;
+        const int mode = temperature_mode(a.temperature[b], &inv_t);
+        __syncthreads();
+        bool bad = !n_ok || sh.flag != 0 || mode < 0 || !v.live;
+
+        const size_t row_base = static_cast<size_t>(b) * M;
+        auto prow = [&](int u) { return row_ptr(a.target, DT, row_base + u, V); };
+        auto qrow = [&](int u) { return row_ptr(a.draft, DT, row_base + u, V); };
+        auto xval = [&](const void* row, int t) { return scale_logit(load_logit(row, DT, t), inv_t); };
+        int u = 0, L = 0, extra = -1;
+        bool draw_here = false;  // this part writes the extra token
+        if (!bad && mode == 0) {
+            // T = 0: step to the lowest-index child holding the target argmax.
+            for (;;) {
+                const int am = tree_argmax<DT, VEC, NT>(v, prow(u), sh);
+                if (am < 0) {
                     bad = true;
                     break;
                 }
-                have_q = true;
-            }
-            // The accept test of child s, in fp64 (every thread computes it).
-            const int t = sh.token[s];
-            const double lse_p = (static_cast<double>(mp) + log2(sp)) / static_cast<double>(kLog2e);
-            const double lse_q = (static_cast<double>(mq) + log2(sq)) / static_cast<double>(kLog2e);
-            const double lp = static_cast<double>(xval(prow(u), t)) - lse_p;
-            const double lq = static_cast<double>(xval(qrow(u), t)) - lse_q;
-            double lpi = lp;
-            if (c > 0.0) {
-                const double d = exp(lp) - c * exp(lq);
-                lpi = d > 0.0 ? log(d) - log(Z) : -__builtin_huge_val();
-            }
-            const Words4 w = verify_block(a.seed, a.offset, static_cast<uint32_t>(b),
-                                          static_cast<uint32_t>(s - 1));
-            const double log_u = log(static_cast<double>(uniform24(w.w0)));
-            if (log_u < lpi - lq) {
+                int next = -1;
+                for (int s = 1; s < n; ++s)
+                    if (sh.parent[s] == u && sh.token[s] == am) {
+                        next = s;
+                        break;
+                    }
+                if (next < 0) {
+                    extra = am;
+                    break;
+                }
                 if (tid == 0)
-                    sh.path[L] = s;
+                    sh.path[L] = next;
                 ++L;
-                u = s;
-                s = 1;
-                c = 0.0;
-                Z = 1.0;
-                have_q = false;
-                ts_current = false;
-                tree_row_norm<DT, VEC, NT>(prow(u), groups, inv_t, sh, &mp, &sp);
-                bad = !(sp > 0.0);
-                continue;
+                u = next;
             }
-            // Rejected: the residual against q_u, in closed form.
-            const double c2 = c + Z;
-            SeqRows rows;
-            rows.prow = prow(u);
-            rows.qrow = qrow(u);
-            rows.p_only = false;
-            rows.inv_t = inv_t;
-            rows.mp = mp;
-            rows.mq = mq;
-            rows.ratio = static_cast<float>(sq / (c2 * sp));
-            const double tot = tree_tile_pass<DT, VEC, NT>(rows, ntiles, groups, lds_ts, sh);
-            const double Z2 = c2 / sq * tot;
-            if (Z2 > 0.0) {
-                c = c2;
-                Z = Z2;
-                ts_current = true;
-            } else {
-                ts_current = false;  // an empty residual (rounding): pi stays
+        } else if (!bad) {
+            float mp = 0.0f, mq = 0.0f;
+            double sp = 0.0, sq = 0.0;
+            // Normalisers of a node's rows: the draft row's only when the
+            // node has children to test, then in the same pass.
+            auto arrive = [&](int x) {
+                bool kids = false;
+                for (int i = x + 1; i < n; ++i)
+                    kids = kids || sh.parent[i] == x;
+                if (!tree_norms<DT, VEC, NT>(v, prow(x), qrow(x), kids, inv_t, sh, &mp, &sp, &mq, &sq))
+                    return false;
+                return sp > 0.0 && (!kids || sq > 0.0);
+            };
+            bad = !arrive(u);
+            double c = 0.0, Z = 1.0;
+            bool ts_current = false;  // lds_ts holds the tile sums of the current (c, Z)
+            double tot_by_part[kTreeParts];
+            int s = 1;
+            while (!bad) {
+                while (s < n && sh.parent[s] != u)
+                    ++s;
+                if (s >= n)
+                    break;  // no child left to try at u
+                // The accept test of child s, in fp64 (every thread computes it).
+                const int t = sh.token[s];
+                const double lse_p = (static_cast<double>(mp) + log2(sp)) / static_cast<double>(kLog2e);
+                const double lse_q = (static_cast<double>(mq) + log2(sq)) / static_cast<double>(kLog2e);
+                const double lp = static_cast<double>(xval(prow(u), t)) - lse_p;
+                const double lq = static_cast<double>(xval(qrow(u), t)) - lse_q;
+                double lpi = lp;
+                if (c > 0.0) {
+                    const double d = exp(lp) - c * exp(lq);
+                    lpi = d > 0.0 ? log(d) - log(Z) : -__builtin_huge_val();
+                }
+                const Words4 w = verify_block(a.seed, a.offset, static_cast<uint32_t>(b),
+                                              static_cast<uint32_t>(s - 1));
+                const double log_u = log(static_cast<double>(uniform24(w.w0)));
+                if (log_u < lpi - lq) {
+                    if (tid == 0)
+                        sh.path[L] = s;
+                    ++L;
+                    u = s;
+                    s = 1;
+                    c = 0.0;
+                    Z = 1.0;
+                    ts_current = false;
+                    bad = !arrive(u);
+                    continue;
+                }
+                // Rejected: the residual against q_u, in closed form.
+                const double c2 = c + Z;
+                SeqRows rows;
+                rows.prow = prow(u);
+                rows.qrow = qrow(u);
+                rows.p_only = false;
+                rows.inv_t = inv_t;
+                rows.mp = mp;
+                rows.mq = mq;
+                rows.ratio = static_cast<float>(sq / (c2 * sp));
+                if (!tree_tile_pass<DT, VEC, NT>(v, rows, lds_ts, sh)) {
+                    bad = true;
+                    break;
+                }
+                double tot = 0.0;
+                for (int j = 0; j < kTreeParts; ++j)
+                    tot += part_d(sh.xp[j], 2);
+                const double Z2 = c2 / sq * tot;
+                if (Z2 > 0.0) {
+                    c = c2;
+                    Z = Z2;
+                    ts_current = true;
+                    for (int j = 0; j < kTreeParts; ++j)
+                        tot_by_part[j] = part_d(sh.xp[j], 2);
+                } else {
+                    ts_current = false;  // an empty residual (rounding): pi stays
+                }
+                ++s;
             }
-            ++s;
+            if (!bad) {
+                SeqRows rows;
+                rows.prow = prow(u);
+                rows.qrow = c > 0.0 ? qrow(u) : prow(u);
+                rows.p_only = !(c > 0.0);
+                rows.inv_t = inv_t;
+                rows.mp = mp;
+                rows.mq = mq;
+                rows.ratio = c > 0.0 ? static_cast<float>(sq / (c * sp)) : 1.0f;
+                if (!ts_current) {
+                    if (!tree_tile_pass<DT, VEC, NT>(v, rows, lds_ts, sh))
+                        bad = true;
+                    else
+                        for (int j = 0; j < kTreeParts; ++j)
+                            tot_by_part[j] = part_d(sh.xp[j], 2);
+                }
+                if (!bad) {
+                    // The draw position over the parts' totals in part order;
+                    // past the total (rounding only) it falls to the last part
+                    // with mass, which then takes its last positive element.
+                    double S = 0.0;
+                    for (int j = 0; j < kTreeParts; ++j)
+                        S += tot_by_part[j];
+                    const Words4 w = verify_block(a.seed, a.offset, static_cast<uint32_t>(b),
+                                                  static_cast<uint32_t>(L));
+                    const float uu = uniform24(w.w1);
+                    if (S > 0.0) {
+                        const double tau = static_cast<double>(uu) * S;
+                        int owner = -1, last = -1;
+                        double P = 0.0, P_owner = 0.0, P_last = 0.0;
+                        for (int j = 0; j < kTreeParts; ++j) {
+                            const double tj = tot_by_part[j];
+                            if (tj > 0.0) {
+                                if (owner < 0 && P + tj > tau) {
+                                    owner = j;
+                                    P_owner = P;
+                                }
+                                last = j;
+                                P_last = P;
+                            }
+                            P += tj;
+                        }
+                        if (owner < 0) {
+                            owner = last;
+                            P_owner = P_last;
+                        }
+                        draw_here = owner == v.part;
+                        if (draw_here && tid < 64) {
+                            SeqRows local = rows;
+                            local.prow = v.sub(rows.prow);
+                            local.qrow = v.sub(rows.qrow);
+                            const int tok = draw_at<DT, VEC, NT>(local, tau - P_owner, lds_ts, v.nt, v.ng);
+                            if (tid == 0)
+                                sh.decision = tok + v.g0 * W;
+                        }
+                    } else {
+                        // Empty residual (rounding only): part 0 draws from p.
+                        draw_here = v.part == 0;
+                        if (draw_here && tid < 64) {
+                            const int tok = draw_p_fallback<DT, VEC, NT>(rows, uu, ntiles, groups);
+                            if (tid == 0)
+                                sh.decision = tok;
+                        }
+                    }
+                    __syncthreads();
+                    extra = sh.decision;
+                }
+            }
         }
-        if (!bad) {
-            SeqRows rows;
-            rows.prow = prow(u);
-            rows.qrow = c > 0.0 ? qrow(u) : prow(u);
-            rows.p_only = !(c > 0.0);
-            rows.inv_t = inv_t;
-            rows.mp = mp;
-            rows.mq = mq;
-            rows.ratio = c > 0.0 ? static_cast<float>(sq / (c * sp)) : 1.0f;
-            if (!ts_current)
-                tree_tile_pass<DT, VEC, NT>(rows, ntiles, groups, lds_ts, sh);
-            const Words4 w = verify_block(a.seed, a.offset, static_cast<uint32_t>(b),
-                                          static_cast<uint32_t>(L));
-            if (tid < 64) {
-                const int tok = draw_token<DT, VEC, NT>(rows, uniform24(w.w1), lds_ts, ntiles, groups);
-                if (tid == 0)
-                    sh.decision = tok;
-            }
-            __syncthreads();
-            extra = sh.decision;
+        if (mode == 0 || bad)
+            draw_here = v.part == 0;
+        // Part 0 writes the length and path; the drawing part the extra token.
+        __syncthreads();
+        if (v.part == 0) {
+            int32_t* path_out = a.out_path + static_cast<size_t>(b) * M;
+            for (int i = tid; i < M; i += kTreeBlock)
+                path_out[i] = !bad && i < L ? sh.path[i] : -1;
+            if (tid == 0)
+                a.out_length[b] = bad ? -1 : L;
         }
-    }
-    __syncthreads();
-    for (int i = tid; i < M; i += kTreeBlock)
-        path_out[i] = !bad && i < L ? sh.path[i] : -1;
-    if (tid == 0) {
-        a.out_length[b] = bad ? -1 : L;
-        a.out_extra[b] = bad ? -1 : extra;
+        if (draw_here && tid == 0)
+            a.out_extra[b] = bad ? -1 : extra;
+        __syncthreads();
     }
 }
 
 template <int DT, bool VEC>
-hipError_t launch_tree_sample_typed(int batch, const TreeSampleArgs& args, hipStream_t stream) {
+hipError_t tree_sample_capacity_typed(int* blocks) {
+    constexpr bool NT = VEC;
+    constexpr int W = Group<DT, VEC>::W;
+    (void)W;
+    int per_cu = 0;
+    // The dynamic LDS of the largest run is at most 16 KiB for any vocabulary
+    // up to 2^22 groups; capacity is taken at that size.
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(tree_sample_kernel<DT, VEC, NT>), kTreeBlock,
+        kTreeLdsBytes);
+    if (e != hipSuccess)
+        return e;
+    int dev = 0, cus = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess)
+        return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return e;
+    *blocks = per_cu * cus;
+    return hipSuccess;
+}
+
+template <int DT, bool VEC>
+hipError_t launch_tree_sample_typed(int n_groups, const TreeSampleArgs& args, hipStream_t stream) {
     constexpr bool NT = VEC;
     constexpr int W = Group<DT, VEC>::W;
     const int ntiles = (args.V / W + kTile - 1) / kTile;
-    tree_sample_kernel<DT, VEC, NT><<<dim3(static_cast<unsigned>(batch)), dim3(kTreeBlock),
-                                       static_cast<size_t>(ntiles) * sizeof(float), stream>>>(args);
+    const int run_tiles = (ntiles + kTreeParts - 1) / kTreeParts;
+    const size_t lds = static_cast<size_t>(run_tiles) * sizeof(float);
+    if (lds > kTreeLdsBytes)
+        return hipErrorInvalidValue;
+    tree_sample_kernel<DT, VEC, NT><<<dim3(static_cast<unsigned>(n_groups * kTreeParts)),
+                                       dim3(kTreeBlock), lds, stream>>>(args);
     return hipGetLastError();
 }
 
@@ -960,20 +1331,50 @@ hipError_t launch_unroll(const Shape& sh, int nsplit, int unroll, int tiles_per_
 
 int residual_tiles_per_row(int vocab) { return (vocab + kTile - 1) / kTile; }
 
+int tree_sample_parts() { return kTreeParts; }
+
+bool tree_sample_fits(int vocab, int dtype) {
+    // The element path (W = 1) has the most tiles.
+    (void)dtype;
+    const long run_tiles = ((static_cast<long>(vocab) + kTile - 1) / kTile + kTreeParts - 1) / kTreeParts;
+    return run_tiles * static_cast<long>(sizeof(float)) <= static_cast<long>(kTreeLdsBytes);
+}
+
+size_t tree_sample_group_bytes() { return 2 * kTreeParts * kShareHalves * sizeof(uint64_t); }
+
+hipError_t tree_sample_max_groups(int dtype, int* out_groups) {
+    int a = 0, b = 0;
+    hipError_t e = dtype == kBF16 ? tree_sample_capacity_typed<kBF16, true>(&a)
+                                  : tree_sample_capacity_typed<kF32, true>(&a);
+    if (e != hipSuccess)
+        return e;
+    e = dtype == kBF16 ? tree_sample_capacity_typed<kBF16, false>(&b)
+                       : tree_sample_capacity_typed<kF32, false>(&b);
+    if (e != hipSuccess)
+        return e;
+    *out_groups = std::min(a, b) / kTreeParts;
+    return hipSuccess;
+}
+
 hipError_t launch_tree_sample(int batch, int max_nodes, int vocab, int dtype, bool vec,
                               const int32_t* parent, const int32_t* token, const int32_t* n_nodes,
                               const void* draft, const void* target, const float* temperature,
                               uint64_t seed, uint64_t offset, int32_t* out_length,
-                              int32_t* out_path, int32_t* out_extra, hipStream_t stream) {
+                              int32_t* out_path, int32_t* out_extra, uint64_t* shares,
+                              int n_groups, uint64_t call, hipStream_t stream) {
     if (batch == 0)
         return hipSuccess;
-    const TreeSampleArgs args{parent, token, n_nodes, draft, target, temperature, max_nodes,
-                              vocab, seed, offset, out_length, out_path, out_extra};
+    if (n_groups < 1 || call < 1 || call >= (1ULL << 43))
+        return hipErrorInvalidValue;
+    const TreeSampleArgs args{parent, token, n_nodes, draft, target, temperature, batch,
+                              max_nodes, vocab, seed, offset, out_length, out_path, out_extra,
+                              shares, call};
+    const int g = std::min(n_groups, batch);
     if (dtype == kBF16)
-        return vec ? launch_tree_sample_typed<kBF16, true>(batch, args, stream)
-                   : launch_tree_sample_typed<kBF16, false>(batch, args, stream);
-    return vec ? launch_tree_sample_typed<kF32, true>(batch, args, stream)
-               : launch_tree_sample_typed<kF32, false>(batch, args, stream);
+        return vec ? launch_tree_sample_typed<kBF16, true>(g, args, stream)
+                   : launch_tree_sample_typed<kBF16, false>(g, args, stream);
+    return vec ? launch_tree_sample_typed<kF32, true>(g, args, stream)
+               : launch_tree_sample_typed<kF32, false>(g, args, stream);
 }
 
 int residual_fused_max_tiles() { return kResidualFusedMaxTiles; }

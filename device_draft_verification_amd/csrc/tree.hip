@@ -261,6 +261,11 @@ struct spec_tree_ctx {
     int B = 0, M = 0, V = 0, dtype = 0, nsplit = 1;
     hipStream_t stream = nullptr;
     ArgPart* part = nullptr;
+    // Sampled verification: trees in flight at once, the parts' exchange
+    // slots, and the number of the last launch.
+    int sample_groups = 0;
+    uint64_t* shares = nullptr;
+    uint64_t call = 0;
 };
 
 extern "C" {
@@ -308,6 +313,21 @@ int spec_tree_verify_init(int batch, int max_nodes, int vocab, int dtype, void* 
     n = std::min(n, std::max(1L, groups / 1024));
     ctx->nsplit = static_cast<int>(std::max(1L, std::min(n, 64L)));
     if (hipMalloc(&ctx->part, static_cast<size_t>(rows) * ctx->nsplit * sizeof(ArgPart)) != hipSuccess) {
+        delete ctx;
+        return SPEC_ENOMEM;
+    }
+    int sample_groups = 0;
+    if (tree_sample_max_groups(dtype, &sample_groups) != hipSuccess || sample_groups < 1) {
+        hipFree(ctx->part);
+        delete ctx;
+        return SPEC_EHIP;
+    }
+    ctx->sample_groups = std::min(sample_groups, batch);
+    const size_t share_bytes = static_cast<size_t>(ctx->sample_groups) * tree_sample_group_bytes();
+    if (hipMalloc(reinterpret_cast<void**>(&ctx->shares), share_bytes) != hipSuccess ||
+        hipMemset(ctx->shares, 0, share_bytes) != hipSuccess) {
+        hipFree(ctx->shares);
+        hipFree(ctx->part);
         delete ctx;
         return SPEC_ENOMEM;
     }
@@ -367,11 +387,19 @@ int spec_tree_verify_sample(spec_tree_ctx* ctx, const int32_t* parent, const int
         !aligned(target, esz) || !aligned(temperature, 4) || !aligned(out_length, 4) ||
         !aligned(out_path, 4) || !aligned(out_extra, 4))
         return SPEC_EINVAL;
+    if (!tree_sample_fits(ctx->V, ctx->dtype))
+        return SPEC_EINVAL;
+    // Exchange tags carry 20 bits of pass count per launch.
+    const long trees_per_group = (ctx->B + ctx->sample_groups - 1) / ctx->sample_groups;
+    if (trees_per_group * (2L * ctx->M + 2) >= (1L << 20))
+        return SPEC_EINVAL;
     const int W = ctx->dtype == SPEC_BF16 ? 8 : 4;
     const bool vec = ctx->V % W == 0 && aligned(draft, 16) && aligned(target, 16);
+    ctx->call += 1;
     const hipError_t e = launch_tree_sample(ctx->B, ctx->M, ctx->V, ctx->dtype, vec, parent, token,
                                             n_nodes, draft, target, temperature, seed, offset,
-                                            out_length, out_path, out_extra, ctx->stream);
+                                            out_length, out_path, out_extra, ctx->shares,
+                                            ctx->sample_groups, ctx->call, ctx->stream);
     return e == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
@@ -382,6 +410,8 @@ int spec_tree_verify_destroy(spec_tree_ctx* ctx) {
     if (hipStreamSynchronize(ctx->stream) != hipSuccess)
         rc = SPEC_EHIP;
     if (ctx->part && hipFree(ctx->part) != hipSuccess)
+        rc = SPEC_EHIP;
+    if (ctx->shares && hipFree(ctx->shares) != hipSuccess)
         rc = SPEC_EHIP;
     delete ctx;
     return rc;
