@@ -1,6 +1,6 @@
 /*
  * spec_tree.h -- C ABI for draft trees on AMD Instinct MI355X (gfx950):
- * confidence-guided pruning and greedy tree verification.
+ * confidence-guided pruning, and greedy and sampled tree verification.
  *
  * Pruning (SpecLA summary, Methodology section 3, target-aligned drafting):
  * low-probability paths of a draft tree are cut by their cumulative draft
@@ -44,8 +44,15 @@
  * (node i + 1 holding draft token i) sees the verifier's uniforms and gives
  * its outcome. T == 0 trees follow the greedy rule above; invalid
  * temperatures are sentinels as in spec_verify.h. Outputs as for the greedy
- * call. Cost: one pass over the two rows of each visited node, one per
- * rejection, one for the draw, by one 1024-thread workgroup per tree.
+ * call. Cost: one pass over the two rows of each visited node with children
+ * (the target row alone at a leaf), one per rejection, one for the draw when
+ * the last node rejected nothing. Each tree is split over four 256-thread
+ * workgroups that own quarters of the vocabulary and exchange per-pass
+ * results through the context's workspace; the launch holds at most as many
+ * trees as the device keeps resident at once (the rest follow in turn), and
+ * calls on one context must not overlap. A part that waits about a second for
+ * a partner (possible only if other work keeps the partner off the device)
+ * gives up and marks the tree invalid.
  *
  * Layouts: dense row-major DEVICE arrays owned by the caller; int32 indices,
  * float32 logq, float64 scores; target logits [B, M, V] in the dtype of
@@ -76,8 +83,9 @@ int spec_tree_prune(int batch, int nodes, const int32_t* parent, const float* lo
 
 typedef struct spec_tree_ctx spec_tree_ctx;
 
-/* Workspace for greedy verification of B trees of at most M nodes over a
- * vocabulary of V logits of the given dtype. */
+/* Workspace for verification of B trees of at most M nodes over a
+ * vocabulary of V logits of the given dtype (greedy: per-split argmax
+ * results; sampled: the parts' exchange slots, zeroed here). */
 int spec_tree_verify_init(int batch, int max_nodes, int vocab, int dtype, void* hip_stream,
                           spec_tree_ctx** out_ctx);
 
@@ -93,7 +101,9 @@ int spec_tree_verify_greedy(spec_tree_ctx* ctx, const int32_t* parent, const int
 /* draft, target [B, M, V] in the context's dtype (draft row u: the
  * distribution u's children were drawn from), temperature [B] fp32, seed and
  * offset as in spec_verify.h; other arguments and outputs as for
- * spec_tree_verify_greedy. No workspace. */
+ * spec_tree_verify_greedy. Uses the context's workspace; SPEC_EINVAL when V
+ * exceeds the 16 KiB of tile sums one part keeps in LDS (V > 1 048 576) or
+ * ceil(B / resident trees) * (2M + 2) >= 2^20. */
 int spec_tree_verify_sample(spec_tree_ctx* ctx, const int32_t* parent, const int32_t* token,
                             const int32_t* n_nodes, const void* draft, const void* target,
                             const float* temperature, uint64_t seed, uint64_t offset,
