@@ -139,10 +139,13 @@ def to_dev_logits(x, dtype):
     return dev(x)
 
 
-def gpu_sample(parent, token, n_nodes, draft, target, temperature, dtype, seed=0, offset=0):
+def gpu_sample(parent, token, n_nodes, draft, target, temperature, dtype, seed=0, offset=0,
+               ctx=None):
     B, M = parent.shape
     V = target.shape[-1]
-    ctx = sv.spec_tree_verify_init(B, M, V, dtype)
+    own = ctx is None
+    if own:
+        ctx = sv.spec_tree_verify_init(B, M, V, dtype)
     L = torch.empty(B, dtype=torch.int32, device="cuda")
     path = torch.empty((B, M), dtype=torch.int32, device="cuda")
     extra = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -150,6 +153,8 @@ def gpu_sample(parent, token, n_nodes, draft, target, temperature, dtype, seed=0
                                to_dev_logits(draft, dtype), to_dev_logits(target, dtype),
                                dev(np.asarray(temperature, np.float32)), seed, offset, L, path, extra)
     torch.cuda.synchronize()
+    if own:
+        sv.spec_tree_verify_destroy(ctx)
     return dict(length=L.cpu().numpy(), path=path.cpu().numpy(), extra=extra.cpu().numpy())
 
 
@@ -194,7 +199,9 @@ def test_sample_chains(cfg, over):
 
 
 @pytest.mark.parametrize("B,M,V,dt", [(16, 12, 1000, "f32"), (32, 20, 4099, "bf16"),
-                                      (8, 64, 32000, "bf16"), (4, 256, 777, "f32")])
+                                      (8, 64, 32000, "bf16"), (4, 256, 777, "f32"),
+                                      (600, 8, 300, "bf16"),   # more trees than resident at once
+                                      (3, 5, 5, "f32")])       # one tile: three parts own nothing
 def test_sample_random_trees(B, M, V, dt):
     trees = specgen.draft_trees(B, M, V, seed=M + V)
     zt = specgen.tree_target_logits(trees, V, seed=1, dtype=dt)
@@ -217,6 +224,29 @@ def test_sample_random_trees(B, M, V, dt):
         assert g["length"][2] == -1 and g["length"][3] == -1
     print(f"  flagged {f}/{B}, lengths {g['length'].tolist()[:12]}", flush=True)
     assert (o["length"] >= 1).any()
+
+
+def test_sample_repeated_calls():
+    """Several calls on one context (the parts' exchange slots keep the previous
+    call's words), with different inputs, offsets and batch contents."""
+    B, M, V = 300, 10, 2048
+    ctx = sv.spec_tree_verify_init(B, M, V, torch.bfloat16)
+    print(f"\n[tree sample repeated B={B} M={M} V={V}]", flush=True)
+    for call in range(3):
+        trees = specgen.draft_trees(B, M, V, seed=50 + call)
+        zt = specgen.tree_target_logits(trees, V, seed=60 + call, dtype="bf16")
+        zq = specgen.tree_target_logits(trees, V, seed=70 + call, dtype="bf16")
+        rng = np.random.default_rng(call)
+        temp = rng.uniform(0.3, 1.5, B).astype(np.float32)
+        temp[rng.random(B) < 0.2] = 0.0
+        n = rng.integers(1, M + 1, B).astype(np.int32)
+        g = gpu_sample(trees["parent"], trees["token"], n, zq, zt, temp, torch.bfloat16,
+                       seed=11, offset=call, ctx=ctx)
+        o = oracle.tree_verify_sample(trees["parent"], trees["token"], n, zq, zt, temp, seed=11,
+                                      offset=call)
+        f = check_sample(g, o, temp)
+        print(f"  call {call}: flagged {f}/{B}, mean length {g['length'].mean():.2f}", flush=True)
+    sv.spec_tree_verify_destroy(ctx)
 
 
 def test_sample_full_workload_sampled():
