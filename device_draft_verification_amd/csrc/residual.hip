@@ -636,6 +636,7 @@ struct TreeShared {
     double red_d[kTreeWaves];
     int red_i[kTreeWaves];
     TreePart xp[kTreeParts];
+    double tot_keep[kTreeParts];  // per-part residual totals of the draw's tile sums
     int flag;
     int decision;
     int ok;
@@ -831,7 +832,7 @@ struct TreePartView {
 // published within the spin limit; the view then stops waiting altogether.
 __device__ inline bool tree_exchange(TreePartView& v, const TreePart mine, TreeShared& sh) {
     constexpr int kPieces = kTreeParts * kShareHalves;
-    static_assert(kPieces <= 64, "one wavefront moves the shares");
+    constexpr int kPerLane = (kPieces + 63) / 64;  // pieces each lane of wavefront 0 collects
     v.tag += 1;
     const uint64_t tag48 = v.tag & ((1ULL << 48) - 1);
     __syncthreads();  // sh.xp of the previous exchange is no longer read
@@ -848,27 +849,39 @@ __device__ inline bool tree_exchange(TreePartView& v, const TreePart mine, TreeS
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         bool ok = v.live;
-        bool have = lane >= kPieces;
-        uint32_t got = 0;
+        bool have[kPerLane];
+        uint32_t got[kPerLane];
+#pragma unroll
+        for (int r = 0; r < kPerLane; ++r) {
+            have[r] = lane + 64 * r >= kPieces;
+            got[r] = 0;
+        }
         int polls = 0;
         while (ok) {
-            if (!have) {
-                const uint64_t x = __hip_atomic_load(slot + lane, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                if ((x >> 16) == tag48) {
-                    got = static_cast<uint32_t>(x & 0xFFFFu);
-                    have = true;
+            bool all = true;
+#pragma unroll
+            for (int r = 0; r < kPerLane; ++r) {
+                if (!have[r]) {
+                    const uint64_t x = __hip_atomic_load(slot + lane + 64 * r, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+                    if ((x >> 16) == tag48) {
+                        got[r] = static_cast<uint32_t>(x & 0xFFFFu);
+                        have[r] = true;
+                    }
                 }
+                all = all && have[r];
             }
-            if (__ballot(!have) == 0)
+            if (__ballot(!all) == 0)
                 break;
             if (++polls > kTreeSpinLimit)
                 ok = false;
             else
                 __builtin_amdgcn_s_sleep(1);
         }
-        if (ok && lane < kPieces)
-            reinterpret_cast<uint16_t*>(sh.xp)[lane] = static_cast<uint16_t>(got);
+#pragma unroll
+        for (int r = 0; r < kPerLane; ++r)
+            if (ok && lane + 64 * r < kPieces)
+                reinterpret_cast<uint16_t*>(sh.xp)[lane + 64 * r] = static_cast<uint16_t>(got[r]);
         if (lane == 0)
             sh.ok = ok ? 1 : 0;
     }
@@ -1041,12 +1054,12 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
             sh.flag = 0;
         __syncthreads();
         const bool n_ok = n >= 1 && n <= M;
-        if (n_ok && tid < n) {
-            const int pr = a.parent[static_cast<size_t>(b) * M + tid];
-            const int tk = a.token[static_cast<size_t>(b) * M + tid];
-            sh.parent[tid] = pr;
-            sh.token[tid] = tk;
-            const bool ok = tid == 0 ? pr == -1 : (pr >= 0 && pr < tid && tk >= 0 && tk < V);
+        for (int i = tid; n_ok && i < n; i += kTreeBlock) {
+            const int pr = a.parent[static_cast<size_t>(b) * M + i];
+            const int tk = a.token[static_cast<size_t>(b) * M + i];
+            sh.parent[i] = pr;
+            sh.token[i] = tk;
+            const bool ok = i == 0 ? pr == -1 : (pr >= 0 && pr < i && tk >= 0 && tk < V);
             if (!ok)
                 atomicOr(&sh.flag, 1);
         }
@@ -1100,7 +1113,6 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
             bad = !arrive(u);
             double c = 0.0, Z = 1.0;
             bool ts_current = false;  // lds_ts holds the tile sums of the current (c, Z)
-            double tot_by_part[kTreeParts];
             int s = 1;
             while (!bad) {
                 while (s < n && sh.parent[s] != u)
@@ -1155,8 +1167,8 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
                     c = c2;
                     Z = Z2;
                     ts_current = true;
-                    for (int j = 0; j < kTreeParts; ++j)
-                        tot_by_part[j] = part_d(sh.xp[j], 2);
+                    if (tid < kTreeParts)
+                        sh.tot_keep[tid] = part_d(sh.xp[tid], 2);
                 } else {
                     ts_current = false;  // an empty residual (rounding): pi stays
                 }
@@ -1174,17 +1186,17 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
                 if (!ts_current) {
                     if (!tree_tile_pass<DT, VEC, NT>(v, rows, lds_ts, sh))
                         bad = true;
-                    else
-                        for (int j = 0; j < kTreeParts; ++j)
-                            tot_by_part[j] = part_d(sh.xp[j], 2);
+                    else if (tid < kTreeParts)
+                        sh.tot_keep[tid] = part_d(sh.xp[tid], 2);
                 }
+                __syncthreads();  // sh.tot_keep
                 if (!bad) {
                     // The draw position over the parts' totals in part order;
                     // past the total (rounding only) it falls to the last part
                     // with mass, which then takes its last positive element.
                     double S = 0.0;
                     for (int j = 0; j < kTreeParts; ++j)
-                        S += tot_by_part[j];
+                        S += sh.tot_keep[j];
                     const Words4 w = verify_block(a.seed, a.offset, static_cast<uint32_t>(b),
                                                   static_cast<uint32_t>(L));
                     const float uu = uniform24(w.w1);
@@ -1193,7 +1205,7 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
                         int owner = -1, last = -1;
                         double P = 0.0, P_owner = 0.0, P_last = 0.0;
                         for (int j = 0; j < kTreeParts; ++j) {
-                            const double tj = tot_by_part[j];
+                            const double tj = sh.tot_keep[j];
                             if (tj > 0.0) {
                                 if (owner < 0 && P + tj > tau) {
                                     owner = j;
