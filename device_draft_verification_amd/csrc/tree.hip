@@ -318,7 +318,7 @@ int spec_tree_verify_init(int batch, int max_nodes, int vocab, int dtype, void* 
     }
     int sample_groups = 0;
     if (tree_sample_max_groups(dtype, &sample_groups) != hipSuccess || sample_groups < 1) {
-        hipFree(ctx->part);
+        (void)hipFree(ctx->part);
         delete ctx;
         return SPEC_EHIP;
     }
@@ -326,8 +326,8 @@ int spec_tree_verify_init(int batch, int max_nodes, int vocab, int dtype, void* 
     const size_t share_bytes = static_cast<size_t>(ctx->sample_groups) * tree_sample_group_bytes();
     if (hipMalloc(reinterpret_cast<void**>(&ctx->shares), share_bytes) != hipSuccess ||
         hipMemset(ctx->shares, 0, share_bytes) != hipSuccess) {
-        hipFree(ctx->shares);
-        hipFree(ctx->part);
+        (void)hipFree(ctx->shares);
+        (void)hipFree(ctx->part);
         delete ctx;
         return SPEC_ENOMEM;
     }

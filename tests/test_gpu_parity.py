@@ -396,3 +396,22 @@ def test_scalar_mode_gamma_zero_and_large_gamma():
     lp = rng.normal(-2, 0.3, size=(300, 70, 2)).astype(np.float32)
     got, ref = _scalar_compare(lp, 123, 456)
     assert got.max() <= 70
+
+
+def test_empty_batch_is_a_no_op():
+    """B = 0: both calls return success and launch nothing (empty tensors give
+    null data pointers, which a zero batch never dereferences); a later call
+    on a non-empty context on the same stream still verifies correctly."""
+    for G in (0, 3):
+        ctx = sv.spec_verify_init(0, G, 1000, torch.bfloat16)
+        e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device="cuda")
+        alen = e(0, dt=torch.int32)
+        sv.spec_verify(ctx, e(0, G, 1000), e(0, G + 1, 1000), e(0, G, dt=torch.int32),
+                       e(0, dt=torch.float32), 0, 0, alen, e(0, G + 1, dt=torch.int32))
+        sv.spec_accept_logprobs(ctx, e(0, G, 2, dt=torch.float32), 0, 0, alen)
+        torch.cuda.synchronize()
+        sv.spec_verify_destroy(ctx)
+    rec = specgen.config(2).replace(batch=3, vocab=2048)
+    d = specgen.generate(rec)
+    gpu = run_gpu(to_device(d))
+    assert_parity(compare(gpu, _oracle(d), d["temperature"]), "after empty calls")
