@@ -257,13 +257,25 @@ __device__ inline int wave_max_int(int v) {
 // The tile sums `ts` (fp32) of one row, cut into 64 contiguous runs: lane l
 // sums run l in fp64 and the wavefront scans the runs; the last lane's prefix
 // is the row total S.
+// With REGS, runs of up to kRunRegs tiles (rows of up to 64 * kRunRegs tiles)
+// are read into registers with reads issued together (clamped into range, the
+// values past the run masked to zero) and walked again from there by
+// locate_tile; otherwise, and for longer runs, they are read in a loop. Both
+// forms add in the same order. The verifier's draw takes REGS (its 1.2 us of
+// dependent LDS reads drop to one round trip); the tree sampler, whose walk
+// holds more registers, the loop.
+constexpr int kRunRegs = 8;
+
 struct TileRuns {
     int a0, a1;       // this lane's run [a0, a1)
     int last_pos;     // its last tile with mass, or -1
+    bool in_regs;     // the run's values are in v (wave-uniform)
     double mine;      // its run's sum
     double inc;       // inclusive prefix of the runs through this lane
+    float v[kRunRegs];
 };
 
+template <bool REGS>
 __device__ inline TileRuns tile_runs(const float* ts, int ntiles) {
     const int lane = threadIdx.x & 63;
     const int per = (ntiles + 63) / 64;
@@ -272,11 +284,29 @@ __device__ inline TileRuns tile_runs(const float* ts, int ntiles) {
     tr.a1 = tr.a0 + per < ntiles ? tr.a0 + per : ntiles;
     tr.mine = 0.0;
     tr.last_pos = -1;
-    for (int t = tr.a0; t < tr.a1; ++t) {
-        const float v = ts[t];
-        tr.mine += static_cast<double>(v);
-        if (v > 0.0f)
-            tr.last_pos = t;
+    tr.in_regs = REGS && ntiles >= 1 && per <= kRunRegs;
+    if (REGS && tr.in_regs) {
+#pragma unroll
+        for (int j = 0; j < kRunRegs; ++j) {
+            const int t = tr.a0 + j < ntiles ? tr.a0 + j : ntiles - 1;
+            const float v = ts[t];
+            tr.v[j] = tr.a0 + j < tr.a1 ? v : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kRunRegs; ++j) {
+            if (tr.a0 + j < tr.a1) {
+                tr.mine += static_cast<double>(tr.v[j]);
+                if (tr.v[j] > 0.0f)
+                    tr.last_pos = tr.a0 + j;
+            }
+        }
+    } else {
+        for (int t = tr.a0; t < tr.a1; ++t) {
+            const float v = ts[t];
+            tr.mine += static_cast<double>(v);
+            if (v > 0.0f)
+                tr.last_pos = t;
+        }
     }
     tr.inc = wave_inclusive_scan(tr.mine);
     return tr;
@@ -286,18 +316,34 @@ __device__ inline TileRuns tile_runs(const float* ts, int ntiles) {
 // Returns the tile and writes the fp64 prefix before it; when tau lies beyond
 // the total (rounding only), returns the last tile with mass and writes -1
 // (take its last positive element).
+template <bool REGS>
 __device__ inline int locate_tile(const float* ts, const TileRuns& tr, double tau, double* P_out) {
     int hit = -1;
     double before = 0.0;
     double acc = tr.inc - tr.mine;
-    for (int t = tr.a0; t < tr.a1 && hit < 0; ++t) {
-        const float v = ts[t];
-        const double next = acc + static_cast<double>(v);
-        if (v > 0.0f && next > tau) {
-            hit = t;
-            before = acc;
+    if (REGS && tr.in_regs) {
+#pragma unroll
+        for (int j = 0; j < kRunRegs; ++j) {
+            if (tr.a0 + j < tr.a1 && hit < 0) {
+                const float v = tr.v[j];
+                const double next = acc + static_cast<double>(v);
+                if (v > 0.0f && next > tau) {
+                    hit = tr.a0 + j;
+                    before = acc;
+                }
+                acc = next;
+            }
         }
-        acc = next;
+    } else {
+        for (int t = tr.a0; t < tr.a1 && hit < 0; ++t) {
+            const float v = ts[t];
+            const double next = acc + static_cast<double>(v);
+            if (v > 0.0f && next > tau) {
+                hit = t;
+                before = acc;
+            }
+            acc = next;
+        }
     }
     const int fl = first_lane(hit >= 0);
     if (fl < 64) {
@@ -382,20 +428,20 @@ __device__ inline int draw_p_fallback(SeqRows& s, float u, int ntiles, int group
 // The token at position tau of the weights whose tile sums are ts.
 template <int DT, bool VEC, bool NT>
 __device__ inline int draw_at(const SeqRows& s, double tau, const float* ts, int ntiles, int groups) {
-    const TileRuns tr = tile_runs(ts, ntiles);
+    const TileRuns tr = tile_runs<false>(ts, ntiles);
     double P;
-    const int tile = locate_tile(ts, tr, tau, &P);
+    const int tile = locate_tile<false>(ts, tr, tau, &P);
     return scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
 }
 
 template <int DT, bool VEC, bool NT>
 __device__ inline int draw_token(SeqRows& s, float u, const float* ts, int ntiles, int groups) {
-    const TileRuns tr = tile_runs(ts, ntiles);
+    const TileRuns tr = tile_runs<true>(ts, ntiles);
     const double S = lane63_f64(tr.inc);
     if (S > 0.0) {
         const double tau = static_cast<double>(u) * S;
         double P;
-        const int tile = locate_tile(ts, tr, tau, &P);
+        const int tile = locate_tile<true>(ts, tr, tau, &P);
         return scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
     }
     return draw_p_fallback<DT, VEC, NT>(s, u, ntiles, groups);
