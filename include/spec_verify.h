@@ -60,8 +60,6 @@
  * uses that has no finite logit gives out_accept_len[b] = -1 and
  * out_tokens[b, :] = -1. Logits equal to +inf or NaN are a precondition
  * violation: the result is unspecified but no out-of-bounds access happens.
- * If a kernel is aborted mid-call the context must be destroyed and created
- * again (its internal counters may be left non-zero).
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -108,8 +106,9 @@ int spec_verify_set_stream(spec_verify_ctx *ctx, void *hip_stream);
  *   out_accept_len [B]          int32: k, or -1 for a rejected sequence
  *   out_tokens     [B, G+1]     int32: tokens[0..k) = draft, tokens[k] =
  *                               the extra token, the rest -1
- * Enqueues three kernels on the context's stream (row normalisers; gather,
- * accept and first rejection; residual or bonus draw) and returns.
+ * Enqueues its kernels on the context's stream and returns: row
+ * normalisers; gather, accept and first rejection; the residual or bonus
+ * draw (one kernel from B = 128, tile sums then locate below that).
  */
 int spec_verify(spec_verify_ctx *ctx, const void *logits_draft,
                 const void *logits_target, const int32_t *draft_tokens,
