@@ -415,3 +415,49 @@ def test_empty_batch_is_a_no_op():
     d = specgen.generate(rec)
     gpu = run_gpu(to_device(d))
     assert_parity(compare(gpu, _oracle(d), d["temperature"]), "after empty calls")
+
+
+def test_graph_capture_replays_match_eager():
+    """The whole call records into a HIP graph (its workspace is allocated at
+    init and nothing on the path clears memory with a memset node). Replays
+    on two input sets copied into the captured buffers, with eager work in
+    between, equal eager calls with the same (seed, offset) bit for bit."""
+    rec = specgen.config(4).replace(batch=24, vocab=20000)
+    sets = [to_device(specgen.generate(rec.replace(seed=s))) for s in (41, 42)]
+    B, G = rec.batch, rec.gamma
+    static = {k: v.clone() for k, v in sets[0].items()}
+    s = torch.cuda.Stream()
+    ctx = sv.spec_verify_init(B, G, rec.vocab, torch.bfloat16, stream=s)
+    alen = torch.empty(B, dtype=torch.int32, device="cuda")
+    toks = torch.empty(B, G + 1, dtype=torch.int32, device="cuda")
+
+    def call():
+        sv.spec_verify(ctx, static["logits_draft"], static["logits_target"],
+                       static["draft_tokens"], static["temperature"], 9, 5, alen, toks)
+
+    eager = []
+    for t in sets:
+        for k in static:
+            static[k].copy_(t[k])
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            call()
+        s.synchronize()
+        eager.append((alen.clone(), toks.clone()))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for r, j in enumerate([1, 0, 1, 0]):
+        for k in static:
+            static[k].copy_(sets[j][k])
+        alen.fill_(-7)
+        toks.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(alen, eager[j][0]), f"replay {r}"
+        assert torch.equal(toks, eager[j][1]), f"replay {r}"
+        _ = (sets[j]["logits_target"].float().sum()).item()  # eager work between replays
+    del g
+    sv.spec_verify_destroy(ctx)
