@@ -90,6 +90,21 @@ enum spec_status {
  * zeroes its counters. The shape is fixed for the context's lifetime.
  * batch * (2*gamma+1) and vocab must each be below 2^31.
  * Returns SPEC_OK and *out_ctx, or a negative status and *out_ctx = NULL.
+ *
+ * The launch geometry is chosen here from the shape. For tuning, these
+ * environment variables, read once by this call, override it (results do not
+ * depend on them, except that the arithmetic order of the split merges
+ * follows the split count):
+ *   SPEC_VERIFY_ROW_SPLIT       vocabulary splits per row of the row kernel
+ *                               (> 0; capped at 64 and at the row's batches)
+ *   SPEC_VERIFY_ROW_UNROLL      16-byte groups in flight per thread: 2, 4, 8
+ *   SPEC_VERIFY_ROW_NT          0: ordinary instead of non-temporal loads
+ *   SPEC_VERIFY_RESIDUAL_FUSED  0/1: one workgroup per sequence for the draw
+ *                               (default from B = 128)
+ *   SPEC_VERIFY_RESIDUAL_SPLIT  vocabulary splits of the tile-sum kernel (> 0;
+ *                               selects the two-kernel draw)
+ *   SPEC_VERIFY_RESIDUAL_UNROLL tiles per batch in that kernel: 2 or 4
+ *   SPEC_VERIFY_OUTCOME_SPLIT   vocabulary splits of spec_verify_outcomes
  */
 int spec_verify_init(int batch, int gamma, int vocab, int dtype, void *hip_stream,
                      spec_verify_ctx **out_ctx);
