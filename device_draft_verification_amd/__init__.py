@@ -9,7 +9,7 @@ the same function names (``binding``) and the build script (``build``).
 """
 from .binding import (  # noqa: F401
     EXPORTED, LIB_PATH, SPEC_BF16, SPEC_F32, Context, SpecVerifyError, dtype_code,
-    load_library, spec_accept_logprobs, spec_verify, spec_verify_copy_lse,
+    load_library, spec_accept_logprobs, spec_verify, spec_verify_copy_lse, spec_verify_offset_ptr,
     spec_verify_destroy, spec_verify_enable_timing, spec_verify_get_geometry,
     spec_verify_init, spec_verify_philox_words, spec_verify_read_timing,
     spec_verify_set_stream, spec_verify_strerror, spec_verify_outcomes, SPEC_OUTCOME_MAX_F,

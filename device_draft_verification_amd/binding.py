@@ -24,7 +24,8 @@ SPEC_ENOMEM = -3
 SPEC_ESTATE = -4
 
 EXPORTED = (
-    "spec_verify_init", "spec_verify_set_stream", "spec_verify", "spec_accept_logprobs",
+    "spec_verify_init", "spec_verify_set_stream", "spec_verify", "spec_verify_offset_ptr",
+    "spec_accept_logprobs",
     "spec_verify_copy_lse", "spec_verify_philox_words", "spec_verify_enable_timing",
     "spec_verify_read_timing", "spec_verify_get_geometry", "spec_verify_destroy",
     "spec_verify_strerror", "spec_verify_outcomes",
@@ -66,6 +67,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_verify_init": ([i32, i32, i32, i32, P, ctypes.POINTER(P)], i32),
         "spec_verify_set_stream": ([P, P], i32),
         "spec_verify": ([P, P, P, P, P, u64, u64, P, P], i32),
+        "spec_verify_offset_ptr": ([P, P, P, P, P, u64, P, P, P], i32),
         "spec_accept_logprobs": ([P, P, u64, u64, P], i32),
         "spec_verify_copy_lse": ([P, P], i32),
         "spec_verify_philox_words": ([P, u64, u64, P], i32),
@@ -192,6 +194,28 @@ def spec_verify(ctx: Context, logits_draft, logits_target, draft_tokens, tempera
     _check("spec_verify", load_library().spec_verify(
         ctx.handle, _ptr(logits_draft) if G > 0 else None, _ptr(logits_target),
         _ptr(draft_tokens) if G > 0 else None, _ptr(temperature), seed, offset,
+        _ptr(out_accept_len), _ptr(out_tokens)))
+
+
+def spec_verify_offset_ptr(ctx: Context, logits_draft, logits_target, draft_tokens, temperature,
+                           seed: int, offset_dev, out_accept_len, out_tokens) -> None:
+    """spec_verify with the Philox offset read on the device from offset_dev, a
+    one-element int64 (or uint64) device tensor holding the offset's bits."""
+    B, G, V = ctx.batch, ctx.gamma, ctx.vocab
+    ldt = torch.bfloat16 if ctx.dtype == SPEC_BF16 else torch.float32
+    if G > 0:
+        _expect(logits_draft, (B, G, V), ldt, "logits_draft")
+        _expect(draft_tokens, (B, G), torch.int32, "draft_tokens")
+    _expect(logits_target, (B, G + 1, V), ldt, "logits_target")
+    _expect(temperature, (B,), torch.float32, "temperature")
+    _expect(out_accept_len, (B,), torch.int32, "out_accept_len")
+    _expect(out_tokens, (B, G + 1), torch.int32, "out_tokens")
+    if offset_dev is None or offset_dev.numel() != 1 or offset_dev.element_size() != 8 \
+            or offset_dev.device.type != "cuda":
+        raise ValueError("offset_dev must be a one-element 64-bit device tensor")
+    _check("spec_verify_offset_ptr", load_library().spec_verify_offset_ptr(
+        ctx.handle, _ptr(logits_draft) if G > 0 else None, _ptr(logits_target),
+        _ptr(draft_tokens) if G > 0 else None, _ptr(temperature), seed, _ptr(offset_dev),
         _ptr(out_accept_len), _ptr(out_tokens)))
 
 

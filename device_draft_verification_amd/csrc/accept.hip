@@ -79,7 +79,8 @@ template <int DT>
 __global__ __launch_bounds__(64) void accept_kernel(
     const void* __restrict__ draft, const void* __restrict__ target,
     const int32_t* __restrict__ tokens, const float* __restrict__ temperature, int gamma,
-    int vocab, int nsplit, uint64_t seed, uint64_t offset, const Partial* __restrict__ part,
+    int vocab, int nsplit, uint64_t seed, uint64_t offset_arg,
+    const uint64_t* __restrict__ offset_dev, const Partial* __restrict__ part,
     const float* __restrict__ gathered, RowNorm* __restrict__ rn, double* __restrict__ lse_out,
     SeqState* __restrict__ seq,
     int32_t* __restrict__ out_len, int32_t* __restrict__ out_tok) {
@@ -87,6 +88,9 @@ __global__ __launch_bounds__(64) void accept_kernel(
     const int lane = threadIdx.x;
     const int G = gamma;
     const int rps = 2 * G + 1;
+    // The Philox offset: the argument, or a word in device memory that the
+    // caller advances between replays of a captured call.
+    const uint64_t offset = offset_dev ? offset_dev[0] : offset_arg;
     const size_t row0 = static_cast<size_t>(b) * rps;
 
     float inv_t = 0.0f;
@@ -253,18 +257,19 @@ __global__ __launch_bounds__(256) void philox_words_kernel(int batch, int gamma,
 
 hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const void* target,
                          const int32_t* tokens, const float* temperature, uint64_t seed,
-                         uint64_t offset, const Partial* part, const float* gathered, RowNorm* rn,
+                         uint64_t offset, const uint64_t* offset_dev, const Partial* part,
+                         const float* gathered, RowNorm* rn,
                          double* lse_out, SeqState* seq, int32_t* out_len, int32_t* out_tok,
                          hipStream_t stream) {
     if (s.batch == 0)
         return hipSuccess;
     if (s.dtype == kBF16)
         accept_kernel<kBF16><<<dim3(s.batch), dim3(64), 0, stream>>>(
-            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, part,
+            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, offset_dev, part,
             gathered, rn, lse_out, seq, out_len, out_tok);
     else
         accept_kernel<kF32><<<dim3(s.batch), dim3(64), 0, stream>>>(
-            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, part,
+            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, offset_dev, part,
             gathered, rn, lse_out, seq, out_len, out_tok);
     return hipGetLastError();
 }

@@ -199,9 +199,16 @@ int spec_verify_set_stream(spec_verify_ctx* ctx, void* hip_stream) {
     return SPEC_OK;
 }
 
-int spec_verify(spec_verify_ctx* ctx, const void* logits_draft, const void* logits_target,
+}  // extern "C"
+
+namespace {
+
+// The verification call; the Philox offset is `offset`, or the device word
+// *offset_dev when that is non-null.
+int verify_impl(spec_verify_ctx* ctx, const void* logits_draft, const void* logits_target,
                 const int32_t* draft_tokens, const float* temperature, uint64_t seed,
-                uint64_t offset, int32_t* out_accept_len, int32_t* out_tokens) {
+                uint64_t offset, const uint64_t* offset_dev, int32_t* out_accept_len,
+                int32_t* out_tokens) {
     if (!ctx)
         return SPEC_EINVAL;
     const Shape& s = ctx->shape;
@@ -238,8 +245,8 @@ int spec_verify(spec_verify_ctx* ctx, const void* logits_draft, const void* logi
     if (ev && hipEventRecord(ev[1], st) != hipSuccess)
         return SPEC_EHIP;
     if (launch_accept(s, ctx->nsplit_rows, logits_draft, logits_target, draft_tokens, temperature,
-                      seed, offset, ctx->part, ctx->gathered, ctx->rn, ctx->lse, ctx->seq,
-                      out_accept_len, out_tokens, st) != hipSuccess)
+                      seed, offset, offset_dev, ctx->part, ctx->gathered, ctx->rn, ctx->lse,
+                      ctx->seq, out_accept_len, out_tokens, st) != hipSuccess)
         return SPEC_EHIP;
     if (ev && hipEventRecord(ev[2], st) != hipSuccess)
         return SPEC_EHIP;
@@ -250,6 +257,27 @@ int spec_verify(spec_verify_ctx* ctx, const void* logits_draft, const void* logi
         return SPEC_EHIP;
     ctx->have_verified = true;
     return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify(spec_verify_ctx* ctx, const void* logits_draft, const void* logits_target,
+                const int32_t* draft_tokens, const float* temperature, uint64_t seed,
+                uint64_t offset, int32_t* out_accept_len, int32_t* out_tokens) {
+    return verify_impl(ctx, logits_draft, logits_target, draft_tokens, temperature, seed, offset,
+                       nullptr, out_accept_len, out_tokens);
+}
+
+int spec_verify_offset_ptr(spec_verify_ctx* ctx, const void* logits_draft,
+                           const void* logits_target, const int32_t* draft_tokens,
+                           const float* temperature, uint64_t seed, const uint64_t* offset_dev,
+                           int32_t* out_accept_len, int32_t* out_tokens) {
+    if (!offset_dev || !aligned(offset_dev, 8))
+        return SPEC_EINVAL;
+    return verify_impl(ctx, logits_draft, logits_target, draft_tokens, temperature, seed, 0,
+                       offset_dev, out_accept_len, out_tokens);
 }
 
 int spec_accept_logprobs(spec_verify_ctx* ctx, const float* logprobs, uint64_t seed,

@@ -42,10 +42,12 @@ hipError_t launch_row_norm(const Shape& s, bool vec, const RowTuning& tu, const 
                            Partial* part, float* gathered, hipStream_t stream);
 
 // Split merge, gather, accept test, first rejection and the emitted prefix:
-// one 64-lane wavefront per sequence.
+// one 64-lane wavefront per sequence. With offset_dev non-null the Philox
+// offset is read from that device word instead of `offset`.
 hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const void* target,
                          const int32_t* tokens, const float* temperature, uint64_t seed,
-                         uint64_t offset, const Partial* part, const float* gathered, RowNorm* rn,
+                         uint64_t offset, const uint64_t* offset_dev, const Partial* part,
+                         const float* gathered, RowNorm* rn,
                          double* lse_out, SeqState* seq, int32_t* out_len, int32_t* out_tok,
                          hipStream_t stream);
 

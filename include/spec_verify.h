@@ -131,6 +131,22 @@ int spec_verify(spec_verify_ctx *ctx, const void *logits_draft,
                 int32_t *out_accept_len, int32_t *out_tokens);
 
 /*
+ * spec_verify with the Philox offset read on the device from *offset_dev
+ * (one uint64 word, device memory, 8-byte aligned, owned by the caller) when
+ * the accept kernel runs, instead of passed by value. A call recorded into a
+ * HIP graph then draws fresh uniforms on every replay if the caller advances
+ * the word between replays (for instance with a one-element add recorded in
+ * the same graph); every other argument and result is as for spec_verify,
+ * which this equals bit for bit when *offset_dev holds the same offset.
+ * Returns SPEC_EINVAL for a NULL or misaligned offset_dev.
+ */
+int spec_verify_offset_ptr(spec_verify_ctx *ctx, const void *logits_draft,
+                           const void *logits_target, const int32_t *draft_tokens,
+                           const float *temperature, uint64_t seed,
+                           const uint64_t *offset_dev, int32_t *out_accept_len,
+                           int32_t *out_tokens);
+
+/*
  * Scalar-only mode: reads only the gathered log-probability pairs, O(B*G)
  * bytes, nothing of size V (FlashSpec summary, Methodology section 1,
  * mechanism and complexity bullets). Device pointers:

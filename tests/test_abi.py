@@ -58,6 +58,11 @@ def test_host_argument_checks(lib):
     assert lib.spec_verify_init(4, 2, 100, 7, None, ctypes.byref(h)) == sv.binding.SPEC_EINVAL
     assert not h.value
     assert lib.spec_verify_init(-1, 2, 100, 1, None, ctypes.byref(h)) == sv.binding.SPEC_EINVAL
+    # no offset word, or a misaligned one: refused before the context is used
+    assert lib.spec_verify_offset_ptr(None, None, None, None, None, 0, None, None,
+                                      None) == sv.binding.SPEC_EINVAL
+    assert lib.spec_verify_offset_ptr(None, None, None, None, None, 0, ctypes.c_void_p(4),
+                                      None, None) == sv.binding.SPEC_EINVAL
     assert lib.spec_verify_init(4, -1, 100, 1, None, ctypes.byref(h)) == sv.binding.SPEC_EINVAL
     assert lib.spec_verify_init(4, 2, 0, 1, None, ctypes.byref(h)) == sv.binding.SPEC_EINVAL
     assert lib.spec_verify_init(4, 2, 10, 1, None, None) == sv.binding.SPEC_EINVAL

@@ -461,3 +461,59 @@ def test_graph_capture_replays_match_eager():
         _ = (sets[j]["logits_target"].float().sum()).item()  # eager work between replays
     del g
     sv.spec_verify_destroy(ctx)
+
+
+def test_offset_from_device_memory_and_graph_replays_with_fresh_uniforms():
+    """spec_verify_offset_ptr equals spec_verify with the same offset bit for
+    bit; captured in a HIP graph together with a one-element add that advances
+    the offset word, each replay equals the eager call at the next offset."""
+    rec = specgen.config(4).replace(batch=24, vocab=20000)
+    d = specgen.generate(rec)
+    t = to_device(d)
+    B, G = rec.batch, rec.gamma
+    s = torch.cuda.Stream()
+    ctx = sv.spec_verify_init(B, G, rec.vocab, torch.bfloat16, stream=s)
+    alen = torch.empty(B, dtype=torch.int32, device="cuda")
+    toks = torch.empty(B, G + 1, dtype=torch.int32, device="cuda")
+    off = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def eager(offset, ptr):
+        with torch.cuda.stream(s):
+            if ptr:
+                off.fill_(offset)
+                sv.spec_verify_offset_ptr(ctx, t["logits_draft"], t["logits_target"],
+                                          t["draft_tokens"], t["temperature"], 3, off, alen, toks)
+            else:
+                sv.spec_verify(ctx, t["logits_draft"], t["logits_target"], t["draft_tokens"],
+                               t["temperature"], 3, offset, alen, toks)
+        s.synchronize()
+        return alen.clone(), toks.clone()
+
+    ref = {o: eager(o, False) for o in range(10, 14)}
+    for o in (10, 11, (1 << 40) + 7):
+        a = eager(o, True)
+        b = eager(o, False) if o not in ref else ref[o]
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), o
+    assert not all(torch.equal(ref[10][1], ref[o][1]) for o in (11, 12, 13))
+
+    off.fill_(10)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        sv.spec_verify_offset_ptr(ctx, t["logits_draft"], t["logits_target"], t["draft_tokens"],
+                                  t["temperature"], 3, off, alen, toks)
+        off.add_(1)
+    torch.cuda.synchronize()
+    off.fill_(10)  # the capture itself ran nothing
+    torch.cuda.synchronize()
+    for o in range(10, 14):
+        alen.fill_(-7)
+        toks.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(alen, ref[o][0]), o
+        assert torch.equal(toks, ref[o][1]), o
+        assert int(off.item()) == o + 1
+    del g
+    sv.spec_verify_destroy(ctx)
