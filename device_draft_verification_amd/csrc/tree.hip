@@ -2,7 +2,8 @@
 //
 // Pruning (SpecLA summary, Methodology section 3): a tree's low-probability
 // paths are cut by their cumulative draft log-probability before the target
-// verifies them. One workgroup per tree, one thread per node (M <= 256):
+// verifies them. One workgroup per tree, one thread per node (M <= 256; up to
+// 64 nodes one wavefront, with shuffles in place of the barriers):
 //   * path scores c(i) = c(parent) + logq(i) are resolved level by level, each
 //     with the one double addition the definition states, so they equal the
 //     root-down sums bit for bit;
@@ -111,6 +112,81 @@ __global__ __launch_bounds__(kTreeThreads) void tree_prune_kernel(
             np = old == 0 ? -1 : ni[par[old]];
         }
         new_parent[base + i] = np;
+    }
+    if (i == 0)
+        count[b] = total;
+}
+
+// Trees of at most 64 nodes: one wavefront per tree, node i on lane i, the
+// same three steps without a barrier. Path scores resolve level by level
+// through lane shuffles (a node adds its own term once, to its parent's final
+// score, so the sums are the root-down ones bit for bit); a node's rank counts
+// the scores broadcast lane by lane; the kept nodes are renumbered by a ballot
+// prefix count.
+__device__ inline double readlane_f64(double v, int j) {
+    const long long u = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffll), j);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), j);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                                static_cast<long long>(static_cast<unsigned>(lo)));
+}
+
+__global__ __launch_bounds__(64) void tree_prune_wave_kernel(
+    const int32_t* __restrict__ parent, const float* __restrict__ logq, int M, double tau,
+    int budget, double* __restrict__ cum, int32_t* __restrict__ new_index,
+    int32_t* __restrict__ new_parent, int32_t* __restrict__ count) {
+    __shared__ int old_of_new[64];
+    const int b = blockIdx.x, i = threadIdx.x;
+    const bool node = i < M;
+    const size_t base = static_cast<size_t>(b) * M;
+    const int p = node ? parent[base + i] : -1;
+    const float lq = node ? logq[base + i] : 0.0f;
+    const bool bad = node && (i == 0 ? p != -1 : (p < 0 || p >= i || !(lq <= 0.0f)));
+    if (__ballot(bad)) {
+        if (node) {
+            cum[base + i] = __builtin_nan("");
+            new_index[base + i] = -1;
+            new_parent[base + i] = -1;
+        }
+        if (i == 0)
+            count[b] = -1;
+        return;
+    }
+    // Every parent now lies in [0, i) (the root's is -1): one level per round.
+    const int src = p >= 0 ? p : 0;
+    double c = 0.0;
+    bool ready = i == 0 || !node;
+    while (__ballot(!ready)) {
+        const double cp = __shfl(c, src, 64);
+        const int rp = __shfl(ready ? 1 : 0, src, 64);
+        if (!ready && rp) {
+            c = cp + static_cast<double>(lq);
+            ready = true;
+        }
+    }
+    int rank = 0;
+    for (int j = 0; j < M; ++j) {
+        const double cj = readlane_f64(c, j);
+        rank += (cj > c || (cj == c && j < i)) ? 1 : 0;
+    }
+    const bool keep = node && c >= tau && rank < budget;
+    const unsigned long long m = __ballot(keep);
+    const int before = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
+    const int total = __popcll(m);
+    const int ni = keep ? before : -1;
+    if (keep)
+        old_of_new[before] = i;
+    __syncthreads();
+    // New node i < total is old node `old`; its new parent is the new index
+    // of old's parent (-1 for the root).
+    const int old = i < total ? old_of_new[i] : 0;
+    const int p_old = __shfl(p, old, 64);
+    const int ni_of_p = __shfl(ni, p_old >= 0 ? p_old : 0, 64);
+    if (node) {
+        cum[base + i] = c;
+        new_index[base + i] = ni;
+        new_parent[base + i] = i < total && old != 0 ? ni_of_p : -1;
     }
     if (i == 0)
         count[b] = total;
@@ -281,10 +357,15 @@ int spec_tree_prune(int batch, int nodes, const int32_t* parent, const float* lo
         !aligned(parent, 4) || !aligned(logq, 4) || !aligned(out_cum, 8) ||
         !aligned(out_new_index, 4) || !aligned(out_new_parent, 4) || !aligned(out_count, 4))
         return SPEC_EINVAL;
-    tree_prune_kernel<<<dim3(static_cast<unsigned>(batch)), dim3(kTreeThreads), 0,
-                        static_cast<hipStream_t>(hip_stream)>>>(parent, logq, nodes, tau, budget,
-                                                                out_cum, out_new_index,
-                                                                out_new_parent, out_count);
+    if (nodes <= 64)
+        tree_prune_wave_kernel<<<dim3(static_cast<unsigned>(batch)), dim3(64), 0,
+                                 static_cast<hipStream_t>(hip_stream)>>>(
+            parent, logq, nodes, tau, budget, out_cum, out_new_index, out_new_parent, out_count);
+    else
+        tree_prune_kernel<<<dim3(static_cast<unsigned>(batch)), dim3(kTreeThreads), 0,
+                            static_cast<hipStream_t>(hip_stream)>>>(parent, logq, nodes, tau,
+                                                                    budget, out_cum, out_new_index,
+                                                                    out_new_parent, out_count);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 

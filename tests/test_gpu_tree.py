@@ -40,7 +40,7 @@ def check_prune(g, o):
     assert np.array_equal(g["cum"].view(np.uint64), o["cum"].view(np.uint64))
 
 
-@pytest.mark.parametrize("B,M", [(7, 1), (16, 24), (256, 64), (40, 256)])
+@pytest.mark.parametrize("B,M", [(7, 1), (16, 24), (256, 64), (9, 65), (40, 256)])
 def test_prune_parity(B, M):
     trees = specgen.draft_trees(B, M, 1000, seed=M)
     for tau, K in ((np.log(1e-3), max(1, M // 2)), (-np.inf, M), (np.log(0.3), 3), (0.0, 1)):
