@@ -260,18 +260,13 @@ hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const vo
                          uint64_t offset, const uint64_t* offset_dev, const Partial* part,
                          const float* gathered, RowNorm* rn,
                          double* lse_out, SeqState* seq, int32_t* out_len, int32_t* out_tok,
-                         hipStream_t stream) {
+                         hipStream_t stream, const LaunchEvents& ev) {
     if (s.batch == 0)
         return hipSuccess;
-    if (s.dtype == kBF16)
-        accept_kernel<kBF16><<<dim3(s.batch), dim3(64), 0, stream>>>(
-            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, offset_dev, part,
-            gathered, rn, lse_out, seq, out_len, out_tok);
-    else
-        accept_kernel<kF32><<<dim3(s.batch), dim3(64), 0, stream>>>(
-            draft, target, tokens, temperature, s.gamma, s.vocab, nsplit, seed, offset, offset_dev, part,
-            gathered, rn, lse_out, seq, out_len, out_tok);
-    return hipGetLastError();
+    return launch(s.dtype == kBF16 ? accept_kernel<kBF16> : accept_kernel<kF32>, dim3(s.batch),
+                  dim3(64), 0, stream, ev, draft, target, tokens, temperature, s.gamma, s.vocab,
+                  nsplit, seed, offset, offset_dev, part, gathered, rn, lse_out, seq, out_len,
+                  out_tok);
 }
 
 hipError_t launch_accept_scalar(int batch, int gamma, const float* logprobs, uint64_t seed,

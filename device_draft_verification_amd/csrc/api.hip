@@ -39,7 +39,7 @@ struct spec_verify_ctx {
 
     int timing_slots = 0;
     int timing_count = 0;
-    std::vector<hipEvent_t> events;  // 4 per slot
+    std::vector<hipEvent_t> events;  // per slot: start and stop of each of the three steps
 };
 
 namespace {
@@ -241,30 +241,28 @@ int verify_impl(spec_verify_ctx* ctx, const void* logits_draft, const void* logi
     const bool vec = (s.vocab % group_width(s.dtype)) == 0 && aligned(logits_target, 16) &&
                      aligned(logits_draft, 16);
 
-    hipEvent_t* ev = nullptr;
+    // Timing mode: each step's start and stop events ride on its kernels'
+    // own dispatches, so they time the kernels alone.
+    LaunchEvents ev_row, ev_acc, ev_res;
     if (ctx->timing_slots > 0) {
-        ev = &ctx->events[static_cast<size_t>(ctx->timing_count % ctx->timing_slots) * 4];
+        hipEvent_t* ev = &ctx->events[static_cast<size_t>(ctx->timing_count % ctx->timing_slots) * 6];
         ++ctx->timing_count;
+        ev_row = LaunchEvents{ev[0], ev[1]};
+        ev_acc = LaunchEvents{ev[2], ev[3]};
+        ev_res = LaunchEvents{ev[4], ev[5]};
     }
     hipStream_t st = ctx->stream;
-    if (ev && hipEventRecord(ev[0], st) != hipSuccess)
-        return SPEC_EHIP;
     const RowTuning tu{ctx->nsplit_rows, ctx->row_unroll, ctx->row_nontemporal};
     if (launch_row_norm(s, vec, tu, logits_draft, logits_target, temperature, draft_tokens,
-                        ctx->part, ctx->gathered, st) != hipSuccess)
-        return SPEC_EHIP;
-    if (ev && hipEventRecord(ev[1], st) != hipSuccess)
+                        ctx->part, ctx->gathered, st, ev_row) != hipSuccess)
         return SPEC_EHIP;
     if (launch_accept(s, ctx->nsplit_rows, logits_draft, logits_target, draft_tokens, temperature,
                       seed, offset, offset_dev, ctx->part, ctx->gathered, ctx->rn, ctx->lse,
-                      ctx->seq, out_accept_len, out_tokens, st) != hipSuccess)
-        return SPEC_EHIP;
-    if (ev && hipEventRecord(ev[2], st) != hipSuccess)
+                      ctx->seq, out_accept_len, out_tokens, st, ev_acc) != hipSuccess)
         return SPEC_EHIP;
     if (launch_residual(s, vec, ctx->nsplit_residual, ctx->residual_unroll, logits_draft,
-                        logits_target, ctx->seq, ctx->tile_sums, out_tokens, st) != hipSuccess)
-        return SPEC_EHIP;
-    if (ev && hipEventRecord(ev[3], st) != hipSuccess)
+                        logits_target, ctx->seq, ctx->tile_sums, out_tokens, st,
+                        ev_res) != hipSuccess)
         return SPEC_EHIP;
     ctx->have_verified = true;
     return SPEC_OK;
@@ -374,7 +372,7 @@ int spec_verify_enable_timing(spec_verify_ctx* ctx, int max_calls) {
     ctx->timing_count = 0;
     if (max_calls == 0)
         return SPEC_OK;
-    ctx->events.resize(static_cast<size_t>(max_calls) * 4, nullptr);
+    ctx->events.resize(static_cast<size_t>(max_calls) * 6, nullptr);
     for (auto& e : ctx->events) {
         if (hipEventCreate(&e) != hipSuccess) {
             for (hipEvent_t x : ctx->events)
@@ -397,12 +395,12 @@ int spec_verify_read_timing(spec_verify_ctx* ctx, float* out_ms, int max_calls) 
     const int first = ctx->timing_count - recorded;
     int written = 0;
     for (int n = 0; n < recorded && written < max_calls; ++n) {
-        hipEvent_t* ev = &ctx->events[static_cast<size_t>((first + n) % ctx->timing_slots) * 4];
-        if (hipEventSynchronize(ev[3]) != hipSuccess)
+        hipEvent_t* ev = &ctx->events[static_cast<size_t>((first + n) % ctx->timing_slots) * 6];
+        if (hipEventSynchronize(ev[5]) != hipSuccess)
             return SPEC_EHIP;
         for (int kk = 0; kk < 3; ++kk) {
             float ms = 0.0f;
-            if (hipEventElapsedTime(&ms, ev[kk], ev[kk + 1]) != hipSuccess)
+            if (hipEventElapsedTime(&ms, ev[2 * kk], ev[2 * kk + 1]) != hipSuccess)
                 return SPEC_EHIP;
             out_ms[written * 3 + kk] = ms;
         }

@@ -1,8 +1,11 @@
 // Host-side launchers of the verification kernels (one per translation unit).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
 
 #include "common.hpp"
 
@@ -27,6 +30,33 @@ struct Shape {
     int batch, gamma, vocab, dtype;
 };
 
+// Start and stop events of a launch in timing mode. They are attached to the
+// kernel's own dispatch (hipExtLaunchKernel), so their interval is the kernel
+// alone, with no marker packet of its own between kernels. Both null: a
+// plain launch.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+template <typename... Params, typename... Args>
+inline hipError_t launch(void (*kern)(Params...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, const LaunchEvents& ev, Args... args) {
+    static_assert(sizeof...(Params) == sizeof...(Args), "one argument per kernel parameter");
+    if (!ev.start && !ev.stop) {
+        kern<<<grid, block, shmem, stream>>>(args...);
+        return hipGetLastError();
+    }
+    std::tuple<Params...> vals{static_cast<Params>(args)...};
+    void* ptrs[sizeof...(Params) > 0 ? sizeof...(Params) : 1];
+    std::apply([&](auto&... v) {
+        size_t i = 0;
+        ((ptrs[i++] = static_cast<void*>(&v)), ...);
+    }, vals);
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs,
+                              shmem, stream, ev.start, ev.stop, 0);
+}
+
 // Launch geometry of the row-normaliser kernel.
 struct RowTuning {
     int nsplit;        // vocabulary splits per row
@@ -39,7 +69,8 @@ struct RowTuning {
 // in gathered[row] (rows of invalid tokens are left untouched).
 hipError_t launch_row_norm(const Shape& s, bool vec, const RowTuning& tu, const void* draft,
                            const void* target, const float* temperature, const int32_t* tokens,
-                           Partial* part, float* gathered, hipStream_t stream);
+                           Partial* part, float* gathered, hipStream_t stream,
+                           const LaunchEvents& ev = LaunchEvents{});
 
 // Split merge, gather, accept test, first rejection and the emitted prefix:
 // one 64-lane wavefront per sequence. With offset_dev non-null the Philox
@@ -49,7 +80,7 @@ hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const vo
                          uint64_t offset, const uint64_t* offset_dev, const Partial* part,
                          const float* gathered, RowNorm* rn,
                          double* lse_out, SeqState* seq, int32_t* out_len, int32_t* out_tok,
-                         hipStream_t stream);
+                         hipStream_t stream, const LaunchEvents& ev = LaunchEvents{});
 
 // Residual / bonus draw at the first rejection: per-tile sums (B * nsplit
 // workgroups, `unroll` tiles per batch per wavefront: 2 or 4), then one
@@ -61,7 +92,8 @@ int residual_tiles_per_row(int vocab);
 int residual_fused_max_tiles();
 hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, const void* draft,
                            const void* target, const SeqState* seq, float* tile_sums,
-                           int32_t* out_tok, hipStream_t stream);
+                           int32_t* out_tok, hipStream_t stream,
+                           const LaunchEvents& ev = LaunchEvents{});
 
 // Sampled verification of draft trees (spec_tree.h): each tree split over
 // tree_sample_parts() workgroups, n_groups trees at a time (at most

@@ -1345,7 +1345,7 @@ hipError_t launch_tree_sample_typed(int n_groups, const TreeSampleArgs& args, hi
 template <int DT, bool VEC, int U>
 hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const void* draft,
                         const void* target, const SeqState* seq, float* tile_sums,
-                        int32_t* out_tok, hipStream_t stream) {
+                        int32_t* out_tok, hipStream_t stream, const LaunchEvents& ev) {
     constexpr bool NT = VEC;
     constexpr int W = Group<DT, VEC>::W;
     if (sh.batch == 0)
@@ -1355,34 +1355,35 @@ hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const vo
     if (nsplit == 0) {
         // Two tiles in flight per wavefront: 16 wavefronts keep 64 KiB in
         // flight per workgroup.
-        residual_fused_kernel<DT, VEC, NT, kFusedBlock><<<dim3(static_cast<unsigned>(sh.batch)),
-                                                           dim3(kFusedBlock),
-                                                           static_cast<size_t>(ntiles) * sizeof(float),
-                                                           stream>>>(
-            draft, target, sh.gamma, sh.vocab, ntiles, seq, out_tok);
-        return hipGetLastError();
+        return launch(residual_fused_kernel<DT, VEC, NT, kFusedBlock>,
+                      dim3(static_cast<unsigned>(sh.batch)), dim3(kFusedBlock),
+                      static_cast<size_t>(ntiles) * sizeof(float), stream, ev, draft, target,
+                      sh.gamma, sh.vocab, ntiles, seq, out_tok);
     }
+    // Timing the split pair: the tile kernel's start to the locate kernel's stop.
     const int per = (ntiles + nsplit - 1) / nsplit;
-    residual_tiles_kernel<DT, VEC, U, NT><<<dim3(static_cast<unsigned>(sh.batch), static_cast<unsigned>(nsplit)),
-                                            dim3(kBlock), 0, stream>>>(
-        draft, target, sh.gamma, sh.vocab, ntiles, per, tiles_per_row, seq, tile_sums);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch(residual_tiles_kernel<DT, VEC, U, NT>,
+                                dim3(static_cast<unsigned>(sh.batch), static_cast<unsigned>(nsplit)),
+                                dim3(kBlock), 0, stream, LaunchEvents{ev.start, nullptr}, draft,
+                                target, sh.gamma, sh.vocab, ntiles, per, tiles_per_row, seq,
+                                tile_sums);
     if (e != hipSuccess)
         return e;
-    residual_locate_kernel<DT, VEC, NT><<<dim3(static_cast<unsigned>(sh.batch)), dim3(64), 0, stream>>>(
-        draft, target, sh.gamma, sh.vocab, ntiles, tiles_per_row, seq, tile_sums, out_tok);
-    return hipGetLastError();
+    return launch(residual_locate_kernel<DT, VEC, NT>, dim3(static_cast<unsigned>(sh.batch)),
+                  dim3(64), 0, stream, LaunchEvents{nullptr, ev.stop}, draft, target, sh.gamma,
+                  sh.vocab, ntiles, tiles_per_row, seq, tile_sums, out_tok);
 }
 
 template <int DT, bool VEC>
 hipError_t launch_unroll(const Shape& sh, int nsplit, int unroll, int tiles_per_row,
                          const void* draft, const void* target, const SeqState* seq,
-                         float* tile_sums, int32_t* out_tok, hipStream_t stream) {
+                         float* tile_sums, int32_t* out_tok, hipStream_t stream,
+                         const LaunchEvents& ev) {
     if (unroll == 2)
         return launch_typed<DT, VEC, 2>(sh, nsplit, tiles_per_row, draft, target, seq, tile_sums,
-                                        out_tok, stream);
+                                        out_tok, stream, ev);
     return launch_typed<DT, VEC, 4>(sh, nsplit, tiles_per_row, draft, target, seq, tile_sums,
-                                    out_tok, stream);
+                                    out_tok, stream, ev);
 }
 
 }  // namespace
@@ -1439,7 +1440,7 @@ int residual_fused_max_tiles() { return kResidualFusedMaxTiles; }
 
 hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, const void* draft,
                            const void* target, const SeqState* seq, float* tile_sums,
-                           int32_t* out_tok, hipStream_t stream) {
+                           int32_t* out_tok, hipStream_t stream, const LaunchEvents& ev) {
     if (nsplit < 0 || nsplit > kMaxSplit)
         return hipErrorInvalidValue;
     if (nsplit == 0 && residual_tiles_per_row(s.vocab) > kResidualFusedMaxTiles)
@@ -1449,13 +1450,13 @@ hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, con
     const int tiles = residual_tiles_per_row(s.vocab);
     if (s.dtype == kBF16)
         return vec ? launch_unroll<kBF16, true>(s, nsplit, unroll, tiles, draft, target, seq,
-                                                tile_sums, out_tok, stream)
+                                                tile_sums, out_tok, stream, ev)
                    : launch_unroll<kBF16, false>(s, nsplit, unroll, tiles, draft, target, seq,
-                                                 tile_sums, out_tok, stream);
+                                                 tile_sums, out_tok, stream, ev);
     return vec ? launch_unroll<kF32, true>(s, nsplit, unroll, tiles, draft, target, seq, tile_sums,
-                                           out_tok, stream)
+                                           out_tok, stream, ev)
                : launch_unroll<kF32, false>(s, nsplit, unroll, tiles, draft, target, seq,
-                                            tile_sums, out_tok, stream);
+                                            tile_sums, out_tok, stream, ev);
 }
 
 }  // namespace specv

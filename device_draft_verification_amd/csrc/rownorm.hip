@@ -280,34 +280,35 @@ __global__ __launch_bounds__(kBlock) void row_norm_kernel(
 template <int DT, bool VEC, int U, bool NT>
 hipError_t launch_typed(const Shape& sh, int nsplit, const void* draft, const void* target,
                         const float* temperature, const int32_t* tokens, Partial* part,
-                        float* gathered, hipStream_t stream) {
+                        float* gathered, hipStream_t stream, const LaunchEvents& ev) {
     const long rows = static_cast<long>(sh.batch) * (2 * sh.gamma + 1);
     const long blocks = rows * nsplit;
     if (blocks == 0)
         return hipSuccess;
-    row_norm_kernel<DT, VEC, U, NT><<<dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream>>>(
-        draft, target, temperature, tokens, sh.gamma, sh.vocab, nsplit, part, gathered);
-    return hipGetLastError();
+    return launch(row_norm_kernel<DT, VEC, U, NT>, dim3(static_cast<unsigned>(blocks)),
+                  dim3(kBlock), 0, stream, ev, draft, target, temperature, tokens, sh.gamma,
+                  sh.vocab, nsplit, part, gathered);
 }
 
 template <int DT, bool VEC>
 hipError_t launch_unroll(const Shape& sh, const RowTuning& tu, const void* draft,
                          const void* target, const float* temperature, const int32_t* tokens,
-                         Partial* part, float* gathered, hipStream_t stream) {
+                         Partial* part, float* gathered, hipStream_t stream,
+                         const LaunchEvents& ev) {
     if constexpr (!VEC) {
-        return launch_typed<DT, false, 8, false>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream);
+        return launch_typed<DT, false, 8, false>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream, ev);
     } else {
         if (tu.nontemporal) {
             switch (tu.unroll) {
-            case 2: return launch_typed<DT, true, 2, true>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream);
-            case 8: return launch_typed<DT, true, 8, true>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream);
-            default: return launch_typed<DT, true, 4, true>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream);
+            case 2: return launch_typed<DT, true, 2, true>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream, ev);
+            case 8: return launch_typed<DT, true, 8, true>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream, ev);
+            default: return launch_typed<DT, true, 4, true>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream, ev);
             }
         }
         switch (tu.unroll) {
-        case 2: return launch_typed<DT, true, 2, false>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream);
-        case 8: return launch_typed<DT, true, 8, false>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream);
-        default: return launch_typed<DT, true, 4, false>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream);
+        case 2: return launch_typed<DT, true, 2, false>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream, ev);
+        case 8: return launch_typed<DT, true, 8, false>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream, ev);
+        default: return launch_typed<DT, true, 4, false>(sh, tu.nsplit, draft, target, temperature, tokens, part, gathered, stream, ev);
         }
     }
 }
@@ -316,12 +317,13 @@ hipError_t launch_unroll(const Shape& sh, const RowTuning& tu, const void* draft
 
 hipError_t launch_row_norm(const Shape& s, bool vec, const RowTuning& tu, const void* draft,
                            const void* target, const float* temperature, const int32_t* tokens,
-                           Partial* part, float* gathered, hipStream_t stream) {
+                           Partial* part, float* gathered, hipStream_t stream,
+                           const LaunchEvents& ev) {
     if (s.dtype == kBF16)
-        return vec ? launch_unroll<kBF16, true>(s, tu, draft, target, temperature, tokens, part, gathered, stream)
-                   : launch_unroll<kBF16, false>(s, tu, draft, target, temperature, tokens, part, gathered, stream);
-    return vec ? launch_unroll<kF32, true>(s, tu, draft, target, temperature, tokens, part, gathered, stream)
-               : launch_unroll<kF32, false>(s, tu, draft, target, temperature, tokens, part, gathered, stream);
+        return vec ? launch_unroll<kBF16, true>(s, tu, draft, target, temperature, tokens, part, gathered, stream, ev)
+                   : launch_unroll<kBF16, false>(s, tu, draft, target, temperature, tokens, part, gathered, stream, ev);
+    return vec ? launch_unroll<kF32, true>(s, tu, draft, target, temperature, tokens, part, gathered, stream, ev)
+               : launch_unroll<kF32, false>(s, tu, draft, target, temperature, tokens, part, gathered, stream, ev);
 }
 
 }  // namespace specv

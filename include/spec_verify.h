@@ -219,8 +219,11 @@ int spec_verify_philox_words(spec_verify_ctx *ctx, uint64_t seed, uint64_t offse
 
 /*
  * Per-kernel timing. spec_verify_enable_timing(ctx, n) makes each following
- * spec_verify call record HIP events around its three kernels, on the
- * context's stream, into a ring of n slots (n = 0 turns it off).
+ * spec_verify call attach a start and a stop HIP event to the dispatches of
+ * its three steps (hipExtLaunchKernel; the split draw's pair of kernels is
+ * timed from the first's start to the second's stop), on the context's
+ * stream, into a ring of n slots (n = 0 turns it off). The events time the
+ * kernels alone and add no packet of their own between them.
  * spec_verify_read_timing waits for the recorded calls, writes up to
  * max_calls rows of three durations in milliseconds (row normalisers,
  * accept, residual) into out_ms (HOST memory, [max_calls, 3]), returns the
