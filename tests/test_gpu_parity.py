@@ -517,3 +517,33 @@ def test_offset_from_device_memory_and_graph_replays_with_fresh_uniforms():
         assert int(off.item()) == o + 1
     del g
     sv.spec_verify_destroy(ctx)
+
+
+@pytest.mark.parametrize("batch", [8, 128])
+def test_dispatch_event_timing_fits_inside_the_call(batch):
+    """Per-kernel durations from the events attached to the kernels'
+    dispatches (split draw at B = 8, fused draw at B = 128) are positive, and
+    their sum is no longer than the whole call timed by events around it."""
+    rec = specgen.config(4).replace(batch=batch, vocab=30000)
+    t = to_device(specgen.generate(rec))
+    B, G = rec.batch, rec.gamma
+    ctx = sv.spec_verify_init(B, G, rec.vocab, torch.bfloat16)
+    assert (sv.spec_verify_get_geometry(ctx)["residual_splits"] == 0) == (batch >= 128)
+    sv.spec_verify_enable_timing(ctx, 4)
+    alen = torch.empty(B, dtype=torch.int32, device="cuda")
+    toks = torch.empty(B, G + 1, dtype=torch.int32, device="cuda")
+    outer = []
+    for i in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sv.spec_verify(ctx, t["logits_draft"], t["logits_target"], t["draft_tokens"],
+                       t["temperature"], 0, i, alen, toks)
+        e1.record()
+        outer.append((e0, e1))
+    torch.cuda.synchronize()
+    times = sv.spec_verify_read_timing(ctx, 4)
+    assert len(times) == 4
+    for (e0, e1), row in zip(outer, times):
+        assert all(x > 0 for x in row)
+        assert sum(row) <= e0.elapsed_time(e1) * 1.01 + 1e-3
+    sv.spec_verify_destroy(ctx)
