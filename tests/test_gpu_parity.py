@@ -75,6 +75,7 @@ CASES = [
     (1, dict(batch=6, vocab=10003)),              # fp32 element path
     (1, dict(batch=6, vocab=12000, gamma=3)),     # fp32 16-byte groups
     (2, dict(batch=3, vocab=700, gamma=70)),      # more positions than one wavefront
+    (4, dict(batch=4, vocab=520, gamma=130)),     # three passes of 64 positions, mixed T
     (2, dict(batch=5, vocab=4096, gamma=0)),      # bonus draw only
     (3, dict(batch=4, vocab=33000)),              # Zipf rows
     (5, dict(batch=9, vocab=257)),                # tiny vocabulary
@@ -224,9 +225,11 @@ def test_sentinel_sequences():
     assert list(gpu["accept_len"][1:]) == [-1] * 6
 
 
-def test_identical_rows_accept_all_and_bonus():
+@pytest.mark.parametrize("B,G,V", [(64, 5, 3000), (6, 130, 600)])
+def test_identical_rows_accept_all_and_bonus(B, G, V):
+    # G = 130: the first rejection is searched over three passes of 64
+    # positions, and the bonus row's coefficients come from the third.
     rng = np.random.default_rng(4)
-    B, G, V = 64, 5, 3000
     base = rng.normal(0, 2.0, size=(G + 1, V)).astype(np.float32)
     zp = np.ascontiguousarray(np.broadcast_to(base, (B, G + 1, V)))
     zq = np.ascontiguousarray(zp[:, :G])
@@ -547,3 +550,28 @@ def test_dispatch_event_timing_fits_inside_the_call(batch):
         assert all(x > 0 for x in row)
         assert sum(row) <= e0.elapsed_time(e1) * 1.01 + 1e-3
     sv.spec_verify_destroy(ctx)
+
+
+def test_first_rejection_in_a_later_pass():
+    """G = 130: every position is accepted (identical rows) except position
+    j*, where the target gives the draft token zero probability, so k = j*
+    for certain; j* falls in the second and third passes of 64 positions and
+    the residual draw runs on that position's rows."""
+    rng = np.random.default_rng(11)
+    G, V = 130, 800
+    stars = [64, 100, 127, 128, 129]
+    B = len(stars)
+    base = rng.normal(0, 1.5, size=(G + 1, V)).astype(np.float32)
+    zp = np.ascontiguousarray(np.broadcast_to(base, (B, G + 1, V))).copy()
+    zq = np.ascontiguousarray(zp[:, :G]).copy()
+    r2 = np.random.default_rng(12)
+    toks = np.stack([specgen.gumbel_max_tokens(base[:G], 1.0, r2) for _ in range(B)])
+    for b, j in enumerate(stars):
+        zp[b, j, toks[b, j]] = -np.inf
+    d = dict(logits_draft=zq, logits_target=zp, draft_tokens=toks,
+             temperature=np.ones(B, np.float32), seq_ids=np.arange(B))
+    gpu = run_gpu(to_device(d))
+    ref = _oracle(d)
+    assert list(ref["accept_len"]) == stars
+    assert list(gpu["accept_len"]) == stars
+    assert_parity(compare(gpu, ref, d["temperature"]), "later-pass rejection")
