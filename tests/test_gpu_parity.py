@@ -72,6 +72,7 @@ CASES = [
     # (config recipe, overrides)
     (4, dict(batch=12, vocab=20008)),             # 16-byte groups, ragged last split
     (4, dict(batch=12, vocab=20011)),             # V % 8 != 0: element path
+    (4, dict(batch=3, vocab=40001, gamma=2)),     # element path, 626 tiles: runs read in a loop
     (1, dict(batch=6, vocab=10003)),              # fp32 element path
     (1, dict(batch=6, vocab=12000, gamma=3)),     # fp32 16-byte groups
     (2, dict(batch=3, vocab=700, gamma=70)),      # more positions than one wavefront
@@ -96,7 +97,7 @@ def test_small_shapes_parity(cfg, over):
         assert_parity(rep, str(over))
 
 
-@pytest.mark.parametrize("cfg,over", [CASES[i] for i in (0, 1, 2, 4, 5, 8, 9)])
+@pytest.mark.parametrize("cfg,over", [CASES[i] for i in (0, 1, 2, 3, 5, 6, 7, 10, 11)])
 @pytest.mark.parametrize("fused", [1, 0], ids=["fused", "split"])
 def test_residual_kernel_choice_parity(cfg, over, fused, monkeypatch):
     """Both residual paths on the same inputs: the fused one-workgroup-per-
