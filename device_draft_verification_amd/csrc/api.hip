@@ -256,13 +256,17 @@ int verify_impl(spec_verify_ctx* ctx, const void* logits_draft, const void* logi
     if (launch_row_norm(s, vec, tu, logits_draft, logits_target, temperature, draft_tokens,
                         ctx->part, ctx->gathered, st, ev_row) != hipSuccess)
         return SPEC_EHIP;
-    if (launch_accept(s, ctx->nsplit_rows, logits_draft, logits_target, draft_tokens, temperature,
-                      seed, offset, offset_dev, ctx->part, ctx->gathered, ctx->rn, ctx->lse,
-                      ctx->seq, out_accept_len, out_tokens, st, ev_acc) != hipSuccess)
+    const AcceptArgs acc{draft_tokens, temperature, s.gamma, s.vocab, ctx->nsplit_rows, seed,
+                         offset, offset_dev, ctx->part, ctx->gathered, ctx->rn, ctx->lse,
+                         ctx->seq, out_accept_len, out_tokens};
+    // On the tile path (small batches) the tile kernel runs the accept step
+    // itself, which saves a launch; the fused draw needs the accept kernel.
+    const bool fold = ctx->nsplit_residual > 0;
+    if (!fold && launch_accept(s.batch, acc, st, ev_acc) != hipSuccess)
         return SPEC_EHIP;
     if (launch_residual(s, vec, ctx->nsplit_residual, ctx->residual_unroll, logits_draft,
-                        logits_target, ctx->seq, ctx->tile_sums, out_tokens, st,
-                        ev_res) != hipSuccess)
+                        logits_target, ctx->seq, ctx->tile_sums, out_tokens, fold ? &acc : nullptr,
+                        st, ev_res) != hipSuccess)
         return SPEC_EHIP;
     ctx->have_verified = true;
     return SPEC_OK;
@@ -399,8 +403,10 @@ int spec_verify_read_timing(spec_verify_ctx* ctx, float* out_ms, int max_calls) 
         if (hipEventSynchronize(ev[5]) != hipSuccess)
             return SPEC_EHIP;
         for (int kk = 0; kk < 3; ++kk) {
+            // the accept step runs inside the draw on the tile path: 0 here
             float ms = 0.0f;
-            if (hipEventElapsedTime(&ms, ev[2 * kk], ev[2 * kk + 1]) != hipSuccess)
+            if ((kk != 1 || ctx->nsplit_residual == 0) &&
+                hipEventElapsedTime(&ms, ev[2 * kk], ev[2 * kk + 1]) != hipSuccess)
                 return SPEC_EHIP;
             out_ms[written * 3 + kk] = ms;
         }

@@ -72,27 +72,41 @@ hipError_t launch_row_norm(const Shape& s, bool vec, const RowTuning& tu, const 
                            Partial* part, float* gathered, hipStream_t stream,
                            const LaunchEvents& ev = LaunchEvents{});
 
+// Everything the accept step reads and writes.
+struct AcceptArgs {
+    const int32_t* tokens;
+    const float* temperature;
+    int gamma, vocab, nsplit;  // nsplit: vocabulary splits of the row kernel
+    uint64_t seed, offset;
+    const uint64_t* offset_dev;  // non-null: the Philox offset is this device word
+    const Partial* part;
+    const float* gathered;
+    RowNorm* rn;
+    double* lse_out;
+    SeqState* seq;
+    int32_t* out_len;
+    int32_t* out_tok;
+};
+
 // Split merge, gather, accept test, first rejection and the emitted prefix:
 // one 64-lane wavefront per sequence. With offset_dev non-null the Philox
 // offset is read from that device word instead of `offset`.
-hipError_t launch_accept(const Shape& s, int nsplit, const void* draft, const void* target,
-                         const int32_t* tokens, const float* temperature, uint64_t seed,
-                         uint64_t offset, const uint64_t* offset_dev, const Partial* part,
-                         const float* gathered, RowNorm* rn,
-                         double* lse_out, SeqState* seq, int32_t* out_len, int32_t* out_tok,
-                         hipStream_t stream, const LaunchEvents& ev = LaunchEvents{});
+hipError_t launch_accept(int batch, const AcceptArgs& a, hipStream_t stream,
+                         const LaunchEvents& ev = LaunchEvents{});
 
 // Residual / bonus draw at the first rejection: per-tile sums (B * nsplit
 // workgroups, `unroll` tiles per batch per wavefront: 2 or 4), then one
 // locating wavefront per sequence. tile_sums holds
 // B * residual_tiles_per_row(vocab) floats. nsplit == 0 selects the fused
 // kernel instead (one workgroup per sequence, tile sums in LDS, one launch),
-// for rows of at most residual_fused_max_tiles() tiles.
+// for rows of at most residual_fused_max_tiles() tiles. With acc non-null
+// (tile path only) the tile kernel also runs the accept step, split 0 writing
+// its outputs, so no accept launch precedes it.
 int residual_tiles_per_row(int vocab);
 int residual_fused_max_tiles();
 hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, const void* draft,
                            const void* target, const SeqState* seq, float* tile_sums,
-                           int32_t* out_tok, hipStream_t stream,
+                           int32_t* out_tok, const AcceptArgs* acc, hipStream_t stream,
                            const LaunchEvents& ev = LaunchEvents{});
 
 // Sampled verification of draft trees (spec_tree.h): each tree split over

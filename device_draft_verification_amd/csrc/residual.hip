@@ -29,8 +29,7 @@
 // p' = 2^(fma(x, log2e, -m)), which the inversion does not see (u * S scales
 // with it) and which costs one fused multiply-add per logit pair. The bonus
 // row uses p' itself.
-#include "launch.hpp"
-#include "philox.hpp"
+#include "accept.hpp"
 
 namespace specv {
 namespace {
@@ -135,23 +134,40 @@ __device__ inline float tile_reduce(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-template <int DT, bool VEC, int U, bool NT>
+// With ACC the kernel also runs the accept step (small batches, where the
+// separate accept launch would be a large part of the call): wavefront 0 of
+// every split decides its sequence, split 0 alone writes the accept outputs,
+// and the state reaches the other wavefronts through LDS.
+template <int DT, bool VEC, int U, bool NT, bool ACC>
 __global__ __launch_bounds__(kBlock) void residual_tiles_kernel(
     const void* __restrict__ draft, const void* __restrict__ target, int gamma, int vocab,
     int ntiles, int tiles_per_split, int tiles_per_row, const SeqState* __restrict__ seq,
-    float* __restrict__ tile_sums) {
+    float* __restrict__ tile_sums, AcceptArgs acc) {
     using IO = GroupIO<DT, VEC, NT>;
     constexpr int W = IO::W;
     // grid: x = sequence, y = vocabulary split
     const int b = blockIdx.x;
-    const SeqState st = seq[b];
+    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
+    SeqState st;
+    if constexpr (ACC) {
+        __shared__ SeqState acc_state;
+        if (wid == 0) {
+            const SeqState s0 = accept_sequence(acc, b, blockIdx.y == 0);
+            if (lane == 0)
+                acc_state = s0;
+        }
+        __syncthreads();
+        st = acc_state;
+    } else {
+        (void)acc;
+        st = seq[b];
+    }
     if (st.mode != 1)
         return;  // greedy or rejected sequence: nothing to draw
     const int groups = vocab / W;
     const int t0 = blockIdx.y * tiles_per_split;
     const int t1 = t0 + tiles_per_split < ntiles ? t0 + tiles_per_split : ntiles;
-    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int lane = threadIdx.x & 63;
     float* out = tile_sums + static_cast<size_t>(b) * tiles_per_row;
 
     // Double-buffered: the loads of the next batch are in flight while this
@@ -1345,7 +1361,8 @@ hipError_t launch_tree_sample_typed(int n_groups, const TreeSampleArgs& args, hi
 template <int DT, bool VEC, int U>
 hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const void* draft,
                         const void* target, const SeqState* seq, float* tile_sums,
-                        int32_t* out_tok, hipStream_t stream, const LaunchEvents& ev) {
+                        int32_t* out_tok, const AcceptArgs* acc, hipStream_t stream,
+                        const LaunchEvents& ev) {
     constexpr bool NT = VEC;
     constexpr int W = Group<DT, VEC>::W;
     if (sh.batch == 0)
@@ -1362,11 +1379,15 @@ hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const vo
     }
     // Timing the split pair: the tile kernel's start to the locate kernel's stop.
     const int per = (ntiles + nsplit - 1) / nsplit;
-    const hipError_t e = launch(residual_tiles_kernel<DT, VEC, U, NT>,
-                                dim3(static_cast<unsigned>(sh.batch), static_cast<unsigned>(nsplit)),
-                                dim3(kBlock), 0, stream, LaunchEvents{ev.start, nullptr}, draft,
-                                target, sh.gamma, sh.vocab, ntiles, per, tiles_per_row, seq,
-                                tile_sums);
+    const dim3 tgrid(static_cast<unsigned>(sh.batch), static_cast<unsigned>(nsplit));
+    const LaunchEvents tev{ev.start, nullptr};
+    const hipError_t e =
+        acc ? launch(residual_tiles_kernel<DT, VEC, U, NT, true>, tgrid, dim3(kBlock), 0, stream,
+                     tev, draft, target, sh.gamma, sh.vocab, ntiles, per, tiles_per_row, seq,
+                     tile_sums, *acc)
+            : launch(residual_tiles_kernel<DT, VEC, U, NT, false>, tgrid, dim3(kBlock), 0, stream,
+                     tev, draft, target, sh.gamma, sh.vocab, ntiles, per, tiles_per_row, seq,
+                     tile_sums, AcceptArgs{});
     if (e != hipSuccess)
         return e;
     return launch(residual_locate_kernel<DT, VEC, NT>, dim3(static_cast<unsigned>(sh.batch)),
@@ -1377,13 +1398,13 @@ hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const vo
 template <int DT, bool VEC>
 hipError_t launch_unroll(const Shape& sh, int nsplit, int unroll, int tiles_per_row,
                          const void* draft, const void* target, const SeqState* seq,
-                         float* tile_sums, int32_t* out_tok, hipStream_t stream,
-                         const LaunchEvents& ev) {
+                         float* tile_sums, int32_t* out_tok, const AcceptArgs* acc,
+                         hipStream_t stream, const LaunchEvents& ev) {
     if (unroll == 2)
         return launch_typed<DT, VEC, 2>(sh, nsplit, tiles_per_row, draft, target, seq, tile_sums,
-                                        out_tok, stream, ev);
+                                        out_tok, acc, stream, ev);
     return launch_typed<DT, VEC, 4>(sh, nsplit, tiles_per_row, draft, target, seq, tile_sums,
-                                    out_tok, stream, ev);
+                                    out_tok, acc, stream, ev);
 }
 
 }  // namespace
@@ -1440,8 +1461,9 @@ int residual_fused_max_tiles() { return kResidualFusedMaxTiles; }
 
 hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, const void* draft,
                            const void* target, const SeqState* seq, float* tile_sums,
-                           int32_t* out_tok, hipStream_t stream, const LaunchEvents& ev) {
-    if (nsplit < 0 || nsplit > kMaxSplit)
+                           int32_t* out_tok, const AcceptArgs* acc, hipStream_t stream,
+                           const LaunchEvents& ev) {
+    if (nsplit < 0 || nsplit > kMaxSplit || (acc && nsplit == 0))
         return hipErrorInvalidValue;
     if (nsplit == 0 && residual_tiles_per_row(s.vocab) > kResidualFusedMaxTiles)
         return hipErrorInvalidValue;
@@ -1450,13 +1472,13 @@ hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, con
     const int tiles = residual_tiles_per_row(s.vocab);
     if (s.dtype == kBF16)
         return vec ? launch_unroll<kBF16, true>(s, nsplit, unroll, tiles, draft, target, seq,
-                                                tile_sums, out_tok, stream, ev)
+                                                tile_sums, out_tok, acc, stream, ev)
                    : launch_unroll<kBF16, false>(s, nsplit, unroll, tiles, draft, target, seq,
-                                                 tile_sums, out_tok, stream, ev);
+                                                 tile_sums, out_tok, acc, stream, ev);
     return vec ? launch_unroll<kF32, true>(s, nsplit, unroll, tiles, draft, target, seq, tile_sums,
-                                           out_tok, stream, ev)
+                                           out_tok, acc, stream, ev)
                : launch_unroll<kF32, false>(s, nsplit, unroll, tiles, draft, target, seq,
-                                            tile_sums, out_tok, stream, ev);
+                                            tile_sums, out_tok, acc, stream, ev);
 }
 
 }  // namespace specv

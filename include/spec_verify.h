@@ -123,7 +123,9 @@ int spec_verify_set_stream(spec_verify_ctx *ctx, void *hip_stream);
  *                               the extra token, the rest -1
  * Enqueues its kernels on the context's stream and returns: row
  * normalisers; gather, accept and first rejection; the residual or bonus
- * draw (one kernel from B = 128, tile sums then locate below that).
+ * draw. From B = 128 these are three kernels (the draw one workgroup per
+ * sequence); below, the accept step runs inside the draw's tile-sum kernel,
+ * followed by a locate kernel.
  */
 int spec_verify(spec_verify_ctx *ctx, const void *logits_draft,
                 const void *logits_target, const int32_t *draft_tokens,
@@ -223,7 +225,9 @@ int spec_verify_philox_words(spec_verify_ctx *ctx, uint64_t seed, uint64_t offse
  * its three steps (hipExtLaunchKernel; the split draw's pair of kernels is
  * timed from the first's start to the second's stop), on the context's
  * stream, into a ring of n slots (n = 0 turns it off). The events time the
- * kernels alone and add no packet of their own between them.
+ * kernels alone and add no packet of their own between them. Below B = 128
+ * the draw's tile kernel runs the accept step itself, so that step's
+ * duration reads 0 and the draw's includes it.
  * spec_verify_read_timing waits for the recorded calls, writes up to
  * max_calls rows of three durations in milliseconds (row normalisers,
  * accept, residual) into out_ms (HOST memory, [max_calls, 3]), returns the
