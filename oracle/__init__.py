@@ -83,11 +83,16 @@ def _load():
     lib.oracle_row_argmax.restype = i32
     lib.oracle_inverse_cdf.argtypes = [P, i32, f64, P]
     lib.oracle_inverse_cdf.restype = i32
+    lib.oracle_inverse_cdf_alt.argtypes = [P, i32, f64, P, P]
+    lib.oracle_inverse_cdf_alt.restype = i32
+    lib.oracle_draw_at.argtypes = [i32, i32, P, ctypes.c_size_t, P, ctypes.c_size_t, i32, f32,
+                                   f64, P, P, P]
+    lib.oracle_draw_at.restype = None
     lib.oracle_verify_sequence.argtypes = [i32, i32, i32, P, ctypes.c_size_t, P,
-                                           ctypes.c_size_t, P, f32, P, P, P, P, P, P, P]
+                                           ctypes.c_size_t, P, f32, P, P, P, P, P, P, P, P]
     lib.oracle_verify_sequence.restype = None
     lib.oracle_verify.argtypes = [i32, i32, i32, i32, P, P, P, P, u64, u64, P,
-                                  P, P, P, P, P]
+                                  P, P, P, P, P, P]
     lib.oracle_verify.restype = None
     lib.oracle_accept_logprobs.argtypes = [i32, i32, P, u64, u64, P, P, P]
     lib.oracle_accept_logprobs.restype = None
@@ -172,6 +177,43 @@ def inverse_cdf(r: np.ndarray, u: float) -> tuple[int, float]:
     return j, m.value
 
 
+def inverse_cdf_alt(r: np.ndarray, u: float) -> tuple[int, float, int]:
+    """As ``inverse_cdf``, plus the token across the nearer edge of the chosen
+    bin (the nearest positive-weight index on that side, -1 if none)."""
+    r = np.ascontiguousarray(r, dtype=np.float64)
+    m = ctypes.c_double(0.0)
+    a = ctypes.c_int32(-1)
+    j = _load().oracle_inverse_cdf_alt(_ptr(r), r.size, float(u), ctypes.byref(m),
+                                       ctypes.byref(a))
+    return j, m.value, a.value
+
+
+def draw_at(draft_row, target_row, temperature: float, u: float) -> tuple[int, float, int]:
+    """The extra token a sequence emits when its first rejection is at the
+    position of these rows (``draft_row`` None: the bonus draw from
+    ``target_row``), at uniform u: (token, log-margin, token across the nearer
+    bin edge)."""
+    zp, dt = _logits(np.ascontiguousarray(target_row).reshape(-1))
+    if draft_row is None:
+        zq, bonus = zp, 1
+    else:
+        zq, dq = _logits(np.ascontiguousarray(draft_row).reshape(-1))
+        assert dq == dt and zq.size == zp.size
+        bonus = 0
+    tok = ctypes.c_int32(-1)
+    m = ctypes.c_double(0.0)
+    a = ctypes.c_int32(-1)
+    _load().oracle_draw_at(zp.size, dt, _ptr(zq), 0, _ptr(zp), 0, bonus,
+                           float(np.float32(temperature)), float(u), ctypes.byref(tok),
+                           ctypes.byref(m), ctypes.byref(a))
+    return tok.value, m.value, a.value
+
+
+def uniform_res(seed: int, offset: int, b: int, i: int) -> float:
+    """The resample uniform of position i of sequence b (Philox word 1)."""
+    return uniform24(int(philox_words(seed, offset, b, i)[1]))
+
+
 def verify_sequence(logits_draft, logits_target, draft_tokens, temperature, u_acc, u_res):
     """One sequence with explicit uniforms. logits_draft [G, V], logits_target [G+1, V]."""
     zp, dt = _logits(logits_target)
@@ -191,12 +233,13 @@ def verify_sequence(logits_draft, logits_target, draft_tokens, temperature, u_ac
     lse = np.zeros(2 * G + 1, dtype=np.float64)
     am = np.zeros(max(G, 1), dtype=np.float64)
     rm = ctypes.c_double(0.0)
+    ra = ctypes.c_int32(-1)
     _load().oracle_verify_sequence(G, V, dt, _ptr(zq), 0, _ptr(zp), 0, _ptr(tok),
                                    float(np.float32(temperature)), _ptr(ua), _ptr(ur),
                                    ctypes.byref(alen), _ptr(tokens), _ptr(lse), _ptr(am),
-                                   ctypes.byref(rm))
+                                   ctypes.byref(rm), ctypes.byref(ra))
     return dict(accept_len=alen.value, tokens=tokens, lse=lse, acc_margin=am[:G],
-                res_margin=rm.value)
+                res_margin=rm.value, res_alt=ra.value)
 
 
 def verify(logits_draft, logits_target, draft_tokens, temperature, seed=0, offset=0,
@@ -224,11 +267,12 @@ def verify(logits_draft, logits_target, draft_tokens, temperature, seed=0, offse
     lse = np.zeros((B, 2 * G + 1), dtype=np.float64)
     am = np.zeros((B, max(G, 1)), dtype=np.float64)
     rm = np.zeros(B, dtype=np.float64)
+    ra = np.zeros(B, dtype=np.int32)
     _load().oracle_verify(B, G, V, dt, _ptr(zq), _ptr(zp), _ptr(tok), _ptr(temp),
                           seed, offset, _ptr(ids), _ptr(alen), _ptr(tokens), _ptr(lse),
-                          _ptr(am), _ptr(rm))
+                          _ptr(am), _ptr(rm), _ptr(ra))
     return dict(accept_len=alen, tokens=tokens, lse=lse, acc_margin=am[:, :G],
-                res_margin=rm)
+                res_margin=rm, res_alt=ra)
 
 
 def accept_logprobs(logprobs, seed=0, offset=0, seq_ids=None):

@@ -190,40 +190,65 @@ int oracle_row_argmax(const void *row_base, int dtype, size_t row_elem0, int voc
  * Also returns the log-margin of the draw: the log-ratio distance of tau to
  * the two edges of the chosen bin, min(log(tau / C_{j-1}), log(C_j / tau)),
  * with C_{-1} = 0 giving +inf, and 0 when tau == 0.
+ * *alt (may be NULL) receives the token on the other side of the nearer edge:
+ * the last index below j with positive weight when tau is nearer C_{j-1}, the
+ * first index above j with positive weight when it is nearer C_j (ties go to
+ * the lower edge); -1 when there is none. A draw taken in another rounding
+ * order can only move to that token when its margin is tiny.
  * Returns -1 when S <= 0.
  */
-int oracle_inverse_cdf(const double *r, int vocab, double u, double *margin)
+int oracle_inverse_cdf_alt(const double *r, int vocab, double u, double *margin, int32_t *alt)
 {
     double total = 0.0;
     for (int v = 0; v < vocab; ++v)
         total += r[v];
-    if (!(total > 0.0)) {
-        if (margin)
-            *margin = 0.0;
+    if (margin)
+        *margin = 0.0;
+    if (alt)
+        *alt = -1;
+    if (!(total > 0.0))
         return -1;
-    }
     double tau = u * total;
     double prefix = 0.0;
     for (int j = 0; j < vocab; ++j) {
         double before = prefix;
         prefix += r[j];
         if (prefix > tau) {
-            if (margin) {
-                if (tau == 0.0) {
-                    *margin = 0.0;
+            double lower = INFINITY, upper = INFINITY;
+            if (tau > 0.0) {
+                lower = before > 0.0 ? log(tau / before) : INFINITY;
+                upper = log(prefix / tau);
+            } else {
+                lower = before > 0.0 ? 0.0 : INFINITY;
+                upper = 0.0;
+            }
+            if (margin)
+                *margin = tau == 0.0 ? 0.0 : (lower < upper ? lower : upper);
+            if (alt) {
+                if (lower <= upper) {
+                    for (int v = j - 1; v >= 0; --v)
+                        if (r[v] > 0.0) {
+                            *alt = v;
+                            break;
+                        }
                 } else {
-                    double lower = before > 0.0 ? log(tau / before) : INFINITY;
-                    double upper = log(prefix / tau);
-                    *margin = lower < upper ? lower : upper;
+                    for (int v = j + 1; v < vocab; ++v)
+                        if (r[v] > 0.0) {
+                            *alt = v;
+                            break;
+                        }
                 }
             }
             return j;
         }
     }
     /* unreachable: tau < total and the last prefix equals total */
-    if (margin)
-        *margin = 0.0;
     return -1;
+}
+
+int oracle_inverse_cdf(const double *r, int vocab, double u, double *margin)
+{
+    return oracle_inverse_cdf_alt(r, vocab, u, margin, NULL);
 }
 
 /* ----------------------------------------------------- the verification -- */
@@ -244,6 +269,42 @@ static int temperature_valid(float t, float *inv_t_out)
 }
 
 /*
+ * The extra token at position k of one sequence (k < gamma: the residual
+ * max(0, p_k - q_k); bonus: p_k itself) from the log-normalisers of its rows,
+ * by the inverse CDF of R7 at uniform u, with the fallback of R8. Element
+ * offsets of the two rows are q0 (unused for the bonus) and p0.
+ */
+static int residual_draw(int vocab, int dtype, const void *logits_draft, size_t q0,
+                         const void *logits_target, size_t p0, int bonus, float inv_t,
+                         double lse_q, double lse_p, double u, double *margin, int32_t *alt)
+{
+    const int V = vocab;
+    double *r = (double *)calloc((size_t)V, sizeof(double));
+    for (int v = 0; v < V; ++v) {
+        double xp = scaled(raw_logit(logits_target, dtype, p0 + (size_t)v), inv_t);
+        double p = exp(xp - lse_p);
+        if (!bonus) {
+            double xq = scaled(raw_logit(logits_draft, dtype, q0 + (size_t)v), inv_t);
+            double q = exp(xq - lse_q);
+            r[v] = p - q > 0.0 ? p - q : 0.0;
+        } else {
+            r[v] = p;
+        }
+    }
+    int j = oracle_inverse_cdf_alt(r, V, u, margin, alt);
+    if (j < 0 && !bonus) {
+        /* R8: empty residual, draw from p at the same position instead. */
+        for (int v = 0; v < V; ++v) {
+            double xp = scaled(raw_logit(logits_target, dtype, p0 + (size_t)v), inv_t);
+            r[v] = exp(xp - lse_p);
+        }
+        j = oracle_inverse_cdf_alt(r, V, u, margin, alt);
+    }
+    free(r);
+    return j;
+}
+
+/*
  * One sequence, with its uniforms given explicitly (the Philox draw is done by
  * the caller, so a test can sweep them). u_acc[i] for i < gamma and u_res[i]
  * for i <= gamma. x_q rows are draft positions 0..gamma-1, x_p rows target
@@ -251,7 +312,9 @@ static int temperature_valid(float t, float *inv_t_out)
  *
  * Outputs: *accept_len, tokens[0..gamma], lse[0..2*gamma] (draft rows first,
  * then target rows; NaN where not computed), acc_margin[0..gamma-1]
- * ((lp - lq) - log u for evaluated positions, NaN elsewhere) and *res_margin.
+ * ((lp - lq) - log u for evaluated positions, NaN elsewhere), *res_margin and
+ * *res_alt (may be NULL): the token across the nearer edge of the draw's bin
+ * (oracle_inverse_cdf_alt), -1 for greedy and sentinel sequences.
  */
 void oracle_verify_sequence(int gamma, int vocab, int dtype,
                             const void *logits_draft, size_t q_row0,
@@ -259,9 +322,12 @@ void oracle_verify_sequence(int gamma, int vocab, int dtype,
                             const int32_t *draft_tokens, float temperature,
                             const double *u_acc, const double *u_res,
                             int32_t *accept_len, int32_t *tokens,
-                            double *lse, double *acc_margin, double *res_margin)
+                            double *lse, double *acc_margin, double *res_margin,
+                            int32_t *res_alt)
 {
     const int G = gamma, V = vocab;
+    if (res_alt)
+        *res_alt = -1;
     for (int i = 0; i <= G; ++i)
         tokens[i] = -1;
     for (int i = 0; i < 2 * G + 1; ++i)
@@ -334,35 +400,19 @@ void oracle_verify_sequence(int gamma, int vocab, int dtype,
     }
 
     /* Residual max(0, p - q) at the first rejection, or p at gamma (bonus). */
-    double *r = (double *)malloc(sizeof(double) * (size_t)V);
-    for (int v = 0; v < V; ++v) {
-        double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)k * V + v), inv_t);
-        double p = exp(xp - lse_p[k]);
-        if (k < G) {
-            double xq = scaled(raw_logit(logits_draft, dtype, q_row0 + (size_t)k * V + v), inv_t);
-            double q = exp(xq - lse_q[k]);
-            r[v] = p - q > 0.0 ? p - q : 0.0;
-        } else {
-            r[v] = p;
-        }
-    }
     double margin = 0.0;
-    int j = oracle_inverse_cdf(r, V, u_res[k], &margin);
-    if (j < 0 && k < G) {
-        /* R8: empty residual, draw from p at the same position instead. */
-        for (int v = 0; v < V; ++v) {
-            double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)k * V + v), inv_t);
-            r[v] = exp(xp - lse_p[k]);
-        }
-        j = oracle_inverse_cdf(r, V, u_res[k], &margin);
-    }
-    free(r);
+    int32_t alt = -1;
+    int j = residual_draw(V, dtype, logits_draft, q_row0 + (size_t)k * V, logits_target,
+                          p_row0 + (size_t)k * V, k == G, inv_t, k < G ? lse_q[k] : 0.0,
+                          lse_p[k], u_res[k], &margin, &alt);
 
     for (int i = 0; i < k; ++i)
         tokens[i] = draft_tokens[i];
     tokens[k] = j;
     *accept_len = k;
     *res_margin = margin;
+    if (res_alt)
+        *res_alt = alt;
 }
 
 /*
@@ -371,14 +421,15 @@ void oracle_verify_sequence(int gamma, int vocab, int dtype,
  * out of a larger batch is verified with the uniforms the full batch uses.
  * Array shapes: draft [B, G, V], target [B, G+1, V], draft_tokens [B, G],
  * temperature [B], accept_len [B], tokens [B, G+1], lse [B, 2G+1],
- * acc_margin [B, G] (may be NULL iff G == 0), res_margin [B].
+ * acc_margin [B, G] (may be NULL iff G == 0), res_margin [B], res_alt [B]
+ * (may be NULL).
  */
 void oracle_verify(int batch, int gamma, int vocab, int dtype,
                    const void *logits_draft, const void *logits_target,
                    const int32_t *draft_tokens, const float *temperature,
                    uint64_t seed, uint64_t offset, const int64_t *seq_ids,
                    int32_t *accept_len, int32_t *tokens, double *lse,
-                   double *acc_margin, double *res_margin)
+                   double *acc_margin, double *res_margin, int32_t *res_alt)
 {
     const int G = gamma;
     double *u_acc = (double *)malloc(sizeof(double) * (size_t)(G + 1));
@@ -400,10 +451,36 @@ void oracle_verify(int batch, int gamma, int vocab, int dtype,
                                tokens + (size_t)b * (G + 1),
                                lse + (size_t)b * (2 * G + 1),
                                G > 0 ? acc_margin + (size_t)b * G : dummy_margin,
-                               res_margin + b);
+                               res_margin + b, res_alt ? res_alt + b : NULL);
     }
     free(u_acc);
     free(u_res);
+}
+
+/*
+ * The extra token one sequence would emit if its first rejection were at
+ * position k (k < gamma), or the bonus token (k == gamma), at uniform u: the
+ * residual draw of the verification (R7, R8) on the rows of position k alone.
+ * Rows: draft row at element offset q0 (unused when k == gamma), target row
+ * at p0. temperature must be > 0. Outputs the token (or -1 when a row has no
+ * finite logit), its log-margin and the token across the nearer bin edge.
+ */
+void oracle_draw_at(int vocab, int dtype, const void *logits_draft, size_t q0,
+                    const void *logits_target, size_t p0, int bonus, float temperature,
+                    double u, int32_t *token, double *margin, int32_t *alt)
+{
+    float inv_t = 0.0f;
+    *token = -1;
+    *margin = NAN;
+    *alt = -1;
+    if (!temperature_valid(temperature, &inv_t) || !(temperature > 0.0f))
+        return;
+    double lse_p = oracle_row_lse(logits_target, dtype, p0, vocab, inv_t);
+    double lse_q = bonus ? 0.0 : oracle_row_lse(logits_draft, dtype, q0, vocab, inv_t);
+    if (!(lse_p > -INFINITY) || !(lse_q > -INFINITY))
+        return;
+    *token = residual_draw(vocab, dtype, logits_draft, q0, logits_target, p0, bonus, inv_t,
+                           lse_q, lse_p, u, margin, alt);
 }
 
 /*

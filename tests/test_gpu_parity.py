@@ -5,7 +5,9 @@ small ones, on a seeded sample of sequences for the three large ones, in the
 same launch configuration the benchmark times), plus small cases that span
 several vocabulary splits and a ragged tail, and the edge cases of the method.
 """
+import concurrent.futures as cf
 import math
+import os
 
 import numpy as np
 import pytest
@@ -14,7 +16,7 @@ import torch
 import device_draft_verification_amd as sv
 import oracle
 import specgen
-from gpu_helpers import assert_parity, compare, run_gpu, to_device
+from gpu_helpers import assert_parity, compare, record, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -23,21 +25,44 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 
 
 def _oracle(d, rows=None, seed=0, offset=0):
-    if rows is None:
+    """The oracle on all sequences of d (or on `rows`), cut into slices run on
+    host threads (the oracle is single-threaded C; ctypes drops the GIL)."""
+    if rows is not None:
+        d = _subset(d, rows)
+    B = d["logits_target"].shape[0]
+    workers = max(1, min(16, os.cpu_count() or 1, B // 8))
+    if workers == 1:
         return oracle.verify(d["logits_draft"], d["logits_target"], d["draft_tokens"],
                              d["temperature"], seed=seed, offset=offset, seq_ids=d["seq_ids"])
+    cuts = np.linspace(0, B, workers + 1).astype(int)
+
+    def part(i):
+        a, b = cuts[i], cuts[i + 1]
+        return oracle.verify(d["logits_draft"][a:b], d["logits_target"][a:b],
+                             d["draft_tokens"][a:b], d["temperature"][a:b], seed=seed,
+                             offset=offset, seq_ids=d["seq_ids"][a:b])
+
+    with cf.ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(part, range(workers)))
+    return {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+
+
+def _subset(d, rows):
     rows = np.asarray(rows)
-    return oracle.verify(np.ascontiguousarray(d["logits_draft"][rows]),
-                         np.ascontiguousarray(d["logits_target"][rows]),
-                         np.ascontiguousarray(d["draft_tokens"][rows]),
-                         d["temperature"][rows], seed=seed, offset=offset,
-                         seq_ids=d["seq_ids"][rows])
+    return dict(logits_draft=np.ascontiguousarray(d["logits_draft"][rows]),
+                logits_target=np.ascontiguousarray(d["logits_target"][rows]),
+                draft_tokens=np.ascontiguousarray(d["draft_tokens"][rows]),
+                temperature=d["temperature"][rows], seq_ids=d["seq_ids"][rows])
 
 
-def _report(label, rep):
-    print(f"\n[{label}] n={rep['n']} exact={rep['exact']} flagged_accept={rep['flagged_accept']} "
-          f"flagged_resample={rep['flagged_resample']} fails={len(rep['fails'])} "
-          f"lse_max_abs={rep['lse_max_abs']:.3g} lse_max_rel={rep['lse_max_rel']:.3g}", flush=True)
+def _check(label, gpu, d, seed=0, offset=0, ref=None, check_lse=True):
+    """Oracle on every sequence of d, comparison, record, assertion."""
+    ref = _oracle(d, seed=seed, offset=offset) if ref is None else ref
+    rep = compare(gpu, ref, d["temperature"], data=d, seed=seed, offset=offset,
+                  check_lse=check_lse)
+    record(label, rep)
+    assert_parity(rep, label)
+    return rep
 
 
 # ------------------------------------------------------------------ Philox --
@@ -60,10 +85,7 @@ def test_philox_words_bitwise(seed, offset):
 def test_small_config_full_parity(cfg):
     d = specgen.generate(specgen.config(cfg))
     gpu = run_gpu(to_device(d))
-    ref = _oracle(d)
-    rep = compare(gpu, ref, d["temperature"])
-    _report(f"config {cfg}", rep)
-    assert_parity(rep, f"config {cfg}")
+    _check(f"config {cfg} ({specgen.config(cfg).name}) full batch", gpu, d)
 
 
 # --------------------------------------- splits, ragged tails, odd shapes --
@@ -91,10 +113,7 @@ def test_small_shapes_parity(cfg, over):
     d = specgen.generate(rec)
     for seed, offset in [(0, 0), (12345, 3)]:
         gpu = run_gpu(to_device(d), seed=seed, offset=offset)
-        ref = _oracle(d, seed=seed, offset=offset)
-        rep = compare(gpu, ref, d["temperature"])
-        _report(f"{rec.name} {over}", rep)
-        assert_parity(rep, str(over))
+        _check(f"shape {rec.name} {over} seed={seed}", gpu, d, seed=seed, offset=offset)
 
 
 @pytest.mark.parametrize("cfg,over", [CASES[i] for i in (0, 1, 2, 3, 5, 6, 7, 10, 11)])
@@ -111,10 +130,7 @@ def test_residual_kernel_choice_parity(cfg, over, fused, monkeypatch):
     geo = sv.spec_verify_get_geometry(ctx)
     assert (geo["residual_splits"] == 0) == bool(fused)
     gpu = run_gpu(t, seed=7, offset=1, ctx=ctx)
-    ref = _oracle(d, seed=7, offset=1)
-    rep = compare(gpu, ref, d["temperature"])
-    _report(f"{rec.name} {over} fused={fused}", rep)
-    assert_parity(rep, str(over))
+    _check(f"draw path {rec.name} {over} fused={fused}", gpu, d, seed=7, offset=1)
     monkeypatch.setenv("SPEC_VERIFY_RESIDUAL_FUSED", str(1 - fused))
     other = run_gpu(t, seed=7, offset=1)
     assert np.array_equal(other["tokens"], gpu["tokens"])
@@ -135,22 +151,11 @@ def big(request):
     torch.cuda.empty_cache()
 
 
-def _sample_rows(rec, d, n=44):
-    rng = np.random.default_rng(1000 + rec.seed)
-    rows = set(rng.choice(rec.batch, size=min(n, rec.batch), replace=False).tolist())
-    greedy = np.nonzero(d["temperature"] == 0)[0]
-    rows.update(greedy[:3].tolist())
-    rows.update([0, rec.batch - 1])
-    return np.array(sorted(rows))
-
-
-def test_large_config_sampled_parity(big):
+def test_large_config_full_parity(big):
+    """Every sequence of the workload against the oracle (the launch
+    configuration the benchmark times)."""
     cfg, rec, d, t, gpu = big
-    rows = _sample_rows(rec, d)
-    ref = _oracle(d, rows=rows)
-    rep = compare(gpu, ref, d["temperature"][rows], rows=rows)
-    _report(f"config {cfg} sampled", rep)
-    assert_parity(rep, f"config {cfg}")
+    _check(f"config {cfg} ({rec.name}) full batch", gpu, d)
 
 
 def test_large_config_invariants(big):
@@ -240,8 +245,7 @@ def test_identical_rows_accept_all_and_bonus(B, G, V):
              temperature=np.full(B, 0.8, np.float32), seq_ids=np.arange(B))
     gpu = run_gpu(to_device(d))
     assert np.all(gpu["accept_len"] == G)
-    rep = compare(gpu, _oracle(d), d["temperature"])
-    assert_parity(rep, "p == q")
+    _check(f"identical rows B={B} G={G} V={V}", gpu, d)
 
 
 def test_disjoint_support_rejects_all():
@@ -259,7 +263,7 @@ def test_disjoint_support_rejects_all():
     gpu = run_gpu(to_device(d))
     assert np.all(gpu["accept_len"] == 0)
     assert np.all(gpu["tokens"][:, 0] >= 32)
-    assert_parity(compare(gpu, _oracle(d), d["temperature"]), "disjoint")
+    _check("disjoint supports", gpu, d)
 
 
 def test_greedy_ties_lowest_index():
@@ -295,9 +299,7 @@ def test_statistical_gate_on_gpu():
              logits_target=np.ascontiguousarray(np.broadcast_to(zp, (N, G + 1, V))),
              draft_tokens=toks, temperature=np.full(N, T, np.float32), seq_ids=np.arange(N))
     gpu = run_gpu(to_device(d), seed=2024, offset=7)
-    rep = compare(gpu, _oracle(d, seed=2024, offset=7), d["temperature"])
-    _report("V=8 gate", rep)
-    assert_parity(rep, "gate")
+    _check("V=8 gate, 10000 draws", gpu, d, seed=2024, offset=7)
     inv_t = np.float32(1.0) / np.float32(T)
     p = softmax((zp * inv_t).astype(np.float64), axis=-1)
     first = gpu["tokens"][:, 0]
@@ -324,9 +326,8 @@ def test_runs_on_a_side_stream_and_times_kernels():
     assert sv.spec_verify_get_geometry(ctx)["residual_splits"] > 0
     assert all(row[0] > 0 and row[1] == 0 and row[2] > 0 for row in times)
     s.synchronize()
-    ref = _oracle(d)
     gpu = dict(accept_len=alen.cpu().numpy(), tokens=toks.cpu().numpy())
-    assert_parity(compare(gpu, ref, d["temperature"], check_lse=False), "side stream")
+    _check("side stream B=8", gpu, d, check_lse=False)
     geo = sv.spec_verify_get_geometry(ctx)
     assert geo["block"] == 256 and geo["row_splits"] >= 1
 
@@ -359,9 +360,7 @@ def test_misaligned_base_pointers_take_the_element_path(cfg):
         assert view.data_ptr() % 16 != 0
         t[key] = view
     gpu = run_gpu(t)
-    rep = compare(gpu, _oracle(d), d["temperature"])
-    _report(f"misaligned {rec.name}", rep)
-    assert_parity(rep, "misaligned")
+    _check(f"misaligned {rec.name}", gpu, d)
 
 
 def _scalar_compare(lp, seed, offset):
@@ -421,7 +420,7 @@ def test_empty_batch_is_a_no_op():
     rec = specgen.config(2).replace(batch=3, vocab=2048)
     d = specgen.generate(rec)
     gpu = run_gpu(to_device(d))
-    assert_parity(compare(gpu, _oracle(d), d["temperature"]), "after empty calls")
+    _check("after empty calls", gpu, d)
 
 
 def test_graph_capture_replays_match_eager():
@@ -580,4 +579,4 @@ def test_first_rejection_in_a_later_pass():
     ref = _oracle(d)
     assert list(ref["accept_len"]) == stars
     assert list(gpu["accept_len"]) == stars
-    assert_parity(compare(gpu, ref, d["temperature"]), "later-pass rejection")
+    _check("first rejection in a later pass", gpu, d, ref=ref)

@@ -10,7 +10,7 @@ from hypothesis import strategies as st
 
 import oracle
 import specgen
-from gpu_helpers import assert_parity, compare, run_gpu, to_device
+from gpu_helpers import assert_parity, compare, record, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -57,5 +57,25 @@ def test_random_shapes_match_oracle(case):
     gpu = run_gpu(to_device(d), seed=seed, offset=offset)
     ref = oracle.verify(d["logits_draft"], d["logits_target"], d["draft_tokens"],
                         d["temperature"], seed=seed, offset=offset)
-    rep = compare(gpu, ref, d["temperature"])
+    rep = compare(gpu, ref, d["temperature"], data=d, seed=seed, offset=offset)
     assert_parity(rep, f"B={d['logits_target'].shape[0]} shape={d['logits_target'].shape}")
+    _TOTALS.append(rep)
+
+
+_TOTALS = []
+
+
+def test_zz_record_random_shape_totals():
+    """Counts summed over the random cases above (run after them)."""
+    if not _TOTALS:
+        pytest.skip("no random cases ran")
+    tot = dict(n=0, exact=0, excused_accept=0, excused_resample=0, fails=[],
+               low_margin_accept=0, low_margin_resample=0, lse_max_abs=0.0, lse_max_rel=0.0)
+    for r in _TOTALS:
+        for k in ("n", "exact", "excused_accept", "excused_resample", "low_margin_accept",
+                  "low_margin_resample"):
+            tot[k] += r[k]
+        tot["fails"] += r["fails"]
+        tot["lse_max_abs"] = max(tot["lse_max_abs"], r["lse_max_abs"])
+        tot["lse_max_rel"] = max(tot["lse_max_rel"], r["lse_max_rel"])
+    record(f"random shapes ({len(_TOTALS)} Hypothesis cases)", tot, cases=len(_TOTALS))

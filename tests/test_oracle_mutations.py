@@ -99,8 +99,8 @@ def test_last_index_on_ties_is_caught():
 
 def test_bonus_from_the_wrong_row_is_caught():
     # the bonus (all accepted) draws from target row G; use row G-1 instead
-    with mutated_oracle("double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)k * V + v), inv_t);\n        double p = exp(xp - lse_p[k]);",
-                        "int kk = k == G && k > 0 ? k - 1 : k;\n        double xp = scaled(raw_logit(logits_target, dtype, p_row0 + (size_t)kk * V + v), inv_t);\n        double p = exp(xp - lse_p[kk]);"):
+    with mutated_oracle("p_row0 + (size_t)k * V, k == G, inv_t, k < G ? lse_q[k] : 0.0,\n                          lse_p[k],",
+                        "p_row0 + (size_t)(k == G && k > 0 ? k - 1 : k) * V, k == G, inv_t,\n                          k < G ? lse_q[k] : 0.0, lse_p[k == G && k > 0 ? k - 1 : k],"):
         fails(pins.test_bonus_distribution_exact_sweep)
 
 
@@ -259,3 +259,14 @@ def test_tree_sampling_uniform_block_off_by_one_is_caught():
     with mutated_oracle("oracle_philox_words(seed, offset, sid, s - 1, words);",
                         "oracle_philox_words(seed, offset, sid, s, words);"):
         fails(tsample.test_chain_is_the_verifier, 2, dict())
+
+
+def test_neighbour_on_the_wrong_side_is_caught():
+    with mutated_oracle("if (lower <= upper) {", "if (lower > upper) {"):
+        fails(pins.test_inverse_cdf_alt_is_the_draw_just_across_the_edge)
+
+
+def test_neighbour_that_keeps_zero_weights_is_caught():
+    with mutated_oracle("for (int v = j - 1; v >= 0; --v)\n                        if (r[v] > 0.0) {",
+                        "for (int v = j - 1; v >= 0; --v)\n                        if (r[v] >= 0.0) {"):
+        fails(pins.test_inverse_cdf_alt_worked_neighbours)

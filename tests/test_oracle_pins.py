@@ -215,6 +215,39 @@ def test_inverse_cdf_exact_bin_counts():
         assert counts[r == 0].sum() == 0
 
 
+def test_inverse_cdf_alt_worked_neighbours():
+    """The token across the nearer edge of the chosen bin, skipping zero weights."""
+    r = np.array([0.0, 1.0, 0.0, 2.0, 3.0, 0.0])            # S = 6, edges 1, 3, 6
+    j, m, a = oracle.inverse_cdf_alt(r, 1.0000001 / 6.0)     # just above the edge C_1 = 1
+    assert (j, a) == (3, 1) and m == pytest.approx(math.log(1.0000001), rel=1e-6)
+    j, m, a = oracle.inverse_cdf_alt(r, 2.9999999 / 6.0)     # just below C_3 = 3
+    assert (j, a) == (3, 4) and m == pytest.approx(math.log(3.0 / 2.9999999), rel=1e-6)
+    assert oracle.inverse_cdf_alt(r, 5.99 / 6.0)[::2] == (4, -1)   # no mass above
+    assert oracle.inverse_cdf_alt(r, 0.5 / 6.0)[::2] == (1, 3)     # lower edge is 0: upper side
+    assert oracle.inverse_cdf_alt(r, 0.0) == (1, 0.0, 3)
+    assert oracle.inverse_cdf_alt(np.zeros(3), 0.5)[::2] == (-1, -1)
+
+
+def test_inverse_cdf_alt_is_the_draw_just_across_the_edge():
+    """Brute force: moving tau across the nearer bin edge by a hair (a tiny
+    change of u, as another summation order would make) lands on the alt
+    token, and the margin is the log distance to that edge."""
+    rng = np.random.default_rng(31)
+    for _ in range(20):
+        r = rng.exponential(size=16)
+        r[rng.choice(16, size=4, replace=False)] = 0.0
+        for u in rng.random(40):
+            j, m, a = oracle.inverse_cdf_alt(r, u)
+            assert j == oracle.inverse_cdf(r, u)[0] and r[j] > 0
+            ud, uu = u * math.exp(-m) * (1 - 1e-9), u * math.exp(m) * (1 + 1e-9)
+            down = oracle.inverse_cdf(r, ud)[0]
+            up = oracle.inverse_cdf(r, uu)[0] if uu < 1 else -1
+            if a >= 0:
+                assert a != j and r[a] > 0 and a in (down, up)
+            else:
+                assert j == np.nonzero(r)[0].max() and down == j
+
+
 # -------------------------------------------------- accept test and residual
 
 def _tiny_case(seed, V=8, G=1, sd=1.5, noise=1.0):
@@ -287,3 +320,30 @@ def test_gathered_logprobs_normalise():
             x = scaled_f32(zf[b, i], d["temperature"][b]).astype(np.float64)
             s = np.exp(x - out["lse"][b, rec.gamma + i]).sum()
             assert abs(s - 1.0) < 1e-12
+
+
+def test_draw_at_matches_the_verification_and_its_distribution():
+    """The draw at a given position equals the verification's own extra token
+    whenever the first rejection (or the bonus) is at that position, and over
+    a grid of uniforms it follows max(0, p - q) / S exactly."""
+    T = 0.9
+    zq, zp = _tiny_case(24, G=2)
+    q0 = softmax(scaled_f32(zq[0], T).astype(np.float64))
+    p0 = softmax(scaled_f32(zp[0], T).astype(np.float64))
+    r = np.maximum(0.0, p0 - q0)
+    t = int(np.argmax(q0 / p0))
+    N = 2048
+    counts = np.zeros(8, np.int64)
+    for k in range(N):
+        u = k / N
+        tok, m, a = oracle.draw_at(zq[0], zp[0], T, u)
+        out = oracle.verify_sequence(zq, zp, [t, 0], T, [1.0 - 2.0 ** -24, 0.0], [u, 0.0, 0.0])
+        assert out["accept_len"] == 0 and out["tokens"][0] == tok
+        assert out["res_margin"] == m and out["res_alt"] == a
+        counts[tok] += 1
+    assert np.all(np.abs(counts - N * r / r.sum()) <= 1.0 + 1e-9)
+    toks = [int(np.argmax(zq[0])), int(np.argmax(zq[1]))]
+    for u in (0.0, 0.123, 0.5, 0.999):
+        out = oracle.verify_sequence(zq, zp, toks, T, [0.0, 0.0], [0.3, 0.3, u])
+        assert out["accept_len"] == 2
+        assert oracle.draw_at(None, zp[2], T, u)[0] == out["tokens"][2]
