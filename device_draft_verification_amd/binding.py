@@ -35,6 +35,7 @@ EXPORTED = (
     "spec_lowrank_head_copy_activation", "spec_lowrank_head_destroy",
     "spec_tree_prune", "spec_tree_verify_init", "spec_tree_verify_set_stream",
     "spec_tree_verify_greedy", "spec_tree_verify_sample", "spec_tree_verify_destroy",
+    "spec_tree_verify_gave_up", "spec_tree_verify_set_spin_limit",
 )
 
 SPEC_TREE_MAX_NODES = 256
@@ -94,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_tree_verify_greedy": ([P, P, P, P, P, P, P, P], i32),
         "spec_tree_verify_sample": ([P, P, P, P, P, P, P, u64, u64, P, P, P], i32),
         "spec_tree_verify_destroy": ([P], i32),
+        "spec_tree_verify_gave_up": ([P, ctypes.POINTER(u64)], i32),
+        "spec_tree_verify_set_spin_limit": ([P, i32], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -505,6 +508,20 @@ def spec_tree_verify_sample(ctx: TreeContext, parent, token, n_nodes, draft, tar
     _check("spec_tree_verify_sample", load_library().spec_tree_verify_sample(
         ctx.handle, _ptr(parent), _ptr(token), _ptr(n_nodes), _ptr(draft), _ptr(target),
         _ptr(temperature), seed, offset, _ptr(out_length), _ptr(out_path), _ptr(out_extra)))
+
+
+def spec_tree_verify_gave_up(ctx: TreeContext) -> int:
+    """Trees reported with length -2 by the sampled calls on ctx so far (syncs its stream)."""
+    n = ctypes.c_uint64(0)
+    _check("spec_tree_verify_gave_up",
+           load_library().spec_tree_verify_gave_up(ctx.handle, ctypes.byref(n)))
+    return n.value
+
+
+def spec_tree_verify_set_spin_limit(ctx: TreeContext, polls: int) -> None:
+    """Test hook: polls before a part gives up waiting for a partner."""
+    _check("spec_tree_verify_set_spin_limit",
+           load_library().spec_tree_verify_set_spin_limit(ctx.handle, int(polls)))
 
 
 def spec_tree_verify_destroy(ctx: TreeContext) -> None:

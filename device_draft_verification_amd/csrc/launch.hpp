@@ -112,10 +112,12 @@ hipError_t launch_residual(const Shape& s, bool vec, int nsplit, int unroll, con
 // Sampled verification of draft trees (spec_tree.h): each tree split over
 // tree_sample_parts() workgroups, n_groups trees at a time (at most
 // tree_sample_max_groups, which the device holds at once). shares holds
-// n_groups * tree_sample_group_bytes() bytes, zeroed once before the first
-// call; call numbers start at 1 and increase by one per launch on the same
-// workspace.
+// n_groups * tree_sample_group_bytes() bytes and ctl three 64-bit words
+// (launches finished, workgroups finished in the running launch, trees given
+// up), all zeroed once before the first call and kept by the kernel itself
+// from then on. A part gives up on a partner after spin_limit polls.
 int tree_sample_parts();
+int tree_sample_default_spin_limit();
 size_t tree_sample_group_bytes();
 hipError_t tree_sample_max_groups(int dtype, int* out_groups);
 bool tree_sample_fits(int vocab, int dtype);
@@ -124,7 +126,7 @@ hipError_t launch_tree_sample(int batch, int max_nodes, int vocab, int dtype, bo
                               const void* draft, const void* target, const float* temperature,
                               uint64_t seed, uint64_t offset, int32_t* out_length,
                               int32_t* out_path, int32_t* out_extra, uint64_t* shares,
-                              int n_groups, uint64_t call, hipStream_t stream);
+                              uint64_t* ctl, int spin_limit, int n_groups, hipStream_t stream);
 
 // Scalar-only accept on gathered log-probability pairs.
 hipError_t launch_accept_scalar(int batch, int gamma, const float* logprobs, uint64_t seed,

@@ -635,13 +635,22 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
 // with device-coherent loads until every tag matches, so one round trip both
 // signals and delivers. Pieces live in two slots by pass parity (a part
 // cannot run two passes ahead of a partner, so the slot it reads holds either
-// the partner's share of this pass or an older one). A tag from an earlier
-// call can only match after 2^28 calls that left the slot untouched. Release
-// and acquire fences are not used: at device scope they write back and
-// invalidate the whole L2 of an XCD, which a thousand workgroups exchanging
-// at once serialise. The grid never exceeds what the device holds at once, so
-// every part becomes resident; every wait is still bounded: a partner missing
-// for kTreeSpinLimit polls marks the tree invalid, and all parts finish.
+// the partner's share of this pass or an older one). The call number is read
+// from a device word at the start of the launch and advanced by the last
+// workgroup to finish it, so every launch (each replay of a captured graph
+// included) tags its exchanges anew; a tag from an earlier launch can only
+// match after 2^28 launches that left the slot untouched. Release and acquire
+// fences are not used: at device scope they write back and invalidate the
+// whole L2 of an XCD, which a thousand workgroups exchanging at once
+// serialise. The grid never exceeds what the device holds at once, so every
+// part becomes resident; every wait is still bounded: a partner missing for
+// the spin limit (kTreeSpinLimit polls unless the context sets another) makes
+// the part give up, and all parts finish.
+//
+// Outputs: part 0 writes the whole outcome of a tree (the drawing part hands
+// it the token through one more exchange), so a tree is reported by the one
+// part that saw every exchange of it: its outcome, -1 for invalid input, or
+// -2 when part 0 or a partner gave up waiting (counted in the control block).
 constexpr int kTreeParts = 4;
 constexpr int kTreeBlock = 256;
 constexpr int kTreeWaves = kTreeBlock / 64;
@@ -687,7 +696,9 @@ struct TreeSampleArgs {
     int32_t* out_path;
     int32_t* out_extra;
     uint64_t* shares;  // [groups][2][kTreeParts][kShareHalves] tagged pieces
-    uint64_t call;     // this call's number (>= 1), increasing per call
+    uint64_t* ctl;     // [0] launches finished, [1] workgroups finished in this
+                       // launch, [2] trees given up (cumulative)
+    int spin_limit;    // polls before a part gives up on a partner
 };
 
 struct TreeShared {
@@ -881,6 +892,7 @@ struct TreePartView {
     int dt;          // dtype
     uint64_t* shares;  // this group's two slots
     uint64_t tag;      // last published tag
+    int spin_limit;    // polls before giving up on a partner
     bool live;       // false once a partner went missing
 
     __device__ inline const void* sub(const void* row) const {
@@ -935,7 +947,7 @@ __device__ inline bool tree_exchange(TreePartView& v, const TreePart mine, TreeS
             }
             if (__ballot(!all) == 0)
                 break;
-            if (++polls > kTreeSpinLimit)
+            if (++polls > v.spin_limit)
                 ok = false;
             else
                 __builtin_amdgcn_s_sleep(1);
@@ -1106,7 +1118,10 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
     v.W = W;
     v.dt = DT;
     v.shares = a.shares + static_cast<size_t>(grp) * 2 * kTreeParts * kShareHalves;
-    v.tag = a.call << 20;
+    // This launch's number: one more than the launches finished before it.
+    const uint64_t call = __hip_atomic_load(a.ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    v.tag = call << 20;
+    v.spin_limit = a.spin_limit;
     v.live = true;
 
     for (int b = grp; b < a.B; b += n_grp) {
@@ -1135,7 +1150,8 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
         auto qrow = [&](int u) { return row_ptr(a.draft, DT, row_base + u, V); };
         auto xval = [&](const void* row, int t) { return scale_logit(load_logit(row, DT, t), inv_t); };
         int u = 0, L = 0, extra = -1;
-        bool draw_here = false;  // this part writes the extra token
+        bool draw_here = false;  // this part draws the extra token
+        int owner = 0;           // the part that draws it
         if (!bad && mode == 0) {
             // T = 0: step to the lowest-index child holding the target argmax.
             for (;;) {
@@ -1264,8 +1280,9 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
                     const float uu = uniform24(w.w1);
                     if (S > 0.0) {
                         const double tau = static_cast<double>(uu) * S;
-                        int owner = -1, last = -1;
+                        int last = -1;
                         double P = 0.0, P_owner = 0.0, P_last = 0.0;
+                        owner = -1;
                         for (int j = 0; j < kTreeParts; ++j) {
                             const double tj = sh.tot_keep[j];
                             if (tj > 0.0) {
@@ -1305,20 +1322,45 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
                 }
             }
         }
-        if (mode == 0 || bad)
-            draw_here = v.part == 0;
-        // Part 0 writes the length and path; the drawing part the extra token.
+        // The drawing part hands its token to part 0 (every part knows the
+        // owner: it follows from the merged totals).
+        if (!bad && mode != 0 && owner > 0) {
+            TreePart mine = part_zero();
+            mine.w[0] = static_cast<uint32_t>(draw_here ? extra : 0);
+            if (!tree_exchange(v, mine, sh))
+                bad = true;
+            else
+                extra = static_cast<int>(sh.xp[owner].w[0]);
+        }
+        // Part 0 writes the outcome: -2 once it or a partner gave up waiting,
+        // -1 for invalid input.
+        const bool gave_up = !v.live;
+        const bool fail = bad || gave_up;
         __syncthreads();
         if (v.part == 0) {
             int32_t* path_out = a.out_path + static_cast<size_t>(b) * M;
             for (int i = tid; i < M; i += kTreeBlock)
-                path_out[i] = !bad && i < L ? sh.path[i] : -1;
-            if (tid == 0)
-                a.out_length[b] = bad ? -1 : L;
+                path_out[i] = !fail && i < L ? sh.path[i] : -1;
+            if (tid == 0) {
+                a.out_length[b] = gave_up ? -2 : (bad ? -1 : L);
+                a.out_extra[b] = fail ? -1 : extra;
+                if (gave_up)
+                    __hip_atomic_fetch_add(a.ctl + 2, 1ULL, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
-        if (draw_here && tid == 0)
-            a.out_extra[b] = bad ? -1 : extra;
         __syncthreads();
+    }
+    // The last workgroup to finish advances the launch counter. Every
+    // workgroup read it at its start, so no part of this launch can see the
+    // new value; the next launch on the stream starts after this one ends.
+    if (tid == 0) {
+        const uint64_t done = __hip_atomic_fetch_add(a.ctl + 1, 1ULL, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done + 1 == gridDim.x) {
+            __hip_atomic_store(a.ctl + 1, 0ULL, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.ctl, call, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -1413,6 +1455,8 @@ int residual_tiles_per_row(int vocab) { return (vocab + kTile - 1) / kTile; }
 
 int tree_sample_parts() { return kTreeParts; }
 
+int tree_sample_default_spin_limit() { return kTreeSpinLimit; }
+
 bool tree_sample_fits(int vocab, int dtype) {
     // The element path (W = 1) has the most tiles.
     (void)dtype;
@@ -1441,14 +1485,14 @@ hipError_t launch_tree_sample(int batch, int max_nodes, int vocab, int dtype, bo
                               const void* draft, const void* target, const float* temperature,
                               uint64_t seed, uint64_t offset, int32_t* out_length,
                               int32_t* out_path, int32_t* out_extra, uint64_t* shares,
-                              int n_groups, uint64_t call, hipStream_t stream) {
+                              uint64_t* ctl, int spin_limit, int n_groups, hipStream_t stream) {
     if (batch == 0)
         return hipSuccess;
-    if (n_groups < 1 || call < 1 || call >= (1ULL << 43))
+    if (n_groups < 1 || spin_limit < 0 || !ctl)
         return hipErrorInvalidValue;
     const TreeSampleArgs args{parent, token, n_nodes, draft, target, temperature, batch,
                               max_nodes, vocab, seed, offset, out_length, out_path, out_extra,
-                              shares, call};
+                              shares, ctl, spin_limit};
     const int g = std::min(n_groups, batch);
     if (dtype == kBF16)
         return vec ? launch_tree_sample_typed<kBF16, true>(g, args, stream)

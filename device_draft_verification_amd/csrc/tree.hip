@@ -338,10 +338,12 @@ struct spec_tree_ctx {
     hipStream_t stream = nullptr;
     ArgPart* part = nullptr;
     // Sampled verification: trees in flight at once, the parts' exchange
-    // slots, and the number of the last launch.
+    // slots followed by the kernel's three control words, and the polls a
+    // part makes before giving up on a partner.
     int sample_groups = 0;
     uint64_t* shares = nullptr;
-    uint64_t call = 0;
+    uint64_t* ctl = nullptr;
+    int spin_limit = 0;
 };
 
 extern "C" {
@@ -405,14 +407,33 @@ int spec_tree_verify_init(int batch, int max_nodes, int vocab, int dtype, void* 
     }
     ctx->sample_groups = std::min(sample_groups, batch);
     const size_t share_bytes = static_cast<size_t>(ctx->sample_groups) * tree_sample_group_bytes();
-    if (hipMalloc(reinterpret_cast<void**>(&ctx->shares), share_bytes) != hipSuccess ||
-        hipMemset(ctx->shares, 0, share_bytes) != hipSuccess) {
+    const size_t ctl_words = 4;
+    ctx->spin_limit = tree_sample_default_spin_limit();
+    if (hipMalloc(reinterpret_cast<void**>(&ctx->shares), share_bytes + ctl_words * 8) != hipSuccess ||
+        hipMemset(ctx->shares, 0, share_bytes + ctl_words * 8) != hipSuccess) {
         (void)hipFree(ctx->shares);
         (void)hipFree(ctx->part);
         delete ctx;
         return SPEC_ENOMEM;
     }
+    ctx->ctl = ctx->shares + share_bytes / 8;
     *out_ctx = ctx;
+    return SPEC_OK;
+}
+
+int spec_tree_verify_set_spin_limit(spec_tree_ctx* ctx, int polls) {
+    if (!ctx || polls < 0)
+        return SPEC_EINVAL;
+    ctx->spin_limit = polls;
+    return SPEC_OK;
+}
+
+int spec_tree_verify_gave_up(spec_tree_ctx* ctx, uint64_t* out_count) {
+    if (!ctx || !out_count)
+        return SPEC_EINVAL;
+    if (hipStreamSynchronize(ctx->stream) != hipSuccess ||
+        hipMemcpy(out_count, ctx->ctl + 2, sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return SPEC_EHIP;
     return SPEC_OK;
 }
 
@@ -476,11 +497,11 @@ int spec_tree_verify_sample(spec_tree_ctx* ctx, const int32_t* parent, const int
         return SPEC_EINVAL;
     const int W = ctx->dtype == SPEC_BF16 ? 8 : 4;
     const bool vec = ctx->V % W == 0 && aligned(draft, 16) && aligned(target, 16);
-    ctx->call += 1;
     const hipError_t e = launch_tree_sample(ctx->B, ctx->M, ctx->V, ctx->dtype, vec, parent, token,
                                             n_nodes, draft, target, temperature, seed, offset,
                                             out_length, out_path, out_extra, ctx->shares,
-                                            ctx->sample_groups, ctx->call, ctx->stream);
+                                            ctx->ctl, ctx->spin_limit, ctx->sample_groups,
+                                            ctx->stream);
     return e == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 

@@ -50,9 +50,13 @@
  * workgroups that own quarters of the vocabulary and exchange per-pass
  * results through the context's workspace; the launch holds at most as many
  * trees as the device keeps resident at once (the rest follow in turn), and
- * calls on one context must not overlap. A part that waits about a second for
- * a partner (possible only if other work keeps the partner off the device)
- * gives up and marks the tree invalid.
+ * calls on one context must not overlap. The exchange tags each launch with a
+ * launch number that the kernel keeps in the context's workspace, so the call
+ * may be captured into a HIP graph and replayed. A part that waits about a
+ * second for a partner (possible only if other work keeps the partner off the
+ * device) gives up; part 0 then reports that tree and the later trees of its
+ * group with length -2 (distinct from the -1 of invalid input), path and extra
+ * token -1, and adds them to a count that spec_tree_verify_gave_up reads.
  *
  * Layouts: dense row-major DEVICE arrays owned by the caller; int32 indices,
  * float32 logq, float64 scores; target logits [B, M, V] in the dtype of
@@ -108,6 +112,16 @@ int spec_tree_verify_sample(spec_tree_ctx* ctx, const int32_t* parent, const int
                             const int32_t* n_nodes, const void* draft, const void* target,
                             const float* temperature, uint64_t seed, uint64_t offset,
                             int32_t* out_length, int32_t* out_path, int32_t* out_extra);
+
+/* Number of trees reported with length -2 (a part gave up waiting for a
+ * partner) by all sampled calls on this context so far. Synchronises the
+ * context's stream. */
+int spec_tree_verify_gave_up(spec_tree_ctx* ctx, uint64_t* out_count);
+
+/* Test hook: the polls a part makes before giving up on a partner (default
+ * 2^20, about a second). A small value makes the bounded wait give up from
+ * the host side while every kernel still exits normally. polls >= 0. */
+int spec_tree_verify_set_spin_limit(spec_tree_ctx* ctx, int polls);
 
 int spec_tree_verify_destroy(spec_tree_ctx* ctx);
 

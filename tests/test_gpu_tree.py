@@ -269,3 +269,98 @@ def test_sample_full_workload_sampled():
     f = check_sample(g, o, temp[rows], rows=rows)
     print(f"  flagged {f}/{rows.size}; GPU mean length {g['length'].mean():.2f}", flush=True)
     assert (g["length"] >= 0).all()
+
+
+def _sample_inputs(B, M, V, seed):
+    trees = specgen.draft_trees(B, M, V, seed=seed)
+    zt = specgen.tree_target_logits(trees, V, seed=seed + 1, dtype="bf16")
+    zq = specgen.tree_target_logits(trees, V, seed=seed + 2, dtype="bf16")
+    rng = np.random.default_rng(seed)
+    temp = rng.uniform(0.3, 1.5, B).astype(np.float32)
+    temp[rng.random(B) < 0.15] = 0.0
+    n = np.full(B, M, np.int32)
+    return trees, zq, zt, temp, n
+
+
+def test_sample_give_up_is_reported_and_counted():
+    """A spin limit of zero polls, set from the host, makes parts give up
+    waiting for partners that are merely late; every kernel still exits. Part 0
+    reports such trees with length -2 and counts them; every other tree is
+    still the oracle's outcome. With the default limit restored the next call
+    on the same context completes every tree."""
+    B, M, V = 64, 8, 2048
+    trees, zq, zt, temp, n = _sample_inputs(B, M, V, 90)
+    ctx = sv.spec_tree_verify_init(B, M, V, torch.bfloat16)
+    before = sv.spec_tree_verify_gave_up(ctx)
+    sv.spec_tree_verify_set_spin_limit(ctx, 0)
+    g = gpu_sample(trees["parent"], trees["token"], n, zq, zt, temp, torch.bfloat16, seed=4,
+                   offset=2, ctx=ctx)
+    gave = sv.spec_tree_verify_gave_up(ctx) - before
+    lost = np.nonzero(g["length"] == -2)[0]
+    print(f"\n[tree give-up] spin limit 0: {lost.size}/{B} trees given up, counted {gave}", flush=True)
+    assert gave == lost.size
+    assert np.all(g["extra"][lost] == -1) and np.all(g["path"][lost] == -1)
+    o = oracle.tree_verify_sample(trees["parent"], trees["token"], n, zq, zt, temp, seed=4, offset=2)
+    kept = np.nonzero(g["length"] != -2)[0]
+    check_sample(g, {k: v[kept] for k, v in o.items()}, temp[kept], rows=kept)
+    sv.spec_tree_verify_set_spin_limit(ctx, 1 << 20)
+    g = gpu_sample(trees["parent"], trees["token"], n, zq, zt, temp, torch.bfloat16, seed=4,
+                   offset=2, ctx=ctx)
+    assert (g["length"] >= 0).all()
+    assert sv.spec_tree_verify_gave_up(ctx) - before == gave
+    check_sample(g, o, temp)
+    sv.spec_tree_verify_destroy(ctx)
+
+
+def test_sample_graph_replays_match_eager():
+    """The sampled call captured into a HIP graph: replays on two input sets
+    copied into the captured buffers, with eager work in between, equal eager
+    calls bit for bit (each launch tags its exchanges with a number the kernel
+    advances itself, so replays never read a previous replay's shares)."""
+    B, M, V = 48, 10, 4096
+    sets = []
+    for sd in (70, 71):
+        trees, zq, zt, temp, n = _sample_inputs(B, M, V, sd)
+        sets.append(dict(parent=dev(trees["parent"]), token=dev(trees["token"]), n=dev(n),
+                         zq=to_dev_logits(zq, torch.bfloat16), zt=to_dev_logits(zt, torch.bfloat16),
+                         temp=dev(temp)))
+    static = {k: v.clone() for k, v in sets[0].items()}
+    s = torch.cuda.Stream()
+    ctx = sv.spec_tree_verify_init(B, M, V, torch.bfloat16, stream=s)
+    L = torch.empty(B, dtype=torch.int32, device="cuda")
+    path = torch.empty((B, M), dtype=torch.int32, device="cuda")
+    extra = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def call():
+        sv.spec_tree_verify_sample(ctx, static["parent"], static["token"], static["n"], static["zq"],
+                                   static["zt"], static["temp"], 6, 3, L, path, extra)
+
+    eager = []
+    for st_ in sets:
+        for k in static:
+            static[k].copy_(st_[k])
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            call()
+        s.synchronize()
+        eager.append((L.clone(), path.clone(), extra.clone()))
+    assert not torch.equal(eager[0][2], eager[1][2])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for r, j in enumerate([1, 0, 1, 0]):
+        for k in static:
+            static[k].copy_(sets[j][k])
+        L.fill_(-7)
+        extra.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(L, eager[j][0]), f"replay {r}"
+        assert torch.equal(path, eager[j][1]), f"replay {r}"
+        assert torch.equal(extra, eager[j][2]), f"replay {r}"
+        _ = (sets[j]["zt"].float().sum()).item()  # eager work between replays
+    del g
+    assert sv.spec_tree_verify_gave_up(ctx) == 0
+    sv.spec_tree_verify_destroy(ctx)
