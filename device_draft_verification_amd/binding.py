@@ -22,6 +22,8 @@ SPEC_EINVAL = -1
 SPEC_EHIP = -2
 SPEC_ENOMEM = -3
 SPEC_ESTATE = -4
+SPEC_ESCRATCH = -5
+SPEC_VERIFY_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = (
     "spec_verify_init", "spec_verify_set_stream", "spec_verify", "spec_verify_offset_ptr",
@@ -36,6 +38,7 @@ EXPORTED = (
     "spec_tree_prune", "spec_tree_verify_init", "spec_tree_verify_set_stream",
     "spec_tree_verify_greedy", "spec_tree_verify_sample", "spec_tree_verify_destroy",
     "spec_tree_verify_gave_up", "spec_tree_verify_set_spin_limit",
+    "spec_verify_noalloc",
 )
 
 SPEC_TREE_MAX_NODES = 256
@@ -69,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_verify_set_stream": ([P, P], i32),
         "spec_verify": ([P, P, P, P, P, u64, u64, P, P], i32),
         "spec_verify_offset_ptr": ([P, P, P, P, P, u64, P, P, P], i32),
+        "spec_verify_noalloc": ([i32, i32, i32, i32, P, P, P, P, P, u64, u64, P, P], i32),
         "spec_accept_logprobs": ([P, P, u64, u64, P], i32),
         "spec_verify_copy_lse": ([P, P], i32),
         "spec_verify_philox_words": ([P, u64, u64, P], i32),
@@ -220,6 +224,31 @@ def spec_verify_offset_ptr(ctx: Context, logits_draft, logits_target, draft_toke
         ctx.handle, _ptr(logits_draft) if G > 0 else None, _ptr(logits_target),
         _ptr(draft_tokens) if G > 0 else None, _ptr(temperature), seed, _ptr(offset_dev),
         _ptr(out_accept_len), _ptr(out_tokens)))
+
+
+def spec_verify_noalloc(logits_draft, logits_target, draft_tokens, temperature, seed: int,
+                        offset: int, out_accept_len, out_tokens, stream=None) -> int:
+    """spec_verify without a context, working in the library's fixed device
+    scratch array (no allocation). Shapes come from logits_target [B, G+1, V].
+    Returns the C status (SPEC_OK, or SPEC_ESCRATCH when the shape's workspace
+    exceeds the array); raises on other errors."""
+    B, G1, V = logits_target.shape
+    G = G1 - 1
+    ldt = logits_target.dtype
+    if G > 0:
+        _expect(logits_draft, (B, G, V), ldt, "logits_draft")
+        _expect(draft_tokens, (B, G), torch.int32, "draft_tokens")
+    _expect(temperature, (B,), torch.float32, "temperature")
+    _expect(out_accept_len, (B,), torch.int32, "out_accept_len")
+    _expect(out_tokens, (B, G + 1), torch.int32, "out_tokens")
+    rc = load_library().spec_verify_noalloc(
+        B, G, V, dtype_code(ldt), _stream_handle(stream),
+        _ptr(logits_draft) if G > 0 else None, _ptr(logits_target),
+        _ptr(draft_tokens) if G > 0 else None, _ptr(temperature), seed, offset,
+        _ptr(out_accept_len), _ptr(out_tokens))
+    if rc not in (SPEC_OK, SPEC_ESCRATCH):
+        _check("spec_verify_noalloc", rc)
+    return rc
 
 
 def spec_accept_logprobs(ctx: Context, logprobs, seed: int, offset: int, out_accept_len) -> None:

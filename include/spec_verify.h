@@ -79,7 +79,9 @@ enum spec_status {
     SPEC_EINVAL = -1, /* bad argument: NULL, shape, dtype, alignment        */
     SPEC_EHIP = -2,   /* a HIP runtime call or kernel launch failed          */
     SPEC_ENOMEM = -3, /* workspace allocation failed                         */
-    SPEC_ESTATE = -4  /* context in the wrong state for this call           */
+    SPEC_ESTATE = -4, /* context in the wrong state for this call           */
+    SPEC_ESCRATCH = -5 /* the shape's workspace exceeds the fixed scratch array
+                          of spec_verify_noalloc                             */
 };
 
 /*
@@ -147,6 +149,34 @@ int spec_verify_offset_ptr(spec_verify_ctx *ctx, const void *logits_draft,
                            const float *temperature, uint64_t seed,
                            const uint64_t *offset_dev, int32_t *out_accept_len,
                            int32_t *out_tokens);
+
+/* Size of the fixed device scratch array of spec_verify_noalloc: 16 MiB. */
+#define SPEC_VERIFY_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * spec_verify without a context: same arguments, definition, launch geometry
+ * (computed per call on the host from the shape, as spec_verify_init does)
+ * and kernels, so it equals spec_verify bit for bit. Its workspace is a fixed
+ * file-scope device array of SPEC_VERIFY_NOALLOC_SCRATCH_BYTES bytes instead
+ * of an allocation; every GPU the library runs on holds its own copy until
+ * the process ends. The call allocates and frees nothing (no hipMalloc,
+ * hipFree or allocating library routine); on its first call on a device it
+ * looks up that device's copy with hipGetSymbolAddress and keeps the address.
+ * Returns SPEC_ESCRATCH, before any launch, when the shape needs more
+ * workspace than the array holds (B = 256, G = 8, V = 152064 needs about
+ * 0.5 MiB), and the statuses of spec_verify otherwise. Calls on one device
+ * share the array, which keeps the last call's contents (every entry a call
+ * reads is written by that call first): calls that overlap in time on one
+ * device (on different streams, or from several host threads) race and give
+ * wrong results. hip_stream is a hipStream_t (NULL = the null stream).
+ */
+int spec_verify_noalloc(int batch, int gamma, int vocab, int dtype, void *hip_stream,
+                        const void *logits_draft, const void *logits_target,
+                        const int32_t *draft_tokens, const float *temperature,
+                        uint64_t seed, uint64_t offset, int32_t *out_accept_len,
+                        int32_t *out_tokens);
 
 /*
  * Scalar-only mode: reads only the gathered log-probability pairs, O(B*G)
