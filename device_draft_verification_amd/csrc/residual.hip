@@ -308,13 +308,12 @@ __device__ inline TileRuns tile_runs(const float* ts, int ntiles) {
             const float v = ts[t];
             tr.v[j] = tr.a0 + j < tr.a1 ? v : 0.0f;
         }
+        // Straight-line code: the values past the run are +0, which adds
+        // nothing to a non-negative sum and never holds mass.
 #pragma unroll
         for (int j = 0; j < kRunRegs; ++j) {
-            if (tr.a0 + j < tr.a1) {
-                tr.mine += static_cast<double>(tr.v[j]);
-                if (tr.v[j] > 0.0f)
-                    tr.last_pos = tr.a0 + j;
-            }
+            tr.mine += static_cast<double>(tr.v[j]);
+            tr.last_pos = tr.v[j] > 0.0f ? tr.a0 + j : tr.last_pos;
         }
     } else {
         for (int t = tr.a0; t < tr.a1; ++t) {
@@ -338,17 +337,16 @@ __device__ inline int locate_tile(const float* ts, const TileRuns& tr, double ta
     double before = 0.0;
     double acc = tr.inc - tr.mine;
     if (REGS && tr.in_regs) {
+        // Straight-line code: the +0 values past the run never hit, and the
+        // running sum is unused once the hit is found.
 #pragma unroll
         for (int j = 0; j < kRunRegs; ++j) {
-            if (tr.a0 + j < tr.a1 && hit < 0) {
-                const float v = tr.v[j];
-                const double next = acc + static_cast<double>(v);
-                if (v > 0.0f && next > tau) {
-                    hit = tr.a0 + j;
-                    before = acc;
-                }
-                acc = next;
-            }
+            const float v = tr.v[j];
+            const double next = acc + static_cast<double>(v);
+            const bool h = hit < 0 && v > 0.0f && next > tau;
+            before = h ? acc : before;
+            hit = h ? tr.a0 + j : hit;
+            acc = next;
         }
     } else {
         for (int t = tr.a0; t < tr.a1 && hit < 0; ++t) {
@@ -370,59 +368,68 @@ __device__ inline int locate_tile(const float* ts, const TileRuns& tr, double ta
     return wave_max_int(tr.last_pos);
 }
 
-// Token inside one tile: lane l recomputes group 64*tile + l exactly as the
-// tile kernel did (a cached re-read), the wavefront scans the group sums in
-// fp64 from P, and the first lane whose elements carry the running prefix past
-// tau names the token. P < 0 asks for the tile's last positive element.
-template <int DT, bool VEC, bool NT>
-__device__ inline int scan_tile(const SeqRows& s, int tile, int groups, double P, double tau) {
-    using IO = GroupIO<DT, VEC, false>;
-    constexpr int W = IO::W;
-    const int lane = threadIdx.x & 63;
-    const int g = tile * kTile + lane;
-    float r[W];
-    float gs = 0.0f;
-    if (g < groups) {
-        IO io;
-        io.load(s, g);
-        io.residual(s, r);
-        gs = pairwise(r);
-    } else {
-#pragma unroll
-        for (int e = 0; e < W; ++e)
-            r[e] = 0.0f;
-    }
-    int my_last = -1;
-#pragma unroll
-    for (int e = 0; e < W; ++e)
-        if (r[e] > 0.0f)
-            my_last = static_cast<int>(g * W + e);
-    if (P < 0.0)
-        return wave_max_int(my_last);
-    const double inc = wave_inclusive_scan(static_cast<double>(gs));
-    int hit = -1;
-    double a = P + (inc - static_cast<double>(gs));
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-        a += static_cast<double>(r[e]);
-        if (hit < 0 && r[e] > 0.0f && a > tau)
-            hit = static_cast<int>(g * W + e);
-    }
-    // a group whose scanned sum crosses tau while its element walk falls
-    // short by rounding: its last positive element
-    if (hit < 0 && gs > 0.0f && P + inc > tau)
-        hit = my_last;
-    const int fl = first_lane(hit >= 0);
-    if (fl < 64)
-        return __shfl(hit, fl, 64);
-    return wave_max_int(my_last);
+// Highest lane whose flag is set, or -1.
+__device__ inline int last_lane(bool flag) {
+    const unsigned long long m = __ballot(flag);
+    return m ? 63 - __clzll(static_cast<long long>(m)) : -1;
 }
 
+// The group and element levels of the draw inside one tile. Lane l holds the
+// sum gs of group 64*tile + l (0 past the row), formed as the tile sums were;
+// P is the fp64 prefix before the tile (P < 0: take the tile's last positive
+// element). The group is the first whose fp64 running sum passes tau; its W
+// elements are then reloaded, one per lane, their residuals formed with the
+// streaming arithmetic, scanned in fp64 from the prefix before the group, and
+// the first element that carries the sum past tau is the token. When rounding
+// leaves the walk short of tau, the chosen group's last positive element is
+// taken. Every lane returns the token.
+template <int DT, bool VEC>
+__device__ inline int locate_in_tile(const SeqRows& s, int tile, float gs, double P, double tau) {
+    constexpr int W = Group<DT, VEC>::W;
+    const int lane = threadIdx.x & 63;
+    const double inc = wave_inclusive_scan(static_cast<double>(gs));
+    bool take_last = P < 0.0;
+    int gl = take_last ? 64 : first_lane(gs > 0.0f && P + inc > tau);
+    double Pg = 0.0;
+    if (gl < 64) {
+        Pg = P + __shfl(inc - static_cast<double>(gs), gl, 64);
+    } else {
+        gl = last_lane(gs > 0.0f);
+        take_last = true;
+        if (gl < 0)
+            gl = 0;  // unreachable: a tile with mass has a group with mass
+    }
+    const long g = static_cast<long>(tile) * kTile + gl;
+    float r = 0.0f;
+    if (lane < W) {
+        const long v = g * W + lane;
+        const float xp = scale_logit(load_logit(s.prow, DT, v), s.inv_t);
+        const float pv = fast_exp2(__builtin_fmaf(xp, kLog2e, -s.mp));
+        if (s.p_only) {
+            r = pv;
+        } else {
+            const float xq = scale_logit(load_logit(s.qrow, DT, v), s.inv_t);
+            const float qv = fast_exp2(__builtin_fmaf(xq, kLog2e, -s.mq));
+            r = fmaxf(__builtin_fmaf(pv, s.ratio, -qv), 0.0f);
+        }
+    }
+    const double einc = wave_inclusive_scan(static_cast<double>(r));
+    int e = take_last ? 64 : first_lane(r > 0.0f && Pg + einc > tau);
+    if (e >= 64) {
+        e = last_lane(r > 0.0f);
+        if (e < 0)
+            e = W - 1;  // unreachable: a group with mass has an element with mass
+    }
+    return static_cast<int>(g * W + e);
+}
+
+// The sum of group 64*tile + l of the row pair (lane l), recomputed with the
+// streaming arithmetic (0 past the row).
 template <int DT, bool VEC, bool NT>
-__device__ inline double tile_sum_of(const SeqRows& s, int t, int groups) {
+__device__ inline float group_sum_of(const SeqRows& s, int tile, int groups) {
     using IO = GroupIO<DT, VEC, NT>;
     constexpr int W = IO::W;
-    const int g = t * kTile + (threadIdx.x & 63);
+    const int g = tile * kTile + (threadIdx.x & 63);
     float gs = 0.0f;
     if (g < groups) {
         IO io;
@@ -431,7 +438,18 @@ __device__ inline double tile_sum_of(const SeqRows& s, int t, int groups) {
         io.residual(s, r);
         gs = pairwise(r);
     }
-    return static_cast<double>(tile_reduce(gs));
+    return gs;
+}
+
+// Token inside one tile, from its group sums recomputed by re-reading it.
+template <int DT, bool VEC, bool NT>
+__device__ inline int scan_tile(const SeqRows& s, int tile, int groups, double P, double tau) {
+    return locate_in_tile<DT, VEC>(s, tile, group_sum_of<DT, VEC, false>(s, tile, groups), P, tau);
+}
+
+template <int DT, bool VEC, bool NT>
+__device__ inline double tile_sum_of(const SeqRows& s, int t, int groups) {
+    return static_cast<double>(tile_reduce(group_sum_of<DT, VEC, NT>(s, t, groups)));
 }
 
 // The draw from the tile sums `ts` (global memory or LDS) of one row pair, by
@@ -459,6 +477,23 @@ __device__ inline int draw_token(SeqRows& s, float u, const float* ts, int ntile
         double P;
         const int tile = locate_tile<true>(ts, tr, tau, &P);
         return scan_tile<DT, VEC, NT>(s, tile, groups, P, tau);
+    }
+    return draw_p_fallback<DT, VEC, NT>(s, u, ntiles, groups);
+}
+
+// The draw with every group sum of the row kept (gs_lds[64 * tile + l]):
+// the tile's group sums are read instead of recomputed.
+template <int DT, bool VEC, bool NT>
+__device__ inline int draw_token_gs(SeqRows& s, float u, const float* ts, const float* gs_lds,
+                                    int ntiles, int groups) {
+    const TileRuns tr = tile_runs<true>(ts, ntiles);
+    const double S = lane63_f64(tr.inc);
+    if (S > 0.0) {
+        const double tau = static_cast<double>(u) * S;
+        double P;
+        const int tile = locate_tile<true>(ts, tr, tau, &P);
+        const float gs = gs_lds[tile * kTile + (threadIdx.x & 63)];
+        return locate_in_tile<DT, VEC>(s, tile, gs, P, tau);
     }
     return draw_p_fallback<DT, VEC, NT>(s, u, ntiles, groups);
 }
@@ -517,7 +552,9 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
 
 // One workgroup of 16 wavefronts per sequence: the wavefronts stream the
 // sequence's tiles with the tile kernel's arithmetic and per-tile sums, keep
-// the tile sums in LDS, and after one barrier wavefront 0 draws the token.
+// the tile sums in LDS (with GS also every group sum, so the draw reads the
+// chosen tile's group sums instead of recomputing them), and after one
+// barrier wavefront 0 draws the token.
 // Used when there are enough sequences to give every CU a workgroup; it saves
 // the second launch and the round trip of the tile sums through memory.
 // Tiles are handed out by an LDS counter (each wavefront holds two in flight
@@ -525,14 +562,15 @@ __global__ __launch_bounds__(64) void residual_locate_kernel(
 // late take fewer tiles and all reach the barrier together.
 constexpr int kFusedBlock = 1024;
 
-template <int DT, bool VEC, bool NT, int BLOCK>
+template <int DT, bool VEC, bool NT, int BLOCK, bool GS>
 __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
     const void* __restrict__ draft, const void* __restrict__ target, int gamma, int vocab,
     int ntiles, const SeqState* __restrict__ seq, int32_t* __restrict__ out_tok) {
     using IO = GroupIO<DT, VEC, NT>;
     constexpr int W = IO::W;
     constexpr int kFusedWaves = BLOCK / 64;
-    extern __shared__ float lds_ts[];
+    extern __shared__ float lds_ts[];  // [ntiles] tile sums, then with GS [64 * ntiles] group sums
+    float* const lds_gs = lds_ts + ntiles;
     __shared__ int next_tile;
     const int b = blockIdx.x;
     const SeqState st = seq[b];
@@ -562,6 +600,8 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
             io.residual(s, r);
             gs = pairwise(r);
         }
+        if constexpr (GS)
+            lds_gs[g] = gs;
         const float ts = tile_reduce(gs);
         if (lane == 0)
             lds_ts[t] = ts;
@@ -595,7 +635,13 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
     __syncthreads();
     if (wid != 0)
         return;
-    locate_emit<DT, VEC, NT>(s, st, lds_ts, ntiles, groups, gamma, b, out_tok);
+    if constexpr (GS) {
+        const int token = draw_token_gs<DT, VEC, NT>(s, st.u_res, lds_ts, lds_gs, ntiles, groups);
+        if (lane == 0)
+            out_tok[static_cast<size_t>(b) * (gamma + 1) + st.k] = token;
+    } else {
+        locate_emit<DT, VEC, NT>(s, st, lds_ts, ntiles, groups, gamma, b, out_tok);
+    }
 }
 
 // ----------------------------------------------- sampled draft trees ---
@@ -1400,6 +1446,22 @@ hipError_t launch_tree_sample_typed(int n_groups, const TreeSampleArgs& args, hi
     return hipGetLastError();
 }
 
+// Largest LDS request of the fused draw with its group sums (the CU has
+// 160 KiB; a workgroup of it is alone on its CU either way).
+constexpr size_t kFusedGsMaxBytes = 144 * 1024;
+
+// The kernel with group sums may ask for up to kFusedGsMaxBytes of dynamic
+// LDS: raised once per instantiation; without it the draw recomputes them.
+template <int DT, bool VEC, bool NT>
+bool fused_gs_allowed() {
+    static const bool ok =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(
+                                residual_fused_kernel<DT, VEC, NT, kFusedBlock, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(kFusedGsMaxBytes)) == hipSuccess;
+    return ok;
+}
+
 template <int DT, bool VEC, int U>
 hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const void* draft,
                         const void* target, const SeqState* seq, float* tile_sums,
@@ -1413,11 +1475,17 @@ hipError_t launch_typed(const Shape& sh, int nsplit, int tiles_per_row, const vo
     const int ntiles = (groups + kTile - 1) / kTile;
     if (nsplit == 0) {
         // Two tiles in flight per wavefront: 16 wavefronts keep 64 KiB in
-        // flight per workgroup.
-        return launch(residual_fused_kernel<DT, VEC, NT, kFusedBlock>,
-                      dim3(static_cast<unsigned>(sh.batch)), dim3(kFusedBlock),
-                      static_cast<size_t>(ntiles) * sizeof(float), stream, ev, draft, target,
-                      sh.gamma, sh.vocab, ntiles, seq, out_tok);
+        // flight per workgroup. The group sums join the tile sums in LDS when
+        // they fit.
+        const size_t ts_bytes = static_cast<size_t>(ntiles) * sizeof(float);
+        const size_t gs_bytes = ts_bytes * (1 + kTile);
+        if (gs_bytes <= kFusedGsMaxBytes && fused_gs_allowed<DT, VEC, NT>())
+            return launch(residual_fused_kernel<DT, VEC, NT, kFusedBlock, true>,
+                          dim3(static_cast<unsigned>(sh.batch)), dim3(kFusedBlock), gs_bytes,
+                          stream, ev, draft, target, sh.gamma, sh.vocab, ntiles, seq, out_tok);
+        return launch(residual_fused_kernel<DT, VEC, NT, kFusedBlock, false>,
+                      dim3(static_cast<unsigned>(sh.batch)), dim3(kFusedBlock), ts_bytes, stream,
+                      ev, draft, target, sh.gamma, sh.vocab, ntiles, seq, out_tok);
     }
     // Timing the split pair: the tile kernel's start to the locate kernel's stop.
     const int per = (ntiles + nsplit - 1) / nsplit;
