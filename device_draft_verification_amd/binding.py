@@ -13,7 +13,10 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+# SPEC_VERIFY_LIB selects another build of the same sources (for instance the
+# host-sanitizer build of the test suite).
+LIB_PATH = os.environ.get("SPEC_VERIFY_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
 
 SPEC_F32 = 0
 SPEC_BF16 = 1

@@ -35,15 +35,20 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 4, out: str | None = None,
+          extra_flags=()) -> str:
+    """Compile every source in csrc/ and link the library at `out` (default:
+    next to this file). extra_flags are added to each compile (the sanitizer
+    test passes host-only sanitizer flags)."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objdir = os.path.join(HERE, "_build")
+    lib_path = out or LIB_PATH
+    objdir = os.path.join(os.path.dirname(lib_path), "_build" if out is None else "_build_extra")
     os.makedirs(objdir, exist_ok=True)
     objs = []
     procs = []
     for src in srcs:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -52,13 +57,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             _wait(procs)
             procs = []
     _wait(procs)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    tmp = lib_path + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra_flags, "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 def _wait(procs):

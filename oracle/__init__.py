@@ -43,20 +43,23 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "spec_oracle.c"), os.path.join(_HERE, "bandit_oracle.c")]
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB selects another build of the same sources (the sanitizer test's).
+LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
 
 
-def build() -> str:
-    """Compile the oracle with gcc: -O2, no fast-math, no FP contraction."""
-    tmp = LIB_PATH + ".tmp"
+def build(out: str | None = None, extra_flags=()) -> str:
+    """Compile the oracle with gcc: -O2, no fast-math, no FP contraction
+    (extra_flags: e.g. the sanitizers of the sanitizer test)."""
+    out = out or LIB_PATH
+    tmp = out + ".tmp"
     cmd = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, *_SRCS, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", *extra_flags, "-o", tmp, *_SRCS, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None

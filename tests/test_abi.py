@@ -135,3 +135,29 @@ def test_binding_refuses_missing_library(tmp_path, lib):
             sv.binding.load_library(str(tmp_path / "missing.so"))
     finally:
         sv.binding._lib = saved
+
+
+def test_noalloc_host_checks(lib):
+    """spec_verify_noalloc refuses bad shapes and pointers, and a shape whose
+    workspace exceeds its fixed scratch array, on the host before any HIP call
+    (so this runs without a GPU: the pointers are never dereferenced)."""
+    E, X = sv.binding.SPEC_EINVAL, sv.binding.SPEC_ESCRATCH
+    p = ctypes.c_void_p(1 << 20)  # aligned stand-in, never touched
+    args = (p, p, p, p, 0, 0, p, p)
+    assert lib.spec_verify_noalloc(4, 2, 100, 7, None, *args) == E          # dtype
+    assert lib.spec_verify_noalloc(4, -1, 100, 1, None, *args) == E         # gamma
+    assert lib.spec_verify_noalloc(4, 2, 0, 1, None, *args) == E            # vocab
+    assert lib.spec_verify_noalloc(4, 2, 100, 1, None, p, None, p, p, 0, 0, p, p) == E
+    assert lib.spec_verify_noalloc(4, 2, 100, 1, None, p, p, p, p, 0, 0, ctypes.c_void_p(2), p) == E
+    assert lib.spec_verify_noalloc(0, 2, 100, 1, None, None, None, None, None, 0, 0, None,
+                                   None) == sv.binding.SPEC_OK            # empty batch
+    # two-kernel draw (B < 128): 127 * ceil(V / 64) tile sums exceed 16 MiB
+    assert lib.spec_verify_noalloc(127, 1, 1 << 25, 1, None, *args) == X
+    assert sv.spec_verify_strerror(X).startswith("the shape's workspace")
+
+
+def test_tree_status_hooks_refuse_null(lib):
+    E = sv.binding.SPEC_EINVAL
+    n = ctypes.c_uint64(0)
+    assert lib.spec_tree_verify_gave_up(None, ctypes.byref(n)) == E
+    assert lib.spec_tree_verify_set_spin_limit(None, 4) == E
