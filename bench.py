@@ -26,19 +26,30 @@ sys.path.insert(0, ROOT)
 METRIC = "verified sequences/sec and achieved HBM GB/s (% of peak) at B×(γ+1)×V"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 WORKLOAD_CONFIG = 4
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rownorm_B256_g8_V152064_traffic.json")
-KERNEL_SOURCES = ["device_draft_verification_amd/csrc/rownorm.hip",
-                  "device_draft_verification_amd/csrc/common.hpp",
-                  "device_draft_verification_amd/csrc/launch.hpp"]
+# Counter records (rocprofv3 FETCH_SIZE / WRITE_SIZE of the B=256 workload's
+# kernels) and the sources each depends on: a record no longer matching its
+# sources is reported as null.
+_CSRC = "device_draft_verification_amd/csrc/"
+TRAFFIC = {
+    "row_norm": dict(kernel="row_norm_kernel",
+                     file=os.path.join(ROOT, "profiles", "rownorm_B256_g8_V152064_traffic.json"),
+                     sources=[_CSRC + "rownorm.hip", _CSRC + "common.hpp", _CSRC + "launch.hpp"]),
+    "residual": dict(kernel="residual_fused_kernel",
+                     file=os.path.join(ROOT, "profiles", "residual_B256_g8_V152064_traffic.json"),
+                     sources=[_CSRC + "residual.hip", _CSRC + "accept.hpp", _CSRC + "philox.hpp",
+                              _CSRC + "common.hpp", _CSRC + "launch.hpp"]),
+}
+PROBE_BYTES = 1 << 30   # read-only probe buffer: four times the last-level cache
+PROBE_BLOCKS = 8192
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(name: str = "row_norm") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in TRAFFIC[name]["sources"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -202,51 +213,77 @@ def _counter_rows(path: str, counter: str):
 
 
 def derive_traffic(fetch_csv: str, write_csv: str) -> int:
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the row-normaliser kernel,
-    each scaled by what the same counter reads for the 1 GiB calibration copy
-    (which moves exactly COPY_BYTES each way)."""
-    def per_kernel(path, counter):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel in TRAFFIC
+    found in the two counter runs, each scaled by what the same counter reads
+    for the 1 GiB calibration copy (which moves exactly COPY_BYTES each way)."""
+    def per_kernel(path, counter, kernel):
         rows = list(_counter_rows(path, counter))
         # sum over the counter's instances per dispatch
         by_dispatch = {}
         for r in rows:
             key = (r["Dispatch_Id"], r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0))
             by_dispatch[key] = by_dispatch.get(key, 0.0) + float(r["Counter_Value"])
-        k1 = [v for (d, name, g), v in by_dispatch.items() if "row_norm_kernel" in name]
+        ks = [v for (d, name, g), v in by_dispatch.items() if kernel in name]
         # the calibration copy is the largest device-to-device copy of the run
         copies = [v for (d, name, g), v in by_dispatch.items() if "copyBuffer" in name]
         copy_kib = max(copies) if copies else None
-        return (sum(k1) / len(k1) if k1 else None), copy_kib
-    fk, fc = per_kernel(fetch_csv, "FETCH_SIZE")
-    wk, wc = per_kernel(write_csv, "WRITE_SIZE")
-    f_scale = COPY_BYTES / (fc * 1024.0)
-    w_scale = COPY_BYTES / (wc * 1024.0)
-    fetch_b = fk * 1024.0 * f_scale
-    write_b = wk * 1024.0 * w_scale
-    rec = {"kernel": "row_norm_kernel", "workload": "B256_g8_V152064_bf16_corr",
-           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
-           "copy_fetch_kib": fc, "copy_write_kib": wc, "copy_bytes": COPY_BYTES,
-           "fetch_scale": f_scale, "write_scale": w_scale,
-           "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
-           "kernel_source_hash": kernel_source_hash()}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
-    print(json.dumps(rec))
-    return 0
+        return (sum(ks) / len(ks) if ks else None), copy_kib
+    written = 0
+    for name, t in TRAFFIC.items():
+        fk, fc = per_kernel(fetch_csv, "FETCH_SIZE", t["kernel"])
+        wk, wc = per_kernel(write_csv, "WRITE_SIZE", t["kernel"])
+        if fk is None or wk is None or not fc or not wc:
+            continue
+        f_scale = COPY_BYTES / (fc * 1024.0)
+        w_scale = COPY_BYTES / (wc * 1024.0)
+        rec = {"kernel": t["kernel"], "workload": "B256_g8_V152064_bf16_corr",
+               "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+               "copy_fetch_kib": fc, "copy_write_kib": wc, "copy_bytes": COPY_BYTES,
+               "fetch_scale": f_scale, "write_scale": w_scale,
+               "hbm_bytes_per_launch": int(round(fk * 1024.0 * f_scale + wk * 1024.0 * w_scale)),
+               "kernel_source_hash": kernel_source_hash(name)}
+        os.makedirs(os.path.dirname(t["file"]), exist_ok=True)
+        with open(t["file"], "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        written += 1
+    return 0 if written else 1
 
 
-def load_traffic(k1_launch_bytes: int):
-    """HBM bytes per launch of the row-normaliser kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None when the kernel source has
-    changed since they were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def load_traffic(name: str = "row_norm"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs, or None when its sources have changed since
+    they were taken."""
+    path = TRAFFIC[name]["file"]
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(name):
         return None
     return int(t["hbm_bytes_per_launch"])
+
+
+def hbm_probe(sv, torch, dev, stream, reps: int = 20) -> dict:
+    """The read-only probe over a 1 GiB buffer: the practical read ceiling of
+    this device, reported beside the vendor figure."""
+    buf = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(PROBE_BLOCKS, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        sv.spec_hbm_read_probe(buf, sink, PROBE_BLOCKS, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        sv.spec_hbm_read_probe(buf, sink, PROBE_BLOCKS, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+    del buf, sink
+    return {"bytes": PROBE_BYTES, "us_median": round(float(np.median(us)), 2),
+            "gbs": round(PROBE_BYTES / (float(np.median(us)) * 1e-6) / 1e9, 1),
+            "blocks": PROBE_BLOCKS, "reps": reps}
 
 
 def main() -> int:
@@ -384,6 +421,7 @@ def main() -> int:
         step(args.warmup + i)
     per_kernel = np.array(sv.spec_verify_read_timing(ctx, args.steps))  # [K, 3] ms
     sv.spec_verify_enable_timing(ctx, 0)
+    k1_med, k3_med = float(np.median(per_kernel[:, 0])), float(np.median(per_kernel[:, 2]))
 
     # Algorithmic bytes per call: outputs are a pure function of (inputs, seed,
     # offset), so each timed call's accept lengths are recomputed untimed.
@@ -531,7 +569,11 @@ def main() -> int:
         f"accept {k2_ms * 1e3:.1f} us, residual {k3_ms * 1e3:.1f} us ({k3_gbs:.0f} GB/s); "
         f"whole call {call_gbs:.0f} GB/s")
 
-    traffic = load_traffic(int(k1_bytes)) if args.workload == WORKLOAD_CONFIG else None
+    on_workload = args.workload == WORKLOAD_CONFIG
+    traffic = load_traffic("row_norm") if on_workload else None
+    traffic_k3 = load_traffic("residual") if on_workload and geo["residual_splits"] == 0 else None
+    probe = hbm_probe(sv, torch, dev, stream)
+    pg = probe["gbs"]
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -555,14 +597,19 @@ def main() -> int:
         "hbm_gbs_whole_call": round(call_gbs, 1),
         "hbm_frac_whole_call": round(call_gbs / HBM_PEAK_GBS, 4),
         "kernels": {
-            "row_norm": {"us": round(k1_ms * 1e3, 2), "bytes": int(k1_bytes),
+            "row_norm": {"us": round(k1_ms * 1e3, 2), "us_median": round(k1_med * 1e3, 2),
+                         "bytes": int(k1_bytes),
                          "gbs": round(k1_gbs, 1), "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                         "frac_probe": round(k1_gbs / pg, 4), "traffic": traffic,
                          "splits": geo["row_splits"]},
             "accept": {"us": round(k2_ms * 1e3, 2), "bytes": int(k2_bytes)},
-            "residual": {"us": round(k3_ms * 1e3, 2), "bytes": int(k3_bytes),
+            "residual": {"us": round(k3_ms * 1e3, 2), "us_median": round(k3_med * 1e3, 2),
+                         "bytes": int(k3_bytes),
                          "gbs": round(k3_gbs, 1), "frac": round(k3_gbs / HBM_PEAK_GBS, 4),
+                         "frac_probe": round(k3_gbs / pg, 4), "traffic": traffic_k3,
                          "splits": geo["residual_splits"]},
         },
+        "hbm_probe": probe,
         "scalar_mode": {"us_per_call": round(scalar_us, 2), "batch": sc_b, "gamma": sc_g,
                         "bytes": sc_b * sc_g * 8 + sc_b * 4,
                         "sequences_per_s": round(sc_b / (scalar_us * 1e-6), 1)},

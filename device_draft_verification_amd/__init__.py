@@ -21,5 +21,5 @@ from .binding import (  # noqa: F401
     SPEC_TREE_MAX_NODES, TreeContext, spec_tree_prune, spec_tree_verify_destroy,
     spec_tree_verify_greedy, spec_tree_verify_init, spec_tree_verify_sample,
     spec_tree_verify_set_stream, spec_tree_verify_gave_up, spec_tree_verify_set_spin_limit,
-    SPEC_ESCRATCH, SPEC_VERIFY_NOALLOC_SCRATCH_BYTES, spec_verify_noalloc,
+    SPEC_ESCRATCH, SPEC_VERIFY_NOALLOC_SCRATCH_BYTES, spec_verify_noalloc, spec_hbm_read_probe,
 )

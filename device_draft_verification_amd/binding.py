@@ -41,7 +41,7 @@ EXPORTED = (
     "spec_tree_prune", "spec_tree_verify_init", "spec_tree_verify_set_stream",
     "spec_tree_verify_greedy", "spec_tree_verify_sample", "spec_tree_verify_destroy",
     "spec_tree_verify_gave_up", "spec_tree_verify_set_spin_limit",
-    "spec_verify_noalloc",
+    "spec_verify_noalloc", "spec_hbm_read_probe",
 )
 
 SPEC_TREE_MAX_NODES = 256
@@ -76,6 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_verify": ([P, P, P, P, P, u64, u64, P, P], i32),
         "spec_verify_offset_ptr": ([P, P, P, P, P, u64, P, P, P], i32),
         "spec_verify_noalloc": ([i32, i32, i32, i32, P, P, P, P, P, u64, u64, P, P], i32),
+        "spec_hbm_read_probe": ([P, u64, P, i32, P], i32),
         "spec_accept_logprobs": ([P, P, u64, u64, P], i32),
         "spec_verify_copy_lse": ([P, P], i32),
         "spec_verify_philox_words": ([P, u64, u64, P], i32),
@@ -252,6 +253,16 @@ def spec_verify_noalloc(logits_draft, logits_target, draft_tokens, temperature, 
     if rc not in (SPEC_OK, SPEC_ESCRATCH):
         _check("spec_verify_noalloc", rc)
     return rc
+
+
+def spec_hbm_read_probe(buf, sink, blocks: int, stream=None) -> None:
+    """Read-only HBM probe over the bytes of device tensor buf (measurement
+    utility); sink is an int32/uint32 device tensor of at least `blocks` words."""
+    if buf.device.type != "cuda" or sink.device.type != "cuda" or sink.numel() < blocks:
+        raise ValueError("buf and sink must be device tensors, sink of at least `blocks` words")
+    nbytes = buf.numel() * buf.element_size()
+    _check("spec_hbm_read_probe", load_library().spec_hbm_read_probe(
+        _ptr(buf), nbytes, _ptr(sink), int(blocks), _stream_handle(stream)))
 
 
 def spec_accept_logprobs(ctx: Context, logprobs, seed: int, offset: int, out_accept_len) -> None:

@@ -275,6 +275,19 @@ int spec_verify_get_geometry(spec_verify_ctx *ctx, int *out);
 /* Free the workspace and the context (waits for the context's stream). */
 int spec_verify_destroy(spec_verify_ctx *ctx);
 
+/*
+ * Measurement utility (not part of the verification): a read-only streaming
+ * probe of HBM, the practical ceiling the streaming kernels are compared with
+ * beside the vendor peak. Reads `bytes` (a multiple of 16) of the device
+ * buffer `buf` (16-byte aligned) with 16-byte non-temporal loads, one
+ * contiguous run per workgroup of 256 threads (`blocks` of them; the row
+ * kernel's access pattern), and writes one word per workgroup into
+ * the device array sink[blocks] (4-byte aligned) so the loads are kept.
+ * Enqueued on hip_stream (a hipStream_t; NULL = the null stream).
+ */
+int spec_hbm_read_probe(const void *buf, uint64_t bytes, uint32_t *sink, int blocks,
+                        void *hip_stream);
+
 /* A static description of a status code. */
 const char *spec_verify_strerror(int code);
 

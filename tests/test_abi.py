@@ -161,3 +161,12 @@ def test_tree_status_hooks_refuse_null(lib):
     n = ctypes.c_uint64(0)
     assert lib.spec_tree_verify_gave_up(None, ctypes.byref(n)) == E
     assert lib.spec_tree_verify_set_spin_limit(None, 4) == E
+
+
+def test_probe_host_checks(lib):
+    E = sv.binding.SPEC_EINVAL
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.spec_hbm_read_probe(None, 1024, p, 4, None) == E
+    assert lib.spec_hbm_read_probe(p, 1000, p, 4, None) == E       # not a multiple of 16
+    assert lib.spec_hbm_read_probe(p, 1024, p, 0, None) == E       # no workgroups
+    assert lib.spec_hbm_read_probe(p, 0, p, 4, None) == sv.binding.SPEC_OK
