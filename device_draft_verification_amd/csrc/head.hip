@@ -455,29 +455,6 @@ __global__ __launch_bounds__(kStreamWaves * 64) void head_up_stream_kernel(
     for (int i = 0; i < kRing - 1; ++i)
         issue(b0 + i);
 
-    // Step for block b: wait until it has landed, publish it, refill the ring
-    // and read its fragments. Loads complete in order, and kLoadsPerBlock *
-    // (kRing - 2) loads were issued after block b's: once at most that many
-    // are outstanding, block b is in LDS. The barrier then makes every
-    // wavefront's part of it visible and frees the slot read one step earlier.
-    auto fetch = [&](int b, bf16x8 (&a)[KS]) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerBlock * (kRing - 2)));
-        __syncthreads();
-        issue(b + kRing - 1);
-        const uint16_t* slot = ring[(b - b0) % kRing];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            a[ks] = __builtin_bit_cast(bf16x8,
-                                       *reinterpret_cast<const u32x4*>(slot + ks * 512 + lane * 8));
-    };
-    // A quarter of the block's K range.
-    auto mma = [&](const bf16x8 (&a)[KS], f32x4 (&acc)[NT], int q) {
-#pragma unroll
-        for (int ks = q * (KS / 4); ks < (q + 1) * (KS / 4); ++ks)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], ub[nt][ks], acc[nt], 0, 0, 0);
-    };
     // Finishing block b: lane l holds logits v0..v0+3 of row n (V % 8 == 0:
     // v0 < V covers all four). Part 2 nt rounds and scales row tile nt and
     // moves its reference; part 2 nt + 1 adds its terms and stores it. Lanes
@@ -520,29 +497,59 @@ __global__ __launch_bounds__(kStreamWaves * 64) void head_up_stream_kernel(
         }
     };
     static_assert(2 * NT == 4, "four finishing parts, one per quarter of K");
+    // Fragments one quarter of K ahead: while the matrix instructions of
+    // quarter q of block b run, the four fragments of the next quarter (of
+    // block b, or quarter 0 of block b + 1) are read from LDS into the other
+    // half of a two-quarter register buffer, so the reads hide behind the
+    // matrix work instead of preceding it.
+    constexpr int QK = KS / 4;  // fragments per quarter
+    auto read_quarter = [&](int b, int q, bf16x8 (&a)[QK]) {
+        const uint16_t* slot = ring[(b - b0) % kRing];
+#pragma unroll
+        for (int i = 0; i < QK; ++i)
+            a[i] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(slot + (q * QK + i) * 512 + lane * 8));
+    };
+    auto mma_q = [&](const bf16x8 (&a)[QK], f32x4 (&acc)[NT], int q) {
+#pragma unroll
+        for (int i = 0; i < QK; ++i)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], ub[nt][q * QK + i], acc[nt],
+                                                                  0, 0, 0);
+    };
+    // Block b + 1 is readable once its loads have landed (loads complete in
+    // order, and kLoadsPerBlock * (kRing - 3) loads were issued after them:
+    // stores issued meanwhile only make this wait stricter) and the barrier
+    // has made every wavefront's part visible. Passing the barrier also means
+    // every wavefront has finished block b - 1, whose slot is refilled next.
+    auto publish_next = [&](int b) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerBlock * (kRing - 3)));
+        __syncthreads();
+        issue(b + kRing - 1);
+    };
+    // Block b0 first: its loads are followed by kRing - 2 blocks' worth.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerBlock * (kRing - 2)));
+    __syncthreads();
+    bf16x8 qa[2][QK];
+    read_quarter(b0, 0, qa[0]);
     // Two-stage pipeline: block b is multiplied while block b - 1 is finished,
-    // a quarter of each at a time.
+    // a quarter of each at a time, and the next quarter's fragments are read.
     f32x4 acc_c[NT], acc_n[NT];
-    {
-        bf16x8 a[KS];
-        fetch(b0, a);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            acc_c[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            mma(a, acc_c, q);
-    }
-    for (int b = b0 + 1; b < b1; ++b) {
-        bf16x8 a[KS];
-        fetch(b, a);
+    for (int b = b0; b < b1; ++b) {
+        publish_next(b);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             acc_n[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            mma(a, acc_n, q);
-            finish(b - 1, acc_c, q);
+            if (q < 3)
+                read_quarter(b, q + 1, qa[(q + 1) & 1]);
+            else
+                read_quarter(b + 1, 0, qa[0]);  // past the run: the reloaded last block, unused
+            mma_q(qa[q & 1], acc_n, q);
+            if (b > b0)
+                finish(b - 1, acc_c, q);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
