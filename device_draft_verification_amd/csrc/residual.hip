@@ -756,10 +756,35 @@ struct TreeShared {
     int red_i[kTreeWaves];
     TreePart xp[kTreeParts];
     double tot_keep[kTreeParts];  // per-part residual totals of the draw's tile sums
+    uint64_t nodes[kTreeBlock / 64];  // a set of nodes, one bit each (node_set)
     int flag;
     int decision;
     int ok;
 };
+
+// The set of nodes i < n (one per thread, M <= kTreeBlock) with pred(i)
+// true, into sh.nodes; every thread then reads it. Two barriers.
+template <class P>
+__device__ inline void node_set(TreeShared& sh, int n, P&& pred) {
+    const int i = threadIdx.x;
+    const uint64_t m = __ballot(i < n && pred(i));
+    __syncthreads();  // earlier readers of sh.nodes are done
+    if ((i & 63) == 0)
+        sh.nodes[i >> 6] = m;
+    __syncthreads();
+}
+
+// The lowest node >= s in sh.nodes, or `none`.
+__device__ inline int node_set_next(const TreeShared& sh, int s, int none) {
+    for (int w = s >> 6; w < kTreeBlock / 64; ++w) {
+        uint64_t m = sh.nodes[w];
+        if (w == (s >> 6))
+            m &= ~0ULL << (s & 63);
+        if (m)
+            return w * 64 + __ffsll(static_cast<long long>(m)) - 1;
+    }
+    return none;
+}
 
 // Block-wide reductions of the tree workgroup (every thread gets the result).
 __device__ inline float tree_block_max(float v, TreeShared& sh) {
@@ -926,8 +951,8 @@ __device__ inline void merge_norm(const TreeShared& sh, bool second, float* m_ou
     *s_out = S;
 }
 
-constexpr int kTreeDepth1 = 4;  // ring depth of a one-row pass
-constexpr int kTreeDepth2 = 2;  // ring depth of a two-row pass
+constexpr int kTreeDepth1 = 6;  // ring depth of a one-row pass
+constexpr int kTreeDepth2 = 3;  // ring depth of a two-row pass
 
 // A part's view of its tree: its run of the vocabulary and the exchange.
 struct TreePartView {
@@ -1194,7 +1219,6 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
         const size_t row_base = static_cast<size_t>(b) * M;
         auto prow = [&](int u) { return row_ptr(a.target, DT, row_base + u, V); };
         auto qrow = [&](int u) { return row_ptr(a.draft, DT, row_base + u, V); };
-        auto xval = [&](const void* row, int t) { return scale_logit(load_logit(row, DT, t), inv_t); };
         int u = 0, L = 0, extra = -1;
         bool draw_here = false;  // this part draws the extra token
         int owner = 0;           // the part that draws it
@@ -1206,12 +1230,8 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
                     bad = true;
                     break;
                 }
-                int next = -1;
-                for (int s = 1; s < n; ++s)
-                    if (sh.parent[s] == u && sh.token[s] == am) {
-                        next = s;
-                        break;
-                    }
+                node_set(sh, n, [&](int i) { return i > u && sh.parent[i] == u && sh.token[i] == am; });
+                const int next = node_set_next(sh, u + 1, -1);
                 if (next < 0) {
                     extra = am;
                     break;
@@ -1224,12 +1244,24 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
         } else if (!bad) {
             float mp = 0.0f, mq = 0.0f;
             double sp = 0.0, sq = 0.0;
-            // Normalisers of a node's rows: the draft row's only when the
-            // node has children to test, then in the same pass.
+            int s = n;  // the child of u to test next (n: none left)
+            float zs_p = 0.0f, zs_q = 0.0f;  // raw logits of its token in u's rows
+            // Child c's token logits in x's rows, loaded a pass ahead of its test.
+            auto fetch = [&](int x, int c) {
+                if (c < n) {
+                    const int t = sh.token[c];
+                    zs_p = load_logit(prow(x), DT, t);
+                    zs_q = load_logit(qrow(x), DT, t);
+                }
+            };
+            // Arrival at x: its children (sh.nodes), the first one's logits,
+            // and the normalisers of x's rows: the draft row's only when x has
+            // children to test, then in the same pass.
             auto arrive = [&](int x) {
-                bool kids = false;
-                for (int i = x + 1; i < n; ++i)
-                    kids = kids || sh.parent[i] == x;
+                node_set(sh, n, [&](int i) { return i > x && sh.parent[i] == x; });
+                s = node_set_next(sh, x + 1, n);
+                const bool kids = s < n;
+                fetch(x, s);
                 if (!tree_norms<DT, VEC, NT>(v, prow(x), qrow(x), kids, inv_t, sh, &mp, &sp, &mq, &sq))
                     return false;
                 return sp > 0.0 && (!kids || sq > 0.0);
@@ -1237,18 +1269,12 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
             bad = !arrive(u);
             double c = 0.0, Z = 1.0;
             bool ts_current = false;  // lds_ts holds the tile sums of the current (c, Z)
-            int s = 1;
-            while (!bad) {
-                while (s < n && sh.parent[s] != u)
-                    ++s;
-                if (s >= n)
-                    break;  // no child left to try at u
+            while (!bad && s < n) {
                 // The accept test of child s, in fp64 (every thread computes it).
-                const int t = sh.token[s];
                 const double lse_p = (static_cast<double>(mp) + log2(sp)) / static_cast<double>(kLog2e);
                 const double lse_q = (static_cast<double>(mq) + log2(sq)) / static_cast<double>(kLog2e);
-                const double lp = static_cast<double>(xval(prow(u), t)) - lse_p;
-                const double lq = static_cast<double>(xval(qrow(u), t)) - lse_q;
+                const double lp = static_cast<double>(scale_logit(zs_p, inv_t)) - lse_p;
+                const double lq = static_cast<double>(scale_logit(zs_q, inv_t)) - lse_q;
                 double lpi = lp;
                 if (c > 0.0) {
                     const double d = exp(lp) - c * exp(lq);
@@ -1262,14 +1288,16 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
                         sh.path[L] = s;
                     ++L;
                     u = s;
-                    s = 1;
                     c = 0.0;
                     Z = 1.0;
                     ts_current = false;
                     bad = !arrive(u);
                     continue;
                 }
-                // Rejected: the residual against q_u, in closed form.
+                // Rejected: the residual against q_u, in closed form; the next
+                // child's logits load behind its pass.
+                const int s_next = node_set_next(sh, s + 1, n);
+                fetch(u, s_next);
                 const double c2 = c + Z;
                 SeqRows rows;
                 rows.prow = prow(u);
@@ -1296,7 +1324,7 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
                 } else {
                     ts_current = false;  // an empty residual (rounding): pi stays
                 }
-                ++s;
+                s = s_next;
             }
             if (!bad) {
                 SeqRows rows;
