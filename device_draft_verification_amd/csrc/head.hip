@@ -5,21 +5,19 @@
 // Both products run on the matrix cores (v_mfma_f32_16x16x32_bf16: bf16
 // operands, binary32 accumulation).
 //
-//   head_down: u = W_down h, split over K into fp32 partials (the activation
-//     is small, N x r, so the split gives the GPU enough workgroups), with the
-//     tile routine below: C[m][n] = sum_k A[m][k] B[n][k], A and B row-major
-//     with K contiguous, 64 x 64 per wavefront, K in chunks of 64 staged
-//     through LDS with double buffering (rows padded to 144 bytes) and two
-//     chunks in flight in registers;
-//   head_down_reduce: u = bf16(sum of the partials, in split order);
+//   head_down: u = bf16(W_down h), one workgroup per 16 x 32 tile of u whose
+//     16 wavefronts split K and add their binary32 partial tiles in LDS;
 //   head_up_stream (rank 256 or 512): z^T = W_up u^T with the vocabulary on
 //     M, one workgroup per CU streaming its run of W_up through an LDS ring
 //     while the batch rows stay in registers; each block of logits is rounded
 //     to bf16, stored, and folded into per-row (m, s) pairs while still in
 //     registers: m = fl32(max x * log2e), s = sum 2^(fma(x, log2e, -m)) with
 //     x = fl32(z * fl32(1/T)), the row kernel's base-2 form;
-//   head_up (other ranks): the same product with the tile routine, 128
-//     vocabulary entries x 256 batch rows per workgroup;
+//   head_up (other ranks): the same product with the tile routine below
+//     (C[m][n] = sum_k A[m][k] B[n][k], A and B row-major with K contiguous,
+//     64 x 64 per wavefront, K in chunks of 64 staged through LDS with double
+//     buffering, rows padded to 144 bytes, and two chunks in flight in
+//     registers), 128 vocabulary entries x 256 batch rows per workgroup;
 //   head_lse: merges a row's (m, s) pairs into its log-normaliser.
 #include <hip/hip_runtime.h>
 
@@ -39,14 +37,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;
 constexpr int kLdsK = kBK + 8;    // bf16 per LDS row of a K chunk (144 bytes)
-constexpr int kThreads = 256;
 constexpr float kHeadLog2e = 1.44269504088896340736f;
 
-// Tile shapes: the first product uses 128 x 128 tiles (rows x rank); the
-// second puts the vocabulary on M and all of a 256-row batch on N, so each
-// W_up slab is read once and every lane ends up holding four consecutive
-// logits of one row.
-constexpr int kDownBM = 128, kDownBN = 128;   // 2 x 2 wavefronts of 64 x 64
+// Tile shape of the second product with the tile routine: the vocabulary on
+// M and all of a 256-row batch on N, so each W_up slab is read once and every
+// lane ends up holding four consecutive logits of one row.
 constexpr int kUpBM = 128, kUpBN = 256;       // 2 x 4 wavefronts of 64 x 64
 constexpr int kUpThreads = 512;
 
@@ -208,55 +203,97 @@ __device__ inline void zero(f32x4 (&acc)[MT][NT]) {
             acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-// partial[z][n][j] = sum over split z's K range of h[n][k] w_down[j][k].
-__global__ __launch_bounds__(kThreads) void head_down_kernel(const uint16_t* __restrict__ h,
-                                                             const uint16_t* __restrict__ w_down,
-                                                             int N, int r, int d, int k_per_split,
-                                                             float* __restrict__ partial) {
-    __shared__ __align__(16) uint16_t lds[lds_elems<kDownBM, kDownBN>()];
-    const TileArgs t{h, w_down, N, r, d, static_cast<int>(blockIdx.x) * kDownBM,
-                     static_cast<int>(blockIdx.y) * kDownBN};
-    const int kb = static_cast<int>(blockIdx.z) * k_per_split;
-    const int ke = kb + k_per_split < d ? kb + k_per_split : d;
-    f32x4 acc[4][4];
-    zero(acc);
-    tile_mma<kDownBM, kDownBN, kThreads>(t, kb, ke, lds, acc);
-    float* out = partial + static_cast<size_t>(blockIdx.z) * N * r;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int wm = w >> 1, wn = w & 1;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = t.m0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + j;
-                const int col = t.n0 + wn * 64 + nt * 16 + (lane & 15);
-                if (row < N && col < r)
-                    out[static_cast<size_t>(row) * r + col] = acc[mt][nt][j];
-            }
-}
+// u[n][j] = bf16(sum_k h[n][k] w_down[j][k]): one workgroup of 16 wavefronts
+// per TM x TN tile of u (rows x rank, 16 MT x 16 NT; 16 x 32, which keeps 256
+// workgroups at N = 256, r = 512: the loads run at the CU's own rate, so
+// larger tiles on fewer CUs were slower). Wavefront w multiplies
+// its own contiguous run of the K steps (32 wide) with its fragments loaded
+// straight from memory, four steps at a time; the 16 binary32 partial tiles
+// are then added in wavefront order through LDS and rounded once, so no
+// partial leaves the CU. Rows past N read row 0 and are not stored. The rank
+// tile is the grid's fastest index: workgroups go to the XCDs in turn, so
+// each XCD works on a few rank tiles and keeps their rows of W_down (with h)
+// in its L2 instead of streaming all of W_down.
+constexpr int kDownWaves = 16;
+constexpr int kDownMT = 1, kDownNT = 2;
+constexpr int kDownTM = 16 * kDownMT, kDownTN = 16 * kDownNT;
+constexpr int kDownBatch = 4;
 
-// n is a multiple of 32 (r is), so every thread takes four consecutive values.
-__global__ __launch_bounds__(256) void head_down_reduce_kernel(const float* __restrict__ partial,
-                                                               int splits, long n,
-                                                               uint16_t* __restrict__ u) {
-    const long n4 = n / 4;
-    for (long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
-         i += static_cast<long>(gridDim.x) * blockDim.x) {
-        float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int z = 0; z < splits; ++z) {
-            const float4 v = reinterpret_cast<const float4*>(partial + static_cast<size_t>(z) * n)[i];
-            s.x += v.x;
-            s.y += v.y;
-            s.z += v.z;
-            s.w += v.w;
+__global__ __launch_bounds__(kDownWaves * 64) void head_down_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_down, int N, int r, int d,
+    uint16_t* __restrict__ u) {
+    __shared__ float red[kDownWaves][kDownTM * kDownTN];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int m0 = static_cast<int>(blockIdx.y) * kDownTM;
+    const int n0 = static_cast<int>(blockIdx.x) * kDownTN;
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+    const uint16_t* pa[kDownMT];
+    const uint16_t* pb[kDownNT];
+#pragma unroll
+    for (int mt = 0; mt < kDownMT; ++mt) {
+        const int row = m0 + mt * 16 + fr;
+        pa[mt] = h + static_cast<size_t>(row < N ? row : 0) * d + fk;
+    }
+#pragma unroll
+    for (int nt = 0; nt < kDownNT; ++nt)
+        pb[nt] = w_down + static_cast<size_t>(n0 + nt * 16 + fr) * d + fk;
+    const int steps = d / 32;
+    const int per = (steps + kDownWaves - 1) / kDownWaves;
+    const int s_begin = w * per < steps ? w * per : steps;
+    const int s_end = s_begin + per < steps ? s_begin + per : steps;
+    f32x4 acc[kDownMT][kDownNT];
+#pragma unroll
+    for (int mt = 0; mt < kDownMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kDownNT; ++nt)
+            acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = s_begin; s0 < s_end; s0 += kDownBatch) {
+        u32x4 a[kDownBatch][kDownMT], b[kDownBatch][kDownNT];
+        // Steps past the run reload the run's first one; they are not multiplied.
+#pragma unroll
+        for (int i = 0; i < kDownBatch; ++i) {
+            const int k = (s0 + i < s_end ? s0 + i : s_begin) * 32;
+#pragma unroll
+            for (int mt = 0; mt < kDownMT; ++mt)
+                a[i][mt] = *reinterpret_cast<const u32x4*>(pa[mt] + k);
+#pragma unroll
+            for (int nt = 0; nt < kDownNT; ++nt)
+                b[i][nt] = *reinterpret_cast<const u32x4*>(pb[nt] + k);
         }
-        const uint32_t lo = bf16_rne(s.x) | (static_cast<uint32_t>(bf16_rne(s.y)) << 16);
-        const uint32_t hi = bf16_rne(s.z) | (static_cast<uint32_t>(bf16_rne(s.w)) << 16);
-        reinterpret_cast<uint2*>(u)[i] = make_uint2(lo, hi);
+#pragma unroll
+        for (int i = 0; i < kDownBatch; ++i) {
+            if (s0 + i < s_end) {
+#pragma unroll
+                for (int mt = 0; mt < kDownMT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < kDownNT; ++nt)
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a[i][mt]), __builtin_bit_cast(bf16x8, b[i][nt]),
+                            acc[mt][nt], 0, 0, 0);
+            }
+        }
+    }
+    // Lane l holds C[mt * 16 + 4 (l / 16) + j][nt * 16 + l % 16] of the tile.
+#pragma unroll
+    for (int mt = 0; mt < kDownMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kDownNT; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                red[w][(mt * 16 + 4 * (lane >> 4) + j) * kDownTN + nt * 16 + (lane & 15)] = acc[mt][nt][j];
+    __syncthreads();
+    for (int t = threadIdx.x; t < kDownTM * kDownTN; t += kDownWaves * 64) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kDownWaves; ++q)
+            sum += red[q][t];
+        const int row = m0 + t / kDownTN, col = n0 + t % kDownTN;
+        if (row < N)
+            u[static_cast<size_t>(row) * r + col] = bf16_rne(sum);
     }
 }
+
 
 // z^T = bf16(W_up u^T) for one 128-vocabulary x 256-row tile, and each row's
 // (m, s) over the tile's 128 vocabulary entries. Lane l of MFMA tile (mt, nt)
@@ -640,12 +677,11 @@ using namespace specv;
 
 struct spec_head_ctx {
     int N = 0, d = 0, r = 0, V = 0;
-    int splits = 1, k_per_split = 0, ntn = 0;
+    int ntn = 0;
     int stream_groups = 0;  // > 0: the streaming second product with this many workgroups
     hipStream_t stream = nullptr;
     void* ws = nullptr;
     uint16_t* u = nullptr;
-    float* partial = nullptr;
     HeadPart* part = nullptr;
     uint2* sink = nullptr;  // 64 words the streaming kernel's idle lanes store to
 };
@@ -658,7 +694,7 @@ int spec_lowrank_head_init(int rows, int hidden, int rank, int vocab, void* hip_
         return SPEC_EINVAL;
     *out_ctx = nullptr;
     if (rows < 1 || hidden < kBK || hidden % kBK || rank < kBK || rank % kBK || vocab < 8 ||
-        vocab % 8 || (rows + kUpBN - 1) / kUpBN > 65535)
+        vocab % 8 || (rows + kDownTM - 1) / kDownTM > 65535)
         return SPEC_EINVAL;
     spec_head_ctx* ctx = new (std::nothrow) spec_head_ctx();
     if (!ctx)
@@ -668,14 +704,6 @@ int spec_lowrank_head_init(int rows, int hidden, int rank, int vocab, void* hip_
     ctx->r = rank;
     ctx->V = vocab;
     ctx->stream = static_cast<hipStream_t>(hip_stream);
-    // Split the small first product over K until there are ~128 workgroups,
-    // keeping at least 4 chunks per split.
-    const int tiles = ((rows + kDownBM - 1) / kDownBM) * ((rank + kDownBN - 1) / kDownBN);
-    const int max_split = std::max(1, hidden / (4 * kBK));
-    ctx->splits = std::max(1, std::min(max_split, (128 + tiles - 1) / tiles));
-    const int chunks = hidden / kBK;
-    ctx->k_per_split = ((chunks + ctx->splits - 1) / ctx->splits) * kBK;
-    ctx->splits = (hidden + ctx->k_per_split - 1) / ctx->k_per_split;
     ctx->ntn = (vocab + kUpBM - 1) / kUpBM;
     if (rank == 256 || rank == 512) {
         // One workgroup per CU, each with at least one 16-row block of W_up.
@@ -693,8 +721,6 @@ int spec_lowrank_head_init(int rows, int hidden, int rank, int vocab, void* hip_
     size_t off = 0;
     const size_t o_u = off;
     off = align_up(off + nr * sizeof(uint16_t), 256);
-    const size_t o_p = off;
-    off = align_up(off + nr * ctx->splits * sizeof(float), 256);
     const size_t o_h = off;
     off = align_up(off + static_cast<size_t>(rows) * ctx->ntn * sizeof(HeadPart), 256);
     const size_t o_s = off;
@@ -705,7 +731,6 @@ int spec_lowrank_head_init(int rows, int hidden, int rank, int vocab, void* hip_
     }
     char* base = static_cast<char*>(ctx->ws);
     ctx->u = reinterpret_cast<uint16_t*>(base + o_u);
-    ctx->partial = reinterpret_cast<float*>(base + o_p);
     ctx->part = reinterpret_cast<HeadPart*>(base + o_h);
     ctx->sink = reinterpret_cast<uint2*>(base + o_s);
     *out_ctx = ctx;
@@ -729,17 +754,11 @@ int spec_lowrank_head(spec_head_ctx* ctx, const void* hidden, const void* w_down
         return SPEC_EINVAL;
     const int N = ctx->N, d = ctx->d, r = ctx->r, V = ctx->V;
     hipStream_t s = ctx->stream;
-    const unsigned mt = static_cast<unsigned>((N + kDownBM - 1) / kDownBM);
-    head_down_kernel<<<dim3(mt, static_cast<unsigned>((r + kDownBN - 1) / kDownBN),
-                            static_cast<unsigned>(ctx->splits)),
-                       dim3(kThreads), 0, s>>>(static_cast<const uint16_t*>(hidden),
-                                              static_cast<const uint16_t*>(w_down), N, r, d,
-                                              ctx->k_per_split, ctx->partial);
-    if (hipGetLastError() != hipSuccess)
-        return SPEC_EHIP;
-    const long nr = static_cast<long>(N) * r;
-    const unsigned rb = static_cast<unsigned>(std::min<long>((nr / 4 + 255) / 256, 4096));
-    head_down_reduce_kernel<<<dim3(rb), dim3(256), 0, s>>>(ctx->partial, ctx->splits, nr, ctx->u);
+    head_down_kernel<<<dim3(static_cast<unsigned>(r / kDownTN),
+                            static_cast<unsigned>((N + kDownTM - 1) / kDownTM)),
+                       dim3(kDownWaves * 64), 0, s>>>(static_cast<const uint16_t*>(hidden),
+                                                      static_cast<const uint16_t*>(w_down), N, r,
+                                                      d, ctx->u);
     if (hipGetLastError() != hipSuccess)
         return SPEC_EHIP;
     if (ctx->stream_groups > 0) {

@@ -25,10 +25,10 @@
  *   temperature [N] float32, out_lse [N] float64.
  * Requirements: d % 64 == 0, r % 64 == 0, V % 8 == 0, every bf16 array 16-byte
  * aligned (SPEC_EINVAL otherwise). All pointers are DEVICE pointers owned by
- * the caller; the library owns only its workspace (about N * r * 70 bytes plus
+ * the caller; the library owns only its workspace (about 2 N r bytes plus
  * N * V / 8 bytes).
  *
- * Asynchrony and errors: as in spec_verify.h. spec_lowrank_head enqueues four
+ * Asynchrony and errors: as in spec_verify.h. spec_lowrank_head enqueues three
  * kernels on the context's stream and returns.
  */
 #ifndef SPEC_HEAD_H

@@ -4,9 +4,10 @@ oracle.lowrank_head.
 Match rule. The GPU accumulates in binary32 on the matrix cores; the oracle
 computes the exact values (double) and rounds them to bf16. A binary32 sum
 of n terms differs from the exact sum by at most about n * 2^-24 times the
-sum of the terms' magnitudes; the longest rounding chain here is below 2^6
-(K / 32 accumulations per split, the split sum, and the 32 products inside
-one MFMA), so the tests allow c = 2^-16 (4x that) of the magnitude:
+sum of the terms' magnitudes; the longest rounding chain here is at most 2^6
+(K / 512 accumulations per wavefront, at most 16 for the K <= 8192 tested,
+the sum over 16 wavefronts, and the 32 products inside one MFMA), so the
+tests allow c = 2^-16 (4x that) of the magnitude:
 * activation u: each bf16 value equals the oracle's rounding, or, where the
   exact value lies within e_j = c * sum|W_down h| of a rounding boundary
   ("flip-possible"), it is within e_j + ulp/2 of the exact value (a binary32
