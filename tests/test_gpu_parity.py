@@ -85,7 +85,7 @@ def test_philox_words_bitwise(seed, offset):
 def test_small_config_full_parity(cfg):
     d = specgen.generate(specgen.config(cfg))
     gpu = run_gpu(to_device(d))
-    _check(f"config {cfg} ({specgen.config(cfg).name}) full batch", gpu, d)
+    _check(f"{specgen.config(cfg).name} full batch", gpu, d)
 
 
 # --------------------------------------- splits, ragged tails, odd shapes --
@@ -155,7 +155,7 @@ def test_large_config_full_parity(big):
     """Every sequence of the workload against the oracle (the launch
     configuration the benchmark times)."""
     cfg, rec, d, t, gpu = big
-    _check(f"config {cfg} ({rec.name}) full batch", gpu, d)
+    _check(f"{rec.name} full batch", gpu, d)
 
 
 def test_large_config_invariants(big):
@@ -201,7 +201,7 @@ def test_config5_scalar_mode():
     for b in diff:
         k = min(got[b], ref["accept_len"][b])
         assert np.min(np.abs(ref["acc_margin"][b, :k + 1])) < 1e-5, b
-    print(f"\n[config 5 scalar] mismatched-but-flagged={len(diff)} of {rec.batch}", flush=True)
+    print(f"\n[{rec.name} scalar mode] mismatched-but-flagged={len(diff)} of {rec.batch}", flush=True)
     # cross-mode: the full call decides the same lengths, up to flagged decisions
     full = run_gpu(to_device(d), with_lse=False)
     cross = np.nonzero(full["accept_len"] != got)[0]
