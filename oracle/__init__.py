@@ -103,6 +103,8 @@ def _load():
     lib.oracle_gather_logprobs.restype = None
     lib.oracle_outcomes.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, P, P, P, P, P, P]
     lib.oracle_outcomes.restype = None
+    lib.oracle_outcome_fanout.argtypes = [i32, i32, i32, P, P, i32, P, P]
+    lib.oracle_outcome_fanout.restype = None
     lib.oracle_lowrank_head.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.oracle_lowrank_head.restype = None
     lib.oracle_tree_prune.argtypes = [i32, i32, P, P, f64, i32, P, P, P, P]
@@ -337,6 +339,21 @@ def outcomes(logits_draft, logits_target, draft_tokens, temperature, F: int,
     if with_dist:
         out.update(dist=dist, scale=scale)
     return out
+
+
+def outcome_fanout(pk, probs, budget: int):
+    """Speculation-cache entries per length for a budget of `budget` entries
+    per sequence (Saguaro's fan-out over likely lengths): pk [B, L] and probs
+    [B, L, F] as float32 values. Returns (n [B, L] int32, hit [B] float64)."""
+    pk = np.ascontiguousarray(pk, dtype=np.float32)
+    probs = np.ascontiguousarray(probs, dtype=np.float32)
+    B, L = pk.shape
+    F = probs.shape[2]
+    assert probs.shape == (B, L, F)
+    n = np.zeros((B, L), np.int32)
+    hit = np.zeros((B,), np.float64)
+    _load().oracle_outcome_fanout(B, L, F, _ptr(pk), _ptr(probs), int(budget), _ptr(n), _ptr(hit))
+    return n, hit
 
 
 def lowrank_head(h, w_down, w_up, temperature, rows=None):

@@ -732,6 +732,62 @@ void oracle_outcomes(int batch, int gamma, int vocab, int dtype,
     free(taken);
 }
 
+/*
+ * Speculation-cache budget per length (Speculative Speculative Decoding
+ * summary, section 2, Saguaro challenge 1: the cache budget is spread over
+ * the lengths unevenly, more speculations for likely lengths and fewer for
+ * unlikely ones, so that a fixed budget hits the cache as often as it can;
+ * the page names a geometric allocation and gives no formula).
+ * Reading R25: a cache entry is a pair (length i, the j-th token of length
+ * i's list), worth v(i, j) = P(k = i) * P(extra = token_j | k = i), the
+ * probability that the verification outcome is that pair; v is taken as 0
+ * when the product is negative or NaN. The budget is handed out one entry at
+ * a time, each to the length whose next unused list entry is worth the most,
+ * the lower length on equal worth, until `budget` entries are placed or every
+ * list is used up. Each length thus gets a prefix of its list, n_i entries;
+ * when every list is non-increasing (as spec_verify_outcomes writes them) the
+ * placed entries are the `budget` most valuable pairs, which maximises the
+ * expected hit rate sum v over the cache. The page's geometric allocation is
+ * the case P(k = i) proportional to alpha^i of a fixed acceptance rate alpha.
+ * out_hit is the sum of the placed values in the order they were placed.
+ * Products and sums in double (a product of two floats is exact in double).
+ * Shapes: pk [B][L], probs [B][L][F], out_n [B][L], out_hit [B] (may be NULL).
+ */
+void oracle_outcome_fanout(int batch, int lengths, int F, const float *pk, const float *probs,
+                           int budget, int32_t *out_n, double *out_hit)
+{
+    const int L = lengths;
+    for (int b = 0; b < batch; ++b) {
+        const float *pk_b = pk + (size_t)b * L;
+        const float *pr_b = probs + (size_t)b * L * F;
+        int32_t *n = out_n + (size_t)b * L;
+        for (int i = 0; i < L; ++i)
+            n[i] = 0;
+        double hit = 0.0;
+        for (int step = 0; step < budget; ++step) {
+            int best = -1;
+            double best_v = 0.0;
+            for (int i = 0; i < L; ++i) {
+                if (n[i] >= F)
+                    continue;
+                double v = (double)pk_b[i] * (double)pr_b[(size_t)i * F + n[i]];
+                if (!(v > 0.0))
+                    v = 0.0;
+                if (best < 0 || v > best_v) {
+                    best = i;
+                    best_v = v;
+                }
+            }
+            if (best < 0)
+                break; /* every list is used up */
+            n[best] += 1;
+            hit += best_v;
+        }
+        if (out_hit)
+            out_hit[b] = hit;
+    }
+}
+
 /* ------------------------------------------------ low-rank draft head -- */
 
 /* binary32 -> bfloat16, round to nearest even (finite inputs). */

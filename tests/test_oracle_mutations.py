@@ -270,3 +270,14 @@ def test_neighbour_that_keeps_zero_weights_is_caught():
     with mutated_oracle("for (int v = j - 1; v >= 0; --v)\n                        if (r[v] > 0.0) {",
                         "for (int v = j - 1; v >= 0; --v)\n                        if (r[v] >= 0.0) {"):
         fails(pins.test_inverse_cdf_alt_worked_neighbours)
+
+
+def test_fanout_ties_to_the_higher_length_are_caught():
+    with mutated_oracle("if (best < 0 || v > best_v) {", "if (best < 0 || v >= best_v) {"):
+        fails(outcomes.fanout_diagonals)
+
+
+def test_fanout_without_the_length_probability_is_caught():
+    with mutated_oracle("double v = (double)pk_b[i] * (double)pr_b[(size_t)i * F + n[i]];",
+                        "double v = (double)pr_b[(size_t)i * F + n[i]];"):
+        fails(outcomes.fanout_is_optimal)

@@ -22,6 +22,8 @@ What pins it (none of these re-types its formulas):
   against the verification oracle's deterministic outcome, V < F padding,
   sentinel sequences.
 """
+import itertools
+
 import numpy as np
 import pytest
 from scipy.special import softmax
@@ -165,3 +167,102 @@ def test_padding_and_sentinels():
     for b in (1, 2):
         assert (out["tokens"][b] == -1).all() and not out["probs"][b].any()
         assert not out["pk"][b].any() and not out["mass"][b].any()
+
+
+# ------------------------------------------------------------------ fan-out ---
+# Speculation-cache budget per length (Speculative Speculative Decoding summary,
+# section 2, Saguaro challenge 1: more of a fixed budget for likely lengths, to
+# hit the cache as often as possible). The oracle places entries one at a time
+# on the most valuable next list entry; these pins check it against an
+# exhaustive search, a closed form and the edge cases.
+
+def _sorted_lists(rng, B, L, F):
+    pk = rng.dirichlet(np.ones(L), size=B).astype(np.float32)
+    probs = np.sort(rng.dirichlet(np.ones(F + 2), size=(B, L))[..., :F], axis=-1)[..., ::-1]
+    return pk, np.ascontiguousarray(probs, dtype=np.float32)
+
+
+def _value(pk, probs, n):
+    """Expected hit rate of a cache holding the first n[i] entries of each list."""
+    return sum(float(pk[i]) * float(probs[i][j]) for i in range(len(n)) for j in range(n[i]))
+
+
+def fanout_is_optimal():
+    rng = np.random.default_rng(11)
+    for L in (1, 2, 3):
+        for F in (1, 2, 3):
+            pk, probs = _sorted_lists(rng, 4, L, F)
+            for budget in range(0, L * F + 2):
+                n, hit = oracle.outcome_fanout(pk, probs, budget)
+                placed = min(budget, L * F)
+                for b in range(4):
+                    assert n[b].sum() == placed and (n[b] >= 0).all() and (n[b] <= F).all()
+                    best = max(_value(pk[b], probs[b], c)
+                               for c in itertools.product(range(F + 1), repeat=L)
+                               if sum(c) == placed)
+                    got = _value(pk[b], probs[b], n[b])
+                    assert abs(got - best) <= 1e-12 * max(1.0, best), (L, F, budget, n[b], got, best)
+                    assert abs(hit[b] - got) <= 1e-12 * max(1.0, got)
+
+
+def test_fanout_maximises_the_hit_rate():
+    """Against every allocation of the same number of entries (L, F <= 3)."""
+    fanout_is_optimal()
+
+
+def fanout_diagonals():
+    # v(i, j) = 2^-i * 2^-j: whole anti-diagonals i + j < d fill first, the
+    # lower length first within one, so d(d+1)/2 entries give n_i = d - i.
+    L, F = 7, 7
+    pk = np.array([[2.0 ** -i for i in range(L)]], np.float32)
+    probs = np.array([[[2.0 ** -j for j in range(F)]] * L], np.float32)
+    for d in range(L + 1):
+        n, hit = oracle.outcome_fanout(pk, probs, d * (d + 1) // 2)
+        assert n[0].tolist() == [max(0, d - i) for i in range(L)], (d, n[0])
+        assert hit[0] == sum((k + 1) * 2.0 ** -k for k in range(d))
+    # one entry more goes to length 0 (the next anti-diagonal, lowest length first)
+    n, _ = oracle.outcome_fanout(pk, probs, 3 * 4 // 2 + 1)
+    assert n[0].tolist() == [4, 2, 1, 0, 0, 0, 0]
+
+
+def test_fanout_closed_form_on_powers_of_two():
+    fanout_diagonals()
+
+
+def test_fanout_follows_a_geometric_law_of_lengths():
+    """With P(k = i) of a fixed acceptance rate alpha (geometric in i below G)
+    and the same list at every length, shorter lengths never get fewer
+    entries than longer ones below G."""
+    rng = np.random.default_rng(5)
+    G, F = 8, 16
+    for alpha in (0.3, 0.6, 0.85):
+        pk = np.array([[alpha ** i * (1 - alpha) for i in range(G)] + [alpha ** G]], np.float32)
+        row = np.sort(rng.dirichlet(np.ones(F + 4))[:F])[::-1]
+        probs = np.array([[row] * (G + 1)], np.float32)
+        for budget in (1, 5, 17, 40, 100, 144):
+            n, _ = oracle.outcome_fanout(pk, probs, budget)
+            assert all(n[0][i] >= n[0][i + 1] for i in range(G - 1)), (alpha, budget, n[0])
+
+
+def test_fanout_edges():
+    rng = np.random.default_rng(3)
+    pk, probs = _sorted_lists(rng, 3, 4, 5)
+    n, hit = oracle.outcome_fanout(pk, probs, 0)
+    assert (n == 0).all() and (hit == 0).all()
+    n, hit = oracle.outcome_fanout(pk, probs, 1000)
+    assert (n == 5).all()
+    for b in range(3):
+        assert abs(hit[b] - _value(pk[b], probs[b], [5] * 4)) <= 1e-12
+    # equal worth everywhere: lists fill in length order
+    n, hit = oracle.outcome_fanout(np.full((1, 3), 0.5, np.float32), np.full((1, 3, 4), 0.25, np.float32), 6)
+    assert n[0].tolist() == [4, 2, 0] and hit[0] == 6 * 0.125
+    # NaN and negative values are worth 0: placed after every positive entry
+    pk1 = np.array([[0.5, np.nan, -1.0]], np.float32)
+    probs1 = np.array([[[0.5, 0.25], [0.9, 0.9], [0.9, 0.9]]], np.float32)
+    n, hit = oracle.outcome_fanout(pk1, probs1, 3)
+    assert n[0].tolist() == [2, 1, 0] and hit[0] == 0.375
+    # a list that is not non-increasing still gets a prefix: the next entry
+    # of length 0 (0.1) loses to length 1's first (0.3) even though 0.9 follows
+    n, hit = oracle.outcome_fanout(np.array([[1.0, 1.0]], np.float32),
+                                   np.array([[[0.5, 0.1, 0.9], [0.3, 0.2, 0.0]]], np.float32), 3)
+    assert n[0].tolist() == [1, 2] and abs(hit[0] - 1.0) < 1e-7
