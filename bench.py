@@ -162,6 +162,12 @@ def cpu_next_rows(rec, d, host: dict, F: int) -> dict:
                                        d["draft_tokens"][:n_seq], d["temperature"][:n_seq], F))
     res["outcomes"] = {"us_per_sequence": round(dt / n_seq * 1e6, 1),
                        "sample": f"outcome law with F = {F} for {n_seq} sequences of the workload"}
+    if "fanout" in host:
+        fx = host["fanout"]
+        dt = timed(lambda: oracle.outcome_fanout(fx["pk"], fx["probs"], fx["budget"]), reps=5)
+        res["outcome_fanout"] = {"us_per_call": round(dt * 1e6, 1),
+                                 "sample": f"cache budget of {fx['budget']} entries for all "
+                                           f"{fx['pk'].shape[0]} sequences of the workload"}
     if "head" in host:
         hx = host["head"]
         rows = [r for r in (0, 1) if r < hx["h"].shape[0]]
@@ -484,6 +490,28 @@ def main() -> int:
     outcome_bytes = algorithmic_bytes(rec, d["temperature"], alen.cpu().numpy())["row_norm"]
     outcome_gbs = outcome_bytes / (outcome_ms * 1e-3) / 1e9
 
+    # Speculation-cache budget per length from that law: FANOUT_BUDGET entries
+    # per sequence (no figure on the pages; 64 is four per length at G = 8, in
+    # units of the lists' F = 16).
+    FANOUT_BUDGET = 64
+    f_n = torch.empty(B, G + 1, dtype=torch.int32, device=dev)
+    f_hit = torch.empty(B, dtype=torch.float64, device=dev)
+
+    def fanout():
+        sv.spec_outcome_fanout(o_pk, o_prob, FANOUT_BUDGET, f_n, f_hit, stream)
+
+    outcomes()
+    for _ in range(args.warmup):
+        fanout()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        fanout()
+    end.record(stream)
+    torch.cuda.synchronize()
+    fanout_ms = start.elapsed_time(end) / args.steps
+    fanout_hit = f_hit.cpu().numpy()
+
     # Low-rank draft head for one draft step of this batch: N = B rows,
     # hidden d = 4096, rank r = d / 8 = 512 (the pages' example ratio), this
     # workload's vocabulary; random bf16 weights made on the device.
@@ -510,6 +538,8 @@ def main() -> int:
     sv.spec_lowrank_head_destroy(hctx)
     host = {}
     if not args.no_cpu_baseline:
+        host["fanout"] = dict(pk=o_pk.cpu().numpy(), probs=o_prob.cpu().numpy(),
+                              budget=FANOUT_BUDGET)
         bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
         host["head"] = dict(h=bits(hh), w_down=bits(wd), w_up=bits(wu),
                             temperature=d["temperature"][:B].copy())
@@ -649,7 +679,9 @@ def main() -> int:
                          "frac_hbm": round(head_bytes / (head_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "outcomes": {"top_f": F_OUT, "us_per_call": round(outcome_ms * 1e3, 2),
                      "bytes": int(outcome_bytes), "gbs": round(outcome_gbs, 1),
-                     "frac": round(outcome_gbs / HBM_PEAK_GBS, 4)},
+                     "frac": round(outcome_gbs / HBM_PEAK_GBS, 4),
+                     "fanout": {"budget": FANOUT_BUDGET, "us_per_call": round(fanout_ms * 1e3, 2),
+                                "hit_rate_mean": round(float(fanout_hit.mean()), 4)}},
         "roofline": {"bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "row_norm_kernel"},

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     spec_verify_destroy, spec_verify_enable_timing, spec_verify_get_geometry,
     spec_verify_init, spec_verify_philox_words, spec_verify_read_timing,
     spec_verify_set_stream, spec_verify_strerror, spec_verify_outcomes, SPEC_OUTCOME_MAX_F,
+    spec_outcome_fanout, SPEC_FANOUT_MAX_LENGTHS,
     SPEC_BANDIT_MAX_ARMS, SPEC_BANDIT_THOMPSON, SPEC_BANDIT_UCB1, BanditContext,
     spec_bandit_destroy, spec_bandit_get_state, spec_bandit_init, spec_bandit_set_state,
     spec_bandit_set_stream, spec_bandit_step,

@@ -33,7 +33,7 @@ EXPORTED = (
     "spec_accept_logprobs",
     "spec_verify_copy_lse", "spec_verify_philox_words", "spec_verify_enable_timing",
     "spec_verify_read_timing", "spec_verify_get_geometry", "spec_verify_destroy",
-    "spec_verify_strerror", "spec_verify_outcomes",
+    "spec_verify_strerror", "spec_verify_outcomes", "spec_outcome_fanout",
     "spec_bandit_init", "spec_bandit_set_stream", "spec_bandit_step", "spec_bandit_get_state",
     "spec_bandit_set_state", "spec_bandit_destroy",
     "spec_lowrank_head_init", "spec_lowrank_head_set_stream", "spec_lowrank_head",
@@ -47,6 +47,7 @@ EXPORTED = (
 SPEC_TREE_MAX_NODES = 256
 
 SPEC_OUTCOME_MAX_F = 64
+SPEC_FANOUT_MAX_LENGTHS = 256
 SPEC_BANDIT_UCB1 = 0
 SPEC_BANDIT_THOMPSON = 1
 SPEC_BANDIT_MAX_ARMS = 64
@@ -86,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_verify_destroy": ([P], i32),
         "spec_verify_strerror": ([i32], ctypes.c_char_p),
         "spec_verify_outcomes": ([P, P, P, P, i32, P, P, P, P], i32),
+        "spec_outcome_fanout": ([i32, i32, i32, P, P, i32, P, P, P], i32),
         "spec_bandit_init": ([i32, i32, i32, i32, i32, P, ctypes.POINTER(P)], i32),
         "spec_bandit_set_stream": ([P, P], i32),
         "spec_bandit_step": ([P, P, P, u64, u64, P], i32),
@@ -292,6 +294,21 @@ def spec_verify_outcomes(ctx: Context, logits_draft, logits_target, draft_tokens
         ctx.handle, _ptr(logits_draft) if G > 0 else None, _ptr(logits_target),
         _ptr(draft_tokens) if G > 0 else None, top_f, _ptr(out_tokens), _ptr(out_probs),
         _ptr(out_pk), _ptr(out_mass)))
+
+
+def spec_outcome_fanout(pk, probs, budget: int, out_n, out_hit=None, stream=None) -> None:
+    """Speculation-cache entries per length for `budget` entries per sequence:
+    pk [B, L] float32 and probs [B, L, F] float32 (spec_verify_outcomes'
+    out_pk and out_probs); out_n [B, L] int32, out_hit [B] float64 or None."""
+    B, L = pk.shape
+    F = probs.shape[2]
+    _expect(pk, (B, L), torch.float32, "pk")
+    _expect(probs, (B, L, F), torch.float32, "probs")
+    _expect(out_n, (B, L), torch.int32, "out_n")
+    _expect(out_hit, (B,), torch.float64, "out_hit")
+    _check("spec_outcome_fanout", load_library().spec_outcome_fanout(
+        B, L, F, _ptr(pk), _ptr(probs), int(budget), _ptr(out_n), _ptr(out_hit),
+        _stream_handle(stream)))
 
 
 def spec_verify_copy_lse(ctx: Context, out_lse) -> None:

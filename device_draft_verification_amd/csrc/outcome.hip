@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include "outcome.hpp"
+#include "spec_verify.h"
 
 namespace specv {
 namespace {
@@ -706,4 +707,253 @@ hipError_t launch_outcomes(const Shape& s, bool vec, int nsplit, int top_f, cons
                                            gathered, work, out_tok, out_prob, out_pk, out_mass, stream);
 }
 
+namespace {
+
+// ----------------------------------------------------- cache budget ---
+//
+// One wavefront per sequence places the budget entry by entry. The lists sit
+// in LDS; lane l owns lengths l, l + 64, ... (up to four) and keeps, for each,
+// the key of its next unused entry and of the one after, so the lane that
+// wins a step has the following key in a register while its LDS read for the
+// one after that completes behind the next step. A key is the worth's binary64
+// bit pattern plus one (worths are >= 0, so keys order like worths; 0 marks a
+// used-up list). A step is a wavefront maximum of the lanes' best keys by DPP
+// moves, then ballots for the lowest length that holds it. Worths are exact
+// binary64 products, so the comparisons and the running hit sum (added in
+// placement order) are reproducible bit for bit.
+constexpr int kFanoutRegs = SPEC_FANOUT_MAX_LENGTHS / 64;
+
+__device__ inline uint64_t fanout_key(float pk, float prob) {
+    const double v = static_cast<double>(pk) * static_cast<double>(prob);
+    return static_cast<uint64_t>(__double_as_longlong(v > 0.0 ? v : 0.0)) + 1;
+}
+
+// max(k, the key DPP pattern CTRL brings from another lane); lanes outside
+// ROW_MASK, or whose source is outside the row, see 0 (below every key).
+template <int CTRL, int ROW_MASK>
+__device__ inline uint64_t max_dpp(uint64_t k) {
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(k & 0xffffffffu), CTRL, ROW_MASK,
+                                               0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(k >> 32), CTRL, ROW_MASK, 0xF,
+                                               false);
+    const uint64_t o = (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+    return o > k ? o : k;
+}
+
+// The largest key of the wavefront, in every lane: butterflies within each
+// row of 16 lanes, then the row broadcasts leave the maximum in lane 63.
+__device__ inline uint64_t wave_max_key(uint64_t k) {
+    k = max_dpp<0xB1, 0xF>(k);   // quad_perm [1,0,3,2]
+    k = max_dpp<0x4E, 0xF>(k);   // quad_perm [2,3,0,1]
+    k = max_dpp<0x141, 0xF>(k);  // row_half_mirror
+    k = max_dpp<0x140, 0xF>(k);  // row_mirror: every lane holds its row's maximum
+    k = max_dpp<0x142, 0xA>(k);  // row_bcast:15 into rows 1 and 3
+    k = max_dpp<0x143, 0xC>(k);  // row_bcast:31 into rows 2 and 3: lane 63 = maximum
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(k & 0xffffffffu), 63));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(k >> 32), 63));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Entry by entry (any lists).
+__device__ inline void fanout_sequential(int L, int F, const float* lists, const float* pk_l,
+                                         int budget, int32_t* out_n, double* out_hit) {
+    const int lane = threadIdx.x;
+    int n[kFanoutRegs];
+    float p[kFanoutRegs];
+    uint64_t cur[kFanoutRegs], nxt[kFanoutRegs];  // keys of the next entry and the one after
+#pragma unroll
+    for (int r = 0; r < kFanoutRegs; ++r) {
+        const int i = lane + 64 * r;
+        n[r] = 0;
+        p[r] = 0.0f;
+        cur[r] = 0;
+        nxt[r] = 0;
+        if (i < L) {
+            p[r] = pk_l[i];
+            cur[r] = fanout_key(p[r], lists[i * F]);
+            if (F > 1)
+                nxt[r] = fanout_key(p[r], lists[i * F + 1]);
+        }
+    }
+    double hit = 0.0;
+    for (int step = 0; step < budget; ++step) {
+        // The lane's best (its lowest length on equal keys), then the wavefront's.
+        uint64_t best = cur[0];
+        int best_r = 0;
+#pragma unroll
+        for (int r = 1; r < kFanoutRegs; ++r)
+            if (cur[r] > best) {
+                best = cur[r];
+                best_r = r;
+            }
+        const uint64_t m = wave_max_key(best);
+        if (m == 0)
+            break;  // every list is used up (wave-uniform)
+        // Lowest length with key m: lengths are lane + 64 r, so the lowest r
+        // first, then the lowest lane.
+        int win_lane = 0, win_r = 0;
+#pragma unroll
+        for (int r = kFanoutRegs - 1; r >= 0; --r) {
+            const uint64_t sel = __ballot(best == m && best_r == r);
+            if (sel) {
+                win_lane = __ffsll(static_cast<long long>(sel)) - 1;
+                win_r = r;
+            }
+        }
+        hit += __longlong_as_double(static_cast<long long>(m - 1));
+        if (lane == win_lane) {
+#pragma unroll
+            for (int r = 0; r < kFanoutRegs; ++r) {
+                if (r == win_r) {
+                    n[r] += 1;
+                    cur[r] = nxt[r];
+                    const int i = lane + 64 * r;
+                    nxt[r] = n[r] + 1 < F ? fanout_key(p[r], lists[i * F + n[r] + 1]) : 0;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kFanoutRegs; ++r) {
+        const int i = lane + 64 * r;
+        if (i < L)
+            out_n[i] = n[r];
+    }
+    if (lane == 0 && out_hit)
+        *out_hit = hit;
+}
+
+
+// All at once, for lists whose worths do not increase along the list and at
+// most kFanoutFastEntries entries: the placement above then takes the
+// `budget` largest keys, the lower length and then the earlier entry first
+// among equal keys, which a search over the key bits finds without stepping.
+// Entry e = i F + j sits in lane e % 64, register e / 64; T is the largest
+// key with at least `placed` keys >= T (one ballot count per key bit); every
+// key above T is placed, and the keys equal to T are placed in entry order
+// until the count is reached. Each length's placed entries are then a prefix
+// of its list, counted in LDS.
+constexpr int kFanoutFastRegs = 4;
+constexpr int kFanoutFastEntries = 64 * kFanoutFastRegs;
+
+__device__ inline void fanout_fast(int L, int F, const float* lists, const float* pk_l, int budget,
+                                   int* counts, int32_t* out_n, double* out_hit) {
+    const int lane = threadIdx.x;
+    const int total = L * F;
+    const int placed = budget < total ? budget : total;
+    uint64_t key[kFanoutFastRegs];
+#pragma unroll
+    for (int k = 0; k < kFanoutFastRegs; ++k) {
+        const int e = lane + 64 * k;
+        key[k] = e < total ? fanout_key(pk_l[e / F], lists[e]) : 0;
+    }
+    auto count_ge = [&](uint64_t t) {
+        int c = 0;
+#pragma unroll
+        for (int k = 0; k < kFanoutFastRegs; ++k)
+            c += __popcll(__ballot(key[k] >= t));
+        return c;
+    };
+    // The largest T with count_ge(T) >= placed (keys >= 1, so T >= 1 when placed >= 1).
+    uint64_t t = 0;
+    if (placed > 0) {
+        for (int bit = 62; bit >= 0; --bit) {
+            const uint64_t c = t | (1ULL << bit);
+            if (count_ge(c) >= placed)
+                t = c;
+        }
+    }
+    const int above = placed > 0 ? count_ge(t + 1) : 0;
+    const int ties = placed - above;  // keys equal to t to place, in entry order
+    for (int i = lane; i < L; i += 64)
+        counts[i] = 0;
+    __syncthreads();
+    double hit = 0.0;
+    int before = 0;  // equal keys in earlier registers
+#pragma unroll
+    for (int k = 0; k < kFanoutFastRegs; ++k) {
+        const int e = lane + 64 * k;
+        const bool eq = placed > 0 && key[k] == t;
+        const uint64_t m = __ballot(eq);
+        const int rank = before + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+        before += __popcll(m);
+        const bool take = e < total && placed > 0 && (key[k] > t || (eq && rank < ties));
+        if (take) {
+            atomicAdd(&counts[e / F], 1);
+            hit += __longlong_as_double(static_cast<long long>(key[k] - 1));
+        }
+    }
+    __syncthreads();
+    for (int i = lane; i < L; i += 64)
+        out_n[i] = counts[i];
+    // The hit rate: lanes' partial sums added in a fixed order.
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        hit += __shfl_xor(hit, off, 64);
+    if (lane == 0 && out_hit)
+        *out_hit = hit;
+}
+
+__global__ __launch_bounds__(64) void outcome_fanout_kernel(int L, int F, const float* __restrict__ pk,
+                                                             const float* __restrict__ probs,
+                                                             int budget, int32_t* __restrict__ out_n,
+                                                             double* __restrict__ out_hit) {
+    extern __shared__ float lds[];  // lists [L][F], then pk [L], then counts [L]
+    float* lists = lds;
+    float* pk_l = lds + L * F;
+    int* counts = reinterpret_cast<int*>(pk_l + L);
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const float* src = probs + static_cast<size_t>(b) * L * F;
+    for (int e = lane; e < L * F; e += 64)
+        lists[e] = src[e];
+    for (int i = lane; i < L; i += 64)
+        pk_l[i] = pk[static_cast<size_t>(b) * L + i];
+    __syncthreads();
+    // Do the worths fall (or stay) along every list?
+    bool rising = false;
+    for (int e = lane; e < L * F; e += 64)
+        if (e % F != 0 && fanout_key(pk_l[e / F], lists[e]) > fanout_key(pk_l[e / F], lists[e - 1]))
+            rising = true;
+    int32_t* n_b = out_n + static_cast<size_t>(b) * L;
+    double* hit_b = out_hit ? out_hit + b : nullptr;
+    if (__ballot(rising) == 0 && L * F <= kFanoutFastEntries)
+        fanout_fast(L, F, lists, pk_l, budget, counts, n_b, hit_b);
+    else
+        fanout_sequential(L, F, lists, pk_l, budget, n_b, hit_b);
+}
+
+bool fanout_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
 }  // namespace specv
+
+extern "C" int spec_outcome_fanout(int batch, int lengths, int top_f, const float* pk,
+                                   const float* probs, int budget, int32_t* out_n,
+                                   double* out_hit, void* hip_stream) {
+    using specv::fanout_aligned;
+    if (batch < 0 || lengths < 1 || lengths > SPEC_FANOUT_MAX_LENGTHS || top_f < 1 ||
+        top_f > SPEC_OUTCOME_MAX_F || budget < 0)
+        return SPEC_EINVAL;
+    if (batch == 0)
+        return SPEC_OK;
+    if (!pk || !probs || !out_n || !fanout_aligned(pk, 4) || !fanout_aligned(probs, 4) ||
+        !fanout_aligned(out_n, 4) || (out_hit && !fanout_aligned(out_hit, 8)))
+        return SPEC_EINVAL;
+    const size_t lds = (static_cast<size_t>(lengths) * top_f + 2 * lengths) * sizeof(float);
+    // The largest shape needs a little over the default 64 KiB of dynamic LDS.
+    static const bool lds_raised =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(specv::outcome_fanout_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>((SPEC_FANOUT_MAX_LENGTHS * SPEC_OUTCOME_MAX_F +
+                                              2 * SPEC_FANOUT_MAX_LENGTHS) * sizeof(float))) ==
+        hipSuccess;
+    if (lds > 65536 && !lds_raised)
+        return SPEC_EHIP;
+    specv::outcome_fanout_kernel<<<dim3(static_cast<unsigned>(batch)), dim3(64), lds,
+                                   static_cast<hipStream_t>(hip_stream)>>>(
+        lengths, top_f, pk, probs, budget, out_n, out_hit);
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+

@@ -234,6 +234,43 @@ int spec_verify_outcomes(spec_verify_ctx *ctx, const void *logits_draft,
                          int32_t *out_tokens, float *out_probs, float *out_pk,
                          float *out_mass);
 
+/* Largest number of lengths spec_outcome_fanout takes. */
+#define SPEC_FANOUT_MAX_LENGTHS 256
+
+/*
+ * Speculation-cache budget per length: how many of each length's listed
+ * tokens to speculate on with a budget of `budget` cache entries per sequence
+ * (Speculative Speculative Decoding summary, section 2, Saguaro challenge 1:
+ * the budget goes unevenly to the lengths, more to likely ones and fewer to
+ * unlikely ones, so that a fixed budget hits the cache as often as it can; the
+ * page names a geometric allocation without a formula). An entry is a pair
+ * (length i, the j-th token of length i's list), worth
+ *   v(i, j) = pk[b,i] * probs[b,i,j]   (product in binary64, exact; 0 when
+ *                                       negative or NaN),
+ * the probability that the verification outcome is that pair. Entries are
+ * placed one at a time, each on the length whose next unused list entry is
+ * worth the most (the lower length on equal worth), until `budget` are placed
+ * or every list is used up. Each length gets a prefix of its list:
+ *   out_n[b,i]  = entries placed at length i (the first out_n[b,i] tokens of
+ *                 its list), sum_i out_n[b,i] = min(budget, lengths * top_f);
+ *   out_hit[b]  = the sum of the placed worths (binary64, summed in an order
+ *                 of the kernel's choosing, the same on every call): the
+ *                 expected cache hit rate.
+ * For lists that are non-increasing, as spec_verify_outcomes writes them, the
+ * placed entries are the `budget` most valuable pairs, which maximises the
+ * hit rate; the page's geometric allocation is the case of pk geometric in i
+ * (a fixed acceptance rate alpha: pk[i] = alpha^i (1 - alpha), alpha^G at G).
+ * Device pointers, float32 / int32 / float64, launched on `hip_stream` (a
+ * hipStream_t, NULL = the null stream), asynchronous:
+ *   pk [B, lengths], probs [B, lengths, top_f] (spec_verify_outcomes' out_pk
+ *   and out_probs, lengths = G + 1), out_n [B, lengths], out_hit [B] (may be
+ *   NULL). 1 <= lengths <= SPEC_FANOUT_MAX_LENGTHS, 1 <= top_f <=
+ *   SPEC_OUTCOME_MAX_F, budget >= 0, batch >= 0; SPEC_EINVAL otherwise (or
+ *   for NULL or misaligned pointers), SPEC_EHIP if the launch fails.
+ */
+int spec_outcome_fanout(int batch, int lengths, int top_f, const float *pk, const float *probs,
+                        int budget, int32_t *out_n, double *out_hit, void *hip_stream);
+
 /*
  * Test hook: copy the row log-normalisers of the last spec_verify call into
  * out_lse [B, 2G+1] float64 (device): draft rows 0..G-1, then target rows

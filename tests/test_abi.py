@@ -127,6 +127,27 @@ def test_tree_host_argument_checks(lib):
     assert lib.spec_tree_verify_destroy(None) == E
 
 
+def test_fanout_host_argument_checks(lib):
+    E = sv.binding.SPEC_EINVAL
+    V = ctypes.c_void_p
+    ok = V(256)
+    # lengths, list length, budget, batch
+    assert lib.spec_outcome_fanout(2, 0, 16, ok, ok, 4, ok, None, None) == E
+    assert lib.spec_outcome_fanout(2, 257, 16, ok, ok, 4, ok, None, None) == E
+    assert lib.spec_outcome_fanout(2, 9, 0, ok, ok, 4, ok, None, None) == E
+    assert lib.spec_outcome_fanout(2, 9, 65, ok, ok, 4, ok, None, None) == E
+    assert lib.spec_outcome_fanout(2, 9, 16, ok, ok, -1, ok, None, None) == E
+    assert lib.spec_outcome_fanout(-1, 9, 16, ok, ok, 4, ok, None, None) == E
+    # missing or misaligned pointers
+    assert lib.spec_outcome_fanout(2, 9, 16, None, ok, 4, ok, None, None) == E
+    assert lib.spec_outcome_fanout(2, 9, 16, ok, None, 4, ok, None, None) == E
+    assert lib.spec_outcome_fanout(2, 9, 16, ok, ok, 4, None, None, None) == E
+    assert lib.spec_outcome_fanout(2, 9, 16, V(258), ok, 4, ok, None, None) == E
+    assert lib.spec_outcome_fanout(2, 9, 16, ok, ok, 4, ok, V(260), None) == E
+    # an empty batch launches nothing
+    assert lib.spec_outcome_fanout(0, 9, 16, None, None, 4, None, None, None) == 0
+
+
 def test_binding_refuses_missing_library(tmp_path, lib):
     saved = sv.binding._lib
     sv.binding._lib = None

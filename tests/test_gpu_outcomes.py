@@ -203,3 +203,96 @@ def test_outcomes_needs_a_verification_first():
         sv.spec_verify_outcomes(ctx, q, z, tk, 65, torch.zeros(2, 3, 65, dtype=torch.int32,
                                                                 device="cuda"),
                                 torch.zeros(2, 3, 65, device="cuda"), pk)
+
+
+# ------------------------------------------------------------------ fan-out ---
+# spec_outcome_fanout against oracle.outcome_fanout on the same float32
+# inputs: entry counts exact. The expected hit rate adds the same exact
+# binary64 products, the oracle in placement order and the kernel in an order
+# of its own; each of the two sums of n <= 16384 non-negative terms is within
+# n 2^-53 < 2e-12 of the exact sum, relative to it, so they may differ by
+# 4e-12 of it.
+
+def run_fanout(pk, probs, budget):
+    pk_d = torch.from_numpy(np.ascontiguousarray(pk, dtype=np.float32)).cuda()
+    pr_d = torch.from_numpy(np.ascontiguousarray(probs, dtype=np.float32)).cuda()
+    B, L = pk.shape
+    n = torch.full((B, L), -7, dtype=torch.int32, device="cuda")
+    hit = torch.full((B,), -7.0, dtype=torch.float64, device="cuda")
+    sv.spec_outcome_fanout(pk_d, pr_d, budget, n, hit)
+    torch.cuda.synchronize()
+    return n.cpu().numpy(), hit.cpu().numpy()
+
+
+def check_fanout(pk, probs, budget, label):
+    n, hit = run_fanout(pk, probs, budget)
+    n_ref, hit_ref = oracle.outcome_fanout(pk, probs, budget)
+    assert np.array_equal(n, n_ref), (label, budget, np.argwhere(n != n_ref)[:4])
+    assert (np.abs(hit - hit_ref) <= 4e-12 * hit_ref).all(), (label, budget, np.abs(hit - hit_ref).max())
+    return n
+
+
+def sorted_lists(rng, B, L, F, levels=None):
+    pk = rng.dirichlet(np.ones(L), size=B)
+    probs = np.sort(rng.dirichlet(np.ones(F + 3), size=(B, L))[..., :F], axis=-1)[..., ::-1]
+    if levels:  # coarse values, so that equal worths (ties) occur
+        pk = np.round(pk * levels) / levels
+        probs = np.round(probs * levels) / levels
+    return pk.astype(np.float32), np.ascontiguousarray(probs, dtype=np.float32)
+
+
+@pytest.mark.parametrize("B,L,F,levels", [
+    (64, 9, 16, None),      # the bench workload's shape of lists
+    (32, 9, 16, 8),         # many equal worths
+    (8, 1, 1, None),        # one length, one entry
+    (8, 64, 3, None),       # one length per lane
+    (8, 65, 5, 4),          # a second length on lane 0
+    (4, 131, 16, None),     # gamma = 130
+    (2, 256, 64, 16),       # the largest shape: four lengths per lane, 64 KiB of lists
+])
+def test_fanout_parity(B, L, F, levels):
+    rng = np.random.default_rng(B * 1000 + L * 10 + F)
+    pk, probs = sorted_lists(rng, B, L, F, levels)
+    print(f"\n[fanout B={B} L={L} F={F} levels={levels}]", flush=True)
+    for budget in sorted({0, 1, 2, F, L, 37, L * F // 3, L * F - 1, L * F, L * F + 5}):
+        if budget >= 0:
+            n = check_fanout(pk, probs, budget, (B, L, F))
+            assert (n.sum(axis=1) == min(budget, L * F)).all()
+
+
+def test_fanout_odd_values():
+    """Zero, negative and NaN worths, lists that are not sorted, and length
+    probabilities of a greedy sequence (0 or 1)."""
+    rng = np.random.default_rng(9)
+    B, L, F = 6, 7, 6
+    pk, probs = sorted_lists(rng, B, L, F)
+    pk[0] = 0.0
+    pk[1, 2] = np.nan
+    pk[2, 3] = -0.5
+    probs[3] = rng.random((L, F)).astype(np.float32)    # unsorted lists
+    probs[4, 1, 2] = np.nan
+    pk[5] = 0.0
+    pk[5, 4] = 1.0                                       # greedy: one certain length
+    probs[5] = 0.0
+    probs[5, :, 0] = 1.0
+    for budget in (1, 3, 10, L * F):
+        check_fanout(pk, probs, budget, "odd")
+    n, hit = run_fanout(pk, probs, 3)
+    assert n[5, 4] == 1 and hit[5] == 1.0
+
+
+def test_fanout_on_the_outcome_law():
+    """End to end: the law of a workload's verification feeds the budget."""
+    rec = specgen.config(2)
+    d = specgen.generate(rec)
+    F = 16
+    gpu = run_outcomes(to_device(d), F)
+    for budget in (4, 32, (rec.gamma + 1) * F):
+        n = check_fanout(gpu["pk"], gpu["probs"], budget, rec.name)
+        # the lists are non-increasing, so the placed entries are the most
+        # valuable ones: none left out is worth more than one placed
+        w = gpu["pk"].astype(np.float64)[:, :, None] * gpu["probs"].astype(np.float64)
+        placed = np.arange(F)[None, None, :] < n[:, :, None]
+        for b in range(rec.batch):
+            if placed[b].any() and (~placed[b]).any():
+                assert w[b][placed[b]].min() >= w[b][~placed[b]].max(), (b, budget)
