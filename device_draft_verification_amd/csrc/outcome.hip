@@ -20,12 +20,14 @@
 //     1 KiB of consecutive memory) and evaluates the scaled residual
 //     r' = max(0, p' * s_q / s_p - q') with p' = 2^(x log2e - m_p), the same
 //     arithmetic as the residual draw. Each wavefront keeps a candidate list
-//     in LDS behind a threshold key that only rises: an element is appended
-//     (ballot + mbcnt, no atomics) only if it beats the F-th best key known,
-//     so after the first tile almost nothing is written. The threshold is
-//     seeded from the first tile by a 64-lane bitonic sort of the lanes'
-//     maxima (the F-th largest lane maximum is a lower bound of the F-th
-//     largest element); the list is cut back to its best F when it fills.
+//     in LDS behind a threshold that only rises: a group whose largest value
+//     reaches it appends its values that do (one prefix count over the lanes
+//     places every lane's run, no atomics). The threshold is seeded from the
+//     first batch (the F-th largest of the lanes' maxima is a lower bound of
+//     the F-th largest element), raised to the F-th best key whenever the
+//     list is cut back to F (once it holds more than kTightenAt), and shared
+//     by the workgroup's four wavefronts: each one's threshold bounds the
+//     workgroup's F-th best from below, so all filter by the largest.
 //     The four wavefront lists are merged by wavefront 0 into F candidates
 //     and one fp64 partial sum per split.
 //   outcome_merge: one wavefront per (sequence, length) merges the splits,
@@ -40,18 +42,16 @@
 namespace specv {
 namespace {
 
-constexpr int kCap = 640;    // candidate slots per wavefront: kTightenAt + one tile
-constexpr int kTightenAt = 128;  // the list is cut back to F once it holds more
+constexpr int kTightenAt = 32;  // the list is cut back to F once it holds more
+// Candidate slots per wavefront: a list is at most max(kTightenAt, F) long
+// before a tile (a cut keeps F), and one tile adds at most 64 * 8 values.
+constexpr int kCap = (kTightenAt > kOutcomeMaxF ? kTightenAt : kOutcomeMaxF) + 64 * 8;
 // the merge kernel's list: every split's F candidates
 constexpr int kMergeCap = kOutcomeMaxSplit * kOutcomeMaxF;
 constexpr int kIdxNone = 0x7fffffff;
 
 __device__ __forceinline__ bool key_gt(float v, int i, float tv, int ti) {
     return v > tv || (v == tv && i < ti);
-}
-
-__device__ __forceinline__ bool key_ge(float v, int i, float tv, int ti) {
-    return v > tv || (v == tv && i <= ti);
 }
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
@@ -95,18 +95,54 @@ struct WaveList {
     int count;
     float tv;
     int ti;
+    // The workgroup's thresholds, one key per wavefront (NULL: not shared).
+    // Every wavefront's threshold is at most the F-th best key it has seen,
+    // so the largest of them bounds the F-th best of the whole workgroup from
+    // below, and a wavefront may filter by it.
+    unsigned long long* shared;
+    int wid;
 };
 
-// Append the lanes whose `ok` is set, in lane order.
-__device__ __forceinline__ void append(WaveList& L, bool ok, float v, int idx) {
-    const unsigned long long m = __ballot(ok);
-    if (m) {
-        const int below = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(m >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(m), 0));
-        if (ok)
-            L.buf[L.count + below] = Cand{v, idx};
-        L.count += __popcll(m);
+// Inclusive prefix of an int over the wavefront's lanes (lane order) by DPP
+// moves: shifts by 1, 2, 4, 8 within each row of 16 lanes, then the row
+// broadcasts carry the row totals forward.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int add_dpp_i(int v) {
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan_i(int v) {
+    v = add_dpp_i<0x111, 0xF>(v);  // row_shr:1
+    v = add_dpp_i<0x112, 0xF>(v);  // row_shr:2
+    v = add_dpp_i<0x114, 0xF>(v);  // row_shr:4
+    v = add_dpp_i<0x118, 0xF>(v);  // row_shr:8
+    v = add_dpp_i<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = add_dpp_i<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// Append every value of the lane's group that reaches the threshold value
+// (a superset of the entries at or above the threshold key, which the cuts
+// sort out), lane after lane: one prefix count over the lanes places each
+// lane's run, so the whole group costs one scan instead of one ballot per
+// element.
+template <int W>
+__device__ __forceinline__ void append_group(WaveList& L, bool used, const float (&val)[W], int idx0) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < W; ++e)
+        c += (used && val[e] >= L.tv) ? 1 : 0;
+    const int incl = wave_inclusive_scan_i(c);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    int pos = L.count + incl - c;
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+        if (used && val[e] >= L.tv) {
+            L.buf[pos] = Cand{val[e], idx0 + e};
+            ++pos;
+        }
     }
+    L.count += total;
 }
 
 // Keys as 64-bit unsigned integers that order like (value, then lower index):
@@ -126,6 +162,29 @@ __device__ __forceinline__ void key_decode(uint64_t k, float* v, int* idx) {
     const uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
     *v = __uint_as_float(u);
     *idx = static_cast<int>(~static_cast<uint32_t>(k));
+}
+
+// Publish this wavefront's threshold to its workgroup.
+__device__ __forceinline__ void publish_threshold(const WaveList& L) {
+    if (L.shared && lane_id() == 0)
+        __hip_atomic_store(L.shared + L.wid, key_code(L.tv, L.ti), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Take the workgroup's largest threshold when it is above this wavefront's
+// (slots start at 0, below every key).
+__device__ __forceinline__ void adopt_threshold(WaveList& L) {
+    if (!L.shared)
+        return;
+    unsigned long long k = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const unsigned long long o =
+            __hip_atomic_load(L.shared + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        k = o > k ? o : k;
+    }
+    if (k > key_code(L.tv, L.ti))
+        key_decode(k, &L.tv, &L.ti);
 }
 
 // Cut the list to its F best candidates (unordered) and raise the threshold
@@ -430,17 +489,18 @@ __device__ __forceinline__ double stream_tiles(const RowCoefs& rc, int groups, i
                 L.ti = kIdxNone;  // the lowest key of that value
             }
             seeded = true;
+            publish_threshold(L);
         }
+        adopt_threshold(L);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (__ballot(used[u] && group_max(val[u]) >= L.tv)) {
                 const int g = (t + u * t_step) * 64 + lane;
-#pragma unroll
-                for (int e = 0; e < W; ++e)
-                    append(L, used[u] && key_ge(val[u][e], g * W + e, L.tv, L.ti), val[u][e],
-                           g * W + e);
-                if (L.count > kTightenAt)
+                append_group<W>(L, used[u], val[u], g * W);
+                if (L.count > kTightenAt) {
                     tighten<kCap / 64>(L, F);
+                    publish_threshold(L);
+                }
             }
         }
     };
@@ -514,6 +574,7 @@ __global__ __launch_bounds__(kBlock) void outcome_topf_kernel(
     __shared__ Cand lds[kWaves][kCap];
     __shared__ double lds_sum[kWaves];
     __shared__ int lds_n[kWaves];
+    __shared__ unsigned long long lds_thr[kWaves];
     const int pair = blockIdx.x / nsplit;
     const int c = blockIdx.x - pair * nsplit;
     const int G = gamma;
@@ -530,7 +591,10 @@ __global__ __launch_bounds__(kBlock) void outcome_topf_kernel(
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane = lane_id();
 
-    WaveList L{lds[wid], 0, -__builtin_huge_valf(), kIdxNone};
+    if (threadIdx.x < kWaves)
+        lds_thr[threadIdx.x] = 0;
+    __syncthreads();
+    WaveList L{lds[wid], 0, -__builtin_huge_valf(), kIdxNone, lds_thr, wid};
     double sum = stream_pair<DT, VEC, NT, 4>(rc, groups, t0 + wid, t1, kWaves, F, L);
     tighten<kCap / 64>(L, F);
     sum = wave_sum_f64(sum);
@@ -626,7 +690,7 @@ __global__ __launch_bounds__(64) void outcome_merge_kernel(
     double S = 0.0;
     for (int c = 0; c < nsplit; ++c)
         S += sums[static_cast<size_t>(pair) * nsplit + c];
-    WaveList L{buf, total, -__builtin_huge_valf(), kIdxNone};
+    WaveList L{buf, total, -__builtin_huge_valf(), kIdxNone, nullptr, 0};
     double mass = 0.0;
     if (st.mode == 1) {
         const size_t row0 = static_cast<size_t>(b) * (2 * G + 1);
