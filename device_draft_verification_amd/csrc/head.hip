@@ -204,12 +204,16 @@ __device__ inline void zero(f32x4 (&acc)[MT][NT]) {
 }
 
 // u[n][j] = bf16(sum_k h[n][k] w_down[j][k]): one workgroup of 16 wavefronts
-// per TM x TN tile of u (rows x rank, 16 MT x 16 NT; 16 x 32, which keeps 256
-// workgroups at N = 256, r = 512: the loads run at the CU's own rate, so
-// larger tiles on fewer CUs were slower). Wavefront w multiplies
-// its own contiguous run of the K steps (32 wide) with its fragments loaded
-// straight from memory, four steps at a time; the 16 binary32 partial tiles
-// are then added in wavefront order through LDS and rounded once, so no
+// per TM x TN tile of u (rows x rank, 16 x 32, which keeps 256 workgroups at
+// N = 256, r = 512). Wavefront w multiplies its own contiguous run of the K
+// steps (32 wide), two steps per pass. A pass's 48 row segments (16 rows of
+// h, 32 of W_down, 128 bytes each) are loaded row by row, eight rows per load
+// instruction, two passes ahead into registers, then written to the
+// wavefront's own LDS region (rows padded to 144 bytes, so a fragment read of
+// 16 rows hits 16 different bank quads) and read back as MFMA fragments. A
+// fragment loaded straight from memory touches 16 rows 8 KB apart per
+// instruction, which ran at about half the rate. The 16 binary32 partial
+// tiles are then added in wavefront order through LDS and rounded once, so no
 // partial leaves the CU. Rows past N read row 0 and are not stored. The rank
 // tile is the grid's fastest index: workgroups go to the XCDs in turn, so
 // each XCD works on a few rank tiles and keeps their rows of W_down (with h)
@@ -217,80 +221,108 @@ __device__ inline void zero(f32x4 (&acc)[MT][NT]) {
 constexpr int kDownWaves = 16;
 constexpr int kDownMT = 1, kDownNT = 2;
 constexpr int kDownTM = 16 * kDownMT, kDownTN = 16 * kDownNT;
-constexpr int kDownBatch = 4;
+constexpr int kDownPass = 2;                           // K steps per pass
+constexpr int kDownRows = kDownTM + kDownTN;           // row segments staged per pass
+constexpr int kDownRowBytes = kDownPass * 32 * 2 + 16; // a segment and its padding
+constexpr int kDownRowLanes = kDownPass * 32 * 2 / 16;  // lanes per row segment (16 bytes each)
+constexpr int kDownRowsPerLoad = 64 / kDownRowLanes;    // segments per load instruction
+constexpr int kDownLoads = kDownRows / kDownRowsPerLoad; // 16-byte loads per lane per pass
+static_assert(kDownRows % kDownRowsPerLoad == 0 && kDownTM % kDownRowsPerLoad == 0, "whole loads");
 
 __global__ __launch_bounds__(kDownWaves * 64) void head_down_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_down, int N, int r, int d,
     uint16_t* __restrict__ u) {
+    __shared__ __align__(16) unsigned char stage[kDownWaves][kDownRows * kDownRowBytes];
     __shared__ float red[kDownWaves][kDownTM * kDownTN];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int m0 = static_cast<int>(blockIdx.y) * kDownTM;
     const int n0 = static_cast<int>(blockIdx.x) * kDownTN;
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
-    const uint16_t* pa[kDownMT];
-    const uint16_t* pb[kDownNT];
-#pragma unroll
-    for (int mt = 0; mt < kDownMT; ++mt) {
-        const int row = m0 + mt * 16 + fr;
-        pa[mt] = h + static_cast<size_t>(row < N ? row : 0) * d + fk;
-    }
-#pragma unroll
-    for (int nt = 0; nt < kDownNT; ++nt)
-        pb[nt] = w_down + static_cast<size_t>(n0 + nt * 16 + fr) * d + fk;
     const int steps = d / 32;
     const int per = (steps + kDownWaves - 1) / kDownWaves;
     const int s_begin = w * per < steps ? w * per : steps;
     const int s_end = s_begin + per < steps ? s_begin + per : steps;
-    f32x4 acc[kDownMT][kDownNT];
+    const int passes = (s_end - s_begin + kDownPass - 1) / kDownPass;
+    // For load q, lane l loads 16 bytes of segment q * kDownRowsPerLoad + l /
+    // kDownRowLanes, columns 8 (l % kDownRowLanes) on.
+    const int sub = lane / kDownRowLanes, col = (lane % kDownRowLanes) * 8;
+    unsigned char* region = stage[w];
+    auto load_pass = [&](u32x4 (&R)[kDownLoads], int pass) {
+        const int sa = s_begin + pass * kDownPass;
+        const int sb = sa + kDownPass < s_end ? sa + kDownPass : s_end;
+        const int kk = 32 * sa + col;
+        const int k = kk < 32 * sb ? kk : 32 * s_begin + col;  // past the run: unused
 #pragma unroll
-    for (int mt = 0; mt < kDownMT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < kDownNT; ++nt)
-            acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s0 = s_begin; s0 < s_end; s0 += kDownBatch) {
-        u32x4 a[kDownBatch][kDownMT], b[kDownBatch][kDownNT];
-        // Steps past the run reload the run's first one; they are not multiplied.
-#pragma unroll
-        for (int i = 0; i < kDownBatch; ++i) {
-            const int k = (s0 + i < s_end ? s0 + i : s_begin) * 32;
-#pragma unroll
-            for (int mt = 0; mt < kDownMT; ++mt)
-                a[i][mt] = *reinterpret_cast<const u32x4*>(pa[mt] + k);
-#pragma unroll
-            for (int nt = 0; nt < kDownNT; ++nt)
-                b[i][nt] = *reinterpret_cast<const u32x4*>(pb[nt] + k);
+        for (int q = 0; q < kDownLoads; ++q) {
+            const int row = kDownRowsPerLoad * q + sub;
+            const uint16_t* src;
+            if (q < kDownTM / kDownRowsPerLoad) {
+                const int hr = m0 + row;
+                src = h + static_cast<size_t>(hr < N ? hr : 0) * d;
+            } else {
+                src = w_down + static_cast<size_t>(n0 + row - kDownTM) * d;
+            }
+            R[q] = *reinterpret_cast<const u32x4*>(src + k);
         }
+    };
+    f32x4 acc[kDownNT];
 #pragma unroll
-        for (int i = 0; i < kDownBatch; ++i) {
-            if (s0 + i < s_end) {
+    for (int nt = 0; nt < kDownNT; ++nt)
+        acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // Stage one pass's rows in the region and multiply its steps.
+    auto run_pass = [&](const u32x4 (&R)[kDownLoads], int pass) {
 #pragma unroll
-                for (int mt = 0; mt < kDownMT; ++mt)
+        for (int q = 0; q < kDownLoads; ++q)
+            *reinterpret_cast<u32x4*>(region + (kDownRowsPerLoad * q + sub) * kDownRowBytes +
+                                      (lane % kDownRowLanes) * 16) = R[q];
+        const int sa = s_begin + pass * kDownPass;
+        const int frag = (lane & 15) * kDownRowBytes + (lane >> 4) * 16;
 #pragma unroll
-                    for (int nt = 0; nt < kDownNT; ++nt)
-                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a[i][mt]), __builtin_bit_cast(bf16x8, b[i][nt]),
-                            acc[mt][nt], 0, 0, 0);
+        for (int j = 0; j < kDownPass; ++j) {
+            if (sa + j < s_end) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(region + frag + j * 64));
+#pragma unroll
+                for (int nt = 0; nt < kDownNT; ++nt) {
+                    const bf16x8 b = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4*>(
+                                    region + (kDownTM + 16 * nt) * kDownRowBytes + frag + j * 64));
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
+                }
             }
         }
+    };
+    // Two passes in flight: slot 0 holds the even passes, slot 1 the odd ones.
+    u32x4 R0[kDownLoads], R1[kDownLoads];
+    if (passes > 0)
+        load_pass(R0, 0);
+    if (passes > 1)
+        load_pass(R1, 1);
+    for (int pass = 0; pass < passes; pass += 2) {
+        run_pass(R0, pass);
+        if (pass + 2 < passes)
+            load_pass(R0, pass + 2);
+        if (pass + 1 < passes) {
+            run_pass(R1, pass + 1);
+            if (pass + 3 < passes)
+                load_pass(R1, pass + 3);
+        }
     }
-    // Lane l holds C[mt * 16 + 4 (l / 16) + j][nt * 16 + l % 16] of the tile.
+    // Lane l holds C[4 (l / 16) + j][nt * 16 + l % 16] of the tile.
 #pragma unroll
-    for (int mt = 0; mt < kDownMT; ++mt)
+    for (int nt = 0; nt < kDownNT; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < kDownNT; ++nt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                red[w][(mt * 16 + 4 * (lane >> 4) + j) * kDownTN + nt * 16 + (lane & 15)] = acc[mt][nt][j];
+        for (int j = 0; j < 4; ++j)
+            red[w][(4 * (lane >> 4) + j) * kDownTN + nt * 16 + (lane & 15)] = acc[nt][j];
     __syncthreads();
     for (int t = threadIdx.x; t < kDownTM * kDownTN; t += kDownWaves * 64) {
         float sum = 0.0f;
 #pragma unroll
         for (int q = 0; q < kDownWaves; ++q)
             sum += red[q][t];
-        const int row = m0 + t / kDownTN, col = n0 + t % kDownTN;
+        const int row = m0 + t / kDownTN, col_u = n0 + t % kDownTN;
         if (row < N)
-            u[static_cast<size_t>(row) * r + col] = bf16_rne(sum);
+            u[static_cast<size_t>(row) * r + col_u] = bf16_rne(sum);
     }
 }
 
