@@ -444,8 +444,11 @@ __global__ __launch_bounds__(kUpThreads) void head_up_kernel(const uint16_t* __r
 //   matrix instructions; 64 rows per wavefront would halve the LDS reads but
 //   leave one wavefront per SIMD, which measured slower);
 // * blocks of W_up stream through a ring of kRing LDS slots, loaded straight
-//   into LDS in MFMA fragment order (fragment ks of a block is 1 KiB, lane l's
-//   16 bytes at offset 16 l), kRing - 1 blocks ahead;
+//   into LDS kRing - 1 blocks ahead, one or two whole rows per load (a load
+//   of MFMA fragments would touch 16 rows per instruction, which measured
+//   slower); a row's 16-byte chunks are stored at positions XORed with the
+//   row number, so a fragment read (16 rows, one chunk each) hits 16
+//   different bank quads;
 // * each block gives every wavefront a 16 x 32 piece of z^T, rounded and
 //   stored as 8-byte runs, and folded into per-row (m, s) pairs online: when a
 //   block raises a row's maximum the pair is rescaled by a binary32 exp2
@@ -472,6 +475,9 @@ __global__ __launch_bounds__(kStreamWaves * 64) void head_up_stream_kernel(
     constexpr int NT = kStreamRows / 16;
     constexpr int K = KS * 32;
     constexpr int kLoadsPerBlock = KS / kStreamWaves;  // per wavefront
+    constexpr int kChunks = KS * 4;                    // 16-byte chunks of a W_up row
+    constexpr int kRowsPerLoad = 64 / kChunks;         // rows of a block one load covers
+    static_assert(kChunks % 16 == 0 && 64 % kChunks == 0, "whole rows per load, 16 bank quads per row");
     __shared__ __align__(16) uint16_t ring[kRing][KS * 512];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -486,14 +492,18 @@ __global__ __launch_bounds__(kStreamWaves * 64) void head_up_stream_kernel(
     // kLoadsPerBlock loads per step, which the waits below count on.
     auto issue = [&](int b) {
         const int bb = b < b1 ? b : b1 - 1;
-        const int v = bb * 16 + (lane & 15);
-        const uint16_t* row = w_up + static_cast<size_t>(v < V ? v : V - 1) * K + (lane >> 4) * 8;
         uint16_t* slot = ring[(b - b0) % kRing];
 #pragma unroll
         for (int i = 0; i < kLoadsPerBlock; ++i) {
+            // Load ks covers rows ks * kRowsPerLoad ...: each lane one 16-byte
+            // chunk, the row's chunk (position ^ row) at the lane's position.
             const int ks = wv + kStreamWaves * i;
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(row + ks * 32),
-                                             slot + ks * 512, 16, 0, 0);
+            const int row = ks * kRowsPerLoad + lane / kChunks;
+            const int v = bb * 16 + row;
+            const uint16_t* src = w_up + static_cast<size_t>(v < V ? v : V - 1) * K +
+                                  ((lane % kChunks) ^ row) * 8;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), slot + ks * 512, 16,
+                                             0, 0);
         }
     };
     float inv_t[NT], mref[NT];
@@ -574,10 +584,14 @@ __global__ __launch_bounds__(kStreamWaves * 64) void head_up_stream_kernel(
     constexpr int QK = KS / 4;  // fragments per quarter
     auto read_quarter = [&](int b, int q, bf16x8 (&a)[QK]) {
         const uint16_t* slot = ring[(b - b0) % kRing];
+        const int r = lane & 15;
 #pragma unroll
-        for (int i = 0; i < QK; ++i)
+        for (int i = 0; i < QK; ++i) {
+            // Row r's chunk c of fragment ks sits at position c ^ r of the row.
+            const int c = 4 * (q * QK + i) + (lane >> 4);
             a[i] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(slot + (q * QK + i) * 512 + lane * 8));
+                bf16x8, *reinterpret_cast<const u32x4*>(slot + (r * kChunks + (c ^ r)) * 8));
+        }
     };
     auto mma_q = [&](const bf16x8 (&a)[QK], f32x4 (&acc)[NT], int q) {
 #pragma unroll
