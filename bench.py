@@ -7,9 +7,12 @@ resident in HBM before the timed region. Three copies of the inputs are
 rotated so no step finds the previous step's rows in the 256 MB last-level
 cache. Before the W warm-up steps, untimed calls run for --settle-ms (300 ms
 by default) so that the timed steps see settled clocks; the timed region is
-exactly K steps. Prints one JSON line.
+exactly K steps. Prints one JSON line. The further sections (outcome law,
+low-rank head, trees) each run their operation untimed for
+--section-settle-ms (40 ms by default) and W times before their K timed calls.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms T] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms T]
+                    [--section-settle-ms T] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -307,6 +310,9 @@ def main() -> int:
                     help="untimed verification calls for about this long before the warm-up "
                          "steps, so that the timed steps run at the clocks of sustained work "
                          "rather than during the ramp from idle")
+    ap.add_argument("--section-settle-ms", type=float, default=40.0,
+                    help="untimed calls of each further section's operation (outcome law, "
+                         "head, trees) for about this long before its warm-up calls")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (counter calibration)")
     ap.add_argument("--derive-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -371,6 +377,21 @@ def main() -> int:
             settle_calls += 1
         torch.cuda.synchronize()
     settle_ms = (time.perf_counter() - t_settle) * 1e3
+
+    def warm(fn):
+        """Untimed calls of a further section's operation: --section-settle-ms
+        of them (indices from 2^40 up), then the W warm-up calls (indices 0 ..
+        W - 1), so that its timed calls see the clocks of its own sustained
+        work, as the verification steps do."""
+        t0, n = time.perf_counter(), 0
+        while (time.perf_counter() - t0) * 1e3 < args.section_settle_ms:
+            for _ in range(4):
+                fn((1 << 40) + n)
+                n += 1
+            torch.cuda.synchronize()
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -478,9 +499,7 @@ def main() -> int:
         sv.spec_verify_outcomes(ctx, zq0 if G else None, zp0, tokens if G else None, F_OUT,
                                 o_tok, o_prob, o_pk, o_mass)
 
-    for _ in range(args.warmup):
-        outcomes()
-    torch.cuda.synchronize()
+    warm(lambda i: outcomes())
     start.record(stream)
     for _ in range(args.steps):
         outcomes()
@@ -501,9 +520,7 @@ def main() -> int:
         sv.spec_outcome_fanout(o_pk, o_prob, FANOUT_BUDGET, f_n, f_hit, stream)
 
     outcomes()
-    for _ in range(args.warmup):
-        fanout()
-    torch.cuda.synchronize()
+    warm(lambda i: fanout())
     start.record(stream)
     for _ in range(args.steps):
         fanout()
@@ -524,9 +541,7 @@ def main() -> int:
     hz = torch.empty(B, V, dtype=torch.bfloat16, device=dev)
     hl = torch.empty(B, dtype=torch.float64, device=dev)
     hctx = sv.spec_lowrank_head_init(B, hd, hr, V, stream=stream)
-    for _ in range(args.warmup):
-        sv.spec_lowrank_head(hctx, hh, wd, wu, temp, hz, hl)
-    torch.cuda.synchronize()
+    warm(lambda i: sv.spec_lowrank_head(hctx, hh, wd, wu, temp, hz, hl))
     start.record(stream)
     for _ in range(args.steps):
         sv.spec_lowrank_head(hctx, hh, wd, wu, temp, hz, hl)
@@ -559,9 +574,7 @@ def main() -> int:
         sv.spec_tree_prune(t_par, t_lq, float(np.log(1e-3)), 32, p_cum, p_ni, p_np, p_cnt,
                            stream=stream)
 
-    for _ in range(args.warmup):
-        prune()
-    torch.cuda.synchronize()
+    warm(lambda i: prune())
     start.record(stream)
     for _ in range(args.steps):
         prune()
@@ -577,9 +590,7 @@ def main() -> int:
     v_path = torch.empty(B, tm, dtype=torch.int32, device=dev)
     v_extra = torch.empty(B, dtype=torch.int32, device=dev)
     tctx = sv.spec_tree_verify_init(B, tm, V, torch.bfloat16, stream=stream)
-    for _ in range(args.warmup):
-        sv.spec_tree_verify_greedy(tctx, v_par, v_tok, v_n, v_tgt, v_len, v_path, v_extra)
-    torch.cuda.synchronize()
+    warm(lambda i: sv.spec_tree_verify_greedy(tctx, v_par, v_tok, v_n, v_tgt, v_len, v_path, v_extra))
     start.record(stream)
     for _ in range(args.steps):
         sv.spec_tree_verify_greedy(tctx, v_par, v_tok, v_n, v_tgt, v_len, v_path, v_extra)
@@ -590,10 +601,8 @@ def main() -> int:
     # Sampled verification of the same trees (multi-step speculative
     # sampling) at the workload's temperatures, with random bf16 draft rows.
     v_q = (torch.randn(B, tm, V, device=dev, generator=gen) * 2.5).to(torch.bfloat16)
-    for i in range(args.warmup):
-        sv.spec_tree_verify_sample(tctx, v_par, v_tok, v_n, v_q, v_tgt, temp, 0, i, v_len, v_path,
-                                   v_extra)
-    torch.cuda.synchronize()
+    warm(lambda i: sv.spec_tree_verify_sample(tctx, v_par, v_tok, v_n, v_q, v_tgt, temp, 0, i,
+                                              v_len, v_path, v_extra))
     start.record(stream)
     for i in range(args.steps):
         sv.spec_tree_verify_sample(tctx, v_par, v_tok, v_n, v_q, v_tgt, temp, 0, args.warmup + i,
@@ -631,7 +640,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "settle": {"calls": settle_calls, "ms": round(settle_ms, 1)},
+        "settle": {"calls": settle_calls, "ms": round(settle_ms, 1),
+                   "section_ms": args.section_settle_ms},
         "ms_per_step": round(ms_per_step, 5),
         "call_us": {"median": round(float(np.median(call_us)), 2),
                     "p10": round(float(np.percentile(call_us, 10)), 2),
