@@ -533,6 +533,15 @@ __global__ __launch_bounds__(kStreamWaves * 64) void head_up_stream_kernel(
 #pragma unroll
     for (int i = 0; i < kRing - 1; ++i)
         issue(b0 + i);
+    // Left alone, the compiler moves the U loads below the first barrier,
+    // next to their first use, so the kernel start takes two memory round
+    // trips (ring, then U). Naming the registers here keeps all of them in
+    // flight together.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            asm volatile("" : "+v"(ub[nt][ks]));
 
     // Finishing block b: lane l holds logits v0..v0+3 of row n (V % 8 == 0:
     // v0 < V covers all four). Part 2 nt rounds and scales row tile nt and
