@@ -574,14 +574,18 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
     __shared__ int next_tile;
     const int b = blockIdx.x;
     const SeqState st = seq[b];
+    // The arguments and the whole state are asked for here, before the first
+    // branch: left to itself the compiler reads the rest of the state and
+    // the other arguments after the mode test, and the draft row's base
+    // after the barrier, each a further scalar round trip before the first
+    // tile's loads can leave.
+    asm volatile("" ::"s"(draft), "s"(target), "s"(gamma), "s"(vocab), "s"(ntiles), "s"(out_tok));
+    asm volatile("" ::"s"(st.k), "s"(st.u_res), "s"(st.inv_t), "s"(st.mp), "s"(st.mq), "s"(st.ratio));
     if (st.mode != 1)
         return;  // greedy or rejected sequence: nothing to draw
     const int groups = vocab / W;
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane = threadIdx.x & 63;
-    if (threadIdx.x == 0)
-        next_tile = 2 * kFusedWaves;  // tiles below are dealt out statically
-    __syncthreads();
     SeqRows s;
     seq_row_ptrs<DT>(s, draft, target, gamma, vocab, b, st.k);
     // Loads are unconditional: a tile past the row reads group 0 instead and
@@ -590,6 +594,14 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
         const int g = t * kTile + lane;
         io.load(s, t < ntiles && g < groups ? g : 0);
     };
+    IO buf_a, buf_b;
+    int ta = wid, tb = wid + kFusedWaves;
+    // The first tile leaves before the barrier, which guards only the
+    // counter.
+    load_tile(buf_a, ta);
+    if (threadIdx.x == 0)
+        next_tile = 2 * kFusedWaves;  // tiles below are dealt out statically
+    __syncthreads();
     auto reduce_tile = [&](const IO& io, int t) {
         if (t >= ntiles)
             return;  // wave-uniform
@@ -615,9 +627,6 @@ __global__ __launch_bounds__(BLOCK) void residual_fused_kernel(
         return v;
     };
     auto uniform = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-    IO buf_a, buf_b;
-    int ta = wid, tb = wid + kFusedWaves;
-    load_tile(buf_a, ta);
     seq_row_coefs(s, st);
     int tn = grab();
     // Counter values only grow, so once ta is past the row so is every later
