@@ -128,16 +128,26 @@ __device__ __forceinline__ int wave_inclusive_scan_i(int v) {
 // element.
 template <int W>
 __device__ __forceinline__ void append_group(WaveList& L, bool used, const float (&val)[W], int idx0) {
+    // An element tied with the threshold value beats the threshold key only
+    // below its index: a group whose indices all lie at or past it compares
+    // with the next float up instead. Without this, a value shared by many
+    // elements (an exact 0 of the residual, a common bf16 logit) lets every
+    // one of them in and the list is cut on every group.
+    float tq = L.tv;
+    if (L.ti <= idx0) {
+        const uint32_t u = __float_as_uint(L.tv);
+        tq = (u << 1) == 0 ? __uint_as_float(1u) : __uint_as_float((u >> 31) ? u - 1 : u + 1);
+    }
     int c = 0;
 #pragma unroll
     for (int e = 0; e < W; ++e)
-        c += (used && val[e] >= L.tv) ? 1 : 0;
+        c += (used && val[e] >= tq) ? 1 : 0;
     const int incl = wave_inclusive_scan_i(c);
     const int total = __builtin_amdgcn_readlane(incl, 63);
     int pos = L.count + incl - c;
 #pragma unroll
     for (int e = 0; e < W; ++e) {
-        if (used && val[e] >= L.tv) {
+        if (used && val[e] >= tq) {
             L.buf[pos] = Cand{val[e], idx0 + e};
             ++pos;
         }

@@ -188,6 +188,35 @@ def test_outcomes_degenerate_rows():
     assert (gpu["tokens"][4] == -1).all() and (gpu["tokens"][5] == -1).all()
 
 
+def test_outcomes_ties_at_the_threshold():
+    """Rows whose F-th value is shared by thousands of tokens: residuals that
+    are exactly 0 outside five tokens (the target equals the draft elsewhere
+    and has more mass there), and greedy rows of coarse logits. The lists are
+    those of a stable descending sort, lowest index first among equal values,
+    so here they equal the oracle's token for token."""
+    rng = np.random.default_rng(11)
+    B, G, V, F = 4, 2, 65536, 16
+    zq = rng.normal(0, 1, size=(B, G, V)).astype(np.float32)
+    zp = np.empty((B, G + 1, V), np.float32)
+    zp[:, :G] = zq
+    zp[:, G] = rng.normal(0, 1, size=(B, V))
+    for b in range(B):
+        for i in range(G):
+            zp[b, i, rng.choice(V, 5, replace=False)] += 3.0
+    zp[2] = np.round(zp[2] * 2) / 2                      # greedy, coarse tied logits
+    temp = np.array([1.0, 0.7, 0.0, 1.3], np.float32)
+    toks = rng.integers(0, V, size=(B, G)).astype(np.int32)
+    d = dict(logits_draft=zq, logits_target=zp, draft_tokens=toks, temperature=temp)
+    gpu = run_outcomes(to_device(d), F)
+    ref = oracle.outcomes(zq, zp, toks, temp, F, with_dist=True)
+    compare(gpu, ref, temp, np.arange(B), F)
+    for b in (0, 1, 3):
+        for i in range(G):
+            assert (ref["dist"][b, i] > 0).sum() == 5, (b, i)
+            assert np.array_equal(gpu["tokens"][b, i], ref["tokens"][b, i]), (b, i)
+    assert np.array_equal(gpu["tokens"][2], ref["tokens"][2])
+
+
 def test_outcomes_needs_a_verification_first():
     ctx = sv.spec_verify_init(2, 2, 64, torch.float32)
     z = torch.zeros(2, 3, 64, device="cuda")
