@@ -33,6 +33,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;
@@ -555,14 +557,17 @@ __global__ __launch_bounds__(kStreamWaves * 64) void head_up_stream_kernel(
         const int v0 = b * 16 + 4 * (lane >> 4);
         const bool on = act[nt] && v0 < V;
         if ((part & 1) == 0) {
-            uint16_t h[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                h[j] = bf16_rne(acc[nt][j]);
-                fx[nt][j] = bf16_to_f32(h[j]) * inv_t[nt];
-            }
-            fpack[nt] = make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16),
-                                   h[2] | (static_cast<uint32_t>(h[3]) << 16));
+            // Two logits per conversion instruction, rounded to nearest even
+            // (the low element in the low half).
+            const uint32_t w0 = __builtin_bit_cast(
+                uint32_t, __builtin_convertvector(f32x2{acc[nt][0], acc[nt][1]}, bf16x2));
+            const uint32_t w1 = __builtin_bit_cast(
+                uint32_t, __builtin_convertvector(f32x2{acc[nt][2], acc[nt][3]}, bf16x2));
+            fx[nt][0] = __uint_as_float(w0 << 16) * inv_t[nt];
+            fx[nt][1] = __uint_as_float(w0 & 0xFFFF0000u) * inv_t[nt];
+            fx[nt][2] = __uint_as_float(w1 << 16) * inv_t[nt];
+            fx[nt][3] = __uint_as_float(w1 & 0xFFFF0000u) * inv_t[nt];
+            fpack[nt] = make_uint2(w0, w1);
             const float bm = on ? fmaxf(fmaxf(fx[nt][0], fx[nt][1]), fmaxf(fx[nt][2], fx[nt][3]))
                                 : -__builtin_huge_valf();
             const float m_new = fmaxf(mref[nt], bm * kHeadLog2e);  // fl32(max x * log2e)
