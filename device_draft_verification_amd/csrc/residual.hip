@@ -795,29 +795,32 @@ __device__ inline int node_set_next(const TreeShared& sh, int s, int none) {
     return none;
 }
 
-// Block-wide reductions of the tree workgroup (every thread gets the result).
-__device__ inline float tree_block_max(float v, TreeShared& sh) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        v = fmaxf(v, __shfl_xor(v, off, 64));
-    __syncthreads();
-    if (lane == 0)
-        sh.red_f[w] = v;
-    __syncthreads();
-    float m = sh.red_f[0];
-#pragma unroll
-    for (int i = 1; i < kTreeWaves; ++i)
-        m = fmaxf(m, sh.red_f[i]);
-    return m;
+// Largest value over the wavefront's lanes, returned to every lane: the
+// inclusive scan's pattern (shifts by 1, 2, 4 and 8 within each row of 16
+// lanes, then the row broadcasts) leaves it in lane 63. A lane whose source
+// is out of range keeps its own value.
+template <int CTRL, int ROW_MASK>
+__device__ inline float max_dpp(float v) {
+    const int t = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK,
+                                              0xF, false);
+    return fmaxf(v, __int_as_float(t));
 }
 
-// Sum in a fixed order: lanes by a butterfly, then the wavefronts in order.
+__device__ inline float wave_max_f32(float v) {
+    v = max_dpp<0x111, 0xF>(v);  // row_shr:1
+    v = max_dpp<0x112, 0xF>(v);  // row_shr:2
+    v = max_dpp<0x114, 0xF>(v);  // row_shr:4
+    v = max_dpp<0x118, 0xF>(v);  // row_shr:8
+    v = max_dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = max_dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Block-wide sum of the tree workgroup in a fixed order (every thread gets
+// it): the lanes by the DPP scan, then the wavefronts in order.
 __device__ inline double tree_block_sum(double v, TreeShared& sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        v += __shfl_xor(v, off, 64);
+    v = lane63_f64(wave_inclusive_scan(v));
     __syncthreads();
     if (lane == 0)
         sh.red_d[w] = v;
@@ -934,12 +937,35 @@ struct OnlineNorm {
         s += static_cast<double>(g);
     }
 
-    // Merge over the workgroup (every thread gets the part's (m, s)).
+    // Merge over the workgroup (every thread gets the part's (m, s)): each
+    // wavefront folds its lanes by DPP (the maximum, then the lanes' sums
+    // scaled to it), and the wavefronts' pairs are merged in wavefront order
+    // through LDS, one exchange for both.
     __device__ inline void finish(TreeShared& sh, float* m_out, double* s_out) const {
-        const float M = tree_block_max(m, sh);
-        const double f = m == M ? 1.0 : static_cast<double>(fast_exp2(m - M));
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const float mw = wave_max_f32(m);
+        const double f = m == mw ? 1.0 : static_cast<double>(fast_exp2(m - mw));
+        const double sw = lane63_f64(wave_inclusive_scan(s > 0.0 ? s * f : 0.0));
+        __syncthreads();  // earlier readers of red_f and red_d are done
+        if (lane == 0) {
+            sh.red_f[w] = mw;
+            sh.red_d[w] = sw;
+        }
+        __syncthreads();
+        float M = sh.red_f[0];
+#pragma unroll
+        for (int i = 1; i < kTreeWaves; ++i)
+            M = fmaxf(M, sh.red_f[i]);
+        double S = 0.0;
+#pragma unroll
+        for (int i = 0; i < kTreeWaves; ++i) {
+            const double si = sh.red_d[i];
+            const float mi = sh.red_f[i];
+            if (si > 0.0)
+                S += mi == M ? si : si * static_cast<double>(fast_exp2(mi - M));
+        }
         *m_out = M;
-        *s_out = tree_block_sum(s > 0.0 ? s * f : 0.0, sh);
+        *s_out = S;
     }
 };
 
