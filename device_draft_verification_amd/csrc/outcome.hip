@@ -21,8 +21,8 @@
 //     r' = max(0, p' * s_q / s_p - q') with p' = 2^(x log2e - m_p), the same
 //     arithmetic as the residual draw. Each wavefront keeps a candidate list
 //     in LDS behind a threshold that only rises: a group whose largest value
-//     reaches it appends its values that do (one prefix count over the lanes
-//     places every lane's run, no atomics). The threshold is seeded from the
+//     reaches it appends its values that beat the threshold key (one prefix
+//     count over the lanes places every lane's run, no atomics). The threshold is seeded from the
 //     first batch (the F-th largest of the lanes' maxima is a lower bound of
 //     the F-th largest element), raised to the F-th best key whenever the
 //     list is cut back to F (once it holds more than kTightenAt), and shared
