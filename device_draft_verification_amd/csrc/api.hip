@@ -65,7 +65,12 @@ namespace {
 constexpr long kRowTargetBlocks = 12288;
 constexpr long kRowFillBlocks = 1024;  // four row workgroups per CU
 constexpr long kResidualTargetBlocks = 4096;
-constexpr long kOutcomeTargetBlocks = 2048;
+// Outcome splits: as many as keep the whole grid within about one wave of
+// resident workgroups (rounded down); larger batches keep one split. At
+// B = 64, V = 128 256 (384 pairs), 2 splits took 54 us per call, 3, 4 and 6
+// splits 62, 58 and 65 us: a partly filled second wave costs more than
+// longer splits.
+constexpr long kOutcomeWaveBlocks = 1024;
 constexpr int kResidualFusedMinBatch = 128;
 
 int env_int(const char* name, int fallback) {
@@ -110,8 +115,12 @@ bool compute_geometry(const Shape& s, Geometry* out) {
     g.nsplit_rows = choose_split(rows, vocab, dtype, kRowTargetBlocks, 4L * kBlock);
     g.nsplit_residual = choose_split(batch, vocab, dtype, kResidualTargetBlocks, 16L * 64);
     const long pairs = static_cast<long>(batch) * (gamma + 1);
-    g.nsplit_outcome = std::min(kOutcomeMaxSplit,
-                                choose_split(pairs, vocab, dtype, kOutcomeTargetBlocks, 16L * 64));
+    {
+        const long by_size = std::max(1L, vocab / group_width(dtype) / (16L * 64));
+        long n = pairs > 0 ? kOutcomeWaveBlocks / pairs : 1;
+        n = std::max(1L, std::min({n, by_size, static_cast<long>(kOutcomeMaxSplit)}));
+        g.nsplit_outcome = static_cast<int>(n);
+    }
     const int oo = env_int("SPEC_VERIFY_OUTCOME_SPLIT", 0);
     if (oo > 0)
         g.nsplit_outcome = std::min(oo, kOutcomeMaxSplit);
