@@ -249,12 +249,16 @@ __device__ inline double wave_inclusive_scan(double v) {
     return v;
 }
 
-__device__ inline double lane63_f64(double v) {
+// Lane `lane`'s value (a wave-uniform lane index) to every lane, without a
+// round trip through LDS.
+__device__ inline double readlane_f64(double v, int lane) {
     const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(v));
-    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffu), 63));
-    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), 63));
+    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffu), lane));
+    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane));
     return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
+
+__device__ inline double lane63_f64(double v) { return readlane_f64(v, 63); }
 
 __device__ inline int first_lane(bool flag) {
     const unsigned long long m = __ballot(flag);
@@ -361,8 +365,8 @@ __device__ inline int locate_tile(const float* ts, const TileRuns& tr, double ta
     }
     const int fl = first_lane(hit >= 0);
     if (fl < 64) {
-        *P_out = __shfl(before, fl, 64);
-        return __shfl(hit, fl, 64);
+        *P_out = readlane_f64(before, fl);
+        return __builtin_amdgcn_readlane(hit, fl);
     }
     *P_out = -1.0;
     return wave_max_int(tr.last_pos);
@@ -392,7 +396,7 @@ __device__ inline int locate_in_tile(const SeqRows& s, int tile, float gs, doubl
     int gl = take_last ? 64 : first_lane(gs > 0.0f && P + inc > tau);
     double Pg = 0.0;
     if (gl < 64) {
-        Pg = P + __shfl(inc - static_cast<double>(gs), gl, 64);
+        Pg = P + readlane_f64(inc - static_cast<double>(gs), gl);
     } else {
         gl = last_lane(gs > 0.0f);
         take_last = true;
