@@ -406,16 +406,16 @@ __device__ inline int locate_in_tile(const SeqRows& s, int tile, float gs, doubl
     const long g = static_cast<long>(tile) * kTile + gl;
     float r = 0.0f;
     if (lane < W) {
+        // Both logits are loaded before either is used (for a bonus row qrow
+        // is prow), and the result is selected, so the two loads share one
+        // memory round trip instead of the second waiting behind the first.
         const long v = g * W + lane;
-        const float xp = scale_logit(load_logit(s.prow, DT, v), s.inv_t);
-        const float pv = fast_exp2(__builtin_fmaf(xp, kLog2e, -s.mp));
-        if (s.p_only) {
-            r = pv;
-        } else {
-            const float xq = scale_logit(load_logit(s.qrow, DT, v), s.inv_t);
-            const float qv = fast_exp2(__builtin_fmaf(xq, kLog2e, -s.mq));
-            r = fmaxf(__builtin_fmaf(pv, s.ratio, -qv), 0.0f);
-        }
+        const float zp = load_logit(s.prow, DT, v);
+        const float zq = load_logit(s.qrow, DT, v);
+        const float pv = fast_exp2(__builtin_fmaf(scale_logit(zp, s.inv_t), kLog2e, -s.mp));
+        const float qv = fast_exp2(__builtin_fmaf(scale_logit(zq, s.inv_t), kLog2e, -s.mq));
+        const float rr = fmaxf(__builtin_fmaf(pv, s.ratio, -qv), 0.0f);
+        r = s.p_only ? pv : rr;
     }
     const double einc = wave_inclusive_scan(static_cast<double>(r));
     int e = take_last ? 64 : first_lane(r > 0.0f && Pg + einc > tau);
