@@ -127,6 +127,18 @@ __device__ inline float load_logit(const void* row, int dtype, long v) {
     return reinterpret_cast<const float*>(row)[v];
 }
 
+// The same logit as raw bits (bf16 in the low half, or fp32), and its value:
+// a load whose conversion is left for later is waited for only there.
+__device__ inline uint32_t load_logit_bits(const void* row, int dtype, long v) {
+    if (dtype == kBF16)
+        return static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(row)[v]);
+    return reinterpret_cast<const uint32_t*>(row)[v];
+}
+
+__device__ inline float logit_of_bits(uint32_t bits, int dtype) {
+    return __uint_as_float(dtype == kBF16 ? bits << 16 : bits);
+}
+
 __device__ inline const void* row_ptr(const void* base, int dtype, size_t row, int vocab) {
     const size_t esz = dtype == kBF16 ? 2 : 4;
     return static_cast<const char*>(base) + row * static_cast<size_t>(vocab) * esz;

@@ -408,10 +408,14 @@ __device__ inline int locate_in_tile(const SeqRows& s, int tile, float gs, doubl
     if (lane < W) {
         // Both logits are loaded before either is used (for a bonus row qrow
         // is prow), and the result is selected, so the two loads share one
-        // memory round trip instead of the second waiting behind the first.
+        // memory round trip instead of the second waiting behind the first
+        // (the empty asm keeps the scheduler from placing a use between them).
         const long v = g * W + lane;
-        const float zp = load_logit(s.prow, DT, v);
-        const float zq = load_logit(s.qrow, DT, v);
+        const uint32_t bp = load_logit_bits(s.prow, DT, v);
+        const uint32_t bq = load_logit_bits(s.qrow, DT, v);
+        asm volatile("" ::"v"(bp), "v"(bq));  // neither is used before both are issued
+        const float zp = logit_of_bits(bp, DT);
+        const float zq = logit_of_bits(bq, DT);
         const float pv = fast_exp2(__builtin_fmaf(scale_logit(zp, s.inv_t), kLog2e, -s.mp));
         const float qv = fast_exp2(__builtin_fmaf(scale_logit(zq, s.inv_t), kLog2e, -s.mq));
         const float rr = fmaxf(__builtin_fmaf(pv, s.ratio, -qv), 0.0f);
@@ -1284,13 +1288,15 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
             float mp = 0.0f, mq = 0.0f;
             double sp = 0.0, sq = 0.0;
             int s = n;  // the child of u to test next (n: none left)
-            float zs_p = 0.0f, zs_q = 0.0f;  // raw logits of its token in u's rows
-            // Child c's token logits in x's rows, loaded a pass ahead of its test.
+            // Child c's token logits in x's rows, loaded a pass ahead of its
+            // test as raw bits and converted only at the test: a conversion
+            // here would wait for the loads before the pass's own loads leave.
+            uint32_t zs_p_bits = 0, zs_q_bits = 0;
             auto fetch = [&](int x, int c) {
                 if (c < n) {
                     const int t = sh.token[c];
-                    zs_p = load_logit(prow(x), DT, t);
-                    zs_q = load_logit(qrow(x), DT, t);
+                    zs_p_bits = load_logit_bits(prow(x), DT, t);
+                    zs_q_bits = load_logit_bits(qrow(x), DT, t);
                 }
             };
             // Arrival at x: its children (sh.nodes), the first one's logits,
@@ -1312,8 +1318,8 @@ __global__ __launch_bounds__(kTreeBlock, 4) void tree_sample_kernel(TreeSampleAr
                 // The accept test of child s, in fp64 (every thread computes it).
                 const double lse_p = (static_cast<double>(mp) + log2(sp)) / static_cast<double>(kLog2e);
                 const double lse_q = (static_cast<double>(mq) + log2(sq)) / static_cast<double>(kLog2e);
-                const double lp = static_cast<double>(scale_logit(zs_p, inv_t)) - lse_p;
-                const double lq = static_cast<double>(scale_logit(zs_q, inv_t)) - lse_q;
+                const double lp = static_cast<double>(scale_logit(logit_of_bits(zs_p_bits, DT), inv_t)) - lse_p;
+                const double lq = static_cast<double>(scale_logit(logit_of_bits(zs_q_bits, DT), inv_t)) - lse_q;
                 double lpi = lp;
                 if (c > 0.0) {
                     const double d = exp(lp) - c * exp(lq);
